@@ -1,0 +1,60 @@
+"""The seeded input generator: determinism, slicing, distributions, mask recipe (CPU)."""
+
+import numpy as np
+import pytest
+
+import synth
+
+
+def test_splitmix_reference_values():
+    # SplitMix64 seeded with 0: the published first outputs of the generator.
+    got = synth.splitmix64(0, 0, 0, 3)
+    assert [int(x) for x in got] == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_counter_based_slices():
+    a = synth.normal_bf16(5, synth.STREAM_K, 5000, 1.0)
+    for s, n in [(0, 1), (1, 7), (1001, 2000), (4999, 1)]:
+        assert np.array_equal(synth.normal_bf16(5, synth.STREAM_K, n, 1.0, start=s), a[s:s + n])
+
+
+def test_window_rows_match_full_pass():
+    full = synth.make_problem(T=300, seed=9)
+    win = synth.make_problem(T=300, q_base=128, seed=9)
+    assert np.array_equal(win.qg, full.qg[128:])
+    assert np.array_equal(win.k, full.k) and np.array_equal(win.v, full.v)
+
+
+def test_distributions():
+    x = synth.bf16_bits_to_f32(synth.normal_bf16(1, 0, 1 << 20, 2.0)).astype(np.float64)
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 2.0) < 0.01
+    assert abs(((x / 2.0) ** 4).mean() - 3.0) < 0.05          # Gaussian kurtosis
+
+
+def test_rope_table_values():
+    cos, sin = synth.rope_table(3000)
+    for p, j in [(0, 0), (1, 0), (2054, 3), (2999, 31)]:
+        ang = p * 1e7 ** (-2 * j / 64)
+        assert cos[p, j] == np.float32(np.cos(ang)) and sin[p, j] == np.float32(np.sin(ang))
+
+
+def test_mask_recipe():
+    S, budget = 600, 64
+    m = synth.visibility_mask(S, budget, seed=4)
+    assert m.dtype == np.uint8 and m.shape == (S, S)
+    assert not np.triu(m, 1).any(), "a future key is visible"
+    assert m.diagonal().all()
+    assert np.array_equal(m.sum(1), np.minimum(np.arange(S) + 1, budget))
+    # Row subsets regenerate the same rows.
+    rows = np.array([0, 63, 64, 599])
+    assert np.array_equal(synth.visibility_mask(S, budget, seed=4, rows=rows), m[rows])
+    # Earlier keys are chosen roughly uniformly.
+    frac = m[400:, :300].mean()
+    assert abs(frac - (budget - 1) / np.arange(400, 600).mean()) < 0.02
+
+
+@pytest.mark.parametrize("name", ["c0_tiny_s64"])
+def test_config_digest_stable(name):
+    p = synth.config_problem(name)
+    assert p.qg.shape == (64, 24, 2, 256) and p.k.shape == (64, 2, 256)
+    assert p.digest() == synth.config_problem(name).digest()
