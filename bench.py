@@ -1,0 +1,207 @@
+"""Benchmark: gated causal attention prefill at S=8192, D=256, bf16 on one MI355X.
+
+One step = one full pass of the hot path over the workload: the key/value
+prologue and the attention kernel (query norm + RoPE, scores, online softmax,
+context, sigmoid gate), i.e. one ``attn_prefill_gated`` call.  Inputs are
+seeded synthetic tensors resident in HBM before the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints one JSON line.  ``value`` is algorithmic TFLOP/s of the whole step
+(4*D FLOPs per visible (row, key, query head) triple).  ``roofline`` is for the
+dominant kernel (attention), timed with HIP events around each launch on the
+launch stream.  ``cpu_baseline`` times the CPU oracle on a bounded row sample
+of the same workload.
+
+``--mode copy`` runs only a plain device copy of known size (used to scale the
+HBM byte counters of a ``rocprofv3 --pmc`` run).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0         # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attention.json")
+KERNEL_SOURCE = os.path.join(ROOT, "gated_gqa_causal_amd", "csrc", "kernels.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed PMC summary, or None
+    when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(p, rows_target: int, threads: int):
+    import numpy as np
+    import oracle
+    orc = oracle.get()
+    stride = max(1, p.rows // rows_target)
+    rows = np.arange(p.rows - 1, -1, -stride, dtype=np.int32)[::-1].copy()
+    kp = orc.prepare_keys(p)
+    t0 = time.perf_counter()
+    orc.attention(p, rows=rows, kp=kp, threads=threads)
+    dt = time.perf_counter() - t0
+    pos = p.q_base + rows.astype(np.int64)
+    flops = 4.0 * p.head_dim * p.n_q_heads * float((pos + 1).sum())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows.size} query rows (every {stride}th, ending at the last row) x "
+                      f"{p.n_q_heads} heads of {p.name}; keys prepared outside the timing; "
+                      f"{dt:.2f} s wall, {flops / 1e9:.1f} GFLOP"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2_dense_s8192_g4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--mode", choices=["attention", "copy"], default="attention")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the path shards by KV head or query rows with no exchange, and no multi-GPU run "
+              "is part of this build.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_gqa_causal_amd as ga
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.mode == "copy":
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 2, dtype=torch.int16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read_per_copy": nbytes,
+                          "bytes_written_per_copy": nbytes, "copies": args.steps}), flush=True)
+        return
+
+    t0 = time.perf_counter()
+    p = synth.config_problem(args.workload)
+    log(f"workload {args.workload}: T={p.T} q_base={p.q_base} Hq={p.n_q_heads} Hkv={p.n_kv_heads} "
+        f"mask={'yes' if p.mask is not None else 'no'}; generated in {time.perf_counter() - t0:.1f}s")
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    qg, k, v = dev_bf16(p.qg), dev_bf16(p.k), dev_bf16(p.v)
+    wq, wk = dev_bf16(p.q_norm_w), dev_bf16(p.k_norm_w)
+    cos = torch.from_numpy(p.cos).to(dev)
+    sin = torch.from_numpy(p.sin).to(dev)
+    mask = None if p.mask is None else torch.from_numpy(p.mask).to(dev)
+    out = torch.empty((p.rows, p.n_q_heads * 256), dtype=torch.bfloat16, device=dev)
+    ctx = ga.Context(p.n_q_heads, p.n_kv_heads, p.T, p.rms_eps)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        if mask is not None:
+            ctx.prefill_masked(qg, k, v, wq, wk, cos, sin, mask, out=out, stream=stream)
+        elif p.q_base:
+            ctx.prefill_prefix(qg, k, v, wq, wk, cos, sin, p.q_base, out=out, stream=stream)
+        else:
+            ctx.prefill_gated(qg, k, v, wq, wk, cos, sin, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    ctx.set_timing(True)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    attn_ms, attn_n = ctx.read_timing(ga.ATTN_KERNEL_ATTENTION)
+    pro_ms, pro_n = ctx.read_timing(ga.ATTN_KERNEL_KV_PROLOGUE)
+    mp_ms, mp_n = ctx.read_timing(ga.ATTN_KERNEL_MASK_PACK)
+    ctx.set_timing(False)
+    ms_per_step = total_ms / args.steps
+    flops = p.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    attn_avg_ms = attn_ms / max(attn_n, 1)
+    achieved = flops / (attn_avg_ms * 1e-3) / 1e12
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; attention {attn_avg_ms:.4f} ms, "
+        f"kv prologue {pro_ms / max(pro_n, 1):.4f} ms, mask pack {mp_ms / max(mp_n, 1):.4f} ms")
+
+    rec = {
+        "metric": "gated causal attention prefill TFLOP/s and ms at S=8192, D=256 bf16",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": p.name, "tokens": p.T, "q_base": p.q_base, "n_q_heads": p.n_q_heads,
+                   "n_kv_heads": p.n_kv_heads, "head_dim": p.head_dim, "rotary_dim": p.rotary_dim,
+                   "masked": p.mask is not None, "seed": p.seed,
+                   "algorithmic_gflop": round(flops / 1e9, 3)},
+        "kernels_ms": {"attention": round(attn_avg_ms, 5),
+                       "kv_prologue": round(pro_ms / max(pro_n, 1), 5),
+                       "mask_pack": round(mp_ms / max(mp_n, 1), 5) if mp_n else None},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(p.name)},
+    }
+    ctx.close()
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        log(f"cpu baseline: oracle on {args.cpu_rows} rows, {threads} threads")
+        rec["cpu_baseline"] = cpu_baseline(p, args.cpu_rows, threads)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,290 @@
+"""Python binding of libgatedattn.so (MI355X gated GQA causal attention prefill).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/gatedattn.h``.  PyTorch supplies
+device memory (``tensor.data_ptr()``) and the stream
+(``torch.cuda.current_stream().cuda_stream``).  There is no fallback: if the
+built library is missing, importing this package raises.
+
+The low-level functions carry the C names (``attn_ctx_create``,
+``attn_prefill_gated``, ...).  ``Context`` wraps a context handle and adds
+tensor-level calls that check dtype, shape, contiguity and device first.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBPATH = os.path.join(_HERE, "libgatedattn.so")
+
+ATTN_ABI_VERSION = 1
+ATTN_HEAD_DIM = 256
+ATTN_ROTARY_DIM = 64
+ATTN_MAX_GROUP = 16
+ATTN_MAX_TOKENS = 32768
+ATTN_QBASE_ALIGN = 128
+
+ATTN_OK = 0
+ATTN_ERR_NULL_ARG = -1
+ATTN_ERR_GEOMETRY = -2
+ATTN_ERR_RANGE = -3
+ATTN_ERR_ALIGN = -4
+ATTN_ERR_DEVICE = -5
+ATTN_ERR_NOMEM = -6
+ATTN_ERR_LAUNCH = -7
+
+ATTN_KERNEL_KV_PROLOGUE = 0
+ATTN_KERNEL_MASK_PACK = 1
+ATTN_KERNEL_ATTENTION = 2
+
+KIND_GATED, KIND_PREFIX, KIND_MASKED = 0, 1, 2
+
+
+class attn_geometry(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("rotary_dim", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("rms_eps", ctypes.c_float)]
+
+
+class attn_inputs(ctypes.Structure):
+    _fields_ = [("qg", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p),
+                ("cos_tab", ctypes.c_void_p), ("sin_tab", ctypes.c_void_p),
+                ("n_pos", ctypes.c_int32)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {attn_status_string(status)} ({status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIBPATH):
+        raise ImportError(f"{LIBPATH} is not built; run __graft_entry__.build() "
+                          "(the HIP library is required, there is no fallback)")
+    lib = ctypes.CDLL(LIBPATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    sig = {
+        "attn_abi_version": (ctypes.c_int, []),
+        "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "attn_validate": (ctypes.c_int, [ctypes.POINTER(attn_geometry), ctypes.POINTER(attn_inputs),
+                                         i32, i32, i32, vp, vp]),
+        "attn_ctx_create": (ctypes.c_int, [ctypes.POINTER(attn_geometry), ctypes.c_int,
+                                           ctypes.POINTER(vp)]),
+        "attn_ctx_destroy": (None, [vp]),
+        "attn_prefill_gated": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, vp]),
+        "attn_prefill_prefix": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp]),
+        "attn_prefill_masked": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, vp, vp]),
+        "attn_debug_prepare": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp, vp]),
+        "attn_ctx_set_timing": (ctypes.c_int, [vp, ctypes.c_int]),
+        "attn_ctx_read_timing": (ctypes.c_int, [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                                ctypes.POINTER(i32)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    if lib.attn_abi_version() != ATTN_ABI_VERSION:
+        raise ImportError(f"{LIBPATH}: ABI {lib.attn_abi_version()}, expected {ATTN_ABI_VERSION}")
+    return lib
+
+
+lib = _load()
+
+
+# ---- the C entry points, same names --------------------------------------
+
+def attn_abi_version() -> int:
+    return lib.attn_abi_version()
+
+
+def attn_status_string(status: int) -> str:
+    return lib.attn_status_string(status).decode()
+
+
+def attn_validate(geom: attn_geometry, inputs: Optional[attn_inputs], T: int, q_base: int, kind: int,
+                  mask: Optional[int], out: Optional[int]) -> int:
+    return lib.attn_validate(ctypes.byref(geom), None if inputs is None else ctypes.byref(inputs),
+                             T, q_base, kind, mask, out)
+
+
+def attn_ctx_create(geom: attn_geometry, device: int) -> int:
+    h = ctypes.c_void_p()
+    rc = lib.attn_ctx_create(ctypes.byref(geom), device, ctypes.byref(h))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_ctx_create")
+    return h.value
+
+
+def attn_ctx_destroy(ctx: Optional[int]) -> None:
+    lib.attn_ctx_destroy(ctx)
+
+
+def attn_prefill_gated(ctx, inputs: attn_inputs, S: int, out: int, stream: int) -> int:
+    return lib.attn_prefill_gated(ctx, ctypes.byref(inputs), S, out, stream)
+
+
+def attn_prefill_prefix(ctx, inputs: attn_inputs, T: int, q_base: int, out: int, stream: int) -> int:
+    return lib.attn_prefill_prefix(ctx, ctypes.byref(inputs), T, q_base, out, stream)
+
+
+def attn_prefill_masked(ctx, inputs: attn_inputs, S: int, mask: int, out: int, stream: int) -> int:
+    return lib.attn_prefill_masked(ctx, ctypes.byref(inputs), S, mask, out, stream)
+
+
+def attn_debug_prepare(ctx, inputs: attn_inputs, T: int, q_base: int, qp_out, kp_out, stream) -> int:
+    return lib.attn_debug_prepare(ctx, ctypes.byref(inputs), T, q_base, qp_out, kp_out, stream)
+
+
+def attn_ctx_set_timing(ctx, enable: bool) -> int:
+    return lib.attn_ctx_set_timing(ctx, 1 if enable else 0)
+
+
+def attn_ctx_read_timing(ctx, kernel: int):
+    ms = ctypes.c_double()
+    n = ctypes.c_int32()
+    rc = lib.attn_ctx_read_timing(ctx, kernel, ctypes.byref(ms), ctypes.byref(n))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_ctx_read_timing")
+    return ms.value, n.value
+
+
+# ---- tensor-level wrapper --------------------------------------------------
+
+def geometry(n_q_heads: int, n_kv_heads: int, max_tokens: int, rms_eps: float = 1e-6) -> attn_geometry:
+    return attn_geometry(n_q_heads, n_kv_heads, ATTN_HEAD_DIM, ATTN_ROTARY_DIM, max_tokens, rms_eps)
+
+
+class Context:
+    """One library context bound to a CUDA (HIP) device; owns its workspace."""
+
+    def __init__(self, n_q_heads: int, n_kv_heads: int, max_tokens: int, rms_eps: float = 1e-6,
+                 device: Optional[int] = None):
+        import torch
+        if device is None:
+            device = torch.cuda.current_device()
+        self.device = int(device)
+        self.geom = geometry(n_q_heads, n_kv_heads, max_tokens, rms_eps)
+        with torch.cuda.device(self.device):
+            self.handle = attn_ctx_create(self.geom, self.device)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            attn_ctx_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # -- helpers
+    def _check(self, name, t, dtype, shape):
+        import torch
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != dtype:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.numel() and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.numel() and (t.device.type != "cuda" or t.device.index != self.device):
+            raise ValueError(f"{name} must be on cuda:{self.device}")
+
+    def inputs(self, qg, k, v, q_norm_w, k_norm_w, cos, sin, rows: int, T: int) -> attn_inputs:
+        import torch
+        g = self.geom
+        Hq, Hkv, D = g.n_q_heads, g.n_kv_heads, ATTN_HEAD_DIM
+        self._check("qg", qg, torch.bfloat16, (rows, Hq, 2, D))
+        self._check("k", k, torch.bfloat16, (T, Hkv, D))
+        self._check("v", v, torch.bfloat16, (T, Hkv, D))
+        self._check("q_norm_w", q_norm_w, torch.bfloat16, (D,))
+        self._check("k_norm_w", k_norm_w, torch.bfloat16, (D,))
+        if cos.dim() != 2 or cos.shape[1] != ATTN_ROTARY_DIM // 2:
+            raise ValueError("cos must be [n_pos][rotary_dim/2]")
+        self._check("cos", cos, torch.float32, tuple(cos.shape))
+        self._check("sin", sin, torch.float32, tuple(cos.shape))
+        return attn_inputs(qg.data_ptr(), k.data_ptr(), v.data_ptr(), q_norm_w.data_ptr(),
+                           k_norm_w.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0])
+
+    @staticmethod
+    def _stream(stream):
+        import torch
+        if stream is None:
+            return torch.cuda.current_stream().cuda_stream
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+    def _out(self, out, rows):
+        import torch
+        g = self.geom
+        if out is None:
+            out = torch.empty((rows, g.n_q_heads * ATTN_HEAD_DIM), dtype=torch.bfloat16,
+                              device=f"cuda:{self.device}")
+        self._check("out", out, torch.bfloat16, (rows, g.n_q_heads * ATTN_HEAD_DIM))
+        return out
+
+    def prefill_gated(self, qg, k, v, q_norm_w, k_norm_w, cos, sin, out=None, stream=None):
+        S = k.shape[0]
+        inp = self.inputs(qg, k, v, q_norm_w, k_norm_w, cos, sin, S, S)
+        out = self._out(out, S)
+        rc = attn_prefill_gated(self.handle, inp, S, out.data_ptr(), self._stream(stream))
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_prefill_gated")
+        return out
+
+    def prefill_prefix(self, qg, k, v, q_norm_w, k_norm_w, cos, sin, q_base: int, out=None, stream=None):
+        T = k.shape[0]
+        inp = self.inputs(qg, k, v, q_norm_w, k_norm_w, cos, sin, T - q_base, T)
+        out = self._out(out, T - q_base)
+        rc = attn_prefill_prefix(self.handle, inp, T, q_base, out.data_ptr(), self._stream(stream))
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_prefill_prefix")
+        return out
+
+    def prefill_masked(self, qg, k, v, q_norm_w, k_norm_w, cos, sin, mask, out=None, stream=None):
+        import torch
+        S = k.shape[0]
+        inp = self.inputs(qg, k, v, q_norm_w, k_norm_w, cos, sin, S, S)
+        self._check("mask", mask, torch.uint8, (S, S))
+        out = self._out(out, S)
+        rc = attn_prefill_masked(self.handle, inp, S, mask.data_ptr(), out.data_ptr(),
+                                 self._stream(stream))
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_prefill_masked")
+        return out
+
+    def debug_prepare(self, qg, k, v, q_norm_w, k_norm_w, cos, sin, q_base: int = 0, stream=None):
+        """Prepared queries [rows][Hq][D] and keys [Hkv][T][D] as the kernels see them."""
+        import torch
+        g = self.geom
+        T = k.shape[0]
+        rows = T - q_base
+        inp = self.inputs(qg, k, v, q_norm_w, k_norm_w, cos, sin, rows, T)
+        dev = f"cuda:{self.device}"
+        qp = torch.empty((rows, g.n_q_heads, ATTN_HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        kp = torch.empty((g.n_kv_heads, T, ATTN_HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        rc = attn_debug_prepare(self.handle, inp, T, q_base, qp.data_ptr() if rows else None,
+                                kp.data_ptr() if T else None, self._stream(stream))
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_debug_prepare")
+        return qp, kp
+
+    def set_timing(self, enable: bool):
+        rc = attn_ctx_set_timing(self.handle, enable)
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_ctx_set_timing")
+
+    def read_timing(self, kernel: int):
+        return attn_ctx_read_timing(self.handle, kernel)

@@ -1,0 +1,401 @@
+// abi.cpp -- the C ABI of libgatedattn.so: argument validation, the context
+// and its workspace, kernel dispatch on the caller's stream, and event timing.
+//
+// Boundary conventions follow the attention-tile page ("cuda: widen the
+// attention query tile on sm_89 and sm_120", review sections
+// "Dispatch/guard" and the device-ownership finding: pre-validate, return the
+// error, never fall back; decisions keyed by the current device) and the QSA
+// kernel page ("What changed": geometry validated before sizing any buffer,
+// a short cos/sin table refused, an empty launch a no-op).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "gatedattn.h"
+#include "kernels.h"
+
+struct attn_ctx {
+    int device = -1;
+    attn_geometry geom{};
+    int tpad = 0;                  // max_tokens rounded up to 64
+    int mask_words = 0;            // 32-key words per mask row at max_tokens
+    uint16_t *kp = nullptr;        // [Hkv][tpad][256]
+    uint16_t *vt = nullptr;        // [Hkv][tpad/32][256][32]
+    uint32_t *mask_bits = nullptr; // [max_tokens][mask_words]
+    uint8_t *tile_vis = nullptr;   // [ceil(max_tokens/64)][mask_words]
+    // timing
+    bool timing = false;
+    std::vector<hipEvent_t> pool;
+    size_t pool_used = 0;
+    struct Rec {
+        int kernel;
+        hipEvent_t a, b;
+    };
+    std::vector<Rec> recs;
+};
+
+namespace {
+
+constexpr int kKinds = 3;   // 0 gated, 1 prefix, 2 masked
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_geometry(const attn_geometry *g)
+{
+    if (!g)
+        return ATTN_ERR_NULL_ARG;
+    if (g->head_dim != ATTN_HEAD_DIM || g->rotary_dim != ATTN_ROTARY_DIM)
+        return ATTN_ERR_GEOMETRY;
+    if (g->n_kv_heads < 1 || g->n_q_heads < 1 || g->n_q_heads % g->n_kv_heads != 0)
+        return ATTN_ERR_GEOMETRY;
+    const int G = g->n_q_heads / g->n_kv_heads;
+    if (G < 1 || G > ATTN_MAX_GROUP || g->n_kv_heads > 1024)
+        return ATTN_ERR_GEOMETRY;
+    if (!(g->rms_eps > 0.0f) || !std::isfinite(g->rms_eps))
+        return ATTN_ERR_GEOMETRY;
+    if (g->max_tokens < 1 || g->max_tokens > ATTN_MAX_TOKENS)
+        return ATTN_ERR_RANGE;
+    return ATTN_OK;
+}
+
+struct Timer {
+    attn_ctx *ctx;
+    hipStream_t stream;
+    int kernel;
+    hipEvent_t a = nullptr, b = nullptr;
+    Timer(attn_ctx *c, hipStream_t s, int k) : ctx(c), stream(s), kernel(k)
+    {
+        if (ctx->timing && ctx->pool_used + 2 <= ctx->pool.size()) {
+            a = ctx->pool[ctx->pool_used++];
+            b = ctx->pool[ctx->pool_used++];
+            (void)hipEventRecord(a, stream);
+        }
+    }
+    void stop()
+    {
+        if (a) {
+            (void)hipEventRecord(b, stream);
+            ctx->recs.push_back({kernel, a, b});
+        }
+    }
+};
+
+int current_device_matches(const attn_ctx *ctx)
+{
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != ctx->device)
+        return ATTN_ERR_DEVICE;
+    return ATTN_OK;
+}
+
+void fill_kv_params(ga::KvPrologueParams &kp, const attn_ctx *ctx, const attn_inputs *in, int T)
+{
+    kp.k = static_cast<const uint16_t *>(in->k);
+    kp.v = static_cast<const uint16_t *>(in->v);
+    kp.wk = static_cast<const uint16_t *>(in->k_norm_w);
+    kp.cos_tab = in->cos_tab;
+    kp.sin_tab = in->sin_tab;
+    kp.kp = ctx->kp;
+    kp.vt = ctx->vt;
+    kp.T = T;
+    kp.Hkv = ctx->geom.n_kv_heads;
+    kp.Tpad = ctx->tpad;
+    kp.eps = ctx->geom.rms_eps;
+}
+
+void fill_attn_params(ga::AttnParams &ap, const attn_ctx *ctx, const attn_inputs *in, int T, int q_base,
+                      void *out)
+{
+    const attn_geometry &g = ctx->geom;
+    ap.qg = static_cast<const uint16_t *>(in->qg);
+    ap.kp = ctx->kp;
+    ap.vt = ctx->vt;
+    ap.wq = static_cast<const uint16_t *>(in->q_norm_w);
+    ap.cos_tab = in->cos_tab;
+    ap.sin_tab = in->sin_tab;
+    ap.bits = ctx->mask_bits;
+    ap.tilevis = ctx->tile_vis;
+    ap.out = static_cast<uint16_t *>(out);
+    ap.S = T - q_base;
+    ap.T = T;
+    ap.q_base = q_base;
+    ap.Hq = g.n_q_heads;
+    ap.Hkv = g.n_kv_heads;
+    ap.G = g.n_q_heads / g.n_kv_heads;
+    ap.n_hg = (ap.G + ga::kHeadsPerBlock - 1) / ga::kHeadsPerBlock;
+    ap.nrb = (ap.S + ga::kRowsPerBlock - 1) / ga::kRowsPerBlock;
+    ap.Tpad = ctx->tpad;
+    ap.W = (T + 31) / 32;
+    ap.eps = g.rms_eps;
+}
+
+int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kind, const uint8_t *mask,
+        void *out, void *stream)
+{
+    if (!ctx)
+        return ATTN_ERR_NULL_ARG;
+    int rc = attn_validate(&ctx->geom, in, T, q_base, kind, mask, out);
+    if (rc != ATTN_OK)
+        return rc;
+    if (T - q_base == 0)
+        return ATTN_OK;
+    rc = current_device_matches(ctx);
+    if (rc != ATTN_OK)
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();   // clear a stale error so the launch status below is ours
+
+    ga::KvPrologueParams kvp;
+    fill_kv_params(kvp, ctx, in, T);
+    {
+        Timer tm(ctx, s, ATTN_KERNEL_KV_PROLOGUE);
+        if (ga::launch_kv_prologue(kvp, (T + ga::kKeysPerTile - 1) / ga::kKeysPerTile, s) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+        tm.stop();
+    }
+    ga::AttnParams ap;
+    fill_attn_params(ap, ctx, in, T, q_base, out);
+    if (kind == 2) {
+        ga::MaskPackParams mp;
+        mp.mask = mask;
+        mp.bits = ctx->mask_bits;
+        mp.tilevis = ctx->tile_vis;
+        mp.S = T;
+        mp.W = ap.W;
+        mp.vec16 = (T % 16 == 0) && aligned16(mask);
+        Timer tm(ctx, s, ATTN_KERNEL_MASK_PACK);
+        if (ga::launch_mask_pack(mp, ap.nrb, s) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+        tm.stop();
+    }
+    {
+        Timer tm(ctx, s, ATTN_KERNEL_ATTENTION);
+        if (ga::launch_attention(ap, kind == 2, s) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+        tm.stop();
+    }
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char *attn_status_string(int status)
+{
+    switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL_ARG: return "null argument";
+    case ATTN_ERR_GEOMETRY: return "unsupported geometry";
+    case ATTN_ERR_RANGE: return "argument out of range";
+    case ATTN_ERR_ALIGN: return "misaligned q_base or pointer";
+    case ATTN_ERR_DEVICE: return "device unavailable or not the context's device";
+    case ATTN_ERR_NOMEM: return "workspace allocation failed";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int attn_validate(const attn_geometry *geom, const attn_inputs *in, int32_t T, int32_t q_base,
+                  int32_t kind, const void *mask, const void *out)
+{
+    int rc = check_geometry(geom);
+    if (rc != ATTN_OK)
+        return rc;
+    if (kind < 0 || kind >= kKinds)
+        return ATTN_ERR_RANGE;
+    if (T < 0 || T > geom->max_tokens)
+        return ATTN_ERR_RANGE;
+    if (q_base < 0 || q_base > T)
+        return ATTN_ERR_RANGE;
+    if (kind != 1 && q_base != 0)
+        return ATTN_ERR_RANGE;
+    if (q_base % ATTN_QBASE_ALIGN != 0)
+        return ATTN_ERR_ALIGN;
+    if (T - q_base == 0)
+        return ATTN_OK;             // empty launch: no-op, pointers unused
+    if (!in || !out)
+        return ATTN_ERR_NULL_ARG;
+    if (!in->qg || !in->k || !in->v || !in->q_norm_w || !in->k_norm_w || !in->cos_tab || !in->sin_tab)
+        return ATTN_ERR_NULL_ARG;
+    if (kind == 2 && !mask)
+        return ATTN_ERR_NULL_ARG;
+    if (in->n_pos < T)
+        return ATTN_ERR_RANGE;
+    if (!aligned16(in->qg) || !aligned16(in->k) || !aligned16(in->v) || !aligned16(in->q_norm_w) ||
+        !aligned16(in->k_norm_w) || !aligned16(in->cos_tab) || !aligned16(in->sin_tab) || !aligned16(out))
+        return ATTN_ERR_ALIGN;
+    return ATTN_OK;
+}
+
+int attn_ctx_create(const attn_geometry *geom, int device, attn_ctx **out)
+{
+    if (!out)
+        return ATTN_ERR_NULL_ARG;
+    *out = nullptr;
+    int rc = check_geometry(geom);
+    if (rc != ATTN_OK)
+        return rc;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) {
+        (void)hipGetLastError();
+        return ATTN_ERR_DEVICE;
+    }
+    if (hipSetDevice(device) != hipSuccess)
+        return ATTN_ERR_DEVICE;
+    attn_ctx *ctx = new (std::nothrow) attn_ctx;
+    if (!ctx)
+        return ATTN_ERR_NOMEM;
+    ctx->device = device;
+    ctx->geom = *geom;
+    ctx->tpad = (geom->max_tokens + 63) / 64 * 64;
+    ctx->mask_words = (geom->max_tokens + 31) / 32;
+    const size_t kv_elems = (size_t)geom->n_kv_heads * ctx->tpad * ATTN_HEAD_DIM;
+    const size_t nrb = (size_t)(geom->max_tokens + 63) / 64;
+    bool ok = hipMalloc(&ctx->kp, kv_elems * 2) == hipSuccess &&
+              hipMalloc(&ctx->vt, kv_elems * 2) == hipSuccess &&
+              hipMalloc(&ctx->mask_bits, (size_t)geom->max_tokens * ctx->mask_words * 4) == hipSuccess &&
+              hipMalloc(&ctx->tile_vis, nrb * ctx->mask_words) == hipSuccess;
+    if (!ok) {
+        (void)hipGetLastError();
+        attn_ctx_destroy(ctx);
+        return ATTN_ERR_NOMEM;
+    }
+    *out = ctx;
+    return ATTN_OK;
+}
+
+void attn_ctx_destroy(attn_ctx *ctx)
+{
+    if (!ctx)
+        return;
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    if (prev != ctx->device)
+        (void)hipSetDevice(ctx->device);
+    (void)hipFree(ctx->kp);
+    (void)hipFree(ctx->vt);
+    (void)hipFree(ctx->mask_bits);
+    (void)hipFree(ctx->tile_vis);
+    for (hipEvent_t e : ctx->pool)
+        (void)hipEventDestroy(e);
+    if (prev >= 0 && prev != ctx->device)
+        (void)hipSetDevice(prev);
+    delete ctx;
+}
+
+int attn_prefill_gated(attn_ctx *ctx, const attn_inputs *in, int32_t S, void *out, void *stream)
+{
+    return run(ctx, in, S, 0, 0, nullptr, out, stream);
+}
+
+int attn_prefill_prefix(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, void *out,
+                        void *stream)
+{
+    return run(ctx, in, T, q_base, 1, nullptr, out, stream);
+}
+
+int attn_prefill_masked(attn_ctx *ctx, const attn_inputs *in, int32_t S, const uint8_t *mask, void *out,
+                        void *stream)
+{
+    return run(ctx, in, S, 0, 2, mask, out, stream);
+}
+
+int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, void *qp_out,
+                       void *kp_out, void *stream)
+{
+    if (!ctx)
+        return ATTN_ERR_NULL_ARG;
+    if (T - q_base != 0 && !qp_out && !kp_out)
+        return ATTN_ERR_NULL_ARG;
+    int rc = attn_validate(&ctx->geom, in, T, q_base, 1, nullptr, qp_out ? qp_out : kp_out);
+    if (rc != ATTN_OK)
+        return rc;
+    if ((qp_out && !aligned16(qp_out)) || (kp_out && !aligned16(kp_out)))
+        return ATTN_ERR_ALIGN;
+    if (T - q_base == 0)
+        return ATTN_OK;
+    rc = current_device_matches(ctx);
+    if (rc != ATTN_OK)
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (kp_out) {
+        ga::KvPrologueParams kvp;
+        fill_kv_params(kvp, ctx, in, T);
+        if (ga::launch_kv_prologue(kvp, (T + ga::kKeysPerTile - 1) / ga::kKeysPerTile, s) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+        const size_t row = (size_t)ATTN_HEAD_DIM * 2;
+        if (hipMemcpy2DAsync(kp_out, (size_t)T * row, ctx->kp, (size_t)ctx->tpad * row, (size_t)T * row,
+                             ctx->geom.n_kv_heads, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+    }
+    if (qp_out) {
+        ga::AttnParams ap;
+        fill_attn_params(ap, ctx, in, T, q_base, nullptr);
+        if (ga::launch_q_prologue_debug(ap, static_cast<uint16_t *>(qp_out), s) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+    }
+    return ATTN_OK;
+}
+
+int attn_ctx_set_timing(attn_ctx *ctx, int enable)
+{
+    if (!ctx)
+        return ATTN_ERR_NULL_ARG;
+    if (current_device_matches(ctx) != ATTN_OK)
+        return ATTN_ERR_DEVICE;
+    if (enable && ctx->pool.empty()) {
+        for (int i = 0; i < 8192; ++i) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess)
+                return ATTN_ERR_NOMEM;
+            ctx->pool.push_back(e);
+        }
+    }
+    ctx->timing = enable != 0;
+    ctx->pool_used = 0;
+    ctx->recs.clear();
+    return ATTN_OK;
+}
+
+int attn_ctx_read_timing(attn_ctx *ctx, int kernel, double *total_ms, int32_t *launches)
+{
+    if (!ctx || !total_ms || !launches)
+        return ATTN_ERR_NULL_ARG;
+    if (kernel < 0 || kernel > ATTN_KERNEL_ATTENTION)
+        return ATTN_ERR_RANGE;
+    if (current_device_matches(ctx) != ATTN_OK)
+        return ATTN_ERR_DEVICE;
+    double sum = 0.0;
+    int n = 0;
+    std::vector<attn_ctx::Rec> keep;
+    for (const auto &r : ctx->recs) {
+        if (r.kernel != kernel) {
+            keep.push_back(r);
+            continue;
+        }
+        if (hipEventSynchronize(r.b) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+        sum += ms;
+        ++n;
+    }
+    ctx->recs.swap(keep);
+    if (ctx->recs.empty())
+        ctx->pool_used = 0;
+    *total_ms = sum;
+    *launches = n;
+    return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// kernels.h -- parameters and launchers shared by kernels.hip and abi.cpp
+// (internal to libgatedattn.so; not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ga {
+
+struct KvPrologueParams {
+    const uint16_t *k;        // [T][Hkv][256]
+    const uint16_t *v;        // [T][Hkv][256]
+    const uint16_t *wk;       // [256]
+    const float *cos_tab;     // [n_pos][32]
+    const float *sin_tab;     // [n_pos][32]
+    uint16_t *kp;             // [Hkv][Tpad][256]
+    uint16_t *vt;             // [Hkv][Tpad/32][256][32]
+    int T, Hkv, Tpad;
+    float eps;
+};
+
+struct MaskPackParams {
+    const uint8_t *mask;      // [S][S]
+    uint32_t *bits;           // [S][W]
+    uint8_t *tilevis;         // [nrb][W]
+    int S, W;
+    int vec16;                // mask rows may be read 16 bytes at a time
+};
+
+struct AttnParams {
+    const uint16_t *qg;       // [S][Hq][2][256]
+    const uint16_t *kp;       // [Hkv][Tpad][256]
+    const uint16_t *vt;       // [Hkv][Tpad/32][256][32]
+    const uint16_t *wq;       // [256]
+    const float *cos_tab;     // [n_pos][32]
+    const float *sin_tab;     // [n_pos][32]
+    const uint32_t *bits;     // [S][W] (masked only)
+    const uint8_t *tilevis;   // [nrb][W] (masked only)
+    uint16_t *out;            // [S][Hq][256]
+    int S, T, q_base;
+    int Hq, Hkv, G, n_hg, nrb, Tpad, W;
+    float eps;
+};
+
+constexpr int kRowsPerBlock = 64;
+constexpr int kKeysPerTile = 32;
+constexpr int kHeadsPerBlock = 4;
+
+hipError_t launch_kv_prologue(const KvPrologueParams &p, int ntiles, hipStream_t stream);
+hipError_t launch_mask_pack(const MaskPackParams &p, int nrb, hipStream_t stream);
+hipError_t launch_attention(const AttnParams &p, bool masked, hipStream_t stream);
+hipError_t launch_q_prologue_debug(const AttnParams &p, uint16_t *qp, hipStream_t stream);
+
+}  // namespace ga

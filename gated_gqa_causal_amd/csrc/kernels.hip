@@ -1,0 +1,590 @@
+// kernels.hip -- gfx950 (CDNA4) kernels for gated GQA causal attention prefill.
+//
+// Three kernels run on the caller's stream:
+//   kv_prologue  : (1+w) RMSNorm + partial RoPE of every key once per KV head
+//                  (the QSA kernel page, "What changed": all query heads of a
+//                  KV head read the same prepared key), and V transposed into
+//                  MFMA-ready key tiles.  Writes the context's workspace.
+//   mask_pack    : masked path only.  uint8 [S][S] visibility -> one bit per
+//                  (row, key) with causality folded in, plus a per (64-row
+//                  block, 32-key tile) flag used to skip fully hidden tiles.
+//   attn_fwd     : one workgroup = 4 waves = 64 query rows x up to 4 query
+//                  heads of one KV head.  Each wave owns 64 rows of one head:
+//                  it norms and rotates its own queries, walks the key tiles
+//                  0..diagonal in ascending order (online softmax, the
+//                  attention-tile page's "Kernel change" recurrence), and
+//                  applies the sigmoid gate in the epilogue.
+//
+// Rounding points follow the QSA kernel page ("Semantics"; final commit
+// message): norms cast once, cos/sin cast to bf16 and the rotation done in
+// bf16, the score rounded to bf16 before the exact 1/16 scale, the weights
+// rounded to bf16 before the context product, the context rounded, the
+// sigmoid rounded before the final product.  The GPU's online softmax rounds
+// the unnormalised weight exp2(y - m) and divides by the fp32 row sum at the
+// end, where the plain definition rounds normalised weights; the two agree to
+// a bf16 rounding per weight.
+//
+// MFMA orientation: scores are computed transposed, S^T[key][query] =
+// K . Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims, B = 16 dims x
+// 32 queries).  The accumulator layout then gives each lane one query column
+// and 16 of the tile's 32 keys, so the row max and row sum are in-lane plus
+// one exchange with lane^32, and the weights feed the P.V MFMA as its B
+// operand with no data movement.  The context is computed transposed too,
+// O^T[d][query] = V^T . P^T, with A = V^T read from a transposed copy of V.
+// The key order inside each 16-key group of that copy is
+// [0..3, 8..11, 4..7, 12..15], matching the accumulator rows a lane holds.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace ga {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 256;          // head dim
+constexpr int HALF_R = 32;      // rotary pairs (rotary dim 64)
+constexpr int KT = 32;          // keys per tile
+constexpr int QW = 64;          // query rows per attention workgroup
+constexpr float LOG2E = 1.4426950408889634f;
+// Scores are x = bf16(q.k); the softmax runs on y = x * (log2(e) / 16).
+constexpr float SCALE_LOG2 = LOG2E * 0.0625f;
+// The running max is only moved when a tile's max exceeds it by more than
+// 8 in the log2 domain (weights then stay below 2^8).  The result is the same
+// softmax; the rescale of the 256-wide accumulator becomes rare.
+constexpr float TAU_X = 8.0f / SCALE_LOG2;
+
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack2(float a, float b)
+{
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f2bf(float a) { return __builtin_bit_cast(uint16_t, (__bf16)a); }
+__device__ __forceinline__ float rbf(float a) { return bf2f(f2bf(a)); }
+
+__device__ __forceinline__ float word_f(const uint4 &u, int t)
+{
+    const uint32_t w = (t < 2) ? u.x : (t < 4) ? u.y : (t < 6) ? u.z : u.w;
+    return (t & 1) ? hi_f(w) : lo_f(w);
+}
+
+// ---------------------------------------------------------------------------
+// K/V prologue.  grid (Tpad/32, Hkv), 256 threads.
+// Kp [Hkv][Tpad][D]: prepared keys, natural key order, zero rows past T.
+// Vt [Hkv][Tpad/32][D][32]: per 32-key tile, V transposed (dims x keys), keys
+// permuted inside each 16-group as [0..3, 8..11, 4..7, 12..15].
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int vt_key_of_pos(int pos)
+{
+    const int w = pos & 15;
+    const int k16 = (w < 4) ? w : (w < 8) ? w + 4 : (w < 12) ? w - 4 : w;
+    return (pos & ~15) | k16;
+}
+
+__global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
+{
+    __shared__ __align__(16) uint16_t ks[KT][D + 8];
+    __shared__ __align__(16) uint16_t vs[KT][D + 8];
+    __shared__ float rs[KT];
+    const int tile = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+    const int t0 = tile * KT;
+
+    for (int it = 0; it < 4; ++it) {
+        const int idx = it * 256 + tid, r = idx >> 5, ch = idx & 31, key = t0 + r;
+        uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+        if (key < p.T) {
+            const size_t off = ((size_t)key * p.Hkv + c) * D + ch * 8;
+            kv = *reinterpret_cast<const uint4 *>(p.k + off);
+            vv = *reinterpret_cast<const uint4 *>(p.v + off);
+        }
+        *reinterpret_cast<uint4 *>(&ks[r][ch * 8]) = kv;
+        *reinterpret_cast<uint4 *>(&vs[r][ch * 8]) = vv;
+    }
+    __syncthreads();
+
+    // Sum of squares in ascending dimension order, one thread per key.
+    if (tid < KT) {
+        float ss = 0.0f;
+        for (int d = 0; d < D; ++d) {
+            const float x = bf2f(ks[tid][d]);
+            ss += x * x;
+        }
+        rs[tid] = 1.0f / sqrtf(ss / (float)D + p.eps);
+    }
+    __syncthreads();
+
+    {
+        // Thread owns dims sub + 8*s of key row r; pairs (j, j+32) are s, s+4.
+        const int r = tid >> 3, sub = tid & 7, key = t0 + r;
+        const float rr = rs[r];
+        float n[32];
+#pragma unroll
+        for (int s = 0; s < 32; ++s) {
+            const int d = sub + 8 * s;
+            n[s] = rbf((bf2f(ks[r][d]) * rr) * (1.0f + bf2f(p.wk[d])));
+        }
+        if (key < p.T) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int j = sub + 8 * s;
+                const float cj = rbf(p.cos_tab[(size_t)key * HALF_R + j]);
+                const float sj = rbf(p.sin_tab[(size_t)key * HALF_R + j]);
+                const float a = n[s], b = n[s + 4];
+                n[s] = rbf(rbf(a * cj) + rbf(-b * sj));
+                n[s + 4] = rbf(rbf(b * cj) + rbf(a * sj));
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 32; ++s)
+            ks[r][sub + 8 * s] = (key < p.T) ? f2bf(n[s]) : (uint16_t)0;
+    }
+    __syncthreads();
+
+    for (int it = 0; it < 4; ++it) {
+        const int idx = it * 256 + tid, r = idx >> 5, ch = idx & 31;
+        *reinterpret_cast<uint4 *>(p.kp + ((size_t)c * p.Tpad + t0 + r) * D + ch * 8) =
+            *reinterpret_cast<const uint4 *>(&ks[r][ch * 8]);
+    }
+
+    {
+        const int d = tid;
+        uint32_t w[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const uint32_t a = vs[vt_key_of_pos(2 * q)][d];
+            const uint32_t b = vs[vt_key_of_pos(2 * q + 1)][d];
+            w[q] = a | (b << 16);
+        }
+        uint4 *dst = reinterpret_cast<uint4 *>(p.vt + (((size_t)c * (p.Tpad / KT) + tile) * D + d) * KT);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dst[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Mask packing.  grid (ceil(W/256), nrb), 256 threads; thread = (row block, word).
+// bits[row][w] bit b = mask[row][32w+b] != 0 && 32w+b <= row && 32w+b < S.
+// tilevis[rb][w] = any bit of the 64 x 32 block.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t nz_bits4(uint32_t u)
+{
+    return ((u & 0x000000ffu) ? 1u : 0u) | ((u & 0x0000ff00u) ? 2u : 0u) |
+           ((u & 0x00ff0000u) ? 4u : 0u) | ((u & 0xff000000u) ? 8u : 0u);
+}
+
+__global__ __launch_bounds__(256) void mask_pack(MaskPackParams p)
+{
+    const int w = blockIdx.x * 256 + threadIdx.x;
+    const int rb = blockIdx.y;
+    if (w >= p.W)
+        return;
+    const int key0 = 32 * w;
+    uint32_t any = 0;
+    for (int r = 0; r < QW; ++r) {
+        const int row = rb * QW + r;
+        if (row >= p.S)
+            break;
+        uint32_t word = 0;
+        if (key0 <= row) {
+            const uint8_t *src = p.mask + (size_t)row * p.S + key0;
+            if (p.vec16 && key0 + 32 <= p.S) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(src);
+                const uint4 b = *reinterpret_cast<const uint4 *>(src + 16);
+                word = nz_bits4(a.x) | (nz_bits4(a.y) << 4) | (nz_bits4(a.z) << 8) |
+                       (nz_bits4(a.w) << 12) | (nz_bits4(b.x) << 16) | (nz_bits4(b.y) << 20) |
+                       (nz_bits4(b.z) << 24) | (nz_bits4(b.w) << 28);
+            } else {
+                for (int b = 0; b < 32; ++b)
+                    if (key0 + b < p.S && src[b] != 0)
+                        word |= 1u << b;
+            }
+            const int last = row - key0;               // keys key0..row are causal
+            if (last < 31)
+                word &= (2u << last) - 1u;
+        }
+        p.bits[(size_t)row * p.W + w] = word;
+        any |= word;
+    }
+    p.tilevis[(size_t)rb * p.W + w] = any ? 1 : 0;
+}
+
+// ---------------------------------------------------------------------------
+// Query prologue of one wave: loads the q half of 32 rows of head h, applies
+// (1+w) RMSNorm (sum of squares in ascending dimension order, the same chain
+// as the key prologue) and partial RoPE, and leaves the MFMA B-operand
+// fragments in qf[c]: lane (j = lane & 31, hh = lane >> 5) holds dims
+// 16c + 8hh .. +7 of query row r0 + j.  Rows at or past S are zero.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void load_queries(const AttnParams &p, int r0, int h, int lane,
+                                             uint4 (&qf)[16])
+{
+    const int j = lane & 31, hh = lane >> 5;
+    const int row = r0 + j;
+    const bool ok = row < p.S;
+    const uint16_t *src = p.qg + (((size_t)(ok ? row : 0) * p.Hq + h) * 2) * D;
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        qf[c] = *reinterpret_cast<const uint4 *>(src + 16 * c + 8 * hh);
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const uint4 own = qf[c];
+        uint4 oth;
+        oth.x = __shfl_xor(own.x, 32);
+        oth.y = __shfl_xor(own.y, 32);
+        oth.z = __shfl_xor(own.z, 32);
+        oth.w = __shfl_xor(own.w, 32);
+        const uint4 first = hh ? oth : own;
+        const uint4 second = hh ? own : oth;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float x = word_f(first, t);
+            ss += x * x;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float x = word_f(second, t);
+            ss += x * x;
+        }
+    }
+    const float rr = 1.0f / sqrtf(ss / (float)D + p.eps);
+    // Dims 0..63 (chunks 0..3) hold the rotary pairs (d, d+32) = chunks
+    // (c, c+2); the remaining chunks are only normalised.
+    {
+        float n[4][8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint4 wv = *reinterpret_cast<const uint4 *>(p.wq + 16 * c + 8 * hh);
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                n[c][t] = rbf((word_f(qf[c], t) * rr) * (1.0f + word_f(wv, t)));
+        }
+        const int pos = p.q_base + (ok ? row : 0);
+        const float *ct = p.cos_tab + (size_t)pos * HALF_R;
+        const float *st = p.sin_tab + (size_t)pos * HALF_R;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const float4 c0 = *reinterpret_cast<const float4 *>(ct + 16 * c + 8 * hh);
+            const float4 c1 = *reinterpret_cast<const float4 *>(ct + 16 * c + 8 * hh + 4);
+            const float4 s0 = *reinterpret_cast<const float4 *>(st + 16 * c + 8 * hh);
+            const float4 s1 = *reinterpret_cast<const float4 *>(st + 16 * c + 8 * hh + 4);
+            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float cj = rbf(cv[t]), sj = rbf(sv[t]);
+                const float a = n[c][t], bb = n[c + 2][t];
+                n[c][t] = rbf(rbf(a * cj) + rbf(-bb * sj));
+                n[c + 2][t] = rbf(rbf(bb * cj) + rbf(a * sj));
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            qf[c] = make_uint4(pack2(n[c][0], n[c][1]), pack2(n[c][2], n[c][3]),
+                               pack2(n[c][4], n[c][5]), pack2(n[c][6], n[c][7]));
+    }
+#pragma unroll
+    for (int c = 4; c < 16; ++c) {
+        const uint4 wv = *reinterpret_cast<const uint4 *>(p.wq + 16 * c + 8 * hh);
+        float n[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            n[t] = rbf((word_f(qf[c], t) * rr) * (1.0f + word_f(wv, t)));
+        qf[c] = make_uint4(pack2(n[0], n[1]), pack2(n[2], n[3]), pack2(n[4], n[5]), pack2(n[6], n[7]));
+    }
+    if (!ok) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            qf[c] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// Debug: prepared queries in a plain [rows][Hq][D] layout.
+// grid (ceil(S/32), ceil(Hq/4)), 256 threads: wave = one head, 32 rows.
+__global__ __launch_bounds__(256) void q_prologue_debug(AttnParams p, uint16_t *qp)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int h = blockIdx.y * 4 + wave;
+    if (h >= p.Hq)
+        return;
+    const int r0 = blockIdx.x * 32;
+    uint4 qf[16];
+    load_queries(p, r0, h, lane, qf);
+    const int j = lane & 31, hh = lane >> 5;
+    const int row = r0 + j;
+    if (row >= p.S)
+        return;
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        *reinterpret_cast<uint4 *>(qp + ((size_t)row * p.Hq + h) * D + 16 * c + 8 * hh) = qf[c];
+}
+
+// ---------------------------------------------------------------------------
+// Attention.  Workgroup = 8 waves = 64 query rows x 4 query heads of one KV
+// head; wave w owns head (w & 3) and rows r0 + 32 * (w >> 2) .. +31.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int AW = 8;                  // waves per attention workgroup
+constexpr int ATHREADS = 64 * AW;
+constexpr int QR = 32;                 // query rows per wave
+
+// K tile in LDS: 32 key rows x 512 B; 16-byte slot s of row i holds the row's
+// global chunk s ^ (i & 7) (conflict-free b128 reads down a column).
+// V^T tile in LDS: 256 dim rows x 64 B; slot q of row d holds global chunk
+// q ^ ((d >> 1) & 3).
+struct __align__(16) TileBuf {
+    uint16_t k[KT * D];
+    uint16_t v[D * KT];
+};
+
+// Each of the 8 waves moves 4 KB of the 32 KB tile straight from global
+// memory into LDS (global_load_lds_dwordx4: lane L of an instruction writes
+// the 16 bytes at LDS base + 16 L).
+__device__ __forceinline__ void issue_tile_loads(const AttnParams &p, TileBuf *buf, int kvh, int tile,
+                                                 int wave, int lane)
+{
+    const uint16_t *ksrc = p.kp + ((size_t)kvh * p.Tpad + (size_t)tile * KT) * D;
+    const uint16_t *vsrc = p.vt + ((size_t)kvh * (p.Tpad / KT) + tile) * (size_t)(D * KT);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int n = wave * 2 + i;                    // K rows 2n, 2n+1
+        const int row = 2 * n + (lane >> 5), slot = lane & 31;
+        const int chunk = slot ^ (row & 7);
+        __builtin_amdgcn_global_load_lds(ksrc + row * D + chunk * 8,
+                                         (lds_void *)((char *)buf->k + n * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int n = wave * 2 + i;                    // V^T dim rows 16n .. 16n+15
+        const int d = 16 * n + (lane >> 2), slot = lane & 3;
+        const int chunk = slot ^ ((d >> 1) & 3);
+        __builtin_amdgcn_global_load_lds(vsrc + d * KT + chunk * 8,
+                                         (lds_void *)((char *)buf->v + n * 1024), 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ bf16x8 lds_k_frag(const TileBuf *buf, int i, int chunk)
+{
+    const int slot = chunk ^ (i & 7);
+    return *reinterpret_cast<const bf16x8 *>((const char *)buf->k + i * 512 + slot * 16);
+}
+
+__device__ __forceinline__ bf16x8 lds_v_frag(const TileBuf *buf, int d, int chunk)
+{
+    const int slot = chunk ^ ((d >> 1) & 3);
+    return *reinterpret_cast<const bf16x8 *>((const char *)buf->v + d * 64 + slot * 16);
+}
+
+template <bool MASKED>
+__global__ __attribute__((amdgpu_flat_work_group_size(ATHREADS, ATHREADS), amdgpu_waves_per_eu(2, 2)))
+void attn_fwd(AttnParams p)
+{
+    __shared__ TileBuf bufs[2];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 31, hh = lane >> 5;
+
+    // Heaviest row blocks first (longest key walks), then KV head, then head group.
+    const int per_rb = p.Hkv * p.n_hg;
+    const int rb = p.nrb - 1 - (int)(blockIdx.x / per_rb);
+    const int rem = blockIdx.x % per_rb;
+    const int kvh = rem / p.n_hg, hg = rem % p.n_hg;
+    const int gidx = hg * 4 + (wave & 3);
+    const int r0 = rb * QW + QR * (wave >> 2);       // this wave's first window row
+    const bool active = gidx < p.G && r0 < p.S;
+    const int h = kvh * p.G + (active ? gidx : 0);
+
+    const int P0 = p.q_base + rb * QW;               // workgroup's first absolute position
+    const int ntiles = min(P0 + QW - 1, p.T - 1) / KT + 1;
+    const int Pw = p.q_base + r0;                    // wave's first absolute position
+    const int wave_tiles = min(Pw + QR - 1, p.T - 1) / KT + 1;   // tiles this wave needs
+    const int diag = Pw / KT;                        // tiles >= diag need the causal test
+    const int pos = Pw + j;
+
+    uint4 qf[16];
+    if (active)
+        load_queries(p, r0, h, lane, qf);
+
+    f32x16 o[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            o[db][e] = 0.0f;
+    float m = -INFINITY, l = 0.0f;
+
+    auto next_tile = [&](int t) -> int {
+        ++t;
+        if (MASKED) {
+            while (t < ntiles && p.tilevis[(size_t)rb * p.W + t] == 0)
+                ++t;
+        }
+        return t;
+    };
+    // Masked path: a tile's visibility word is loaded one iteration ahead,
+    // issued before that tile's K/V loads, so no wait lands mid-tile.
+    const bool row_ok = active && (r0 + j) < p.S;
+    auto load_bits = [&](int tile) -> uint32_t {
+        return (MASKED && row_ok && tile < wave_tiles) ? p.bits[(size_t)(r0 + j) * p.W + tile] : 0u;
+    };
+
+    int t = MASKED ? next_tile(-1) : 0;
+    int cur = 0;
+    uint32_t bits_cur = MASKED ? load_bits(t) : 0u;
+    if (t < ntiles)
+        issue_tile_loads(p, &bufs[0], kvh, t, wave, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    while (t < ntiles) {
+        const int tn = next_tile(t);
+        const uint32_t bits_next = MASKED ? load_bits(tn) : 0u;
+        if (tn < ntiles)
+            issue_tile_loads(p, &bufs[cur ^ 1], kvh, tn, wave, lane);
+        const TileBuf *buf = &bufs[cur];
+
+        if (active && t < wave_tiles) {
+            // S^T = K . Q^T: lane holds query j, keys 8g + 4hh + r (e = 4g + r).
+            f32x16 s;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                s[e] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const bf16x8 kf = lds_k_frag(buf, j, 2 * c + hh);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8, qf[c]), s, 0, 0, 0);
+            }
+
+            const bool need_pred = MASKED || t >= diag;
+            const uint32_t bits = MASKED ? bits_cur : 0xffffffffu;
+            float x[16];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int kk = 8 * (e >> 2) + 4 * hh + (e & 3);      // key within the tile
+                float xv = rbf(s[e]);
+                if (need_pred) {
+                    const bool vis = (t * KT + kk <= pos) && ((bits >> kk) & 1u);
+                    xv = vis ? xv : -INFINITY;
+                }
+                x[e] = xv;
+                mt = fmaxf(mt, xv);
+            }
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            const float mo = m;
+            const float mn = (mt > mo + TAU_X) ? mt : mo;
+            const float alpha = (mn == mo) ? 1.0f : __builtin_amdgcn_exp2f((mo - mn) * SCALE_LOG2);
+            m = mn;
+            const float base = (mn == -INFINITY) ? 0.0f : mn * SCALE_LOG2;
+            float ls = 0.0f;
+            uint32_t pk[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * q], SCALE_LOG2, -base));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * q + 1], SCALE_LOG2, -base));
+                ls += p0;
+                ls += p1;
+                pk[q] = pack2(p0, p1);
+            }
+            l = l * alpha + ls;
+            if (__any(alpha != 1.0f)) {
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        o[db][e] *= alpha;
+            }
+
+            // O^T += V^T . P^T; P chunk kc = keys 16kc .. 16kc+15 = pk[4kc .. 4kc+3].
+            const uint4 p0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            const uint4 p1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const bf16x8 v0 = lds_v_frag(buf, 32 * db + j, hh);
+                const bf16x8 v1 = lds_v_frag(buf, 32 * db + j, 2 + hh);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, __builtin_bit_cast(bf16x8, p0), o[db], 0, 0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, __builtin_bit_cast(bf16x8, p1), o[db], 0, 0, 0);
+            }
+        }
+
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        cur ^= 1;
+        t = tn;
+        bits_cur = bits_next;
+    }
+
+    if (!active)
+        return;
+
+    // Epilogue: ctx = bf16(O / l), out = bf16(ctx * bf16(sigmoid(gate))).
+    const float lt = l + __shfl_xor(l, 32);
+    const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
+    const int row = r0 + j;
+    if (row >= p.S)
+        return;
+    const uint16_t *gsrc = p.qg + (((size_t)row * p.Hq + h) * 2 + 1) * D;
+    uint16_t *dst = p.out + ((size_t)row * p.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d0 = 32 * db + 8 * g + 4 * hh;
+            const uint2 gw = *reinterpret_cast<const uint2 *>(gsrc + d0);
+            const float gv[4] = {lo_f(gw.x), hi_f(gw.x), lo_f(gw.y), hi_f(gw.y)};
+            float ov[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ctx = rbf(o[db][4 * g + r] * inv);
+                const float sg = rbf(1.0f / (1.0f + __builtin_amdgcn_exp2f(-gv[r] * LOG2E)));
+                ov[r] = ctx * sg;
+            }
+            *reinterpret_cast<uint2 *>(dst + d0) = make_uint2(pack2(ov[0], ov[1]), pack2(ov[2], ov[3]));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+hipError_t launch_kv_prologue(const KvPrologueParams &p, int ntiles, hipStream_t stream)
+{
+    hipLaunchKernelGGL(kv_prologue, dim3(ntiles, p.Hkv), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_mask_pack(const MaskPackParams &p, int nrb, hipStream_t stream)
+{
+    hipLaunchKernelGGL(mask_pack, dim3((p.W + 255) / 256, nrb), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnParams &p, bool masked, hipStream_t stream)
+{
+    const int nblocks = p.nrb * p.Hkv * p.n_hg;
+    if (masked)
+        hipLaunchKernelGGL(attn_fwd<true>, dim3(nblocks), dim3(ATHREADS), 0, stream, p);
+    else
+        hipLaunchKernelGGL(attn_fwd<false>, dim3(nblocks), dim3(ATHREADS), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_q_prologue_debug(const AttnParams &p, uint16_t *qp, hipStream_t stream)
+{
+    hipLaunchKernelGGL(q_prologue_debug, dim3((p.S + 31) / 32, (p.Hq + 3) / 4), dim3(256), 0,
+                       stream, p, qp);
+    return hipGetLastError();
+}
+
+}  // namespace ga

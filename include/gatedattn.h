@@ -1,0 +1,180 @@
+/*
+ * gatedattn.h -- C ABI of the MI355X (gfx950) gated GQA causal attention
+ * prefill library, libgatedattn.so.
+ *
+ * The operation (per query row i at absolute position p, per query head h):
+ *   q, gate  = the two halves of head h's slice of the fused q|gate row;
+ *   q', k'   = (1+w) RMSNorm, then rotate-half RoPE on the first 64 of 256
+ *              dims from the caller's fp32 cos/sin table at the token's
+ *              absolute position;
+ *   s_j      = bf16(q' . k'_j) / 16 for every visible key j of KV head h/G;
+ *   w        = softmax over the visible s_j (fp32), weights rounded to bf16;
+ *   ctx      = bf16(sum_j w_j v_j);
+ *   out      = bf16(ctx * bf16(sigmoid(gate))).
+ * Key j is visible to row i iff j <= p and, in the masked entry point,
+ * mask[i][j] != 0.  A row with no visible key outputs zeros.
+ *
+ * Sources: the QSA kernel page ("feat(qwen4): add the QSA sparse-attention
+ * kernel and its golden"), sections "Summary", "What changed" and "Semantics"
+ * (q|gate split, (1+w) norms, 64-of-256 partial RoPE from a shared table,
+ * q.k/sqrt(256), mask polarity, fp32 softmax over bf16 scores, bf16 weights,
+ * sigmoid gate before o_proj; geometry validated before sizing any buffer; an
+ * empty launch is a no-op) and the attention-tile page ("cuda: widen the
+ * attention query tile on sm_89 and sm_120"), review sections "Dispatch/guard"
+ * and "Kernel change" (extern "C" entry points that pre-validate and return
+ * errors with no silent fallback; prefix windows at an aligned q_base equal
+ * the full pass), and the shared-prefix page ("run shared prompt prefixes
+ * once": the rotary table is indexed by absolute position from the window
+ * start).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are device memory on the context's GPU, owned
+ *     by the caller; the library never frees them.  bf16 is IEEE bfloat16
+ *     stored as 16-bit words.  All tensors are dense, row-major, contiguous.
+ *   - Returns ATTN_OK (0) or one negative attn_status.  Arguments are fully
+ *     validated on the host before any device work; a refused call leaves the
+ *     device untouched.  There is no fallback path.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*,
+ *     NULL = the null stream); the caller synchronises.
+ *   - A context is bound to one device and owns a workspace sized at
+ *     creation, so calls never allocate.  A context is not thread safe and
+ *     its workspace is reused: use one context per stream.
+ */
+#ifndef GATEDATTN_H
+#define GATEDATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define ATTN_EXPORT __attribute__((visibility("default")))
+#else
+#define ATTN_EXPORT
+#endif
+
+#define ATTN_ABI_VERSION 1
+#define ATTN_HEAD_DIM 256
+#define ATTN_ROTARY_DIM 64
+#define ATTN_MAX_GROUP 16         /* query heads per KV head, 1..16          */
+#define ATTN_MAX_TOKENS 32768     /* cap on T (keys); max_tokens <= this     */
+#define ATTN_QBASE_ALIGN 128      /* q_base must be a multiple of this       */
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL_ARG = -1,   /* a required pointer is NULL                    */
+    ATTN_ERR_GEOMETRY = -2,   /* unsupported head counts / dims / eps          */
+    ATTN_ERR_RANGE = -3,      /* T, q_base, rows or n_pos out of range         */
+    ATTN_ERR_ALIGN = -4,      /* q_base not a multiple of 128, or a pointer
+                                 not 16-byte aligned                           */
+    ATTN_ERR_DEVICE = -5,     /* no device, bad index, or the current device
+                                 is not the context's device                   */
+    ATTN_ERR_NOMEM = -6,      /* workspace allocation failed (create only)     */
+    ATTN_ERR_LAUNCH = -7      /* a kernel launch or HIP runtime call failed    */
+} attn_status;
+
+typedef struct attn_ctx attn_ctx;     /* opaque */
+
+typedef struct {
+    int32_t n_q_heads;    /* Hq; a multiple of n_kv_heads                      */
+    int32_t n_kv_heads;   /* Hkv >= 1; G = Hq / Hkv in 1..ATTN_MAX_GROUP       */
+    int32_t head_dim;     /* must be ATTN_HEAD_DIM                             */
+    int32_t rotary_dim;   /* must be ATTN_ROTARY_DIM                           */
+    int32_t max_tokens;   /* 1..ATTN_MAX_TOKENS; sizes the workspace           */
+    float rms_eps;        /* finite, > 0 (1e-6 for the Qwen-style models)     */
+} attn_geometry;
+
+typedef struct {
+    const void *qg;        /* device bf16 [rows][Hq][2][D]: per head q then gate;
+                              rows = the query rows of the call             */
+    const void *k;         /* device bf16 [T][Hkv][D], raw (before norm/RoPE) */
+    const void *v;         /* device bf16 [T][Hkv][D]                         */
+    const void *q_norm_w;  /* device bf16 [D], applied as (1 + w)            */
+    const void *k_norm_w;  /* device bf16 [D], applied as (1 + w)            */
+    const float *cos_tab;  /* device fp32 [n_pos][rotary_dim/2]              */
+    const float *sin_tab;  /* device fp32 [n_pos][rotary_dim/2]              */
+    int32_t n_pos;         /* rows of the tables; must be >= T               */
+} attn_inputs;
+
+/* ABI version of the loaded library (ATTN_ABI_VERSION when it matches). */
+ATTN_EXPORT int attn_abi_version(void);
+
+/* Static, human-readable name of a status code; never NULL. */
+ATTN_EXPORT const char *attn_status_string(int status);
+
+/*
+ * Host-only check of one call, the same one every entry point runs first.
+ * kind: 0 = gated full pass (q_base must be 0), 1 = prefix window,
+ * 2 = masked (q_base must be 0, mask required).  T keys, query rows
+ * T - q_base.  Touches no device; usable without a GPU.
+ */
+ATTN_EXPORT int attn_validate(const attn_geometry *geom, const attn_inputs *in, int32_t T, int32_t q_base,
+                  int32_t kind, const void *mask, const void *out);
+
+/*
+ * Creates a context on `device` for `geom`, allocating its workspace (about
+ * 2 * Hkv * max_tokens * D * 2 bytes for prepared keys and values, plus
+ * max_tokens^2 / 8 bytes of packed mask bits).  The device becomes current
+ * on the calling thread.  On success *out holds the context; on failure
+ * *out is NULL and nothing stays allocated.
+ */
+ATTN_EXPORT int attn_ctx_create(const attn_geometry *geom, int device, attn_ctx **out);
+
+/* Frees the context and its workspace.  NULL is a no-op.  Not stream-ordered:
+   the caller must have synchronised work that uses the context. */
+ATTN_EXPORT void attn_ctx_destroy(attn_ctx *ctx);
+
+/*
+ * Dense causal full pass over S tokens: query rows = keys = positions 0..S-1.
+ * out: device bf16 [S][Hq * D] (head-major within a row: the o_proj input).
+ * S == 0 is a no-op returning ATTN_OK.
+ */
+ATTN_EXPORT int attn_prefill_gated(attn_ctx *ctx, const attn_inputs *in, int32_t S, void *out, void *stream);
+
+/*
+ * Prefix-continuation window: keys at positions 0..T-1, query rows at
+ * positions q_base..T-1 (qg holds T - q_base rows; out is device bf16
+ * [T - q_base][Hq * D]).  q_base must be a multiple of ATTN_QBASE_ALIGN and
+ * <= T; q_base == T is a no-op.  Each output row equals, bit for bit, the
+ * same row of attn_prefill_gated over all T tokens.
+ */
+ATTN_EXPORT int attn_prefill_prefix(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base,
+                        void *out, void *stream);
+
+/*
+ * Masked full pass over S tokens: key j is visible to row i iff j <= i and
+ * mask[i * S + j] != 0.  mask: device uint8 [S][S] (any alignment).
+ * Key tiles hidden for a whole block of rows are skipped.  With an
+ * all-visible mask the output equals attn_prefill_gated bit for bit.
+ */
+ATTN_EXPORT int attn_prefill_masked(attn_ctx *ctx, const attn_inputs *in, int32_t S, const uint8_t *mask,
+                        void *out, void *stream);
+
+/*
+ * Test hook: writes the prepared (normed, rotated) queries and keys the
+ * kernels use, in plain layouts.  qp_out: device bf16 [T - q_base][Hq][D]
+ * (may be NULL); kp_out: device bf16 [Hkv][T][D] (may be NULL).
+ */
+ATTN_EXPORT int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base,
+                       void *qp_out, void *kp_out, void *stream);
+
+/*
+ * Per-kernel timing with HIP events recorded on the call's stream around
+ * each launch.  enable != 0 creates an event pool (outside any timed
+ * region) and starts recording; 0 stops.  attn_ctx_read_timing waits for the
+ * recorded events, returns the summed duration (ms) and launch count of one
+ * kernel since the last read, and clears them.  kernel: ATTN_KERNEL_*.
+ */
+#define ATTN_KERNEL_KV_PROLOGUE 0
+#define ATTN_KERNEL_MASK_PACK 1
+#define ATTN_KERNEL_ATTENTION 2
+ATTN_EXPORT int attn_ctx_set_timing(attn_ctx *ctx, int enable);
+ATTN_EXPORT int attn_ctx_read_timing(attn_ctx *ctx, int kernel, double *total_ms, int32_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GATEDATTN_H */

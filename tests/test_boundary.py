@@ -1,0 +1,151 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+refuses bad calls with the documented status before touching any device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gatedattn.h")
+
+
+@pytest.fixture(scope="module")
+def ga():
+    import gated_gqa_causal_amd
+    return gated_gqa_causal_amd
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"ATTN_EXPORT\s+[\w\s\*]*?\b(attn_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["attn_ctx_create", "attn_prefill_gated", "attn_prefill_prefix", "attn_prefill_masked",
+              "attn_ctx_destroy", "attn_abi_version", "attn_status_string", "attn_validate"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(ga):
+    lib = ctypes.CDLL(ga.LIBPATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_header_constants_match_binding(ga):
+    src = open(HEADER).read()
+    for name in ["ATTN_ABI_VERSION", "ATTN_HEAD_DIM", "ATTN_ROTARY_DIM", "ATTN_MAX_GROUP",
+                 "ATTN_MAX_TOKENS", "ATTN_QBASE_ALIGN", "ATTN_KERNEL_KV_PROLOGUE",
+                 "ATTN_KERNEL_MASK_PACK", "ATTN_KERNEL_ATTENTION"]:
+        m = re.search(rf"#define {name}\s+(\d+)", src)
+        assert m and int(m.group(1)) == getattr(ga, name), name
+    for name in ["ATTN_OK", "ATTN_ERR_NULL_ARG", "ATTN_ERR_GEOMETRY", "ATTN_ERR_RANGE",
+                 "ATTN_ERR_ALIGN", "ATTN_ERR_DEVICE", "ATTN_ERR_NOMEM", "ATTN_ERR_LAUNCH"]:
+        m = re.search(rf"{name}\s*=\s*(-?\d+)", src)
+        assert m and int(m.group(1)) == getattr(ga, name), name
+    assert ga.attn_abi_version() == ga.ATTN_ABI_VERSION
+
+
+def test_status_strings(ga):
+    for s in range(-7, 1):
+        assert ga.attn_status_string(s) not in ("", "unknown status")
+    assert ga.attn_status_string(-99) == "unknown status"
+
+
+FAKE = 0x1000   # 16-byte aligned, never dereferenced: validation is host-only
+
+
+def _inputs(ga, n_pos=64, base=FAKE):
+    return ga.attn_inputs(base, base, base, base, base, base, base, n_pos)
+
+
+def _geom(ga, **kw):
+    g = dict(n_q_heads=24, n_kv_heads=2, max_tokens=256, rms_eps=1e-6)
+    g.update(kw)
+    return ga.geometry(**g)
+
+
+REFUSALS = [
+    # (geometry overrides, T, q_base, kind, mask, out, inputs overrides, expected)
+    (dict(n_q_heads=24, n_kv_heads=5), 64, 0, 0, None, FAKE, {}, "GEOMETRY"),
+    (dict(n_q_heads=34, n_kv_heads=2), 64, 0, 0, None, FAKE, {}, "GEOMETRY"),   # G = 17
+    (dict(rms_eps=0.0), 64, 0, 0, None, FAKE, {}, "GEOMETRY"),
+    (dict(rms_eps=float("nan")), 64, 0, 0, None, FAKE, {}, "GEOMETRY"),
+    (dict(max_tokens=0), 0, 0, 0, None, FAKE, {}, "RANGE"),
+    (dict(max_tokens=40000), 64, 0, 0, None, FAKE, {}, "RANGE"),
+    ({}, 257, 0, 0, None, FAKE, {}, "RANGE"),                      # T > max_tokens
+    ({}, -1, 0, 0, None, FAKE, {}, "RANGE"),
+    ({}, 200, 256, 1, None, FAKE, {}, "RANGE"),                    # q_base > T
+    ({}, 200, 64, 1, None, FAKE, {}, "ALIGN"),                     # q_base % 128
+    ({}, 200, 128, 0, None, FAKE, {}, "RANGE"),                    # q_base on the full pass
+    ({}, 200, 0, 3, None, FAKE, {}, "RANGE"),                      # bad kind
+    ({}, 64, 0, 0, None, FAKE, dict(n_pos=63), "RANGE"),           # short cos/sin table
+    ({}, 64, 0, 0, None, None, {}, "NULL_ARG"),                    # out
+    ({}, 64, 0, 2, None, FAKE, {}, "NULL_ARG"),                    # mask
+    ({}, 64, 0, 0, None, FAKE, dict(qg=0), "NULL_ARG"),
+    ({}, 64, 0, 0, None, FAKE, dict(k=0), "NULL_ARG"),
+    ({}, 64, 0, 0, None, FAKE, dict(v=0), "NULL_ARG"),
+    ({}, 64, 0, 0, None, FAKE, dict(q_norm_w=0), "NULL_ARG"),
+    ({}, 64, 0, 0, None, FAKE, dict(k_norm_w=0), "NULL_ARG"),
+    ({}, 64, 0, 0, None, FAKE, dict(cos_tab=0), "NULL_ARG"),
+    ({}, 64, 0, 0, None, FAKE, dict(sin_tab=0), "NULL_ARG"),
+    ({}, 64, 0, 0, None, FAKE + 8, {}, "ALIGN"),                   # out misaligned
+    ({}, 64, 0, 0, None, FAKE, dict(qg=FAKE + 2), "ALIGN"),
+]
+
+
+@pytest.mark.parametrize("case", REFUSALS, ids=lambda c: f"{c[-1]}")
+def test_refusals(ga, case):
+    geo, T, qb, kind, mask, out, inov, want = case
+    inp = _inputs(ga)
+    for k, v in inov.items():
+        setattr(inp, k, v)
+    rc = ga.attn_validate(_geom(ga, **geo), inp, T, qb, kind, mask, out)
+    assert rc == getattr(ga, "ATTN_ERR_" + want), (rc, ga.attn_status_string(rc))
+
+
+def test_null_geometry(ga):
+    rc = ga.lib.attn_validate(None, None, 0, 0, 0, None, None)
+    assert rc == ga.ATTN_ERR_NULL_ARG
+
+
+@pytest.mark.parametrize("T,qb,kind", [(0, 0, 0), (0, 0, 2), (256, 256, 1), (128, 128, 1)])
+def test_empty_launch_is_ok_without_pointers(ga, T, qb, kind):
+    # Zero query rows: a no-op, even with every pointer NULL (torch gives 0 for empty tensors).
+    assert ga.attn_validate(_geom(ga), None, T, qb, kind, None, None) == ga.ATTN_OK
+
+
+def test_valid_calls_pass(ga):
+    assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 0, 0, None, FAKE) == ga.ATTN_OK
+    assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 128, 1, None, FAKE) == ga.ATTN_OK
+    assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 0, 2, FAKE + 3, FAKE) == ga.ATTN_OK
+    for G in [1, 2, 3, 12, 16]:
+        assert ga.attn_validate(_geom(ga, n_q_heads=2 * G), _inputs(ga), 64, 0, 0, None, FAKE) == 0
+
+
+def test_null_context_refused(ga):
+    inp = _inputs(ga)
+    assert ga.attn_prefill_gated(None, inp, 64, FAKE, None) == ga.ATTN_ERR_NULL_ARG
+    assert ga.attn_prefill_prefix(None, inp, 64, 0, FAKE, None) == ga.ATTN_ERR_NULL_ARG
+    assert ga.attn_prefill_masked(None, inp, 64, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
+    assert ga.attn_debug_prepare(None, inp, 64, 0, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
+    assert ga.attn_ctx_set_timing(None, 1) == ga.ATTN_ERR_NULL_ARG
+    ga.attn_ctx_destroy(None)      # no-op
+
+
+def test_create_refuses_bad_geometry_before_device(ga):
+    with pytest.raises(ga.AttnError) as e:
+        ga.attn_ctx_create(_geom(ga, n_q_heads=5, n_kv_heads=2), 0)
+    assert e.value.status == ga.ATTN_ERR_GEOMETRY
+
+
+def test_create_without_a_device_fails_cleanly(ga):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(ga.AttnError) as e:
+        ga.attn_ctx_create(_geom(ga), 0)
+    assert e.value.status == ga.ATTN_ERR_DEVICE

@@ -1,0 +1,282 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Tolerance per bf16 output element: |gpu - oracle| <= 1e-2 + 1e-2 * |oracle|.
+Index and mask handling are checked bit-exactly (zero patterns, identities).
+The prologue (norm + RoPE) reproduces the oracle's arithmetic in the same
+order, so prepared queries and keys are compared bit for bit.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        if os.environ.get("ATTN_REQUIRE_GPU") == "1":
+            pytest.fail("ATTN_REQUIRE_GPU=1 but no GPU is visible")
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    _need_gpu()
+    import gated_gqa_causal_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+
+
+from gpu_util import DevProblem, bits_to_f32, gpu_out, make_ctx, parity_report, run, to_bits  # noqa: E402
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_rows(orc, p, rows, threads=8):
+    return orc.attention(p, rows=rows, threads=threads)
+
+
+def sample_rows(n_rows, k=48, seed=0):
+    """First/last rows, every tile-boundary neighbourhood in a stride, plus random rows."""
+    r = np.random.default_rng(seed)
+    s = set(range(min(4, n_rows))) | set(range(max(0, n_rows - 4), n_rows))
+    for b in range(0, n_rows, max(64, n_rows // 8)):
+        s |= {x for x in (b - 1, b, b + 31, b + 32, b + 63) if 0 <= x < n_rows}
+    s |= set(r.integers(0, n_rows, size=k).tolist())
+    return np.array(sorted(s), dtype=np.int32)
+
+
+# --------------------------------------------------------------------------
+# Prologue: bit-exact prepared queries and keys
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,Hq,Hkv,qb", [(64, 24, 2, 0), (200, 16, 4, 0), (300, 4, 2, 128), (33, 2, 1, 0)])
+def test_prologue_bit_exact(orc, T, Hq, Hkv, qb):
+    say(f"prologue T={T} Hq={Hq} Hkv={Hkv} q_base={qb}")
+    p = synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, q_base=qb, seed=T)
+    ctx = make_ctx(p)
+    dp = DevProblem(p)
+    qp, kp = ctx.debug_prepare(*dp.args(), q_base=qb)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(kp), orc.prepare_keys(p)), "prepared keys differ"
+    assert np.array_equal(to_bits(qp), orc.prepare_queries(p)), "prepared queries differ"
+    ctx.close()
+
+
+# --------------------------------------------------------------------------
+# Whole-output parity at sizes the oracle covers fully
+# --------------------------------------------------------------------------
+
+FULL_CASES = [
+    # name, make_problem kwargs
+    ("c0_tiny_s64", dict(T=64, n_q_heads=24, n_kv_heads=2, seed=0)),
+    ("s1", dict(T=1, n_q_heads=24, n_kv_heads=2, seed=5)),
+    ("s33_g1", dict(T=33, n_q_heads=2, n_kv_heads=2, seed=6)),
+    ("s200_ragged", dict(T=200, n_q_heads=24, n_kv_heads=2, seed=7)),
+    ("s333_g4", dict(T=333, n_q_heads=16, n_kv_heads=4, seed=8, gate_sigma=2.0)),
+    ("s130_g16", dict(T=130, n_q_heads=32, n_kv_heads=2, seed=9)),
+    ("s97_g6", dict(T=97, n_q_heads=6, n_kv_heads=1, seed=10)),
+    ("prefix_t300_qb128", dict(T=300, n_q_heads=24, n_kv_heads=2, q_base=128, seed=11)),
+    ("prefix_t513_qb256", dict(T=513, n_q_heads=8, n_kv_heads=2, q_base=256, seed=12)),
+    ("masked_s300_b40", dict(T=300, n_q_heads=24, n_kv_heads=2, seed=13, mask_budget=40)),
+    ("masked_s257_b7_g4", dict(T=257, n_q_heads=8, n_kv_heads=2, seed=14, mask_budget=7)),
+]
+
+
+@pytest.mark.parametrize("name,kw", FULL_CASES, ids=[c[0] for c in FULL_CASES])
+def test_parity_full(orc, name, kw):
+    say(f"parity_full {name} {kw}")
+    p = synth.make_problem(name=name, **kw)
+    got = gpu_out(p)
+    want = orc.attention(p, threads=8)
+    bad, frac = parity_report(got, want)
+    say(f"  bad={bad} of {got.size}  worst bound fraction={frac:.3f}  "
+        f"identical={np.mean(got == want):.4f}")
+    assert bad == 0
+
+
+# --------------------------------------------------------------------------
+# The five workloads at full size, in the benchmark's launch configuration,
+# on sampled rows the oracle computes one by one
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(synth.CONFIGS))
+def test_parity_configs_sampled(orc, name):
+    say(f"config {name}")
+    p = synth.config_problem(name)
+    got = gpu_out(p)
+    rows = sample_rows(p.rows, k=24 if p.T > 4096 else 64, seed=1)
+    want = oracle_rows(orc, p, rows)
+    bad, frac = parity_report(got[rows], want)
+    say(f"  rows={rows.size} bad={bad} worst bound fraction={frac:.3f} "
+        f"identical={np.mean(got[rows] == want):.4f}")
+    assert bad == 0
+    assert np.isfinite(bits_to_f32(got)).all()
+
+
+# --------------------------------------------------------------------------
+# Bit-exact identities on the GPU
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,qb,Hq,Hkv", [(700, 128, 24, 2), (2048, 1024, 16, 4), (8192, 1024, 24, 2)])
+def test_prefix_window_equals_full_pass(T, qb, Hq, Hkv):
+    say(f"prefix==full T={T} q_base={qb}")
+    full = synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=21)
+    win = synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, q_base=qb, seed=21)
+    ctx = make_ctx(full)
+    a = gpu_out(full, ctx)
+    b = gpu_out(win, ctx)
+    ctx.close()
+    assert np.array_equal(a[qb:], b)
+
+
+@pytest.mark.parametrize("T", [300, 2048])
+def test_all_visible_mask_equals_dense(T):
+    say(f"mask all visible T={T}")
+    p = synth.make_problem(T=T, seed=22)
+    pm = synth.Problem(**{**p.__dict__, "mask": np.full((T, T), 3, np.uint8)})
+    ctx = make_ctx(p)
+    assert np.array_equal(gpu_out(p, ctx), gpu_out(pm, ctx))
+    ctx.close()
+
+
+def test_gqa_copy_equals_grouped():
+    say("gqa copy")
+    p = synth.make_problem(T=260, n_q_heads=12, n_kv_heads=2, seed=23)
+    p12 = synth.Problem(**{**p.__dict__, "n_kv_heads": 12, "k": np.repeat(p.k, 6, axis=1),
+                           "v": np.repeat(p.v, 6, axis=1)})
+    assert np.array_equal(gpu_out(p), gpu_out(p12))
+
+
+def test_gate_closed_forms(orc):
+    """Gate logit 32 gives sigmoid 1 (out = ctx); logit 0 gives 1/2 (out = ctx / 2, exact)."""
+    say("gate closed forms")
+    p = synth.make_problem(T=150, n_q_heads=8, n_kv_heads=2, seed=24)
+    outs = {}
+    for gv in [0.0, 32.0]:
+        q = p.qg.copy()
+        q[:, :, 1, :] = synth.f32_to_bf16_bits(np.full(1, gv, np.float32))[0]
+        outs[gv] = bits_to_f32(gpu_out(synth.Problem(**{**p.__dict__, "qg": q})))
+    assert np.array_equal(outs[0.0] * 2, outs[32.0])
+    # and the saturated output is the ungated context within the tolerance
+    ctx_ref = orc.attention(p, want_ctx=True)["ctx"]
+    bad, _ = parity_report(synth.f32_to_bf16_bits(outs[32.0]), ctx_ref)
+    assert bad == 0
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_one_hot_v_zero_pattern(masked):
+    """One-hot V and a saturated gate expose each key's weight: hidden keys give
+    exactly +0, visible keys a positive weight; repeated over 256-key windows."""
+    T, Hq, Hkv = 512, 8, 2
+    say(f"one-hot masked={masked}")
+    p = synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=25,
+                           mask_budget=37 if masked else None)
+    v = np.zeros((T, Hkv, 256), np.float32)
+    for j in range(T):
+        v[j, :, j % 256] = 1.0
+    q = p.qg.copy()
+    q[:, :, 1, :] = synth.f32_to_bf16_bits(np.full(1, 32.0, np.float32))[0]
+    pp = synth.Problem(**{**p.__dict__, "qg": q, "v": synth.f32_to_bf16_bits(v)})
+    got = bits_to_f32(gpu_out(pp)).reshape(T, Hq, 256)
+    vis = np.tril(np.ones((T, T), bool))
+    if pp.mask is not None:
+        vis &= pp.mask != 0
+    for i in range(T):
+        # weights fold onto dims j % 256; rows < 256 see each dim at most once
+        if i >= 256:
+            break
+        want_nz = vis[i, :256]
+        g = got[i]
+        assert np.all(g[:, ~want_nz] == 0.0), f"row {i}: hidden key leaked"
+        assert np.all(g[:, want_nz] > 0.0), f"row {i}: visible key dropped"
+        assert not np.signbit(g).any()
+    # keys 256..511 fold onto the same dims; rows >= 256: dim d carries keys d and d+256
+    for i in range(256, T, 17):
+        both = vis[i, :256] | vis[i, 256:512]
+        g = got[i]
+        assert np.all(g[:, ~both] == 0.0) and np.all(g[:, both] > 0.0), f"row {i}"
+
+
+def test_row_sums_at_max_tokens():
+    """With V = 1 the context is the sum of the row's weights: 1 within bf16 rounding,
+    for every row up to the token cap (the walk covers every visible key)."""
+    import gated_gqa_causal_amd as ga
+    T = 8192
+    say("row sums at 8192")
+    p = synth.make_problem(T=T, n_q_heads=4, n_kv_heads=1, seed=26)
+    q = p.qg.copy()
+    q[:, :, 1, :] = synth.f32_to_bf16_bits(np.full(1, 32.0, np.float32))[0]
+    pp = synth.Problem(**{**p.__dict__, "qg": q, "v": np.full_like(p.v, 0x3F80)})
+    ctx = ga.Context(4, 1, T)
+    got = bits_to_f32(gpu_out(pp, ctx))
+    ctx.close()
+    assert np.all(np.abs(got - 1.0) <= 2e-3 * 4 + 2 ** -8), np.abs(got - 1).max()
+
+
+# --------------------------------------------------------------------------
+# Negative controls: the gate is not vacuous
+# --------------------------------------------------------------------------
+
+def test_control_kv_head_swap_fails(orc):
+    say("control: kv swap")
+    p = synth.make_problem(T=200, n_q_heads=24, n_kv_heads=2, seed=27)
+    swapped = synth.Problem(**{**p.__dict__, "k": p.k[:, ::-1].copy(), "v": p.v[:, ::-1].copy()})
+    bad, _ = parity_report(gpu_out(swapped), orc.attention(p, threads=8))
+    assert bad > 0
+
+
+def test_control_causal_for_mask_fails(orc):
+    say("control: causal in place of the mask")
+    p = synth.make_problem(T=600, n_q_heads=8, n_kv_heads=2, seed=28, mask_budget=64)
+    dense = synth.Problem(**{**p.__dict__, "mask": None})
+    rows = np.arange(300, 600, 7, dtype=np.int32)
+    bad, _ = parity_report(gpu_out(dense)[rows], orc.attention(p, rows=rows, threads=8))
+    assert bad > 0
+
+
+# --------------------------------------------------------------------------
+# Edges of the boundary on a real device
+# --------------------------------------------------------------------------
+
+def test_empty_and_refusals_on_device():
+    import gated_gqa_causal_amd as ga
+    say("edges")
+    p = synth.make_problem(T=256, n_q_heads=4, n_kv_heads=2, seed=29)
+    ctx = make_ctx(p)
+    dp = DevProblem(p)
+    inp = ctx.inputs(*dp.args(), 256, 256)
+    out = torch.empty((256, 4 * 256), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert ga.attn_prefill_gated(ctx.handle, inp, 0, None, s) == ga.ATTN_OK
+    assert ga.attn_prefill_prefix(ctx.handle, inp, 256, 256, None, s) == ga.ATTN_OK
+    assert ga.attn_prefill_prefix(ctx.handle, inp, 256, 64, out.data_ptr(), s) == ga.ATTN_ERR_ALIGN
+    assert ga.attn_prefill_gated(ctx.handle, inp, 257, out.data_ptr(), s) == ga.ATTN_ERR_RANGE
+    assert ga.attn_prefill_masked(ctx.handle, inp, 256, None, out.data_ptr(), s) == ga.ATTN_ERR_NULL_ARG
+    torch.cuda.synchronize()
+    ctx.close()
+
+
+def test_timing_hooks():
+    import gated_gqa_causal_amd as ga
+    p = synth.make_problem(T=512, n_q_heads=8, n_kv_heads=2, seed=30)
+    ctx = make_ctx(p)
+    dp = DevProblem(p)
+    ctx.set_timing(True)
+    for _ in range(3):
+        run(ctx, dp)
+    ms, n = ctx.read_timing(ga.ATTN_KERNEL_ATTENTION)
+    assert n == 3 and ms > 0
+    ms, n = ctx.read_timing(ga.ATTN_KERNEL_KV_PROLOGUE)
+    assert n == 3 and ms > 0
+    ctx.set_timing(False)
+    ctx.close()
