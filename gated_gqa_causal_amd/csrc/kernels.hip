@@ -373,16 +373,121 @@ __device__ __forceinline__ void issue_tile_loads(const AttnParams &p, TileBuf *b
     }
 }
 
-__device__ __forceinline__ bf16x8 lds_k_frag(const TileBuf *buf, int i, int chunk)
+// Sum and max of a value with its partner lane (lane ^ 32).  v_permlane32_swap
+// exchanges the upper half of one register with the lower half of the other;
+// fed the same value twice, each lane ends with its own value in one result
+// and the partner's in the other, whichever way round.
+__device__ __forceinline__ float pair_sum(float x)
 {
-    const int slot = chunk ^ (i & 7);
-    return *reinterpret_cast<const bf16x8 *>((const char *)buf->k + i * 512 + slot * 16);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ bf16x8 lds_v_frag(const TileBuf *buf, int d, int chunk)
+// Per-lane LDS byte offsets of the MFMA operand fragments (swizzles folded in).
+// K fragment for dims 16c + 8hh.. (c = 4a + b) of key row j:
+//   j*512 + 16*((2b + hh) ^ (j & 7)) + 128*a
+// V^T fragment for dim row 32db + j, keys 16kc + 8hh.. of the tile:
+//   (32db + j)*64 + 16*((2kc + hh) ^ ((j >> 1) & 3))  (= voff[kc] + 2048*db)
+struct FragOffsets {
+    int k[4];
+    int v[2];
+};
+
+__device__ __forceinline__ FragOffsets frag_offsets(int j, int hh)
 {
-    const int slot = chunk ^ ((d >> 1) & 3);
-    return *reinterpret_cast<const bf16x8 *>((const char *)buf->v + d * 64 + slot * 16);
+    FragOffsets f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        f.k[b] = j * 512 + 16 * ((2 * b + hh) ^ (j & 7));
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+        f.v[kc] = j * 64 + 16 * ((2 * kc + hh) ^ ((j >> 1) & 3));
+    return f;
+}
+
+// One 32-key tile for one wave (32 query rows of one head).
+//   pred: apply `vis` (bit kk = key kk of the tile is visible to this lane's
+//   query); wave-uniform, true only on the diagonal tile or in the masked path.
+template <bool MASKED>
+__device__ __forceinline__ void attend_tile(const char *kb, const char *vb, const FragOffsets &fo,
+                                            const uint4 (&qf)[16], f32x16 (&o)[8], float &m, float &l,
+                                            bool pred, uint32_t vis, int hh)
+{
+    // S^T = K . Q^T: lane holds query j, keys 8g + 4hh + r (e = 4g + r).
+    f32x16 s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        s[e] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        // Keep at most four fragments in flight (the Q fragments and the context
+        // accumulators hold 192 of the 256 registers).
+        if ((c & 3) == 0)
+            __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + fo.k[c & 3] + 128 * (c >> 2));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8, qf[c]), s, 0, 0, 0);
+    }
+
+    float x[16];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const uint32_t w = pack2(s[2 * q], s[2 * q + 1]);     // bf16(q . k)
+        x[2 * q] = lo_f(w);
+        x[2 * q + 1] = hi_f(w);
+    }
+    if (pred) {
+        // This lane's keys are 8g + 4hh + r: shift the lane's half into place once.
+        const uint32_t vh = vis >> (4 * hh);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            x[e] = ((vh >> (8 * (e >> 2) + (e & 3))) & 1u) ? x[e] : -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(x[0], x[1]), x[2]);
+#pragma unroll
+    for (int e = 3; e < 16; e += 2)
+        mt = fmaxf(fmaxf(mt, x[e]), x[e + 1 < 16 ? e + 1 : e]);
+    mt = pair_max(mt);
+    const float mo = m;
+    const float mn = (mt > mo + TAU_X) ? mt : mo;
+    const float alpha = (mn == mo) ? 1.0f : __builtin_amdgcn_exp2f((mo - mn) * SCALE_LOG2);
+    m = mn;
+    const float base = (mn == -INFINITY) ? 0.0f : mn * SCALE_LOG2;
+    float ls = 0.0f;
+    uint32_t pk[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * q], SCALE_LOG2, -base));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * q + 1], SCALE_LOG2, -base));
+        ls += p0;
+        ls += p1;
+        pk[q] = pack2(p0, p1);
+    }
+    l = l * alpha + ls;
+    if (__builtin_expect(__any(alpha != 1.0f), 0)) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                o[db][e] *= alpha;
+    }
+
+    // O^T += V^T . P^T; P chunk kc = keys 16kc .. 16kc+15 = pk[4kc .. 4kc+3].
+    const uint4 p0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    const uint4 p1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+        if ((db & 1) == 0)
+            __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 v0 = *reinterpret_cast<const bf16x8 *>(vb + fo.v[0] + 2048 * db);
+        const bf16x8 v1 = *reinterpret_cast<const bf16x8 *>(vb + fo.v[1] + 2048 * db);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, __builtin_bit_cast(bf16x8, p0), o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, __builtin_bit_cast(bf16x8, p1), o[db], 0, 0, 0);
+    }
 }
 
 template <bool MASKED>
@@ -407,14 +512,14 @@ void attn_fwd(AttnParams p)
 
     const int P0 = p.q_base + rb * QW;               // workgroup's first absolute position
     const int ntiles = min(P0 + QW - 1, p.T - 1) / KT + 1;
-    const int Pw = p.q_base + r0;                    // wave's first absolute position
-    const int wave_tiles = min(Pw + QR - 1, p.T - 1) / KT + 1;   // tiles this wave needs
-    const int diag = Pw / KT;                        // tiles >= diag need the causal test
+    const int Pw = p.q_base + r0;                    // wave's first absolute position (multiple of 32)
+    const int diag = Pw / KT;                        // the wave's one diagonal tile (its last)
     const int pos = Pw + j;
 
     uint4 qf[16];
     if (active)
         load_queries(p, r0, h, lane, qf);
+    const FragOffsets fo = frag_offsets(j, hh);
 
     f32x16 o[8];
 #pragma unroll
@@ -436,88 +541,33 @@ void attn_fwd(AttnParams p)
     // issued before that tile's K/V loads, so no wait lands mid-tile.
     const bool row_ok = active && (r0 + j) < p.S;
     auto load_bits = [&](int tile) -> uint32_t {
-        return (MASKED && row_ok && tile < wave_tiles) ? p.bits[(size_t)(r0 + j) * p.W + tile] : 0u;
+        return (MASKED && row_ok && tile <= diag) ? p.bits[(size_t)(r0 + j) * p.W + tile] : 0u;
     };
 
+    // Causal visibility inside the wave's diagonal tile (keys Pw..Pw+31 against
+    // rows Pw..Pw+31): bit kk set iff kk <= j.
+    const uint32_t diag_vis = (j == 31) ? 0xffffffffu : ((2u << j) - 1u);
+
     int t = MASKED ? next_tile(-1) : 0;
-    int cur = 0;
     uint32_t bits_cur = MASKED ? load_bits(t) : 0u;
     if (t < ntiles)
         issue_tile_loads(p, &bufs[0], kvh, t, wave, lane);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
+    int cur = 0;
     while (t < ntiles) {
         const int tn = next_tile(t);
         const uint32_t bits_next = MASKED ? load_bits(tn) : 0u;
         if (tn < ntiles)
             issue_tile_loads(p, &bufs[cur ^ 1], kvh, tn, wave, lane);
-        const TileBuf *buf = &bufs[cur];
-
-        if (active && t < wave_tiles) {
-            // S^T = K . Q^T: lane holds query j, keys 8g + 4hh + r (e = 4g + r).
-            f32x16 s;
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                s[e] = 0.0f;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const bf16x8 kf = lds_k_frag(buf, j, 2 * c + hh);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8, qf[c]), s, 0, 0, 0);
-            }
-
-            const bool need_pred = MASKED || t >= diag;
-            const uint32_t bits = MASKED ? bits_cur : 0xffffffffu;
-            float x[16];
-            float mt = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int kk = 8 * (e >> 2) + 4 * hh + (e & 3);      // key within the tile
-                float xv = rbf(s[e]);
-                if (need_pred) {
-                    const bool vis = (t * KT + kk <= pos) && ((bits >> kk) & 1u);
-                    xv = vis ? xv : -INFINITY;
-                }
-                x[e] = xv;
-                mt = fmaxf(mt, xv);
-            }
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float mo = m;
-            const float mn = (mt > mo + TAU_X) ? mt : mo;
-            const float alpha = (mn == mo) ? 1.0f : __builtin_amdgcn_exp2f((mo - mn) * SCALE_LOG2);
-            m = mn;
-            const float base = (mn == -INFINITY) ? 0.0f : mn * SCALE_LOG2;
-            float ls = 0.0f;
-            uint32_t pk[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * q], SCALE_LOG2, -base));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * q + 1], SCALE_LOG2, -base));
-                ls += p0;
-                ls += p1;
-                pk[q] = pack2(p0, p1);
-            }
-            l = l * alpha + ls;
-            if (__any(alpha != 1.0f)) {
-#pragma unroll
-                for (int db = 0; db < 8; ++db)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        o[db][e] *= alpha;
-            }
-
-            // O^T += V^T . P^T; P chunk kc = keys 16kc .. 16kc+15 = pk[4kc .. 4kc+3].
-            const uint4 p0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-            const uint4 p1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-#pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const bf16x8 v0 = lds_v_frag(buf, 32 * db + j, hh);
-                const bf16x8 v1 = lds_v_frag(buf, 32 * db + j, 2 + hh);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, __builtin_bit_cast(bf16x8, p0), o[db], 0, 0, 0);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, __builtin_bit_cast(bf16x8, p1), o[db], 0, 0, 0);
-            }
+        if (active && t <= diag) {
+            const char *kb = reinterpret_cast<const char *>(bufs[cur].k);
+            const char *vb = reinterpret_cast<const char *>(bufs[cur].v);
+            const bool on_diag = t == diag;
+            const uint32_t vis = MASKED ? (on_diag ? (bits_cur & diag_vis) : bits_cur) : diag_vis;
+            attend_tile<MASKED>(kb, vb, fo, qf, o, m, l, MASKED || on_diag, vis, hh);
         }
-
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         cur ^= 1;
@@ -529,7 +579,7 @@ void attn_fwd(AttnParams p)
         return;
 
     // Epilogue: ctx = bf16(O / l), out = bf16(ctx * bf16(sigmoid(gate))).
-    const float lt = l + __shfl_xor(l, 32);
+    const float lt = pair_sum(l);
     const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
     const int row = r0 + j;
     if (row >= p.S)
