@@ -24,8 +24,8 @@ struct attn_ctx {
     attn_geometry geom{};
     int tpad = 0;                  // max_tokens rounded up to 64
     int mask_words = 0;            // 32-key words per mask row at max_tokens
-    uint16_t *kp = nullptr;        // [Hkv][tpad][256]
-    uint16_t *vt = nullptr;        // [Hkv][tpad/32][256][32]
+    uint16_t *kp = nullptr;        // prepared keys, [Hkv][tpad/32] tiles of 32 x 256
+    uint16_t *vt = nullptr;        // transposed values, [Hkv][tpad/32] tiles of 256 x 32
     uint32_t *mask_bits = nullptr; // [max_tokens][mask_words]
     uint8_t *tile_vis = nullptr;   // [ceil(max_tokens/64)][mask_words]
     // timing
@@ -332,9 +332,8 @@ int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t 
         fill_kv_params(kvp, ctx, in, T);
         if (ga::launch_kv_prologue(kvp, (T + ga::kKeysPerTile - 1) / ga::kKeysPerTile, s) != hipSuccess)
             return ATTN_ERR_LAUNCH;
-        const size_t row = (size_t)ATTN_HEAD_DIM * 2;
-        if (hipMemcpy2DAsync(kp_out, (size_t)T * row, ctx->kp, (size_t)ctx->tpad * row, (size_t)T * row,
-                             ctx->geom.n_kv_heads, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        if (ga::launch_kp_unpack(ctx->kp, ctx->tpad, T, ctx->geom.n_kv_heads, static_cast<uint16_t *>(kp_out),
+                                 s) != hipSuccess)
             return ATTN_ERR_LAUNCH;
     }
     if (qp_out) {

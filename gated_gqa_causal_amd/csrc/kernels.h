@@ -13,8 +13,8 @@ struct KvPrologueParams {
     const uint16_t *wk;       // [256]
     const float *cos_tab;     // [n_pos][32]
     const float *sin_tab;     // [n_pos][32]
-    uint16_t *kp;             // [Hkv][Tpad][256]
-    uint16_t *vt;             // [Hkv][Tpad/32][256][32]
+    uint16_t *kp;             // [Hkv][Tpad/32] tiles of 32 keys, chunk-major
+    uint16_t *vt;             // [Hkv][Tpad/32] tiles of V^T, chunk-major
     int T, Hkv, Tpad;
     float eps;
 };
@@ -29,8 +29,8 @@ struct MaskPackParams {
 
 struct AttnParams {
     const uint16_t *qg;       // [S][Hq][2][256]
-    const uint16_t *kp;       // [Hkv][Tpad][256]
-    const uint16_t *vt;       // [Hkv][Tpad/32][256][32]
+    const uint16_t *kp;       // [Hkv][Tpad/32] tiles of 32 keys, chunk-major
+    const uint16_t *vt;       // [Hkv][Tpad/32] tiles of V^T, chunk-major
     const uint16_t *wq;       // [256]
     const float *cos_tab;     // [n_pos][32]
     const float *sin_tab;     // [n_pos][32]
@@ -49,6 +49,7 @@ constexpr int kHeadsPerBlock = 4;
 hipError_t launch_kv_prologue(const KvPrologueParams &p, int ntiles, hipStream_t stream);
 hipError_t launch_mask_pack(const MaskPackParams &p, int nrb, hipStream_t stream);
 hipError_t launch_attention(const AttnParams &p, bool masked, hipStream_t stream);
+hipError_t launch_kp_unpack(const uint16_t *kp, int Tpad, int T, int Hkv, uint16_t *out, hipStream_t stream);
 hipError_t launch_q_prologue_debug(const AttnParams &p, uint16_t *qp, hipStream_t stream);
 
 }  // namespace ga

@@ -78,9 +78,14 @@ __device__ __forceinline__ float word_f(const uint4 &u, int t)
 
 // ---------------------------------------------------------------------------
 // K/V prologue.  grid (Tpad/32, Hkv), 256 threads.
-// Kp [Hkv][Tpad][D]: prepared keys, natural key order, zero rows past T.
-// Vt [Hkv][Tpad/32][D][32]: per 32-key tile, V transposed (dims x keys), keys
-// permuted inside each 16-group as [0..3, 8..11, 4..7, 12..15].
+// Both outputs are stored as 16 KB tiles of 32 keys in the order the attention
+// kernel's MFMA operand reads want them in LDS ("chunk-major": the 16-byte
+// chunk index outermost), so a tile moves to LDS as one contiguous copy and
+// every 16-lane group of an operand read touches 256 contiguous LDS bytes.
+// Kp tile (key r, dim d): 16-byte piece (d / 8) * 32 + r, element d % 8.
+// Vt tile (dim d, key slot s): piece (s / 8) * 256 + d, element s % 8, where
+// slot s holds key [0..3, 8..11, 4..7, 12..15] of each 16 (V transposed, keys
+// permuted to match the score accumulator layout).  Keys past T are zero.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int vt_key_of_pos(int pos)
 {
@@ -148,25 +153,37 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
     }
     __syncthreads();
 
+    const size_t tile_off = ((size_t)c * (p.Tpad / KT) + tile) * (size_t)(KT * D);
+    uint4 *kdst = reinterpret_cast<uint4 *>(p.kp + tile_off);
     for (int it = 0; it < 4; ++it) {
-        const int idx = it * 256 + tid, r = idx >> 5, ch = idx & 31;
-        *reinterpret_cast<uint4 *>(p.kp + ((size_t)c * p.Tpad + t0 + r) * D + ch * 8) =
-            *reinterpret_cast<const uint4 *>(&ks[r][ch * 8]);
+        const int piece = it * 256 + tid, ch = piece >> 5, r = piece & 31;
+        kdst[piece] = *reinterpret_cast<const uint4 *>(&ks[r][ch * 8]);
     }
 
-    {
+    uint4 *vdst = reinterpret_cast<uint4 *>(p.vt + tile_off);
+    for (int q = 0; q < 4; ++q) {
         const int d = tid;
-        uint32_t w[16];
+        uint32_t w[4];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const uint32_t a = vs[vt_key_of_pos(2 * q)][d];
-            const uint32_t b = vs[vt_key_of_pos(2 * q + 1)][d];
-            w[q] = a | (b << 16);
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t a = vs[vt_key_of_pos(8 * q + 2 * e)][d];
+            const uint32_t b = vs[vt_key_of_pos(8 * q + 2 * e + 1)][d];
+            w[e] = a | (b << 16);
         }
-        uint4 *dst = reinterpret_cast<uint4 *>(p.vt + (((size_t)c * (p.Tpad / KT) + tile) * D + d) * KT);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            dst[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+        vdst[q * 256 + d] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// Debug: prepared keys from the tiled layout back to plain [Hkv][T][D].
+// grid (ceil(T/32), Hkv), 256 threads.
+__global__ __launch_bounds__(256) void kp_unpack(const uint16_t *kp, int Tpad, int T, uint16_t *out)
+{
+    const int tile = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+    const uint4 *src = reinterpret_cast<const uint4 *>(kp + ((size_t)c * (Tpad / KT) + tile) * (size_t)(KT * D));
+    for (int it = 0; it < 4; ++it) {
+        const int piece = it * 256 + tid, ch = piece >> 5, r = piece & 31, key = tile * KT + r;
+        if (key < T)
+            *reinterpret_cast<uint4 *>(out + ((size_t)c * T + key) * D + ch * 8) = src[piece];
     }
 }
 
@@ -338,10 +355,8 @@ constexpr int AW = 8;                  // waves per attention workgroup
 constexpr int ATHREADS = 64 * AW;
 constexpr int QR = 32;                 // query rows per wave
 
-// K tile in LDS: 32 key rows x 512 B; 16-byte slot s of row i holds the row's
-// global chunk s ^ (i & 7) (conflict-free b128 reads down a column).
-// V^T tile in LDS: 256 dim rows x 64 B; slot q of row d holds global chunk
-// q ^ ((d >> 1) & 3).
+// A tile buffer holds the chunk-major K and V^T tiles exactly as stored in
+// HBM (see kv_prologue).
 struct __align__(16) TileBuf {
     uint16_t k[KT * D];
     uint16_t v[D * KT];
@@ -349,26 +364,19 @@ struct __align__(16) TileBuf {
 
 // Each of the 8 waves moves 4 KB of the 32 KB tile straight from global
 // memory into LDS (global_load_lds_dwordx4: lane L of an instruction writes
-// the 16 bytes at LDS base + 16 L).
+// the 16 bytes at LDS base + 16 L, from consecutive global addresses).
 __device__ __forceinline__ void issue_tile_loads(const AttnParams &p, TileBuf *buf, int kvh, int tile,
                                                  int wave, int lane)
 {
-    const uint16_t *ksrc = p.kp + ((size_t)kvh * p.Tpad + (size_t)tile * KT) * D;
-    const uint16_t *vsrc = p.vt + ((size_t)kvh * (p.Tpad / KT) + tile) * (size_t)(D * KT);
+    const size_t tile_off = ((size_t)kvh * (p.Tpad / KT) + tile) * (size_t)(KT * D);
+    const uint16_t *ksrc = p.kp + tile_off;
+    const uint16_t *vsrc = p.vt + tile_off;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int n = wave * 2 + i;                    // K rows 2n, 2n+1
-        const int row = 2 * n + (lane >> 5), slot = lane & 31;
-        const int chunk = slot ^ (row & 7);
-        __builtin_amdgcn_global_load_lds(ksrc + row * D + chunk * 8,
+        const int n = wave * 2 + i;
+        __builtin_amdgcn_global_load_lds(ksrc + n * 512 + lane * 8,
                                          (lds_void *)((char *)buf->k + n * 1024), 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int n = wave * 2 + i;                    // V^T dim rows 16n .. 16n+15
-        const int d = 16 * n + (lane >> 2), slot = lane & 3;
-        const int chunk = slot ^ ((d >> 1) & 3);
-        __builtin_amdgcn_global_load_lds(vsrc + d * KT + chunk * 8,
+        __builtin_amdgcn_global_load_lds(vsrc + n * 512 + lane * 8,
                                          (lds_void *)((char *)buf->v + n * 1024), 16, 0, 0);
     }
 }
@@ -388,26 +396,19 @@ __device__ __forceinline__ float pair_max(float x)
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Per-lane LDS byte offsets of the MFMA operand fragments (swizzles folded in).
-// K fragment for dims 16c + 8hh.. (c = 4a + b) of key row j:
-//   j*512 + 16*((2b + hh) ^ (j & 7)) + 128*a
-// V^T fragment for dim row 32db + j, keys 16kc + 8hh.. of the tile:
-//   (32db + j)*64 + 16*((2kc + hh) ^ ((j >> 1) & 3))  (= voff[kc] + 2048*db)
+// Per-lane LDS byte offsets of the MFMA operand fragments.
+// K fragment (dims 16c + 8hh .. +7 of key row j): piece (2c + hh) * 32 + j
+//   -> hh * 512 + j * 16 + 1024 * c.
+// V^T fragment (dim row 32db + j, key slots 16kc + 8hh .. +7):
+//   piece (2kc + hh) * 256 + 32db + j -> hh * 4096 + j * 16 + 8192 * kc + 512 * db.
 struct FragOffsets {
-    int k[4];
-    int v[2];
+    int k;
+    int v;
 };
 
 __device__ __forceinline__ FragOffsets frag_offsets(int j, int hh)
 {
-    FragOffsets f;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-        f.k[b] = j * 512 + 16 * ((2 * b + hh) ^ (j & 7));
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-        f.v[kc] = j * 64 + 16 * ((2 * kc + hh) ^ ((j >> 1) & 3));
-    return f;
+    return FragOffsets{hh * 512 + j * 16, hh * 4096 + j * 16};
 }
 
 // One 32-key tile for one wave (32 query rows of one head).
@@ -429,7 +430,7 @@ __device__ __forceinline__ void attend_tile(const char *kb, const char *vb, cons
         // accumulators hold 192 of the 256 registers).
         if ((c & 3) == 0)
             __builtin_amdgcn_sched_barrier(0);
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + fo.k[c & 3] + 128 * (c >> 2));
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + fo.k + 1024 * c);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8, qf[c]), s, 0, 0, 0);
     }
 
@@ -483,8 +484,8 @@ __device__ __forceinline__ void attend_tile(const char *kb, const char *vb, cons
     for (int db = 0; db < 8; ++db) {
         if ((db & 1) == 0)
             __builtin_amdgcn_sched_barrier(0);
-        const bf16x8 v0 = *reinterpret_cast<const bf16x8 *>(vb + fo.v[0] + 2048 * db);
-        const bf16x8 v1 = *reinterpret_cast<const bf16x8 *>(vb + fo.v[1] + 2048 * db);
+        const bf16x8 v0 = *reinterpret_cast<const bf16x8 *>(vb + fo.v + 512 * db);
+        const bf16x8 v1 = *reinterpret_cast<const bf16x8 *>(vb + fo.v + 8192 + 512 * db);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, __builtin_bit_cast(bf16x8, p0), o[db], 0, 0, 0);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, __builtin_bit_cast(bf16x8, p1), o[db], 0, 0, 0);
     }
@@ -627,6 +628,12 @@ hipError_t launch_attention(const AttnParams &p, bool masked, hipStream_t stream
         hipLaunchKernelGGL(attn_fwd<true>, dim3(nblocks), dim3(ATHREADS), 0, stream, p);
     else
         hipLaunchKernelGGL(attn_fwd<false>, dim3(nblocks), dim3(ATHREADS), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_kp_unpack(const uint16_t *kp, int Tpad, int T, int Hkv, uint16_t *out, hipStream_t stream)
+{
+    hipLaunchKernelGGL(kp_unpack, dim3((T + KT - 1) / KT, Hkv), dim3(256), 0, stream, kp, Tpad, T, out);
     return hipGetLastError();
 }
 
