@@ -354,32 +354,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int AW = 8;                  // waves per attention workgroup
 constexpr int ATHREADS = 64 * AW;
 constexpr int QR = 32;                 // query rows per wave
-
-// A tile buffer holds the chunk-major K and V^T tiles exactly as stored in
-// HBM (see kv_prologue).
-struct __align__(16) TileBuf {
-    uint16_t k[KT * D];
-    uint16_t v[D * KT];
-};
-
-// Each of the 8 waves moves 4 KB of the 32 KB tile straight from global
-// memory into LDS (global_load_lds_dwordx4: lane L of an instruction writes
-// the 16 bytes at LDS base + 16 L, from consecutive global addresses).
-__device__ __forceinline__ void issue_tile_loads(const AttnParams &p, TileBuf *buf, int kvh, int tile,
-                                                 int wave, int lane)
-{
-    const size_t tile_off = ((size_t)kvh * (p.Tpad / KT) + tile) * (size_t)(KT * D);
-    const uint16_t *ksrc = p.kp + tile_off;
-    const uint16_t *vsrc = p.vt + tile_off;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int n = wave * 2 + i;
-        __builtin_amdgcn_global_load_lds(ksrc + n * 512 + lane * 8,
-                                         (lds_void *)((char *)buf->k + n * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vsrc + n * 512 + lane * 8,
-                                         (lds_void *)((char *)buf->v + n * 1024), 16, 0, 0);
-    }
-}
+constexpr int MAX_TILES = 32768 / KT;  // tile list capacity (token cap / 32)
 
 // Sum and max of a value with its partner lane (lane ^ 32).  v_permlane32_swap
 // exchanges the upper half of one register with the lower half of the other;
@@ -411,29 +386,40 @@ __device__ __forceinline__ FragOffsets frag_offsets(int j, int hh)
     return FragOffsets{hh * 512 + j * 16, hh * 4096 + j * 16};
 }
 
-// One 32-key tile for one wave (32 query rows of one head).
-//   pred: apply `vis` (bit kk = key kk of the tile is visible to this lane's
-//   query); wave-uniform, true only on the diagonal tile or in the masked path.
-template <bool MASKED>
-__device__ __forceinline__ void attend_tile(const char *kb, const char *vb, const FragOffsets &fo,
-                                            const uint4 (&qf)[16], f32x16 (&o)[8], float &m, float &l,
-                                            bool pred, uint32_t vis, int hh)
+// S^T = K . Q^T for one tile: lane holds query j, keys 8g + 4hh + r (e = 4g + r).
+__device__ __forceinline__ void tile_scores(const char *kb, const FragOffsets &fo, const uint4 (&qf)[16],
+                                            f32x16 &s)
 {
-    // S^T = K . Q^T: lane holds query j, keys 8g + 4hh + r (e = 4g + r).
-    f32x16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e)
         s[e] = 0.0f;
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-        // Keep at most four fragments in flight (the Q fragments and the context
+        // At most four fragments in flight (the Q fragments and the context
         // accumulators hold 192 of the 256 registers).
         if ((c & 3) == 0)
             __builtin_amdgcn_sched_barrier(0);
         const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + fo.k + 1024 * c);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8, qf[c]), s, 0, 0, 0);
     }
+}
 
+// Scores of hidden keys become -inf (they round to bf16 -inf and weigh exactly
+// 0).  vis bit kk = key kk of the tile is visible to this lane's query; this
+// lane holds keys 8g + 4hh + r.
+__device__ __forceinline__ void hide_scores(f32x16 &s, uint32_t vis, int hh)
+{
+    const uint32_t vh = vis >> (4 * hh);
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        s[e] = ((vh >> (8 * (e >> 2) + (e & 3))) & 1u) ? s[e] : -INFINITY;
+}
+
+// Online softmax of one tile's scores -> bf16 weights pk (relative to the
+// running max), updating (m, l) and rescaling O when the max moves.
+__device__ __forceinline__ void tile_softmax(const f32x16 &s, float &m, float &l, uint32_t (&pk)[8],
+                                             f32x16 (&o)[8])
+{
     float x[16];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -441,17 +427,11 @@ __device__ __forceinline__ void attend_tile(const char *kb, const char *vb, cons
         x[2 * q] = lo_f(w);
         x[2 * q + 1] = hi_f(w);
     }
-    if (pred) {
-        // This lane's keys are 8g + 4hh + r: shift the lane's half into place once.
-        const uint32_t vh = vis >> (4 * hh);
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            x[e] = ((vh >> (8 * (e >> 2) + (e & 3))) & 1u) ? x[e] : -INFINITY;
-    }
     float mt = fmaxf(fmaxf(x[0], x[1]), x[2]);
 #pragma unroll
-    for (int e = 3; e < 16; e += 2)
-        mt = fmaxf(fmaxf(mt, x[e]), x[e + 1 < 16 ? e + 1 : e]);
+    for (int e = 3; e < 15; e += 2)
+        mt = fmaxf(fmaxf(mt, x[e]), x[e + 1]);
+    mt = fmaxf(mt, x[15]);
     mt = pair_max(mt);
     const float mo = m;
     const float mn = (mt > mo + TAU_X) ? mt : mo;
@@ -459,7 +439,6 @@ __device__ __forceinline__ void attend_tile(const char *kb, const char *vb, cons
     m = mn;
     const float base = (mn == -INFINITY) ? 0.0f : mn * SCALE_LOG2;
     float ls = 0.0f;
-    uint32_t pk[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * q], SCALE_LOG2, -base));
@@ -476,8 +455,12 @@ __device__ __forceinline__ void attend_tile(const char *kb, const char *vb, cons
             for (int e = 0; e < 16; ++e)
                 o[db][e] *= alpha;
     }
+}
 
-    // O^T += V^T . P^T; P chunk kc = keys 16kc .. 16kc+15 = pk[4kc .. 4kc+3].
+// O^T += V^T . P^T; P chunk kc = keys 16kc .. 16kc+15 = pk[4kc .. 4kc+3].
+__device__ __forceinline__ void tile_context(const char *vb, const FragOffsets &fo, const uint32_t (&pk)[8],
+                                             f32x16 (&o)[8])
+{
     const uint4 p0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     const uint4 p1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
 #pragma unroll
@@ -491,14 +474,53 @@ __device__ __forceinline__ void attend_tile(const char *kb, const char *vb, cons
     }
 }
 
+// The matrix half of an interval: O += V^T . P^T for the previous tile and
+// S^T = K . Q^T for the current one, issued alternately.  The 16 score MFMAs
+// form one accumulation chain; putting an independent context MFMA between
+// consecutive links keeps the matrix pipe busy while each link completes.
+__device__ __forceinline__ void matrix_half(const char *kb, const char *vb, const FragOffsets &fo,
+                                            const uint4 (&qf)[16], const uint32_t (&pk)[8], f32x16 (&o)[8],
+                                            f32x16 &s)
+{
+    const uint4 p0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    const uint4 p1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        s[e] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        // Two (score, context) pairs of fragments in flight at a time.
+        if ((c & 1) == 0)
+            __builtin_amdgcn_sched_barrier(0);
+        const int db = c >> 1, kc = c & 1;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + fo.k + 1024 * c);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vb + fo.v + 8192 * kc + 512 * db);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8, qf[c]), s, 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, kc ? p1 : p0), o[db], 0,
+                                                       0, 0);
+    }
+}
+
+// Key walk.  Interval k (between two workgroup barriers) reads K(k) and
+// V(k-1) from LDS while K(k+1) and V(k) load into the other buffers.  Each
+// wave's tile work has a matrix half M(k) = [O += V(k-1) P(k-1); S = K(k) Q^T]
+// and a vector half V(k) = softmax(S) -> P(k).  Group A (waves 0..3) runs
+// M(k) then V(k) in interval k; group B (waves 4..7) runs V(k-1) then M(k).
+// Waves w and w + 4 share a SIMD, so in each half of an interval one of them
+// feeds the matrix pipe while the other runs the softmax.
 template <bool MASKED>
 __global__ __attribute__((amdgpu_flat_work_group_size(ATHREADS, ATHREADS), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd(AttnParams p)
 {
-    __shared__ TileBuf bufs[2];
+    __shared__ __align__(16) uint16_t kbuf[2][KT * D];
+    __shared__ __align__(16) uint16_t vbuf[2][D * KT];
+    __shared__ uint32_t bitsbuf[3][QW];
+    __shared__ int tile_list[MASKED ? MAX_TILES : 1];
+    __shared__ int tile_count;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave >> 2;                       // 0: rows r0.. (group A), 1: rows r0+32.. (B)
     const int j = lane & 31, hh = lane >> 5;
 
     // Heaviest row blocks first (longest key walks), then KV head, then head group.
@@ -507,20 +529,70 @@ void attn_fwd(AttnParams p)
     const int rem = blockIdx.x % per_rb;
     const int kvh = rem / p.n_hg, hg = rem % p.n_hg;
     const int gidx = hg * 4 + (wave & 3);
-    const int r0 = rb * QW + QR * (wave >> 2);       // this wave's first window row
+    const int r0 = rb * QW + QR * grp;               // this wave's first window row
     const bool active = gidx < p.G && r0 < p.S;
     const int h = kvh * p.G + (active ? gidx : 0);
 
     const int P0 = p.q_base + rb * QW;               // workgroup's first absolute position
     const int ntiles = min(P0 + QW - 1, p.T - 1) / KT + 1;
-    const int Pw = p.q_base + r0;                    // wave's first absolute position (multiple of 32)
-    const int diag = Pw / KT;                        // the wave's one diagonal tile (its last)
-    const int pos = Pw + j;
+    const int diag = (P0 + QR * grp) / KT;           // the wave's diagonal tile (its last)
 
+    // The workgroup's tile sequence: every tile up to the diagonal, or (masked)
+    // the tiles with a visible key for some row of the block, ascending.
+    int n = ntiles;
+    if (MASKED) {
+        if (wave == 0) {
+            int cnt = 0;
+            for (int t0 = 0; t0 < ntiles; t0 += 64) {
+                const int t = t0 + lane;
+                const bool on = t < ntiles && p.tilevis[(size_t)rb * p.W + t] != 0;
+                const uint64_t bal = __ballot(on);
+                const int at = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+                if (on)
+                    tile_list[at] = t;
+                cnt += __popcll(bal);
+            }
+            if (lane == 0)
+                tile_count = cnt;
+        }
+        __syncthreads();
+        n = tile_count;
+    }
+    auto tile_at = [&](int u) -> int { return MASKED ? tile_list[u] : u; };
+
+    // Each of the 8 waves moves 2 KB of each 16 KB tile straight from global
+    // memory into LDS (global_load_lds_dwordx4: lane L of an instruction
+    // writes the 16 bytes at LDS base + 16 L, from consecutive addresses).
+    auto load_tile = [&](const uint16_t *base, int tile, uint16_t *dst) {
+        const uint16_t *src = base + ((size_t)kvh * (p.Tpad / KT) + tile) * (size_t)(KT * D);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int nn = wave * 2 + i;
+            __builtin_amdgcn_global_load_lds(src + nn * 512 + lane * 8, (lds_void *)((char *)dst + nn * 1024),
+                                             16, 0, 0);
+        }
+    };
+    // Masked path: the 64 rows' visibility words of a tile, next to its K load.
+    auto load_bits = [&](int tile, uint32_t *dst) {
+        if (MASKED && wave == 0) {
+            const int row = min(rb * QW + lane, p.S - 1);   // rows past S read a real row
+            __builtin_amdgcn_global_load_lds(p.bits + (size_t)row * p.W + tile, (lds_void *)dst, 4, 0, 0);
+        }
+    };
+
+    if (n > 0) {
+        load_tile(p.kp, tile_at(0), kbuf[0]);
+        load_bits(tile_at(0), bitsbuf[0]);
+    }
+
+    // Every wave prepares its fragments (an idle wave's are never used); keeping
+    // the definition unconditional keeps them in registers.
     uint4 qf[16];
-    if (active)
-        load_queries(p, r0, h, lane, qf);
+    load_queries(p, r0, h, lane, qf);
     const FragOffsets fo = frag_offsets(j, hh);
+    // Causal visibility inside the wave's diagonal tile (keys and rows both
+    // start at 32 * diag): bit kk set iff kk <= j.
+    const uint32_t diag_vis = (j == 31) ? 0xffffffffu : ((2u << j) - 1u);
 
     f32x16 o[8];
 #pragma unroll
@@ -529,51 +601,79 @@ void attn_fwd(AttnParams p)
         for (int e = 0; e < 16; ++e)
             o[db][e] = 0.0f;
     float m = -INFINITY, l = 0.0f;
+    f32x16 s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        s[e] = 0.0f;
+    uint32_t pk[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 
-    auto next_tile = [&](int t) -> int {
-        ++t;
-        if (MASKED) {
-            while (t < ntiles && p.tilevis[(size_t)rb * p.W + t] == 0)
-                ++t;
-        }
-        return t;
-    };
-    // Masked path: a tile's visibility word is loaded one iteration ahead,
-    // issued before that tile's K/V loads, so no wait lands mid-tile.
-    const bool row_ok = active && (r0 + j) < p.S;
-    auto load_bits = [&](int tile) -> uint32_t {
-        return (MASKED && row_ok && tile <= diag) ? p.bits[(size_t)(r0 + j) * p.W + tile] : 0u;
-    };
-
-    // Causal visibility inside the wave's diagonal tile (keys Pw..Pw+31 against
-    // rows Pw..Pw+31): bit kk set iff kk <= j.
-    const uint32_t diag_vis = (j == 31) ? 0xffffffffu : ((2u << j) - 1u);
-
-    int t = MASKED ? next_tile(-1) : 0;
-    uint32_t bits_cur = MASKED ? load_bits(t) : 0u;
-    if (t < ntiles)
-        issue_tile_loads(p, &bufs[0], kvh, t, wave, lane);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    int cur = 0;
-    while (t < ntiles) {
-        const int tn = next_tile(t);
-        const uint32_t bits_next = MASKED ? load_bits(tn) : 0u;
-        if (tn < ntiles)
-            issue_tile_loads(p, &bufs[cur ^ 1], kvh, tn, wave, lane);
-        if (active && t <= diag) {
-            const char *kb = reinterpret_cast<const char *>(bufs[cur].k);
-            const char *vb = reinterpret_cast<const char *>(bufs[cur].v);
-            const bool on_diag = t == diag;
-            const uint32_t vis = MASKED ? (on_diag ? (bits_cur & diag_vis) : bits_cur) : diag_vis;
-            attend_tile<MASKED>(kb, vb, fo, qf, o, m, l, MASKED || on_diag, vis, hh);
+    // Matrix half M(k) and vector half V(u) of this wave.  Tiles past the
+    // wave's diagonal get all-hidden scores, an exact no-op (running max
+    // unchanged, alpha = 1, P = 0), so both halves run on every tile of the
+    // workgroup's walk; an idle wave's results are never stored.
+    auto scores = [&](int k) { tile_scores(reinterpret_cast<const char *>(kbuf[k & 1]), fo, qf, s); };
+    auto context = [&](int k) { tile_context(reinterpret_cast<const char *>(vbuf[k & 1]), fo, pk, o); };
+    auto vector_half = [&](int u) {
+        const int t = tile_at(u);
+        if (MASKED || t >= diag) {
+            uint32_t vis = (t == diag) ? diag_vis : (t < diag ? 0xffffffffu : 0u);
+            if (MASKED)
+                vis &= bitsbuf[u % 3][QR * grp + j];
+            hide_scores(s, vis, hh);
         }
+        tile_softmax(s, m, l, pk, o);
+    };
+    // Interval k's loads: K(k+1) (+ its row words) and V(k).
+    auto loads = [&](int k) {
+        if (k + 1 < n) {
+            load_tile(p.kp, tile_at(k + 1), kbuf[(k + 1) & 1]);
+            load_bits(tile_at(k + 1), bitsbuf[(k + 1) % 3]);
+        }
+        if (k < n)
+            load_tile(p.vt, tile_at(k), vbuf[k & 1]);
+    };
+    auto close_interval = [&]() {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        cur ^= 1;
-        t = tn;
-        bits_cur = bits_next;
+    };
+
+    if (n > 0) {
+        if (grp == 0) {
+            // Group A: interval k = [O += V(k-1) P(k-1); S(k)] then softmax(k).
+            loads(0);
+            scores(0);
+            vector_half(0);
+            close_interval();
+#pragma clang loop unroll(disable)
+            for (int k = 1; k < n; ++k) {
+                loads(k);
+                matrix_half(reinterpret_cast<const char *>(kbuf[k & 1]),
+                            reinterpret_cast<const char *>(vbuf[(k - 1) & 1]), fo, qf, pk, o, s);
+                vector_half(k);
+                close_interval();
+            }
+            context(n - 1);
+            close_interval();
+        } else {
+            // Group B: interval k = softmax(k-1) then [O += V(k-1) P(k-1); S(k)].
+            loads(0);
+            scores(0);
+            close_interval();
+#pragma clang loop unroll(disable)
+            for (int k = 1; k < n; ++k) {
+                loads(k);
+                vector_half(k - 1);
+                matrix_half(reinterpret_cast<const char *>(kbuf[k & 1]),
+                            reinterpret_cast<const char *>(vbuf[(k - 1) & 1]), fo, qf, pk, o, s);
+                close_interval();
+            }
+            vector_half(n - 1);
+            context(n - 1);
+            close_interval();
+        }
     }
 
     if (!active)
