@@ -356,6 +356,33 @@ constexpr int ATHREADS = 64 * AW;
 constexpr int QR = 32;                 // query rows per wave
 constexpr int MAX_TILES = 32768 / KT;  // tile list capacity (token cap / 32)
 
+// Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane L
+// writes LDS bytes [lds + 16 L, lds + 16 L + 16) from gbase + voff.  gbase and
+// lds must be wave-uniform.  Issued through inline asm so the compiler does
+// not guard later LDS reads of *other* buffers with a wait on this load; the
+// caller orders it with an explicit s_waitcnt vmcnt before the barrier that
+// publishes the buffer.
+__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(gbase)
+                 : "memory", "m0");
+}
+// Same for 4 bytes per lane (global_load_lds_dword): lane L writes lds + 4 L.
+__device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(gbase)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const lds_void *)p;
+}
+
 // Sum and max of a value with its partner lane (lane ^ 32).  v_permlane32_swap
 // exchanges the upper half of one register with the lower half of the other;
 // fed the same value twice, each lane ends with its own value in one result
@@ -502,7 +529,8 @@ __device__ __forceinline__ void matrix_half(const char *kb, const char *vb, cons
 }
 
 // Key walk.  Interval k (between two workgroup barriers) reads K(k) and
-// V(k-1) from LDS while K(k+1) and V(k) load into the other buffers.  Each
+// V(k-1) from LDS while K(k+2) and V(k+1) load into the third buffers (three
+// per operand: loads run two intervals ahead of their use).  Each
 // wave's tile work has a matrix half M(k) = [O += V(k-1) P(k-1); S = K(k) Q^T]
 // and a vector half V(k) = softmax(S) -> P(k).  Group A (waves 0..3) runs
 // M(k) then V(k) in interval k; group B (waves 4..7) runs V(k-1) then M(k).
@@ -512,9 +540,9 @@ template <bool MASKED>
 __global__ __attribute__((amdgpu_flat_work_group_size(ATHREADS, ATHREADS), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd(AttnParams p)
 {
-    __shared__ __align__(16) uint16_t kbuf[2][KT * D];
-    __shared__ __align__(16) uint16_t vbuf[2][D * KT];
-    __shared__ uint32_t bitsbuf[3][QW];
+    __shared__ __align__(16) uint16_t kbuf[3][KT * D];
+    __shared__ __align__(16) uint16_t vbuf[3][D * KT];
+    __shared__ uint32_t bitsbuf[4][QW];
     __shared__ int tile_list[MASKED ? MAX_TILES : 1];
     __shared__ int tile_count;
 
@@ -564,25 +592,37 @@ void attn_fwd(AttnParams p)
     // memory into LDS (global_load_lds_dwordx4: lane L of an instruction
     // writes the 16 bytes at LDS base + 16 L, from consecutive addresses).
     auto load_tile = [&](const uint16_t *base, int tile, uint16_t *dst) {
+        tile = __builtin_amdgcn_readfirstlane(tile);
         const uint16_t *src = base + ((size_t)kvh * (p.Tpad / KT) + tile) * (size_t)(KT * D);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int nn = wave * 2 + i;
-            __builtin_amdgcn_global_load_lds(src + nn * 512 + lane * 8, (lds_void *)((char *)dst + nn * 1024),
-                                             16, 0, 0);
+            dma16(src, (uint32_t)(nn * 1024 + lane * 16), lds_addr(dst) + nn * 1024);
         }
     };
-    // Masked path: the 64 rows' visibility words of a tile, next to its K load.
+    // Masked path: the 64 rows' visibility words of a tile, next to its K
+    // load; wave w moves the words of rows 8w .. 8w+7 (lanes outside that
+    // range are masked off, lane L still writes word L).
     auto load_bits = [&](int tile, uint32_t *dst) {
-        if (MASKED && wave == 0) {
-            const int row = min(rb * QW + lane, p.S - 1);   // rows past S read a real row
-            __builtin_amdgcn_global_load_lds(p.bits + (size_t)row * p.W + tile, (lds_void *)dst, 4, 0, 0);
+        if (MASKED) {
+            tile = __builtin_amdgcn_readfirstlane(tile);
+            if ((lane >> 3) == wave) {
+                const int row = min(rb * QW + lane, p.S - 1);   // rows past S read a real row
+                dma4(p.bits, (uint32_t)(((size_t)row * p.W + tile) * 4), lds_addr(dst));
+            }
         }
     };
+    // Every interval issues the same loads per wave (tiles past the end are
+    // clamped to the last one and land in a buffer nobody reads), so the
+    // wait for the previous interval's loads is one fixed count.
+    auto tile_clamped = [&](int u) { return tile_at(min(u, n - 1)); };
 
     if (n > 0) {
-        load_tile(p.kp, tile_at(0), kbuf[0]);
-        load_bits(tile_at(0), bitsbuf[0]);
+        load_tile(p.kp, tile_clamped(0), kbuf[0]);
+        load_bits(tile_clamped(0), bitsbuf[0]);
+        load_tile(p.kp, tile_clamped(1), kbuf[1]);
+        load_bits(tile_clamped(1), bitsbuf[1]);
+        load_tile(p.vt, tile_clamped(0), vbuf[0]);
     }
 
     // Every wave prepares its fragments (an idle wave's are never used); keeping
@@ -614,29 +654,31 @@ void attn_fwd(AttnParams p)
     // wave's diagonal get all-hidden scores, an exact no-op (running max
     // unchanged, alpha = 1, P = 0), so both halves run on every tile of the
     // workgroup's walk; an idle wave's results are never stored.
-    auto scores = [&](int k) { tile_scores(reinterpret_cast<const char *>(kbuf[k & 1]), fo, qf, s); };
-    auto context = [&](int k) { tile_context(reinterpret_cast<const char *>(vbuf[k & 1]), fo, pk, o); };
+    auto scores = [&](int k) { tile_scores(reinterpret_cast<const char *>(kbuf[k % 3]), fo, qf, s); };
+    auto context = [&](int k) { tile_context(reinterpret_cast<const char *>(vbuf[k % 3]), fo, pk, o); };
     auto vector_half = [&](int u) {
         const int t = tile_at(u);
         if (MASKED || t >= diag) {
             uint32_t vis = (t == diag) ? diag_vis : (t < diag ? 0xffffffffu : 0u);
             if (MASKED)
-                vis &= bitsbuf[u % 3][QR * grp + j];
+                vis &= bitsbuf[u & 3][QR * grp + j];
             hide_scores(s, vis, hh);
         }
         tile_softmax(s, m, l, pk, o);
     };
-    // Interval k's loads: K(k+1) (+ its row words) and V(k).
+    // Interval k's loads: K(k+2) (+ its row words) and V(k+1).
     auto loads = [&](int k) {
-        if (k + 1 < n) {
-            load_tile(p.kp, tile_at(k + 1), kbuf[(k + 1) & 1]);
-            load_bits(tile_at(k + 1), bitsbuf[(k + 1) % 3]);
-        }
-        if (k < n)
-            load_tile(p.vt, tile_at(k), vbuf[k & 1]);
+        load_tile(p.kp, tile_clamped(k + 2), kbuf[(k + 2) % 3]);
+        load_bits(tile_clamped(k + 2), bitsbuf[(k + 2) & 3]);
+        load_tile(p.vt, tile_clamped(k + 1), vbuf[(k + 1) % 3]);
     };
+    // Wait for the previous interval's loads (this interval's stay in flight:
+    // 4 per wave, 5 with the mask words), then the barrier.
     auto close_interval = [&]() {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (MASKED)
+            asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
         __syncthreads();
     };
 
@@ -650,11 +692,12 @@ void attn_fwd(AttnParams p)
 #pragma clang loop unroll(disable)
             for (int k = 1; k < n; ++k) {
                 loads(k);
-                matrix_half(reinterpret_cast<const char *>(kbuf[k & 1]),
-                            reinterpret_cast<const char *>(vbuf[(k - 1) & 1]), fo, qf, pk, o, s);
+                matrix_half(reinterpret_cast<const char *>(kbuf[k % 3]),
+                            reinterpret_cast<const char *>(vbuf[(k - 1) % 3]), fo, qf, pk, o, s);
                 vector_half(k);
                 close_interval();
             }
+            loads(n);
             context(n - 1);
             close_interval();
         } else {
@@ -666,14 +709,16 @@ void attn_fwd(AttnParams p)
             for (int k = 1; k < n; ++k) {
                 loads(k);
                 vector_half(k - 1);
-                matrix_half(reinterpret_cast<const char *>(kbuf[k & 1]),
-                            reinterpret_cast<const char *>(vbuf[(k - 1) & 1]), fo, qf, pk, o, s);
+                matrix_half(reinterpret_cast<const char *>(kbuf[k % 3]),
+                            reinterpret_cast<const char *>(vbuf[(k - 1) % 3]), fo, qf, pk, o, s);
                 close_interval();
             }
+            loads(n);
             vector_half(n - 1);
             context(n - 1);
             close_interval();
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
     if (!active)
