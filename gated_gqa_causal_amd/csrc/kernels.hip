@@ -362,20 +362,25 @@ constexpr int MAX_TILES = 32768 / KT;  // tile list capacity (token cap / 32)
 // not guard later LDS reads of *other* buffers with a wait on this load; the
 // caller orders it with an explicit s_waitcnt vmcnt before the barrier that
 // publishes the buffer.
+// M0 is reserved by the compiler: it is saved and restored around the copy.
 __device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
                  : "s"(lds), "v"(voff), "s"(gbase)
-                 : "memory", "m0");
+                 : "memory");
 }
 // Same for 4 bytes per lane (global_load_lds_dword): lane L writes lds + 4 L.
 __device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t lds)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-                 :
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
                  : "s"(lds), "v"(voff), "s"(gbase)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
@@ -743,7 +748,9 @@ void attn_fwd(AttnParams p)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float ctx = rbf(o[db][4 * g + r] * inv);
-                const float sg = rbf(1.0f / (1.0f + __builtin_amdgcn_exp2f(-gv[r] * LOG2E)));
+                // Hardware reciprocal (exact at 1 and 2: a saturated logit gives
+                // exactly 1, a zero logit exactly 1/2).
+                const float sg = rbf(__builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv[r] * LOG2E)));
                 ov[r] = ctx * sg;
             }
             *reinterpret_cast<uint2 *>(dst + d0) = make_uint2(pack2(ov[0], ov[1]), pack2(ov[2], ov[3]));
