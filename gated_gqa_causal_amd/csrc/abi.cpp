@@ -10,6 +10,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -21,6 +22,7 @@
 
 struct attn_ctx {
     int device = -1;
+    int num_cus = 0;               // compute units of the device
     attn_geometry geom{};
     int tpad = 0;                  // max_tokens rounded up to 64
     int mask_words = 0;            // 32-key words per mask row at max_tokens
@@ -132,6 +134,9 @@ void fill_attn_params(ga::AttnParams &ap, const attn_ctx *ctx, const attn_inputs
     ap.Tpad = ctx->tpad;
     ap.W = (T + 31) / 32;
     ap.eps = g.rms_eps;
+    // One workgroup per compute unit at most; each walks its share of the
+    // work items (see the attention kernel).
+    ap.n_wg = (int)std::min<int64_t>((int64_t)ap.nrb * ap.Hkv * ap.n_hg, ctx->num_cus);
 }
 
 int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kind, const uint8_t *mask,
@@ -255,6 +260,12 @@ int attn_ctx_create(const attn_geometry *geom, int device, attn_ctx **out)
         return ATTN_ERR_NOMEM;
     ctx->device = device;
     ctx->geom = *geom;
+    if (hipDeviceGetAttribute(&ctx->num_cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+        ctx->num_cus <= 0) {
+        (void)hipGetLastError();
+        delete ctx;
+        return ATTN_ERR_DEVICE;
+    }
     ctx->tpad = (geom->max_tokens + 63) / 64 * 64;
     ctx->mask_words = (geom->max_tokens + 31) / 32;
     const size_t kv_elems = (size_t)geom->n_kv_heads * ctx->tpad * ATTN_HEAD_DIM;

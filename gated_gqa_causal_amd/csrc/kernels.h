@@ -39,6 +39,7 @@ struct AttnParams {
     uint16_t *out;            // [S][Hq][256]
     int S, T, q_base;
     int Hq, Hkv, G, n_hg, nrb, Tpad, W;
+    int n_wg;                 // attention workgroups (<= work items)
     float eps;
 };
 

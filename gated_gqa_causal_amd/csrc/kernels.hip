@@ -254,14 +254,16 @@ __device__ __forceinline__ void load_queries(const AttnParams &p, int r0, int h,
     float ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
+        // v_permlane32_swap of a register with itself: the first result holds
+        // the lower half-wave's value (dims 16c .. 16c+7 of the row), the
+        // second the upper half-wave's (16c+8 .. 16c+15), in every lane.
         const uint4 own = qf[c];
-        uint4 oth;
-        oth.x = __shfl_xor(own.x, 32);
-        oth.y = __shfl_xor(own.y, 32);
-        oth.z = __shfl_xor(own.z, 32);
-        oth.w = __shfl_xor(own.w, 32);
-        const uint4 first = hh ? oth : own;
-        const uint4 second = hh ? own : oth;
+        const auto sx = __builtin_amdgcn_permlane32_swap(own.x, own.x, false, false);
+        const auto sy = __builtin_amdgcn_permlane32_swap(own.y, own.y, false, false);
+        const auto sz = __builtin_amdgcn_permlane32_swap(own.z, own.z, false, false);
+        const auto sw = __builtin_amdgcn_permlane32_swap(own.w, own.w, false, false);
+        const uint4 first = make_uint4(sx[0], sy[0], sz[0], sw[0]);
+        const uint4 second = make_uint4(sx[1], sy[1], sz[1], sw[1]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const float x = word_f(first, t);
@@ -350,11 +352,14 @@ __global__ __launch_bounds__(256) void q_prologue_debug(AttnParams p, uint16_t *
 // head; wave w owns head (w & 3) and rows r0 + 32 * (w >> 2) .. +31.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int AW = 8;                  // waves per attention workgroup
+constexpr int AW = 4;                    // waves per attention workgroup (one per SIMD)
 constexpr int ATHREADS = 64 * AW;
-constexpr int QR = 32;                 // query rows per wave
-constexpr int MAX_TILES = 32768 / KT;  // tile list capacity (token cap / 32)
+constexpr int QB = 32;                   // query rows per MFMA block; a wave owns two
+constexpr int MAX_TILES = 32768 / KT;    // tile list capacity (token cap / 32)
+constexpr int TILE_BYTES = KT * D * 2;   // one K or V^T tile: 16 KB
+constexpr int EP_STRIDE = 2 * D + 16;    // epilogue staging: bytes per row
 
 // Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane L
 // writes LDS bytes [lds + 16 L, lds + 16 L + 16) from gbase + voff.  gbase and
@@ -418,342 +423,697 @@ __device__ __forceinline__ FragOffsets frag_offsets(int j, int hh)
     return FragOffsets{hh * 512 + j * 16, hh * 4096 + j * 16};
 }
 
-// S^T = K . Q^T for one tile: lane holds query j, keys 8g + 4hh + r (e = 4g + r).
-__device__ __forceinline__ void tile_scores(const char *kb, const FragOffsets &fo, const uint4 (&qf)[16],
-                                            f32x16 &s)
+// ---------------------------------------------------------------------------
+// Context accumulators.  O^T of a wave's two 32-row blocks is 2 x 8 groups of
+// (32 dims x 32 queries) fp32 = exactly the 256 AGPRs; the VGPRs hold the
+// queries, scores and weights.  The context MFMAs are inline asm with AGPR
+// accumulators.  The compiler does not track their latency, so the software
+// wait states the ISA requires around them are inserted here: VALU access to
+// an accumulator waits (up to 19 states) for the last MFMA on it, and each
+// MFMA waits (a few states) for weights a VALU may have just written.  Taking
+// the accumulators as operands keeps the nops between the two.
+// ---------------------------------------------------------------------------
+// The weights operand b is VALU-written.  Where that write may be close
+// before (the first MFMA on each operand word) a leading nop covers the
+// dependency; the build checks every inline MFMA's operands in the final code.
+template <bool NOP>
+__device__ __forceinline__ void mfma_o(f32x16 &acc, const bf16x8 &a, const u32x4 &b)
+{
+    if (NOP)
+        asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ void acc_wait(f32x16 (&o)[8])
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]),
+                   "+a"(o[7]));
+}
+
+
+// ---------------------------------------------------------------------------
+// Online softmax of one block's tile as a program of 32 steps, one per MFMA
+// slot.  A wave issues about four VALU instructions in the shadow of each
+// 32-cycle MFMA of its own; a step holds about that many, none depending on
+// another of the same step, so the matrix pipe does not wait on them.
+//   lane (j, hh) holds query j and keys 8g + 4hh + r of the tile (e = 4g + r).
+//   steps 0..3  : tile max (a tree of max3 on the fp32 scores; rounding is
+//                 monotonic, so rounding the max afterwards gives the max of
+//                 the rounded scores); the scores rounded to bf16 in pairs;
+//   steps 4..7  : max with the partner lane (the tile's other 16 keys),
+//                 rounded; the rounded scores unpacked in place;
+//   steps 8..13 : running max (moved only past the threshold), alpha, base;
+//   steps 12..29: weights p = exp2(x log2(e)/16 - base), two per pair of
+//                 steps, packed to the bf16 MFMA operand; the row sum adds the
+//                 packed bf16 weights (the values the context product uses);
+//   steps 30, 31: l = l alpha + sum.
+// Masked path: 8 steps before these hide the scores of invisible keys.
+// ---------------------------------------------------------------------------
+constexpr int SM_STEPS = 32;
+constexpr int HIDE_STEPS = 8;
+constexpr uint32_t BF16_ONES = 0x3f803f80u;     // (1.0, 1.0) as packed bf16
+
+// Materialises a value at this point of the instruction stream (the
+// compiler would otherwise sink the softmax arithmetic past the rescale
+// branch to its first use, out of the MFMA gaps it was placed in).
+__device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+
+// The softmax steps use these opaque forms so that the compiler keeps them
+// as written (it would otherwise quieten NaNs before each max, and split a
+// packed rounding into two single ones when only unpacked halves are used).
+__device__ __forceinline__ float max3f(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float max2f(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ uint32_t pack2_op(float a, float b)
+{
+    uint32_t r;
+    asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+struct SmTmp {
+    float a, b, c, d, e, f, g, mt, mt2, t1, mn, dd, bn, nb, ar, L0, L1;
+    bool up, minf, same, ninf;
+    uint32_t w[8];
+};
+
+__device__ __forceinline__ void hide_step(int i, f32x16 &s, uint32_t vh)
 {
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-        s[e] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        // At most four fragments in flight (the Q fragments and the context
-        // accumulators hold 192 of the 256 registers).
-        if ((c & 3) == 0)
-            __builtin_amdgcn_sched_barrier(0);
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + fo.k + 1024 * c);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8, qf[c]), s, 0, 0, 0);
+    for (int e = 2 * i; e < 2 * i + 2; ++e) {
+        const int sh = 8 * (e >> 2) + (e & 3);
+        const uint32_t keep = (uint32_t)((int32_t)(vh << (31 - sh)) >> 31);
+        s[e] = __uint_as_float((__float_as_uint(s[e]) & keep) | (0xff800000u & ~keep));
     }
 }
 
-// Scores of hidden keys become -inf (they round to bf16 -inf and weigh exactly
-// 0).  vis bit kk = key kk of the tile is visible to this lane's query; this
-// lane holds keys 8g + 4hh + r.
-__device__ __forceinline__ void hide_scores(f32x16 &s, uint32_t vis, int hh)
+__device__ __forceinline__ void hide_all(f32x16 &s, uint32_t vh)
 {
-    const uint32_t vh = vis >> (4 * hh);
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-        s[e] = ((vh >> (8 * (e >> 2) + (e & 3))) & 1u) ? s[e] : -INFINITY;
+    for (int i = 0; i < 8; ++i)
+        hide_step(i, s, vh);
 }
 
-// Online softmax of one tile's scores -> bf16 weights pk (relative to the
-// running max), updating (m, l) and rescaling O when the max moves.
-__device__ __forceinline__ void tile_softmax(const f32x16 &s, float &m, float &l, uint32_t (&pk)[8],
-                                             f32x16 (&o)[8])
+// Weight pair q: F = the two exponent arguments, E = the two exp2, C = pack
+// to bf16 (the MFMA operand word), D = add the pair to a partial row sum.
+__device__ __forceinline__ void sm_pair_F(int q, f32x16 &s, const SmTmp &t)
 {
-    float x[16];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const uint32_t w = pack2(s[2 * q], s[2 * q + 1]);     // bf16(q . k)
-        x[2 * q] = lo_f(w);
-        x[2 * q + 1] = hi_f(w);
+    s[2 * q] = __builtin_fmaf(s[2 * q], SCALE_LOG2, t.nb);
+    s[2 * q + 1] = __builtin_fmaf(s[2 * q + 1], SCALE_LOG2, t.nb);
+}
+__device__ __forceinline__ void sm_pair_E(int q, f32x16 &s)
+{
+    s[2 * q] = __builtin_amdgcn_exp2f(s[2 * q]);
+    s[2 * q + 1] = __builtin_amdgcn_exp2f(s[2 * q + 1]);
+}
+__device__ __forceinline__ void sm_pair_C(int q, const f32x16 &s, u32x4 (&pw)[2])
+{
+    const uint32_t pq = pack2_op(s[2 * q], s[2 * q + 1]);
+    pw[q >> 2][q & 3] = pq;
+}
+__device__ __forceinline__ void sm_pair_D(int q, const u32x4 (&pw)[2], SmTmp &t)
+{
+    const uint32_t pq = pw[q >> 2][q & 3];
+    if (q & 1)
+        t.L1 = dot2_bf16(pq, BF16_ONES, q == 1 ? 0.0f : t.L1);
+    else
+        t.L0 = dot2_bf16(pq, BF16_ONES, q == 0 ? 0.0f : t.L0);
+}
+
+__device__ __forceinline__ void sm_step(int i, f32x16 &s, float &m, float &l, float &alpha, u32x4 (&pw)[2],
+                                        SmTmp &t)
+{
+    if (i == 0) {
+        t.a = max3f(s[0], s[1], s[2]);
+        t.b = max3f(s[3], s[4], s[5]);
+        t.c = max3f(s[6], s[7], s[8]);
+        t.d = max3f(s[9], s[10], s[11]);
+    } else if (i == 1) {
+        t.e = max3f(s[12], s[13], s[14]);
+        t.w[0] = pack2_op(s[0], s[1]);
+        t.w[1] = pack2_op(s[2], s[3]);
+        t.w[2] = pack2_op(s[4], s[5]);
+    } else if (i == 2) {
+        t.f = max3f(t.a, t.b, t.c);
+        t.g = max3f(t.d, t.e, s[15]);
+        t.w[3] = pack2_op(s[6], s[7]);
+        t.w[4] = pack2_op(s[8], s[9]);
+    } else if (i == 3) {
+        t.mt = max2f(t.f, t.g);
+        t.w[5] = pack2_op(s[10], s[11]);
+        t.w[6] = pack2_op(s[12], s[13]);
+        t.w[7] = pack2_op(s[14], s[15]);
+    } else if (i == 4) {
+        // Partner lane's max: v_permlane32_swap fed the value twice leaves
+        // this lane's and the partner's value in the two results.
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t.mt), __float_as_uint(t.mt), false, false);
+        t.mt = __uint_as_float(r[0]);
+        t.mt2 = __uint_as_float(r[1]);
+        t.t1 = m + TAU_X;
+    } else if (i == 5) {
+        t.mt = max2f(t.mt, t.mt2);
+        s[0] = lo_f(t.w[0]);
+        s[1] = hi_f(t.w[0]);
+        s[2] = lo_f(t.w[1]);
+    } else if (i == 6) {
+        t.w[0] = pack2_op(t.mt, t.mt);
+        s[3] = hi_f(t.w[1]);
+        s[4] = lo_f(t.w[2]);
+        s[5] = hi_f(t.w[2]);
+    } else if (i == 7) {
+        t.mt = lo_f(t.w[0]);                    // bf16-rounded tile max
+        s[6] = lo_f(t.w[3]);
+        s[7] = hi_f(t.w[3]);
+        s[8] = lo_f(t.w[4]);
+    } else if (i == 8) {
+        t.up = t.mt > t.t1;
+        t.minf = (m == -INFINITY);
+        s[9] = hi_f(t.w[4]);
+        s[10] = lo_f(t.w[5]);
+    } else if (i == 9) {
+        t.mn = t.up ? t.mt : m;
+        s[11] = hi_f(t.w[5]);
+        s[12] = lo_f(t.w[6]);
+        s[13] = hi_f(t.w[6]);
+    } else if (i == 10) {
+        t.dd = m - t.mn;
+        t.same = (t.mn == m);
+        t.bn = t.mn * -SCALE_LOG2;
+        t.ninf = (t.mn == -INFINITY);
+    } else if (i == 11) {
+        t.dd = t.dd * SCALE_LOG2;
+        t.nb = t.ninf ? 0.0f : t.bn;            // a finite base while nothing is visible
+        s[14] = lo_f(t.w[7]);
+        s[15] = hi_f(t.w[7]);
+    } else if (i == 12) {
+        t.ar = __builtin_amdgcn_exp2f(t.dd);
+        sm_pair_F(0, s, t);
+    } else if (i == 13) {
+        // While nothing was visible (m = -inf) O and l are zero: no rescale.
+        alpha = (t.same || t.minf) ? 1.0f : t.ar;
+        pin(alpha);
+        m = t.mn;
+        sm_pair_E(0, s);
+    } else if (i < 28) {
+        // 14, 16, .., 26: F(q+1), C(q) for q = (i-14)/2;  15, .., 27: E(q+1), D(q).
+        const int q = (i - 14) >> 1;
+        if ((i & 1) == 0) {
+            sm_pair_F(q + 1, s, t);
+            sm_pair_C(q, s, pw);
+        } else {
+            sm_pair_E(q + 1, s);
+            sm_pair_D(q, pw, t);
+        }
+    } else if (i == 28) {
+        sm_pair_C(7, s, pw);
+    } else if (i == 29) {
+        sm_pair_D(7, pw, t);
+    } else if (i == 30) {
+        t.L0 = t.L0 + t.L1;
+    } else if (i == 31) {
+        l = __builtin_fmaf(l, alpha, t.L0);
+        pin(l);
     }
-    float mt = fmaxf(fmaxf(x[0], x[1]), x[2]);
-#pragma unroll
-    for (int e = 3; e < 15; e += 2)
-        mt = fmaxf(fmaxf(mt, x[e]), x[e + 1]);
-    mt = fmaxf(mt, x[15]);
-    mt = pair_max(mt);
-    const float mo = m;
-    const float mn = (mt > mo + TAU_X) ? mt : mo;
-    const float alpha = (mn == mo) ? 1.0f : __builtin_amdgcn_exp2f((mo - mn) * SCALE_LOG2);
-    m = mn;
-    const float base = (mn == -INFINITY) ? 0.0f : mn * SCALE_LOG2;
-    float ls = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * q], SCALE_LOG2, -base));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * q + 1], SCALE_LOG2, -base));
-        ls += p0;
-        ls += p1;
-        pk[q] = pack2(p0, p1);
+}
+
+// One softmax step per MFMA slot, starting at slot `first`; with MASKED the
+// hide steps come first (vh = this lane's visibility bits >> 4hh).
+template <bool MASKED>
+__device__ __forceinline__ void sm_slot(int slot, int first, f32x16 &s, uint32_t vh, float &m, float &l,
+                                        float &alpha, u32x4 (&pw)[2], SmTmp &t)
+{
+    int i = slot - first;
+    if (i < 0)
+        return;
+    if (MASKED) {
+        if (i < HIDE_STEPS) {
+            hide_step(i, s, vh);
+            return;
+        }
+        i -= HIDE_STEPS;
     }
-    l = l * alpha + ls;
+    if (i < SM_STEPS)
+        sm_step(i, s, m, l, alpha, pw, t);
+}
+
+template <bool MASKED>
+constexpr int sm_slots()
+{
+    return (MASKED ? HIDE_STEPS : 0) + SM_STEPS;
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>((uintptr_t)addr);
+}
+
+// Scores half of an interval: S^T = K . Q^T for both blocks of one tile (every
+// K fragment read from LDS feeds two MFMAs), with the softmax of block 1's
+// previous tile in the gaps.  kaddr = LDS address of this lane's fragment 0;
+// kpre holds fragments 0 and 1, read ahead.  Near its end the half reads the
+// first two V^T fragments of the context half (vaddr_next) into vpre.
+// issue(slot) places the interval's global->LDS copies among the MFMAs.
+template <bool MASKED, bool DO_S, bool DO_SM, typename Issue>
+__device__ __forceinline__ void scores_half(uint32_t kaddr, const bf16x8 (&kpre)[2], uint32_t vaddr_next,
+                                            bf16x8 (&vpre)[2], const uint4 (&qf)[2][16], f32x16 (&s)[2],
+                                            f32x16 &sp, uint32_t vh, float &m, float &l, float &alpha,
+                                            u32x4 (&pw)[2], Issue &&issue)
+{
+    SmTmp t;
+    bf16x8 kf[16];
+    kf[0] = kpre[0];
+    kf[1] = kpre[1];
+    constexpr int NSLOT = DO_SM ? (sm_slots<MASKED>() > 32 ? sm_slots<MASKED>() : 32) : 32;
+#pragma clang loop unroll(full)
+    for (int slot = 0; slot < NSLOT; ++slot) {
+        const int c = slot >> 1, b = slot & 1;
+        if (DO_S && c < 16) {
+            if (b == 0 && c + 2 < 16)
+                kf[c + 2] = lds_read16(kaddr + 1024 * (c + 2));
+            const f32x16 z = {};
+            s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], __builtin_bit_cast(bf16x8, qf[b][c]),
+                                                           c ? s[b] : z, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);     // the MFMA leads its slot
+        }
+        if (slot == 28) {
+            vpre[0] = lds_read16(vaddr_next);
+            vpre[1] = lds_read16(vaddr_next + 512);
+        }
+        issue(slot);
+        if (DO_SM)
+            sm_slot<MASKED>(slot, 0, sp, vh, m, l, alpha, pw, t);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Context half of an interval: O^T += V^T . P^T for both blocks of the
+// previous tile (every V fragment feeds two MFMAs), with the softmax of block
+// 0's current tile in the gaps; its first step waits one slot for the last
+// score MFMAs.  vaddr = LDS address of this lane's fragment (kc 0, db 0);
+// vpre holds fragments 0 and 1.  Near its end the half reads the first two K
+// fragments of the next interval (kaddr_next) into kpre.
+template <bool MASKED, bool DO_PV, bool DO_SM>
+__device__ __forceinline__ void context_half(uint32_t vaddr, const bf16x8 (&vpre)[2], uint32_t kaddr_next,
+                                             bf16x8 (&kpre)[2], const u32x4 (&w0)[2], const u32x4 (&w1)[2],
+                                             f32x16 (&o)[2][8], f32x16 &s, uint32_t vh, float &m, float &l,
+                                             float &alpha, u32x4 (&pw)[2])
+{
+    SmTmp t;
+    bf16x8 vf[16];
+    constexpr int FIRST = 1;
+    vf[0] = vpre[0];
+    vf[1] = vpre[1];
+    constexpr int NSLOT =
+        DO_SM ? (FIRST + sm_slots<MASKED>() > 32 ? FIRST + sm_slots<MASKED>() : 32) : 32;
+#pragma clang loop unroll(full)
+    for (int slot = 0; slot < NSLOT; ++slot) {
+        const int i = slot >> 1, b = slot & 1;     // fragment i: kc = i / 8, db = i % 8
+        if (DO_PV && i < 16) {
+            if (b == 0 && i + 2 < 16) {
+                const int n2 = i + 2;
+                vf[n2] = lds_read16(vaddr + 8192 * (n2 >> 3) + 512 * (n2 & 7));
+            }
+            if ((i & 7) == 0)
+                mfma_o<true>(o[b][i & 7], vf[i], b ? w1[i >> 3] : w0[i >> 3]);
+            else
+                mfma_o<false>(o[b][i & 7], vf[i], b ? w1[i >> 3] : w0[i >> 3]);
+        }
+        if (slot == 28) {
+            kpre[0] = lds_read16(kaddr_next);
+            kpre[1] = lds_read16(kaddr_next + 1024);
+        }
+        if (DO_SM)
+            sm_slot<MASKED>(slot, FIRST, s, vh, m, l, alpha, pw, t);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+__device__ __forceinline__ void rescale(f32x16 (&o)[8], float alpha)
+{
     if (__builtin_expect(__any(alpha != 1.0f), 0)) {
+        acc_wait(o);
+        // In place in the AGPRs (a VGPR round trip visible to the compiler
+        // would make it keep the accumulators in VGPRs across the branch).
 #pragma unroll
         for (int db = 0; db < 8; ++db)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                o[db][e] *= alpha;
-    }
-}
-
-// O^T += V^T . P^T; P chunk kc = keys 16kc .. 16kc+15 = pk[4kc .. 4kc+3].
-__device__ __forceinline__ void tile_context(const char *vb, const FragOffsets &fo, const uint32_t (&pk)[8],
-                                             f32x16 (&o)[8])
-{
-    const uint4 p0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    const uint4 p1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-        if ((db & 1) == 0)
-            __builtin_amdgcn_sched_barrier(0);
-        const bf16x8 v0 = *reinterpret_cast<const bf16x8 *>(vb + fo.v + 512 * db);
-        const bf16x8 v1 = *reinterpret_cast<const bf16x8 *>(vb + fo.v + 8192 + 512 * db);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, __builtin_bit_cast(bf16x8, p0), o[db], 0, 0, 0);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, __builtin_bit_cast(bf16x8, p1), o[db], 0, 0, 0);
-    }
-}
-
-// The matrix half of an interval: O += V^T . P^T for the previous tile and
-// S^T = K . Q^T for the current one, issued alternately.  The 16 score MFMAs
-// form one accumulation chain; putting an independent context MFMA between
-// consecutive links keeps the matrix pipe busy while each link completes.
-__device__ __forceinline__ void matrix_half(const char *kb, const char *vb, const FragOffsets &fo,
-                                            const uint4 (&qf)[16], const uint32_t (&pk)[8], f32x16 (&o)[8],
-                                            f32x16 &s)
-{
-    const uint4 p0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    const uint4 p1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-        s[e] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        // Two (score, context) pairs of fragments in flight at a time.
-        if ((c & 1) == 0)
-            __builtin_amdgcn_sched_barrier(0);
-        const int db = c >> 1, kc = c & 1;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + fo.k + 1024 * c);
-        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vb + fo.v + 8192 * kc + 512 * db);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8, qf[c]), s, 0, 0, 0);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, kc ? p1 : p0), o[db], 0,
-                                                       0, 0);
+            for (int e = 0; e < 16; ++e) {
+                float x = o[db][e];
+                float tmp;
+                asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                             : "+a"(x), "=&v"(tmp)
+                             : "v"(alpha));
+                o[db][e] = x;
+            }
+        acc_wait(o);
     }
 }
 
 // Key walk.  Interval k (between two workgroup barriers) reads K(k) and
-// V(k-1) from LDS while K(k+2) and V(k+1) load into the third buffers (three
-// per operand: loads run two intervals ahead of their use).  Each
-// wave's tile work has a matrix half M(k) = [O += V(k-1) P(k-1); S = K(k) Q^T]
-// and a vector half V(k) = softmax(S) -> P(k).  Group A (waves 0..3) runs
-// M(k) then V(k) in interval k; group B (waves 4..7) runs V(k-1) then M(k).
-// Waves w and w + 4 share a SIMD, so in each half of an interval one of them
-// feeds the matrix pipe while the other runs the softmax.
+// V(k-1) from LDS while K(k+3) and V(k+1) load (four K and three V^T
+// buffers: K runs three intervals ahead, so the next tile's first K
+// fragments can be read during this interval).  In interval k each wave runs
+//   scores half : S(k) for both blocks           | softmax of block 1, tile k-1
+//   context half: O += V(k-1) P(k-1), both blocks | softmax of block 0, tile k
+// so each half pairs 32 MFMAs with one block's softmax.  A block's O is
+// rescaled (rarely) between its last product with the old running max and its
+// first with the new one.
 template <bool MASKED>
-__global__ __attribute__((amdgpu_flat_work_group_size(ATHREADS, ATHREADS), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(ATHREADS, ATHREADS), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd(AttnParams p)
 {
-    __shared__ __align__(16) uint16_t kbuf[3][KT * D];
-    __shared__ __align__(16) uint16_t vbuf[3][D * KT];
-    __shared__ uint32_t bitsbuf[4][QW];
+    __shared__ __align__(16) char smem[7 * TILE_BYTES];   // K tiles 0..3, V^T tiles 4..6; epilogue staging
+    __shared__ uint32_t bitsbuf[8][QW];
     __shared__ int tile_list[MASKED ? MAX_TILES : 1];
     __shared__ int tile_count;
 
-    const int lane = threadIdx.x & 63;
+    const int lane_id = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int grp = wave >> 2;                       // 0: rows r0.. (group A), 1: rows r0+32.. (B)
-    const int j = lane & 31, hh = lane >> 5;
 
-    // Heaviest row blocks first (longest key walks), then KV head, then head group.
+    // Work items (64-row block, KV head, head group) are numbered heaviest row
+    // block first (longest key walk).  The launch has at most one workgroup
+    // per compute unit; workgroup b of P takes items in a snake order,
+    // b, 2P-1-b, 2P+b, 4P-1-b, ..., so that each pass pairs the heavy end of
+    // the list with the light end and the workgroups' totals stay level.
     const int per_rb = p.Hkv * p.n_hg;
-    const int rb = p.nrb - 1 - (int)(blockIdx.x / per_rb);
-    const int rem = blockIdx.x % per_rb;
-    const int kvh = rem / p.n_hg, hg = rem % p.n_hg;
-    const int gidx = hg * 4 + (wave & 3);
-    const int r0 = rb * QW + QR * grp;               // this wave's first window row
-    const bool active = gidx < p.G && r0 < p.S;
-    const int h = kvh * p.G + (active ? gidx : 0);
+    const int n_items = p.nrb * per_rb;
+    const int P = (int)gridDim.x;
+#pragma clang loop unroll(disable)
+    for (int pass = 0;; ++pass) {
+        const int item = pass * P + ((pass & 1) ? P - 1 - (int)blockIdx.x : (int)blockIdx.x);
+        if (item >= n_items)
+            break;
+        if (pass > 0)
+            __syncthreads();                         // the previous item is done with LDS
+        // Lane-derived values are recomputed per item from an opaque copy of
+        // the lane id (hoisted out of this loop they would stay live across
+        // the key walk and crowd its registers).
+        int lane = lane_id;
+        asm volatile("" : "+v"(lane));
+        const int j = lane & 31, hh = lane >> 5;
+        const int rb = p.nrb - 1 - item / per_rb;
+        const int rem = item % per_rb;
+        const int kvh = rem / p.n_hg, hg = rem % p.n_hg;
+        const int gidx = hg * 4 + wave;
+        const bool active = gidx < p.G;
+        const int h = kvh * p.G + (active ? gidx : 0);
+        const int r0 = rb * QW;                          // the wave's rows r0 .. r0 + 63
 
-    const int P0 = p.q_base + rb * QW;               // workgroup's first absolute position
-    const int ntiles = min(P0 + QW - 1, p.T - 1) / KT + 1;
-    const int diag = (P0 + QR * grp) / KT;           // the wave's diagonal tile (its last)
+        const int P0 = p.q_base + r0;                    // first absolute position (a multiple of 64)
+        const int ntiles = min(P0 + QW - 1, p.T - 1) / KT + 1;
+        const int diag0 = P0 / KT;                       // block b's diagonal tile is diag0 + b
 
-    // The workgroup's tile sequence: every tile up to the diagonal, or (masked)
-    // the tiles with a visible key for some row of the block, ascending.
-    int n = ntiles;
-    if (MASKED) {
-        if (wave == 0) {
-            int cnt = 0;
-            for (int t0 = 0; t0 < ntiles; t0 += 64) {
-                const int t = t0 + lane;
-                const bool on = t < ntiles && p.tilevis[(size_t)rb * p.W + t] != 0;
-                const uint64_t bal = __ballot(on);
-                const int at = cnt + __popcll(bal & ((1ull << lane) - 1ull));
-                if (on)
-                    tile_list[at] = t;
-                cnt += __popcll(bal);
-            }
-            if (lane == 0)
-                tile_count = cnt;
-        }
-        __syncthreads();
-        n = tile_count;
-    }
-    auto tile_at = [&](int u) -> int { return MASKED ? tile_list[u] : u; };
-
-    // Each of the 8 waves moves 2 KB of each 16 KB tile straight from global
-    // memory into LDS (global_load_lds_dwordx4: lane L of an instruction
-    // writes the 16 bytes at LDS base + 16 L, from consecutive addresses).
-    auto load_tile = [&](const uint16_t *base, int tile, uint16_t *dst) {
-        tile = __builtin_amdgcn_readfirstlane(tile);
-        const uint16_t *src = base + ((size_t)kvh * (p.Tpad / KT) + tile) * (size_t)(KT * D);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int nn = wave * 2 + i;
-            dma16(src, (uint32_t)(nn * 1024 + lane * 16), lds_addr(dst) + nn * 1024);
-        }
-    };
-    // Masked path: the 64 rows' visibility words of a tile, next to its K
-    // load; wave w moves the words of rows 8w .. 8w+7 (lanes outside that
-    // range are masked off, lane L still writes word L).
-    auto load_bits = [&](int tile, uint32_t *dst) {
+        // The workgroup's tile sequence: every tile up to the diagonal, or (masked)
+        // the tiles with a visible key for some row of the block, ascending.
+        int n = ntiles;
         if (MASKED) {
+            if (wave == 0) {
+                int cnt = 0;
+                for (int t0 = 0; t0 < ntiles; t0 += 64) {
+                    const int t = t0 + lane;
+                    const bool on = t < ntiles && p.tilevis[(size_t)rb * p.W + t] != 0;
+                    const uint64_t bal = __ballot(on);
+                    const int at = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+                    if (on)
+                        tile_list[at] = t;
+                    cnt += __popcll(bal);
+                }
+                if (lane == 0)
+                    tile_count = cnt;
+            }
+            __syncthreads();
+            n = tile_count;
+        }
+        auto tile_at = [&](int u) -> int { return MASKED ? tile_list[u] : u; };
+        auto kbuf = [&](int i) { return smem + TILE_BYTES * i; };
+        auto vbuf = [&](int i) { return smem + TILE_BYTES * (4 + i); };
+
+        // Each of the 4 waves moves 4 KB of each 16 KB tile straight from global
+        // memory into LDS (global_load_lds_dwordx4: lane L of an instruction
+        // writes the 16 bytes at LDS base + 16 L, from consecutive addresses).
+        auto load_tile = [&](const uint16_t *base, int tile, char *dst) {
             tile = __builtin_amdgcn_readfirstlane(tile);
-            if ((lane >> 3) == wave) {
-                const int row = min(rb * QW + lane, p.S - 1);   // rows past S read a real row
-                dma4(p.bits, (uint32_t)(((size_t)row * p.W + tile) * 4), lds_addr(dst));
+            const uint16_t *src = base + ((size_t)kvh * (p.Tpad / KT) + tile) * (size_t)(KT * D);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int nn = wave * 4 + i;
+                dma16(src, (uint32_t)(nn * 1024 + lane * 16), lds_addr(dst) + nn * 1024);
             }
-        }
-    };
-    // Every interval issues the same loads per wave (tiles past the end are
-    // clamped to the last one and land in a buffer nobody reads), so the
-    // wait for the previous interval's loads is one fixed count.
-    auto tile_clamped = [&](int u) { return tile_at(min(u, n - 1)); };
-
-    if (n > 0) {
-        load_tile(p.kp, tile_clamped(0), kbuf[0]);
-        load_bits(tile_clamped(0), bitsbuf[0]);
-        load_tile(p.kp, tile_clamped(1), kbuf[1]);
-        load_bits(tile_clamped(1), bitsbuf[1]);
-        load_tile(p.vt, tile_clamped(0), vbuf[0]);
-    }
-
-    // Every wave prepares its fragments (an idle wave's are never used); keeping
-    // the definition unconditional keeps them in registers.
-    uint4 qf[16];
-    load_queries(p, r0, h, lane, qf);
-    const FragOffsets fo = frag_offsets(j, hh);
-    // Causal visibility inside the wave's diagonal tile (keys and rows both
-    // start at 32 * diag): bit kk set iff kk <= j.
-    const uint32_t diag_vis = (j == 31) ? 0xffffffffu : ((2u << j) - 1u);
-
-    f32x16 o[8];
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            o[db][e] = 0.0f;
-    float m = -INFINITY, l = 0.0f;
-    f32x16 s;
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-        s[e] = 0.0f;
-    uint32_t pk[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    // Matrix half M(k) and vector half V(u) of this wave.  Tiles past the
-    // wave's diagonal get all-hidden scores, an exact no-op (running max
-    // unchanged, alpha = 1, P = 0), so both halves run on every tile of the
-    // workgroup's walk; an idle wave's results are never stored.
-    auto scores = [&](int k) { tile_scores(reinterpret_cast<const char *>(kbuf[k % 3]), fo, qf, s); };
-    auto context = [&](int k) { tile_context(reinterpret_cast<const char *>(vbuf[k % 3]), fo, pk, o); };
-    auto vector_half = [&](int u) {
-        const int t = tile_at(u);
-        if (MASKED || t >= diag) {
-            uint32_t vis = (t == diag) ? diag_vis : (t < diag ? 0xffffffffu : 0u);
+        };
+        // Masked path: the 64 rows' visibility words of a tile, next to its K
+        // load; wave w moves the words of rows 16w .. 16w+15 (lanes outside that
+        // range are masked off, lane L still writes word L).
+        auto load_bits = [&](int tile, uint32_t *dst) {
+            if (MASKED) {
+                tile = __builtin_amdgcn_readfirstlane(tile);
+                if ((lane >> 4) == wave) {
+                    const int row = min(r0 + lane, p.S - 1);   // rows past S read a real row
+                    dma4(p.bits, (uint32_t)(((size_t)row * p.W + tile) * 4), lds_addr(dst));
+                }
+            }
+        };
+        // Every interval issues the same loads per wave (tiles past the end are
+        // clamped to the last one and land in a buffer nobody reads), so the
+        // wait for the previous interval's loads is one fixed count.
+        auto tile_clamped = [&](int u) { return tile_at(min(u, n - 1)); };
+        // Interval k's copies, one per issue slot: K(k+3) in 4 parts, its mask
+        // words, V(k+1) in 4 parts (spread over the scores half: a copy occupies
+        // the wave's issue for tens of cycles, which the MFMAs then cover).
+        auto load_part = [&](int k, int part) {
+            if (part == 4) {
+                load_bits(tile_clamped(k + 3), bitsbuf[(k + 3) & 7]);
+                return;
+            }
+            const bool is_k = part < 4;
+            const int tile = __builtin_amdgcn_readfirstlane(tile_clamped(is_k ? k + 3 : k + 1));
+            const uint16_t *src = (is_k ? p.kp : p.vt) + ((size_t)kvh * (p.Tpad / KT) + tile) * (size_t)(KT * D);
+            const char *dst = is_k ? kbuf((k + 3) & 3) : vbuf((k + 1) % 3);
+            const int nn = wave * 4 + (is_k ? part : part - 5);
+            dma16(src, (uint32_t)(nn * 1024 + lane * 16), lds_addr(dst) + nn * 1024);
+        };
+        auto issue_loads = [&](int k) {
+            return [&, k](int slot) {
+                if (slot % 3 == 1 && slot / 3 < 9)
+                    load_part(k, slot / 3);
+            };
+        };
+        auto no_issue = [](int) {};
+        // Wait for the previous interval's loads (this interval's stay in flight:
+        // 8 per wave, 9 with the mask words), then the barrier.
+        auto close_interval = [&]() {
             if (MASKED)
-                vis &= bitsbuf[u & 3][QR * grp + j];
-            hide_scores(s, vis, hh);
-        }
-        tile_softmax(s, m, l, pk, o);
-    };
-    // Interval k's loads: K(k+2) (+ its row words) and V(k+1).
-    auto loads = [&](int k) {
-        load_tile(p.kp, tile_clamped(k + 2), kbuf[(k + 2) % 3]);
-        load_bits(tile_clamped(k + 2), bitsbuf[(k + 2) & 3]);
-        load_tile(p.vt, tile_clamped(k + 1), vbuf[(k + 1) % 3]);
-    };
-    // Wait for the previous interval's loads (this interval's stay in flight:
-    // 4 per wave, 5 with the mask words), then the barrier.
-    auto close_interval = [&]() {
-        if (MASKED)
-            asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        __syncthreads();
-    };
+                asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            __syncthreads();
+        };
 
-    if (n > 0) {
-        if (grp == 0) {
-            // Group A: interval k = [O += V(k-1) P(k-1); S(k)] then softmax(k).
-            loads(0);
-            scores(0);
-            vector_half(0);
+        if (n > 0) {
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                load_tile(p.kp, tile_clamped(u), kbuf(u));
+                load_bits(tile_clamped(u), bitsbuf[u]);
+            }
+            load_tile(p.vt, tile_clamped(0), vbuf(0));
+        }
+
+        // Every wave prepares its queries (an idle wave's results are never
+        // stored); keeping the definition unconditional keeps them in registers.
+        uint4 qf[2][16];
+        load_queries(p, r0, h, lane, qf[0]);
+        load_queries(p, r0 + QB, h, lane, qf[1]);
+        const FragOffsets fo = frag_offsets(j, hh);
+        // Causal visibility inside a block's diagonal tile (keys and rows both
+        // start at 32 * (diag0 + b)): bit kk set iff kk <= j.
+        const uint32_t diag_vis = (j == 31) ? 0xffffffffu : ((2u << j) - 1u);
+
+        // The accumulators start as AGPR values (written by an MFMA of zeros), so
+        // that no path into the key walk carries them in VGPRs.
+        f32x16 o[2][8];
+        {
+            const bf16x8 zero = {};
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+                    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(o[b][db]) : "v"(zero));
+        }
+        float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f}, alpha[2] = {1.0f, 1.0f};
+        f32x16 s[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            s[0][e] = 0.0f;
+            s[1][e] = 0.0f;
+        }
+        // Weights of each block's latest tile, as the two MFMA operand words.
+        u32x4 pw0[2] = {}, pw1[2] = {};
+
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+
+        // Visibility of tile u (walk index) for block b, as this lane's bits >> 4hh.
+        // Unmasked: applied only on tiles at or past the block's diagonal (a
+        // uniform branch before the half); masked: always, inside the half.
+        auto masked_vh = [&](int u, int b) -> uint32_t {
+            return MASKED ? (bitsbuf[u & 7][QB * b + j] >> (4 * hh)) : 0u;
+        };
+        auto causal_hide = [&](int u, int b, f32x16 &sc) {
+            if (!MASKED) {
+                const int t = u;                       // unmasked: walk index = tile index
+                const int dg = diag0 + b;
+                if (t >= dg) {
+                    const uint32_t vis = (t == dg) ? diag_vis : 0u;
+                    hide_all(sc, vis >> (4 * hh));
+                }
+            }
+        };
+        // LDS addresses of this lane's fragment 0 in the K / V^T buffer of tile k
+        // (kept opaque so every fragment read uses the instruction's offset field).
+        const uint32_t smem_base = lds_addr(smem);
+        auto kaddr_of = [&](int k) {
+            uint32_t a = smem_base + TILE_BYTES * (k & 3) + fo.k;
+            asm volatile("" : "+v"(a));
+            return a;
+        };
+        auto vaddr_of = [&](int k) {
+            uint32_t a = smem_base + TILE_BYTES * (4 + k % 3) + fo.v;
+            asm volatile("" : "+v"(a));
+            return a;
+        };
+
+        const int cc = lane & 31;                       // epilogue: 16-byte chunk of a row (dims 8cc .. 8cc+7)
+        uint4 gw[2][16];
+        auto load_gates = [&](int b) {
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+                const int row = min(r0 + QB * b + 2 * it + hh, p.S - 1);
+                gw[b][it] = *reinterpret_cast<const uint4 *>(p.qg + (((size_t)row * p.Hq + h) * 2 + 1) * D + 8 * cc);
+            }
+        };
+        // The unmasked walk always has a tile (row r0 < S sees key 0).
+        if (!MASKED || n > 0) {
+            bf16x8 kpre[2], vpre[2];
+            {
+                const uint32_t a0 = kaddr_of(0);
+                kpre[0] = lds_read16(a0);
+                kpre[1] = lds_read16(a0 + 1024);
+            }
+            // Interval 0: S(0); softmax of block 0 on tile 0.
+            {
+                f32x16 unused = s[1];
+                scores_half<MASKED, true, false>(kaddr_of(0), kpre, vaddr_of(0), vpre, qf, s, unused, 0u, m[1], l[1],
+                                                 alpha[1], pw1, issue_loads(0));
+            }
+            causal_hide(0, 0, s[0]);
+            {
+                const u32x4 w0[2] = {pw0[0], pw0[1]}, w1[2] = {pw1[0], pw1[1]};
+                context_half<MASKED, false, true>(vaddr_of(0), vpre, kaddr_of(1), kpre, w0, w1, o, s[0],
+                                                  masked_vh(0, 0), m[0], l[0], alpha[0], pw0);
+            }
+            rescale(o[0], alpha[0]);
             close_interval();
 #pragma clang loop unroll(disable)
             for (int k = 1; k < n; ++k) {
-                loads(k);
-                matrix_half(reinterpret_cast<const char *>(kbuf[k % 3]),
-                            reinterpret_cast<const char *>(vbuf[(k - 1) % 3]), fo, qf, pk, o, s);
-                vector_half(k);
+                f32x16 s1p = s[1];
+                causal_hide(k - 1, 1, s1p);
+                scores_half<MASKED, true, true>(kaddr_of(k), kpre, vaddr_of(k - 1), vpre, qf, s, s1p,
+                                                masked_vh(k - 1, 1), m[1], l[1], alpha[1], pw1, issue_loads(k));
+                rescale(o[1], alpha[1]);
+                causal_hide(k, 0, s[0]);
+                const u32x4 w0[2] = {pw0[0], pw0[1]}, w1[2] = {pw1[0], pw1[1]};
+                context_half<MASKED, true, true>(vaddr_of(k - 1), vpre, kaddr_of(k + 1), kpre, w0, w1, o, s[0],
+                                                 masked_vh(k, 0), m[0], l[0], alpha[0], pw0);
+                rescale(o[0], alpha[0]);
                 close_interval();
             }
-            loads(n);
-            context(n - 1);
-            close_interval();
-        } else {
-            // Group B: interval k = softmax(k-1) then [O += V(k-1) P(k-1); S(k)].
-            loads(0);
-            scores(0);
-            close_interval();
-#pragma clang loop unroll(disable)
-            for (int k = 1; k < n; ++k) {
-                loads(k);
-                vector_half(k - 1);
-                matrix_half(reinterpret_cast<const char *>(kbuf[k % 3]),
-                            reinterpret_cast<const char *>(vbuf[(k - 1) % 3]), fo, qf, pk, o, s);
-                close_interval();
+            // Unmasked: block 0's gate rows load now (the query registers are
+            // free, and the last interval covers the latency).  The masked walk
+            // has no registers to spare for them here.
+            if (!MASKED)
+                load_gates(0);
+            // Interval n: softmax of block 1 on tile n-1; O += V(n-1) P(n-1).
+            {
+                f32x16 s1p = s[1];
+                causal_hide(n - 1, 1, s1p);
+                scores_half<MASKED, false, true>(kaddr_of(n), kpre, vaddr_of(n - 1), vpre, qf, s, s1p,
+                                                 masked_vh(n - 1, 1), m[1], l[1], alpha[1], pw1, no_issue);
             }
-            loads(n);
-            vector_half(n - 1);
-            context(n - 1);
-            close_interval();
+            rescale(o[1], alpha[1]);
+            {
+                f32x16 unused = s[0];
+                u32x4 pw_unused[2] = {};
+                const u32x4 w0[2] = {pw0[0], pw0[1]}, w1[2] = {pw1[0], pw1[1]};
+                context_half<MASKED, true, false>(vaddr_of(n - 1), vpre, kaddr_of(n + 1), kpre, w0, w1, o, unused, 0u,
+                                                  m[0], l[0], alpha[0], pw_unused);
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+        __syncthreads();                                 // all waves are done with the tile buffers
 
-    if (!active)
-        return;
-
-    // Epilogue: ctx = bf16(O / l), out = bf16(ctx * bf16(sigmoid(gate))).
-    const float lt = pair_sum(l);
-    const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
-    const int row = r0 + j;
-    if (row >= p.S)
-        return;
-    const uint16_t *gsrc = p.qg + (((size_t)row * p.Hq + h) * 2 + 1) * D;
-    uint16_t *dst = p.out + ((size_t)row * p.Hq + h) * D;
+        // Epilogue: ctx = bf16(O / l), out = bf16(ctx * bf16(sigmoid(gate))).
+        // The context goes through LDS (row-major, one 528-byte row per query) so
+        // that the gate reads and output writes are whole 512-byte rows.
+        char *ep = smem + wave * QB * EP_STRIDE;
+        if (MASKED)
+            load_gates(0);
+        load_gates(1);                               // covered by block 0's epilogue
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+        for (int b = 0; b < 2; ++b) {
+            const float lt = pair_sum(l[b]);
+            const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
+            acc_wait(o[b]);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int d0 = 32 * db + 8 * g + 4 * hh;
-            const uint2 gw = *reinterpret_cast<const uint2 *>(gsrc + d0);
-            const float gv[4] = {lo_f(gw.x), hi_f(gw.x), lo_f(gw.y), hi_f(gw.y)};
-            float ov[4];
+            for (int db = 0; db < 8; ++db)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float ctx = rbf(o[db][4 * g + r] * inv);
-                // Hardware reciprocal (exact at 1 and 2: a saturated logit gives
-                // exactly 1, a zero logit exactly 1/2).
-                const float sg = rbf(__builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv[r] * LOG2E)));
-                ov[r] = ctx * sg;
+                for (int g = 0; g < 4; ++g) {
+                    const int d0 = 32 * db + 8 * g + 4 * hh;
+                    const uint2 cw = make_uint2(pack2(o[b][db][4 * g] * inv, o[b][db][4 * g + 1] * inv),
+                                                pack2(o[b][db][4 * g + 2] * inv, o[b][db][4 * g + 3] * inv));
+                    *reinterpret_cast<uint2 *>(ep + j * EP_STRIDE + 2 * d0) = cw;
+                }
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+                const int rr = 2 * it + hh;
+                const int row = r0 + QB * b + rr;
+                const uint4 cv = *reinterpret_cast<const uint4 *>(ep + rr * EP_STRIDE + 16 * cc);
+                const uint32_t cws[4] = {cv.x, cv.y, cv.z, cv.w};
+                const uint32_t gws[4] = {gw[b][it].x, gw[b][it].y, gw[b][it].z, gw[b][it].w};
+                uint32_t ow[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float ov[2];
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const float ctx = hf ? hi_f(cws[q]) : lo_f(cws[q]);
+                        const float gv = hf ? hi_f(gws[q]) : lo_f(gws[q]);
+                        // Hardware reciprocal (exact at 1 and 2: a saturated logit
+                        // gives exactly 1, a zero logit exactly 1/2).
+                        const float sg = rbf(__builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * LOG2E)));
+                        ov[hf] = ctx * sg;
+                    }
+                    ow[q] = pack2(ov[0], ov[1]);
+                }
+                if (active && row < p.S)
+                    *reinterpret_cast<uint4 *>(p.out + ((size_t)row * p.Hq + h) * D + 8 * cc) =
+                        make_uint4(ow[0], ow[1], ow[2], ow[3]);
             }
-            *reinterpret_cast<uint2 *>(dst + d0) = make_uint2(pack2(ov[0], ov[1]), pack2(ov[2], ov[3]));
         }
     }
 }
@@ -775,7 +1135,7 @@ hipError_t launch_mask_pack(const MaskPackParams &p, int nrb, hipStream_t stream
 
 hipError_t launch_attention(const AttnParams &p, bool masked, hipStream_t stream)
 {
-    const int nblocks = p.nrb * p.Hkv * p.n_hg;
+    const int nblocks = p.n_wg;
     if (masked)
         hipLaunchKernelGGL(attn_fwd<true>, dim3(nblocks), dim3(ATHREADS), 0, stream, p);
     else
