@@ -135,7 +135,9 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        if mask is not None:
+        if not p.causal:
+            ctx.prefill_bidirectional(qg, k, v, wq, wk, cos, sin, out=out, stream=stream)
+        elif mask is not None:
             ctx.prefill_masked(qg, k, v, wq, wk, cos, sin, mask, out=out, stream=stream)
         elif p.q_base:
             ctx.prefill_prefix(qg, k, v, wq, wk, cos, sin, p.q_base, out=out, stream=stream)

@@ -79,6 +79,7 @@ def _load():
         "attn_prefill_gated": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, vp]),
         "attn_prefill_prefix": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp]),
         "attn_prefill_masked": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, vp, vp]),
+        "attn_prefill_bidirectional": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, vp]),
         "attn_debug_prepare": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp, vp]),
         "attn_ctx_set_timing": (ctypes.c_int, [vp, ctypes.c_int]),
         "attn_ctx_read_timing": (ctypes.c_int, [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
@@ -134,6 +135,10 @@ def attn_prefill_prefix(ctx, inputs: attn_inputs, T: int, q_base: int, out: int,
 
 def attn_prefill_masked(ctx, inputs: attn_inputs, S: int, mask: int, out: int, stream: int) -> int:
     return lib.attn_prefill_masked(ctx, ctypes.byref(inputs), S, mask, out, stream)
+
+
+def attn_prefill_bidirectional(ctx, inputs: attn_inputs, S: int, out: int, stream: int) -> int:
+    return lib.attn_prefill_bidirectional(ctx, ctypes.byref(inputs), S, out, stream)
 
 
 def attn_debug_prepare(ctx, inputs: attn_inputs, T: int, q_base: int, qp_out, kp_out, stream) -> int:
@@ -242,6 +247,15 @@ class Context:
         rc = attn_prefill_gated(self.handle, inp, S, out.data_ptr(), self._stream(stream))
         if rc != ATTN_OK:
             raise AttnError(rc, "attn_prefill_gated")
+        return out
+
+    def prefill_bidirectional(self, qg, k, v, q_norm_w, k_norm_w, cos, sin, out=None, stream=None):
+        S = k.shape[0]
+        inp = self.inputs(qg, k, v, q_norm_w, k_norm_w, cos, sin, S, S)
+        out = self._out(out, S)
+        rc = attn_prefill_bidirectional(self.handle, inp, S, out.data_ptr(), self._stream(stream))
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_prefill_bidirectional")
         return out
 
     def prefill_prefix(self, qg, k, v, q_norm_w, k_norm_w, cos, sin, q_base: int, out=None, stream=None):

@@ -43,7 +43,7 @@ struct attn_ctx {
 
 namespace {
 
-constexpr int kKinds = 3;   // 0 gated, 1 prefix, 2 masked
+constexpr int kKinds = 4;   // 0 gated, 1 prefix, 2 masked, 3 bidirectional
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -180,7 +180,9 @@ int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kin
     }
     {
         Timer tm(ctx, s, ATTN_KERNEL_ATTENTION);
-        if (ga::launch_attention(ap, kind == 2, s) != hipSuccess)
+        if (ga::launch_attention(ap, kind == 2 ? ga::AttnMode::Masked
+                                     : kind == 3 ? ga::AttnMode::Bidirectional : ga::AttnMode::Causal,
+                                 s) != hipSuccess)
             return ATTN_ERR_LAUNCH;
         tm.stop();
     }
@@ -317,6 +319,11 @@ int attn_prefill_masked(attn_ctx *ctx, const attn_inputs *in, int32_t S, const u
                         void *stream)
 {
     return run(ctx, in, S, 0, 2, mask, out, stream);
+}
+
+int attn_prefill_bidirectional(attn_ctx *ctx, const attn_inputs *in, int32_t S, void *out, void *stream)
+{
+    return run(ctx, in, S, 0, 3, nullptr, out, stream);
 }
 
 int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, void *qp_out,

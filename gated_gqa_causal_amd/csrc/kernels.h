@@ -49,7 +49,8 @@ constexpr int kHeadsPerBlock = 4;
 
 hipError_t launch_kv_prologue(const KvPrologueParams &p, int ntiles, hipStream_t stream);
 hipError_t launch_mask_pack(const MaskPackParams &p, int nrb, hipStream_t stream);
-hipError_t launch_attention(const AttnParams &p, bool masked, hipStream_t stream);
+enum class AttnMode { Causal, Masked, Bidirectional };
+hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stream);
 hipError_t launch_kp_unpack(const uint16_t *kp, int Tpad, int T, int Hkv, uint16_t *out, hipStream_t stream);
 hipError_t launch_q_prologue_debug(const AttnParams &p, uint16_t *qp, hipStream_t stream);
 

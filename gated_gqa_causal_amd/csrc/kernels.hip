@@ -795,7 +795,9 @@ __device__ __forceinline__ void rescale(f32x16 (&o)[8], float alpha)
 // so each half pairs 32 MFMAs with one block's softmax.  A block's O is
 // rescaled (rarely) between its last product with the old running max and its
 // first with the new one.
-template <bool MASKED>
+// MASKED: per-row visibility bits ANDed with causality.  BIDIR: no causal
+// predicate (every row walks all key tiles; only keys past T are hidden).
+template <bool MASKED, bool BIDIR>
 __global__ __attribute__((amdgpu_flat_work_group_size(ATHREADS, ATHREADS), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd(AttnParams p)
 {
@@ -837,7 +839,7 @@ void attn_fwd(AttnParams p)
         const int r0 = rb * QW;                          // the wave's rows r0 .. r0 + 63
 
         const int P0 = p.q_base + r0;                    // first absolute position (a multiple of 64)
-        const int ntiles = min(P0 + QW - 1, p.T - 1) / KT + 1;
+        const int ntiles = BIDIR ? (p.T + KT - 1) / KT : min(P0 + QW - 1, p.T - 1) / KT + 1;
         const int diag0 = P0 / KT;                       // block b's diagonal tile is diag0 + b
 
         // The workgroup's tile sequence: every tile up to the diagonal, or (masked)
@@ -975,7 +977,11 @@ void attn_fwd(AttnParams p)
             return MASKED ? (bitsbuf[u & 7][QB * b + j] >> (4 * hh)) : 0u;
         };
         auto causal_hide = [&](int u, int b, f32x16 &sc) {
-            if (!MASKED) {
+            if (BIDIR) {
+                // Only the last tile can hold keys past T (zero-padded): hide them.
+                if (u == ntiles - 1 && (p.T & (KT - 1)) != 0)
+                    hide_all(sc, ((1u << (p.T & (KT - 1))) - 1u) >> (4 * hh));
+            } else if (!MASKED) {
                 const int t = u;                       // unmasked: walk index = tile index
                 const int dg = diag0 + b;
                 if (t >= dg) {
@@ -1133,13 +1139,19 @@ hipError_t launch_mask_pack(const MaskPackParams &p, int nrb, hipStream_t stream
     return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnParams &p, bool masked, hipStream_t stream)
+hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stream)
 {
     const int nblocks = p.n_wg;
-    if (masked)
-        hipLaunchKernelGGL(attn_fwd<true>, dim3(nblocks), dim3(ATHREADS), 0, stream, p);
-    else
-        hipLaunchKernelGGL(attn_fwd<false>, dim3(nblocks), dim3(ATHREADS), 0, stream, p);
+    switch (mode) {
+    case AttnMode::Masked:
+        hipLaunchKernelGGL((attn_fwd<true, false>), dim3(nblocks), dim3(ATHREADS), 0, stream, p);
+        break;
+    case AttnMode::Bidirectional:
+        hipLaunchKernelGGL((attn_fwd<false, true>), dim3(nblocks), dim3(ATHREADS), 0, stream, p);
+        break;
+    default:
+        hipLaunchKernelGGL((attn_fwd<false, false>), dim3(nblocks), dim3(ATHREADS), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

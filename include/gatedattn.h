@@ -107,8 +107,9 @@ ATTN_EXPORT const char *attn_status_string(int status);
 /*
  * Host-only check of one call, the same one every entry point runs first.
  * kind: 0 = gated full pass (q_base must be 0), 1 = prefix window,
- * 2 = masked (q_base must be 0, mask required).  T keys, query rows
- * T - q_base.  Touches no device; usable without a GPU.
+ * 2 = masked (q_base must be 0, mask required), 3 = bidirectional full pass
+ * (q_base must be 0).  T keys, query rows T - q_base.  Touches no device;
+ * usable without a GPU.
  */
 ATTN_EXPORT int attn_validate(const attn_geometry *geom, const attn_inputs *in, int32_t T, int32_t q_base,
                   int32_t kind, const void *mask, const void *out);
@@ -151,6 +152,17 @@ ATTN_EXPORT int attn_prefill_prefix(attn_ctx *ctx, const attn_inputs *in, int32_
  */
 ATTN_EXPORT int attn_prefill_masked(attn_ctx *ctx, const attn_inputs *in, int32_t S, const uint8_t *mask,
                         void *out, void *stream);
+
+/*
+ * Bidirectional full pass over S tokens (no causal predicate: every row
+ * sees keys 0..S-1), the variant the system1-omni gated-attention page
+ * ("cuda: widen the attention query tile on sm_89 and sm_120") runs for the
+ * vision path through the same launch.  Same inputs, layouts and errors as
+ * attn_prefill_gated; out: device bf16 [S][Hq * D].  S == 0 is a no-op.
+ * The last row equals attn_prefill_gated's last row bit for bit.
+ */
+ATTN_EXPORT int attn_prefill_bidirectional(attn_ctx *ctx, const attn_inputs *in, int32_t S, void *out,
+                                           void *stream);
 
 /*
  * Test hook: writes the prepared (normed, rotated) queries and keys the

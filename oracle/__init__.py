@@ -49,6 +49,7 @@ class _Problem(ctypes.Structure):
         ("cos_tab", ctypes.c_void_p), ("sin_tab", ctypes.c_void_p),
         ("n_pos", ctypes.c_int32),
         ("mask", ctypes.c_void_p), ("kp", ctypes.c_void_p),
+        ("causal", ctypes.c_int32),
     ]
 
 
@@ -56,16 +57,23 @@ def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+ORACLE_ABI = 2      # layout of _Problem; oracle.c's oracle_abi() must agree
+
+
 class Oracle:
-    """Handle on one build of the oracle library."""
+    """Handle on one build of the oracle library.  The default library is
+    (re)built when it is missing or older than oracle.c."""
 
     def __init__(self, libpath: str = LIBPATH):
-        if not os.path.exists(libpath):
-            if libpath != LIBPATH:
-                raise FileNotFoundError(libpath)
-            build()
+        if libpath == LIBPATH:
+            if not os.path.exists(libpath) or os.path.getmtime(libpath) < os.path.getmtime(SOURCE):
+                build()
+        elif not os.path.exists(libpath):
+            raise FileNotFoundError(libpath)
         self.lib = ctypes.CDLL(libpath)
         L = self.lib
+        if L.oracle_abi() != ORACLE_ABI:
+            raise RuntimeError(f"{libpath}: oracle ABI {L.oracle_abi()}, expected {ORACLE_ABI}; rebuild it")
         L.oracle_bf16_round.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
         L.oracle_norm_rope.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int32, ctypes.c_int32,
                                                                ctypes.c_float, ctypes.c_void_p]
@@ -109,7 +117,8 @@ class Oracle:
         s = _Problem(p.n_q_heads, p.n_kv_heads, p.head_dim, p.rotary_dim, p.rms_eps, p.T,
                      p.q_base, _ptr(arrs["qg"]), _ptr(arrs["k"]), _ptr(arrs["v"]),
                      _ptr(arrs["wq"]), _ptr(arrs["wk"]), _ptr(arrs["cos"]), _ptr(arrs["sin"]),
-                     arrs["cos"].shape[0], _ptr(arrs["mask"]), _ptr(kp))
+                     arrs["cos"].shape[0], _ptr(arrs["mask"]), _ptr(kp),
+                     1 if getattr(p, "causal", True) else 0)
         return s, arrs
 
     def prepare_keys(self, p) -> np.ndarray:

@@ -23,8 +23,10 @@
  *   6. Context = bf16(sum_j w_j v_j), fp32 accumulation.
  *   7. Output = bf16(ctx * bf16(sigmoid(g))).
  *
- * Visibility: key j is visible to row i iff j <= p and, when a mask is given,
- * mask[i][j] != 0 (non-zero = visible).  A row with no visible key outputs 0.
+ * Visibility: key j is visible to row i iff j <= p (causal pass; the
+ * bidirectional pass drops this predicate, every key 0..T-1 is a candidate)
+ * and, when a mask is given, mask[i][j] != 0 (non-zero = visible).  A row with
+ * no visible key outputs 0.
  * KV head of query head h is h / (Hq / Hkv).
  *
  * Every sum runs in ascending index order in fp32.  Build with
@@ -86,9 +88,10 @@ typedef struct {
     int32_t n_pos;
     const uint8_t *mask;    /* [T-q_base][T] or NULL                        */
     const bf16_t *kp;       /* prepared keys [Hkv][T][D] from oracle_prepare_keys */
+    int32_t causal;         /* 1: causal pass; 0: bidirectional (q_base 0)   */
 } oracle_problem;
 
-int oracle_abi(void) { return 1; }
+int oracle_abi(void) { return 2; }   /* 2: oracle_problem.causal */
 int oracle_mutation(void) { return ORACLE_MUTATION; }
 
 void oracle_bf16_round(const float *in, bf16_t *out, int64_t n)
@@ -187,11 +190,15 @@ int oracle_prepare_queries(const oracle_problem *p, bf16_t *qp)
 static int visible(const oracle_problem *p, int32_t i, int32_t j)
 {
     const int32_t pos = p->q_base + i;
+#if ORACLE_MUTATION == 14
+    if (j > pos)                                          /* causal in the bidirectional pass */
+        return 0;
+#endif
 #if ORACLE_MUTATION == 8
-    if (j >= pos)                                         /* strict causality */
+    if (p->causal && j >= pos)                            /* strict causality */
         return 0;
 #else
-    if (j > pos)
+    if (p->causal && j > pos)
         return 0;
 #endif
     if (p->mask) {
@@ -286,9 +293,9 @@ int oracle_attention(const oracle_problem *p, const int32_t *rows, int32_t n_row
                     wsum += wt[j];
                 }
 #if ORACLE_MUTATION == 12
-                const int32_t jend = pos;                  /* drops the last visible key */
+                const int32_t jend = p->causal ? pos : T - 1;   /* drops the last visible key */
 #else
-                const int32_t jend = pos + 1;
+                const int32_t jend = p->causal ? pos + 1 : T;
 #endif
                 for (int32_t j = 0; j < jend && j < T; ++j) {
                     if (!vis[j])

@@ -171,6 +171,7 @@ class Problem:
     mask: Optional[np.ndarray] = None   # [rows][T] uint8 or None
     rms_eps: float = 1e-6
     seed: int = 0
+    causal: bool = True    # False: bidirectional pass (every row sees keys 0..T-1)
 
     @property
     def rows(self) -> int:
@@ -183,6 +184,8 @@ class Problem:
     def visible_pairs_per_head(self) -> int:
         if self.mask is not None:
             return int(self.mask.astype(bool).sum())
+        if not self.causal:
+            return self.rows * self.T
         n = self.rows
         return n * self.q_base + n * (n + 1) // 2
 
@@ -203,7 +206,7 @@ def make_problem(*, T: int, n_q_heads: int = 24, n_kv_heads: int = 2, head_dim: 
                  rotary_dim: int = 64, q_base: int = 0, seed: int = 0, q_sigma: float = 1.0,
                  gate_sigma: float = 1.0, kv_sigma: float = 1.0, w_sigma: float = 0.1,
                  mask_budget: Optional[int] = None, theta: float = 1e7, n_pos: Optional[int] = None,
-                 name: str = "custom") -> Problem:
+                 causal: bool = True, name: str = "custom") -> Problem:
     """Draws one problem in the fixed order qg(q), qg(gate), K, V, w_q, w_k, mask."""
     rows = T - q_base
     Hq, Hkv, D = n_q_heads, n_kv_heads, head_dim
@@ -224,18 +227,23 @@ def make_problem(*, T: int, n_q_heads: int = 24, n_kv_heads: int = 2, head_dim: 
     if mask_budget is not None:
         assert q_base == 0, "masked problems start at q_base 0"
         mask = visibility_mask(T, mask_budget, seed)
+    if not causal:
+        assert q_base == 0 and mask_budget is None, "a bidirectional pass starts at q_base 0, unmasked"
     return Problem(name=name, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, rotary_dim=rotary_dim,
                    T=T, q_base=q_base, qg=qg, k=k, v=v, q_norm_w=wq, k_norm_w=wk, cos=cos,
-                   sin=sin, mask=mask, seed=seed)
+                   sin=sin, mask=mask, seed=seed, causal=causal)
 
 
-# The five workloads: (keys, q heads, kv heads, q_base, seed, gate sigma, mask budget).
+# The workloads: (keys, q heads, kv heads, q_base, seed, gate sigma, mask budget, causal).
+# c5 is the bidirectional pass (vision-path attention, no causal predicate) at c2's shape.
 CONFIGS = {
     "c0_tiny_s64": dict(T=64, n_q_heads=24, n_kv_heads=2, q_base=0, seed=0),
     "c1_dense_s2048": dict(T=2048, n_q_heads=24, n_kv_heads=2, q_base=0, seed=1),
     "c2_dense_s8192_g4": dict(T=8192, n_q_heads=16, n_kv_heads=4, q_base=0, seed=2, gate_sigma=2.0),
     "c3_prefix_t8192_qb1024": dict(T=8192, n_q_heads=24, n_kv_heads=2, q_base=1024, seed=3),
     "c4_masked_s8192": dict(T=8192, n_q_heads=24, n_kv_heads=2, q_base=0, seed=4, mask_budget=2048),
+    "c5_bidir_s8192_g4": dict(T=8192, n_q_heads=16, n_kv_heads=4, q_base=0, seed=5, gate_sigma=2.0,
+                              causal=False),
 }
 
 

@@ -41,12 +41,12 @@ def rope_f64(x: np.ndarray, pos, rotary_dim: int = 64, theta: float = 1e7) -> np
 
 
 def sdpa_f64(qp: np.ndarray, kp: np.ndarray, v: np.ndarray, q_base: int, mask=None,
-             scale: float = 1.0 / 16.0) -> np.ndarray:
+             scale: float = 1.0 / 16.0, causal: bool = True) -> np.ndarray:
     """Exact attention of prepared queries/keys.
 
     qp [rows][Hq][D], kp [Hkv][T][D], v [T][Hkv][D] (float64 values);
-    returns ctx [rows][Hq][D].  Visibility is causal on absolute positions,
-    ANDed with ``mask`` [rows][T] when given.
+    returns ctx [rows][Hq][D].  Visibility is causal on absolute positions
+    (every key when ``causal`` is False), ANDed with ``mask`` [rows][T] when given.
     """
     rows, Hq, D = qp.shape
     Hkv, T, _ = kp.shape
@@ -55,6 +55,8 @@ def sdpa_f64(qp: np.ndarray, kp: np.ndarray, v: np.ndarray, q_base: int, mask=No
     vv = torch.from_numpy(np.ascontiguousarray(np.asarray(v, np.float64).transpose(1, 0, 2)))[None]
     pos = q_base + np.arange(rows)
     vis = np.arange(T)[None, :] <= pos[:, None]
+    if not causal:
+        vis = np.ones((rows, T), bool)
     if mask is not None:
         vis &= np.asarray(mask) != 0
     m = torch.from_numpy(vis)
@@ -63,7 +65,7 @@ def sdpa_f64(qp: np.ndarray, kp: np.ndarray, v: np.ndarray, q_base: int, mask=No
     return o[0].numpy().transpose(1, 0, 2)
 
 
-def score_max_f64(qp, kp, q_base, mask=None, scale=1.0 / 16.0) -> np.ndarray:
+def score_max_f64(qp, kp, q_base, mask=None, scale=1.0 / 16.0, causal=True) -> np.ndarray:
     """max_j |s_j| over visible keys, per (row, q head): [rows][Hq]."""
     rows, Hq, D = qp.shape
     Hkv, T, _ = kp.shape
@@ -72,6 +74,8 @@ def score_max_f64(qp, kp, q_base, mask=None, scale=1.0 / 16.0) -> np.ndarray:
     s = np.einsum("rhd,htd->rht", qp, kk) * scale
     pos = q_base + np.arange(rows)
     vis = np.arange(T)[None, :] <= pos[:, None]
+    if not causal:
+        vis = np.ones((rows, T), bool)
     if mask is not None:
         vis &= np.asarray(mask) != 0
     s = np.where(vis[:, None, :], np.abs(s), 0.0)

@@ -47,6 +47,8 @@ def run(ctx, dp: DevProblem, out=None) -> torch.Tensor:
     p = dp.p
     if p.mask is not None:
         return ctx.prefill_masked(*dp.args(), dp.mask, out=out)
+    if not p.causal:
+        return ctx.prefill_bidirectional(*dp.args(), out=out)
     if p.q_base:
         return ctx.prefill_prefix(*dp.args(), p.q_base, out=out)
     return ctx.prefill_gated(*dp.args(), out=out)

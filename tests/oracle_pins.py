@@ -43,9 +43,9 @@ def _bf16_bits(x):
     return synth.f32_to_bf16_bits(np.asarray(x, np.float32))
 
 
-def _problem(T, Hq=4, Hkv=2, q_base=0, seed=0, mask_budget=None, gate_sigma=1.0):
+def _problem(T, Hq=4, Hkv=2, q_base=0, seed=0, mask_budget=None, gate_sigma=1.0, causal=True):
     return synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, q_base=q_base, seed=seed,
-                              mask_budget=mask_budget, gate_sigma=gate_sigma)
+                              mask_budget=mask_budget, gate_sigma=gate_sigma, causal=causal)
 
 
 # --------------------------------------------------------------------------
@@ -212,6 +212,37 @@ def pin_attention_vs_sdpa(o):
         bad = np.abs(got - want) > tol
         assert not bad.any(), (f"context vs float64 attention, geometry {n}: "
                                f"{bad.sum()} of {bad.size}, worst {np.max(np.abs(got - want) - tol)}")
+
+
+def pin_bidirectional_vs_sdpa(o):
+    """Bidirectional pass (no causal predicate; the survey's vision-path variant):
+    ungated context against float64 attention over every key, same bound as above."""
+    for n, (T, Hq, Hkv) in enumerate([(1, 2, 1), (5, 4, 2), (37, 6, 2), (70, 8, 2)]):
+        p = _problem(T, Hq, Hkv, seed=140 + n, causal=False)
+        r = o.attention(p, want_ctx=True)
+        qp = bf(o.prepare_queries(p))
+        kp = bf(o.prepare_keys(p))
+        v = bf(p.v)
+        want = sdpa_f64(qp, kp, v, 0, causal=False)
+        absv = sdpa_f64(qp, kp, np.abs(v), 0, causal=False)
+        smax = score_max_f64(qp, kp, 0, causal=False)
+        got = bf(r["ctx"]).reshape(want.shape)
+        tol = 1.5 * (U * np.abs(want) + U * (1.0 + 2.0 * smax[..., None]) * absv) + 1e-7
+        bad = np.abs(got - want) > tol
+        assert not bad.any(), (f"bidirectional context vs float64 attention, geometry {n}: "
+                               f"{bad.sum()} of {bad.size}")
+
+
+def pin_bidirectional_last_row_equals_causal(o):
+    """The last row sees every key in both passes: identical outputs, bit for bit.
+    Earlier rows see later keys only in the bidirectional pass, so they differ."""
+    for T in [9, 64]:
+        pc = _problem(T, 4, 2, seed=150)
+        pb = _problem(T, 4, 2, seed=150, causal=False)
+        assert np.array_equal(pc.qg, pb.qg) and np.array_equal(pc.k, pb.k)
+        oc, ob = o.attention(pc), o.attention(pb)
+        assert np.array_equal(oc[-1], ob[-1]), f"last row, T={T}"
+        assert not np.array_equal(oc[0], ob[0]), f"row 0 should see later keys, T={T}"
 
 
 def pin_row0_closed_form(o):

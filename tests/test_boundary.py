@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["attn_ctx_create", "attn_prefill_gated", "attn_prefill_prefix", "attn_prefill_masked",
-              "attn_ctx_destroy", "attn_abi_version", "attn_status_string", "attn_validate"]:
+              "attn_prefill_bidirectional", "attn_ctx_destroy", "attn_abi_version", "attn_status_string",
+              "attn_validate"]:
         assert n in names
 
 
@@ -81,7 +82,11 @@ REFUSALS = [
     ({}, 200, 256, 1, None, FAKE, {}, "RANGE"),                    # q_base > T
     ({}, 200, 64, 1, None, FAKE, {}, "ALIGN"),                     # q_base % 128
     ({}, 200, 128, 0, None, FAKE, {}, "RANGE"),                    # q_base on the full pass
-    ({}, 200, 0, 3, None, FAKE, {}, "RANGE"),                      # bad kind
+    ({}, 200, 0, 4, None, FAKE, {}, "RANGE"),                      # bad kind
+    ({}, 200, 0, -1, None, FAKE, {}, "RANGE"),                     # negative kind
+    ({}, 200, -128, 1, None, FAKE, {}, "RANGE"),                   # negative q_base
+    ({}, 200, 128, 3, None, FAKE, {}, "RANGE"),                    # q_base on the bidirectional pass
+    ({}, 64, 0, 3, None, FAKE, dict(v=0), "NULL_ARG"),
     ({}, 64, 0, 0, None, FAKE, dict(n_pos=63), "RANGE"),           # short cos/sin table
     ({}, 64, 0, 0, None, None, {}, "NULL_ARG"),                    # out
     ({}, 64, 0, 2, None, FAKE, {}, "NULL_ARG"),                    # mask
@@ -112,7 +117,7 @@ def test_null_geometry(ga):
     assert rc == ga.ATTN_ERR_NULL_ARG
 
 
-@pytest.mark.parametrize("T,qb,kind", [(0, 0, 0), (0, 0, 2), (256, 256, 1), (128, 128, 1)])
+@pytest.mark.parametrize("T,qb,kind", [(0, 0, 0), (0, 0, 2), (256, 256, 1), (128, 128, 1), (0, 0, 3)])
 def test_empty_launch_is_ok_without_pointers(ga, T, qb, kind):
     # Zero query rows: a no-op, even with every pointer NULL (torch gives 0 for empty tensors).
     assert ga.attn_validate(_geom(ga), None, T, qb, kind, None, None) == ga.ATTN_OK
@@ -122,6 +127,7 @@ def test_valid_calls_pass(ga):
     assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 0, 0, None, FAKE) == ga.ATTN_OK
     assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 128, 1, None, FAKE) == ga.ATTN_OK
     assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 0, 2, FAKE + 3, FAKE) == ga.ATTN_OK
+    assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 0, 3, None, FAKE) == ga.ATTN_OK
     for G in [1, 2, 3, 12, 16]:
         assert ga.attn_validate(_geom(ga, n_q_heads=2 * G), _inputs(ga), 64, 0, 0, None, FAKE) == 0
 
@@ -131,6 +137,7 @@ def test_null_context_refused(ga):
     assert ga.attn_prefill_gated(None, inp, 64, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_prefill_prefix(None, inp, 64, 0, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_prefill_masked(None, inp, 64, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
+    assert ga.attn_prefill_bidirectional(None, inp, 64, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_debug_prepare(None, inp, 64, 0, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_ctx_set_timing(None, 1) == ga.ATTN_ERR_NULL_ARG
     ga.attn_ctx_destroy(None)      # no-op

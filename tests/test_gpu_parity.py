@@ -89,6 +89,10 @@ FULL_CASES = [
     ("prefix_t513_qb256", dict(T=513, n_q_heads=8, n_kv_heads=2, q_base=256, seed=12)),
     ("masked_s300_b40", dict(T=300, n_q_heads=24, n_kv_heads=2, seed=13, mask_budget=40)),
     ("masked_s257_b7_g4", dict(T=257, n_q_heads=8, n_kv_heads=2, seed=14, mask_budget=7)),
+    ("bidir_s64", dict(T=64, n_q_heads=24, n_kv_heads=2, seed=15, causal=False)),
+    ("bidir_s1", dict(T=1, n_q_heads=4, n_kv_heads=2, seed=16, causal=False)),
+    ("bidir_s200_ragged", dict(T=200, n_q_heads=16, n_kv_heads=4, seed=17, gate_sigma=2.0, causal=False)),
+    ("bidir_s333_g6", dict(T=333, n_q_heads=6, n_kv_heads=1, seed=18, causal=False)),
 ]
 
 
@@ -105,7 +109,7 @@ def test_parity_full(orc, name, kw):
 
 
 # --------------------------------------------------------------------------
-# The five workloads at full size, in the benchmark's launch configuration,
+# The workloads at full size, in the benchmark's launch configuration,
 # on sampled rows the oracle computes one by one
 # --------------------------------------------------------------------------
 
@@ -137,6 +141,21 @@ def test_prefix_window_equals_full_pass(T, qb, Hq, Hkv):
     b = gpu_out(win, ctx)
     ctx.close()
     assert np.array_equal(a[qb:], b)
+
+
+@pytest.mark.parametrize("T,Hq,Hkv", [(300, 24, 2), (2048, 16, 4)])
+def test_bidirectional_last_row_equals_causal(T, Hq, Hkv):
+    """The last row sees every key in both passes: the same row bit for bit; the
+    first row differs (it sees later keys only in the bidirectional pass)."""
+    say(f"bidirectional last row T={T}")
+    pc = synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=25)
+    pb = synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=25, causal=False)
+    ctx = make_ctx(pc)
+    a = gpu_out(pc, ctx)
+    b = gpu_out(pb, ctx)
+    ctx.close()
+    assert np.array_equal(a[-1], b[-1])
+    assert not np.array_equal(a[0], b[0])
 
 
 @pytest.mark.parametrize("T", [300, 2048])

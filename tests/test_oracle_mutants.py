@@ -28,6 +28,7 @@ MUTANTS = {
     11: "query position ignores q_base",
     12: "last visible key dropped from the context",
     13: "K read in place of V",
+    14: "causal predicate kept in the bidirectional pass",
 }
 
 
