@@ -86,6 +86,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--mode", choices=["attention", "copy"], default="attention")
+    ap.add_argument("--cached", action="store_true",
+                    help="prefix workloads: keys before q_base come from a prepared K/V cache "
+                         "(attn_prefill_append); only the window's keys are prepared per step")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -134,8 +137,22 @@ def main():
     ctx = ga.Context(p.n_q_heads, p.n_kv_heads, p.T, p.rms_eps)
     stream = torch.cuda.current_stream()
 
+    cache = None
+    if args.cached:
+        if not p.q_base or mask is not None or not p.causal:
+            raise SystemExit("--cached needs a prefix workload (q_base > 0, causal, unmasked)")
+        cache = ctx.kv_cache()
+        qb = p.q_base
+        # The prefix's keys, prepared once outside the timing (their query rows are
+        # not part of this workload: a zero qg block stands in for them).
+        zero_qg = torch.zeros((qb,) + tuple(qg.shape[1:]), dtype=torch.bfloat16, device=dev)
+        ctx.prefill_append(zero_qg, k[:qb], v[:qb], wq, wk, cos, sin, qb, 0, cache)
+        k_new, v_new = k[qb:], v[qb:]
+
     def step():
-        if not p.causal:
+        if cache is not None:
+            ctx.prefill_append(qg, k_new, v_new, wq, wk, cos, sin, p.T, p.q_base, cache, out=out, stream=stream)
+        elif not p.causal:
             ctx.prefill_bidirectional(qg, k, v, wq, wk, cos, sin, out=out, stream=stream)
         elif mask is not None:
             ctx.prefill_masked(qg, k, v, wq, wk, cos, sin, mask, out=out, stream=stream)
@@ -186,7 +203,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": p.name, "tokens": p.T, "q_base": p.q_base, "n_q_heads": p.n_q_heads,
                    "n_kv_heads": p.n_kv_heads, "head_dim": p.head_dim, "rotary_dim": p.rotary_dim,
-                   "masked": p.mask is not None, "seed": p.seed,
+                   "masked": p.mask is not None, "causal": p.causal, "cached_prefix": bool(args.cached),
+                   "seed": p.seed,
                    "algorithmic_gflop": round(flops / 1e9, 3)},
         "kernels_ms": {"attention": round(attn_avg_ms, 5),
                        "kv_prologue": round(pro_ms / max(pro_n, 1), 5),

@@ -80,6 +80,8 @@ def _load():
         "attn_prefill_prefix": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp]),
         "attn_prefill_masked": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, vp, vp]),
         "attn_prefill_bidirectional": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, vp]),
+        "attn_kv_cache_bytes": (ctypes.c_int, [ctypes.POINTER(attn_geometry), ctypes.POINTER(ctypes.c_size_t)]),
+        "attn_prefill_append": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp, vp]),
         "attn_debug_prepare": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp, vp]),
         "attn_ctx_set_timing": (ctypes.c_int, [vp, ctypes.c_int]),
         "attn_ctx_read_timing": (ctypes.c_int, [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
@@ -139,6 +141,18 @@ def attn_prefill_masked(ctx, inputs: attn_inputs, S: int, mask: int, out: int, s
 
 def attn_prefill_bidirectional(ctx, inputs: attn_inputs, S: int, out: int, stream: int) -> int:
     return lib.attn_prefill_bidirectional(ctx, ctypes.byref(inputs), S, out, stream)
+
+
+def attn_kv_cache_bytes(geom: attn_geometry):
+    """(status, bytes) of a K/V cache for the geometry."""
+    n = ctypes.c_size_t()
+    rc = lib.attn_kv_cache_bytes(ctypes.byref(geom), ctypes.byref(n))
+    return rc, n.value
+
+
+def attn_prefill_append(ctx, inputs: attn_inputs, T: int, q_base: int, kv_cache: int, out: int,
+                        stream: int) -> int:
+    return lib.attn_prefill_append(ctx, ctypes.byref(inputs), T, q_base, kv_cache, out, stream)
 
 
 def attn_debug_prepare(ctx, inputs: attn_inputs, T: int, q_base: int, qp_out, kp_out, stream) -> int:
@@ -247,6 +261,32 @@ class Context:
         rc = attn_prefill_gated(self.handle, inp, S, out.data_ptr(), self._stream(stream))
         if rc != ATTN_OK:
             raise AttnError(rc, "attn_prefill_gated")
+        return out
+
+    def kv_cache(self):
+        """A zeroed device K/V cache for this context's geometry (uint8 tensor)."""
+        import torch
+        rc, n = attn_kv_cache_bytes(self.geom)
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_kv_cache_bytes")
+        return torch.zeros(n, dtype=torch.uint8, device=f"cuda:{self.device}")
+
+    def prefill_append(self, qg, k_new, v_new, q_norm_w, k_norm_w, cos, sin, T: int, q_base: int, kv_cache,
+                       out=None, stream=None):
+        """Rows q_base..T-1 over cache keys 0..T-1; k_new / v_new are the raw rows of
+        positions q_base..T-1, prepared into kv_cache by this call."""
+        import torch
+        rows = T - q_base
+        inp = self.inputs(qg, k_new, v_new, q_norm_w, k_norm_w, cos, sin, rows, rows)
+        rc, n = attn_kv_cache_bytes(self.geom)
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_kv_cache_bytes")
+        self._check("kv_cache", kv_cache, torch.uint8, (n,))
+        out = self._out(out, rows)
+        rc = attn_prefill_append(self.handle, inp, T, q_base, kv_cache.data_ptr(), out.data_ptr(),
+                                 self._stream(stream))
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_prefill_append")
         return out
 
     def prefill_bidirectional(self, qg, k, v, q_norm_w, k_norm_w, cos, sin, out=None, stream=None):

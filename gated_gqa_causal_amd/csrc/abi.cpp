@@ -43,7 +43,7 @@ struct attn_ctx {
 
 namespace {
 
-constexpr int kKinds = 4;   // 0 gated, 1 prefix, 2 masked, 3 bidirectional
+constexpr int kKinds = 5;   // 0 gated, 1 prefix, 2 masked, 3 bidirectional, 4 append to a K/V cache
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -107,7 +107,17 @@ void fill_kv_params(ga::KvPrologueParams &kp, const attn_ctx *ctx, const attn_in
     kp.T = T;
     kp.Hkv = ctx->geom.n_kv_heads;
     kp.Tpad = ctx->tpad;
+    kp.tile0 = 0;
+    kp.k_row0 = 0;
     kp.eps = ctx->geom.rms_eps;
+}
+
+// Bytes of a caller-owned K/V cache for a geometry: prepared keys and
+// transposed values, max_tokens rounded up to 64, in the workspace's layout.
+size_t kv_cache_bytes(const attn_geometry &g)
+{
+    const size_t tpad = ((size_t)g.max_tokens + 63) / 64 * 64;
+    return 2 * (size_t)g.n_kv_heads * tpad * ATTN_HEAD_DIM * 2;
 }
 
 void fill_attn_params(ga::AttnParams &ap, const attn_ctx *ctx, const attn_inputs *in, int T, int q_base,
@@ -139,6 +149,8 @@ void fill_attn_params(ga::AttnParams &ap, const attn_ctx *ctx, const attn_inputs
     ap.n_wg = (int)std::min<int64_t>((int64_t)ap.nrb * ap.Hkv * ap.n_hg, ctx->num_cus);
 }
 
+// kind 4: `mask` is the caller's K/V cache; the prologue writes keys
+// q_base..T-1 into it (k and v hold only those rows) and attention reads it.
 int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kind, const uint8_t *mask,
         void *out, void *stream)
 {
@@ -155,16 +167,32 @@ int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kin
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();   // clear a stale error so the launch status below is ours
 
+    uint16_t *cache_k = nullptr, *cache_v = nullptr;
+    if (kind == 4) {
+        cache_k = reinterpret_cast<uint16_t *>(const_cast<uint8_t *>(mask));
+        cache_v = cache_k + (size_t)ctx->geom.n_kv_heads * ctx->tpad * ATTN_HEAD_DIM;
+    }
     ga::KvPrologueParams kvp;
     fill_kv_params(kvp, ctx, in, T);
+    if (kind == 4) {
+        kvp.kp = cache_k;
+        kvp.vt = cache_v;
+        kvp.tile0 = q_base / ga::kKeysPerTile;
+        kvp.k_row0 = q_base;
+    }
     {
         Timer tm(ctx, s, ATTN_KERNEL_KV_PROLOGUE);
-        if (ga::launch_kv_prologue(kvp, (T + ga::kKeysPerTile - 1) / ga::kKeysPerTile, s) != hipSuccess)
+        const int tiles = (T + ga::kKeysPerTile - 1) / ga::kKeysPerTile - kvp.tile0;
+        if (ga::launch_kv_prologue(kvp, tiles, s) != hipSuccess)
             return ATTN_ERR_LAUNCH;
         tm.stop();
     }
     ga::AttnParams ap;
     fill_attn_params(ap, ctx, in, T, q_base, out);
+    if (kind == 4) {
+        ap.kp = cache_k;
+        ap.vt = cache_v;
+    }
     if (kind == 2) {
         ga::MaskPackParams mp;
         mp.mask = mask;
@@ -222,7 +250,7 @@ int attn_validate(const attn_geometry *geom, const attn_inputs *in, int32_t T, i
         return ATTN_ERR_RANGE;
     if (q_base < 0 || q_base > T)
         return ATTN_ERR_RANGE;
-    if (kind != 1 && q_base != 0)
+    if (kind != 1 && kind != 4 && q_base != 0)
         return ATTN_ERR_RANGE;
     if (q_base % ATTN_QBASE_ALIGN != 0)
         return ATTN_ERR_ALIGN;
@@ -232,12 +260,14 @@ int attn_validate(const attn_geometry *geom, const attn_inputs *in, int32_t T, i
         return ATTN_ERR_NULL_ARG;
     if (!in->qg || !in->k || !in->v || !in->q_norm_w || !in->k_norm_w || !in->cos_tab || !in->sin_tab)
         return ATTN_ERR_NULL_ARG;
-    if (kind == 2 && !mask)
+    if ((kind == 2 || kind == 4) && !mask)
         return ATTN_ERR_NULL_ARG;
     if (in->n_pos < T)
         return ATTN_ERR_RANGE;
     if (!aligned16(in->qg) || !aligned16(in->k) || !aligned16(in->v) || !aligned16(in->q_norm_w) ||
         !aligned16(in->k_norm_w) || !aligned16(in->cos_tab) || !aligned16(in->sin_tab) || !aligned16(out))
+        return ATTN_ERR_ALIGN;
+    if (kind == 4 && !aligned16(mask))
         return ATTN_ERR_ALIGN;
     return ATTN_OK;
 }
@@ -319,6 +349,24 @@ int attn_prefill_masked(attn_ctx *ctx, const attn_inputs *in, int32_t S, const u
                         void *stream)
 {
     return run(ctx, in, S, 0, 2, mask, out, stream);
+}
+
+int attn_kv_cache_bytes(const attn_geometry *geom, size_t *bytes)
+{
+    if (!bytes)
+        return ATTN_ERR_NULL_ARG;
+    *bytes = 0;
+    const int rc = check_geometry(geom);
+    if (rc != ATTN_OK)
+        return rc;
+    *bytes = kv_cache_bytes(*geom);
+    return ATTN_OK;
+}
+
+int attn_prefill_append(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, void *kv_cache,
+                        void *out, void *stream)
+{
+    return run(ctx, in, T, q_base, 4, static_cast<const uint8_t *>(kv_cache), out, stream);
 }
 
 int attn_prefill_bidirectional(attn_ctx *ctx, const attn_inputs *in, int32_t S, void *out, void *stream)

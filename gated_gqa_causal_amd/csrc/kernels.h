@@ -16,6 +16,8 @@ struct KvPrologueParams {
     uint16_t *kp;             // [Hkv][Tpad/32] tiles of 32 keys, chunk-major
     uint16_t *vt;             // [Hkv][Tpad/32] tiles of V^T, chunk-major
     int T, Hkv, Tpad;
+    int tile0;                // first tile written (grid x = tile - tile0)
+    int k_row0;               // position of row 0 of k and v
     float eps;
 };
 

@@ -77,7 +77,9 @@ __device__ __forceinline__ float word_f(const uint4 &u, int t)
 }
 
 // ---------------------------------------------------------------------------
-// K/V prologue.  grid (Tpad/32, Hkv), 256 threads.
+// K/V prologue.  grid (tiles, Hkv), 256 threads: tiles tile0 .. tile0 + tiles - 1
+// (keys up to T); k and v rows start at position k_row0 (0, or the first new
+// key when appending to a cache).
 // Both outputs are stored as 16 KB tiles of 32 keys in the order the attention
 // kernel's MFMA operand reads want them in LDS ("chunk-major": the 16-byte
 // chunk index outermost), so a tile moves to LDS as one contiguous copy and
@@ -99,14 +101,14 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
     __shared__ __align__(16) uint16_t ks[KT][D + 8];
     __shared__ __align__(16) uint16_t vs[KT][D + 8];
     __shared__ float rs[KT];
-    const int tile = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+    const int tile = p.tile0 + (int)blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
     const int t0 = tile * KT;
 
     for (int it = 0; it < 4; ++it) {
         const int idx = it * 256 + tid, r = idx >> 5, ch = idx & 31, key = t0 + r;
         uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
         if (key < p.T) {
-            const size_t off = ((size_t)key * p.Hkv + c) * D + ch * 8;
+            const size_t off = ((size_t)(key - p.k_row0) * p.Hkv + c) * D + ch * 8;
             kv = *reinterpret_cast<const uint4 *>(p.k + off);
             vv = *reinterpret_cast<const uint4 *>(p.v + off);
         }

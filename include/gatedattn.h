@@ -43,6 +43,7 @@
 #ifndef GATEDATTN_H
 #define GATEDATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -108,8 +109,9 @@ ATTN_EXPORT const char *attn_status_string(int status);
  * Host-only check of one call, the same one every entry point runs first.
  * kind: 0 = gated full pass (q_base must be 0), 1 = prefix window,
  * 2 = masked (q_base must be 0, mask required), 3 = bidirectional full pass
- * (q_base must be 0).  T keys, query rows T - q_base.  Touches no device;
- * usable without a GPU.
+ * (q_base must be 0), 4 = append to a K/V cache (`mask` is then the cache
+ * pointer: required, 16-byte aligned; k and v hold the T - q_base new rows).
+ * T keys, query rows T - q_base.  Touches no device; usable without a GPU.
  */
 ATTN_EXPORT int attn_validate(const attn_geometry *geom, const attn_inputs *in, int32_t T, int32_t q_base,
                   int32_t kind, const void *mask, const void *out);
@@ -163,6 +165,27 @@ ATTN_EXPORT int attn_prefill_masked(attn_ctx *ctx, const attn_inputs *in, int32_
  */
 ATTN_EXPORT int attn_prefill_bidirectional(attn_ctx *ctx, const attn_inputs *in, int32_t S, void *out,
                                            void *stream);
+
+/*
+ * Cached prefix continuation (the prefix state of the system1-omni
+ * "run shared prompt prefixes once" page keeps a prefix's K/V per
+ * attention layer).  A caller-owned device buffer of attn_kv_cache_bytes()
+ * holds prepared (normed, rotated) keys and transposed values in the
+ * library's tile layout for one geometry (max_tokens positions).
+ *
+ * attn_prefill_append: positions q_base..T-1 are new.  in->k and in->v hold
+ * their raw rows only (bf16 [T - q_base][Hkv][D]); qg holds their query rows
+ * ([T - q_base][Hq][2][D]).  The call prepares the new keys into the cache,
+ * then computes the query rows q_base..T-1 over cache keys 0..T-1, whose
+ * positions 0..q_base-1 earlier calls on the same cache prepared.  q_base
+ * must be a multiple of ATTN_QBASE_ALIGN; q_base == 0 starts a cache.
+ * out: bf16 [T - q_base][Hq * D].  Each row equals, bit for bit, the same row
+ * of attn_prefill_gated over all T tokens.  Calls on one cache must be
+ * stream-ordered; T - q_base == 0 is a no-op.
+ */
+ATTN_EXPORT int attn_kv_cache_bytes(const attn_geometry *geom, size_t *bytes);
+ATTN_EXPORT int attn_prefill_append(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base,
+                                    void *kv_cache, void *out, void *stream);
 
 /*
  * Test hook: writes the prepared (normed, rotated) queries and keys the

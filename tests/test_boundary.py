@@ -25,8 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["attn_ctx_create", "attn_prefill_gated", "attn_prefill_prefix", "attn_prefill_masked",
-              "attn_prefill_bidirectional", "attn_ctx_destroy", "attn_abi_version", "attn_status_string",
-              "attn_validate"]:
+              "attn_prefill_bidirectional", "attn_prefill_append", "attn_kv_cache_bytes", "attn_ctx_destroy",
+              "attn_abi_version", "attn_status_string", "attn_validate"]:
         assert n in names
 
 
@@ -82,11 +82,15 @@ REFUSALS = [
     ({}, 200, 256, 1, None, FAKE, {}, "RANGE"),                    # q_base > T
     ({}, 200, 64, 1, None, FAKE, {}, "ALIGN"),                     # q_base % 128
     ({}, 200, 128, 0, None, FAKE, {}, "RANGE"),                    # q_base on the full pass
-    ({}, 200, 0, 4, None, FAKE, {}, "RANGE"),                      # bad kind
+    ({}, 200, 0, 5, None, FAKE, {}, "RANGE"),                      # bad kind
     ({}, 200, 0, -1, None, FAKE, {}, "RANGE"),                     # negative kind
     ({}, 200, -128, 1, None, FAKE, {}, "RANGE"),                   # negative q_base
     ({}, 200, 128, 3, None, FAKE, {}, "RANGE"),                    # q_base on the bidirectional pass
     ({}, 64, 0, 3, None, FAKE, dict(v=0), "NULL_ARG"),
+    ({}, 200, 128, 4, None, FAKE, dict(n_pos=256), "NULL_ARG"),    # append without a cache
+    ({}, 200, 128, 4, FAKE + 4, FAKE, dict(n_pos=256), "ALIGN"),   # misaligned cache
+    ({}, 200, 64, 4, FAKE, FAKE, dict(n_pos=256), "ALIGN"),        # append q_base % 128
+    ({}, 200, 256, 4, FAKE, FAKE, dict(n_pos=256), "RANGE"),       # append q_base > T
     ({}, 64, 0, 0, None, FAKE, dict(n_pos=63), "RANGE"),           # short cos/sin table
     ({}, 64, 0, 0, None, None, {}, "NULL_ARG"),                    # out
     ({}, 64, 0, 2, None, FAKE, {}, "NULL_ARG"),                    # mask
@@ -117,7 +121,8 @@ def test_null_geometry(ga):
     assert rc == ga.ATTN_ERR_NULL_ARG
 
 
-@pytest.mark.parametrize("T,qb,kind", [(0, 0, 0), (0, 0, 2), (256, 256, 1), (128, 128, 1), (0, 0, 3)])
+@pytest.mark.parametrize("T,qb,kind", [(0, 0, 0), (0, 0, 2), (256, 256, 1), (128, 128, 1), (0, 0, 3),
+                                       (128, 128, 4)])
 def test_empty_launch_is_ok_without_pointers(ga, T, qb, kind):
     # Zero query rows: a no-op, even with every pointer NULL (torch gives 0 for empty tensors).
     assert ga.attn_validate(_geom(ga), None, T, qb, kind, None, None) == ga.ATTN_OK
@@ -128,6 +133,8 @@ def test_valid_calls_pass(ga):
     assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 128, 1, None, FAKE) == ga.ATTN_OK
     assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 0, 2, FAKE + 3, FAKE) == ga.ATTN_OK
     assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 0, 3, None, FAKE) == ga.ATTN_OK
+    assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 128, 4, FAKE, FAKE) == ga.ATTN_OK
+    assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 0, 4, FAKE, FAKE) == ga.ATTN_OK
     for G in [1, 2, 3, 12, 16]:
         assert ga.attn_validate(_geom(ga, n_q_heads=2 * G), _inputs(ga), 64, 0, 0, None, FAKE) == 0
 
@@ -138,6 +145,7 @@ def test_null_context_refused(ga):
     assert ga.attn_prefill_prefix(None, inp, 64, 0, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_prefill_masked(None, inp, 64, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_prefill_bidirectional(None, inp, 64, FAKE, None) == ga.ATTN_ERR_NULL_ARG
+    assert ga.attn_prefill_append(None, inp, 256, 128, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_debug_prepare(None, inp, 64, 0, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_ctx_set_timing(None, 1) == ga.ATTN_ERR_NULL_ARG
     ga.attn_ctx_destroy(None)      # no-op
@@ -156,3 +164,13 @@ def test_create_without_a_device_fails_cleanly(ga):
     with pytest.raises(ga.AttnError) as e:
         ga.attn_ctx_create(_geom(ga), 0)
     assert e.value.status == ga.ATTN_ERR_DEVICE
+
+
+def test_kv_cache_bytes(ga):
+    g = _geom(ga, n_q_heads=16, n_kv_heads=4, max_tokens=1000)
+    rc, n = ga.attn_kv_cache_bytes(g)
+    assert rc == ga.ATTN_OK
+    assert n == 2 * 4 * 1024 * 256 * 2          # K and V^T, max_tokens rounded up to 64
+    rc, n = ga.attn_kv_cache_bytes(_geom(ga, n_q_heads=24, n_kv_heads=5))
+    assert rc == ga.ATTN_ERR_GEOMETRY and n == 0
+    assert ga.lib.attn_kv_cache_bytes(g, None) == ga.ATTN_ERR_NULL_ARG

@@ -158,6 +158,44 @@ def test_bidirectional_last_row_equals_causal(T, Hq, Hkv):
     assert not np.array_equal(a[0], b[0])
 
 
+@pytest.mark.parametrize("T,chunks,Hq,Hkv", [(700, [256, 512], 24, 2), (8192, [1024, 4096], 16, 4)])
+def test_append_chunks_equal_full_pass(T, chunks, Hq, Hkv):
+    """Appending chunks to a K/V cache (prepared keys kept from earlier calls)
+    reproduces the full pass's rows bit for bit."""
+    say(f"append chunks T={T} at {chunks}")
+    full = synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=26)
+    ctx = make_ctx(full)
+    want = gpu_out(full, ctx)
+    dp = DevProblem(full)
+    cache = ctx.kv_cache()
+    bounds = [0] + list(chunks) + [T]
+    outs = [ctx.prefill_append(dp.qg[a:b], dp.k[a:b], dp.v[a:b], dp.wq, dp.wk, dp.cos, dp.sin, b, a, cache)
+            for a, b in zip(bounds[:-1], bounds[1:])]
+    torch.cuda.synchronize()
+    got = to_bits(torch.cat(outs))
+    ctx.close()
+    assert np.array_equal(got, want)
+
+
+def test_append_window_vs_oracle(orc):
+    """The last appended chunk against the oracle's prefix window."""
+    say("append window vs oracle")
+    T, qb = 650, 512
+    full = synth.make_problem(T=T, n_q_heads=8, n_kv_heads=2, seed=27)
+    win = synth.make_problem(T=T, n_q_heads=8, n_kv_heads=2, q_base=qb, seed=27)
+    ctx = make_ctx(full)
+    dp = DevProblem(full)
+    cache = ctx.kv_cache()
+    ctx.prefill_append(dp.qg[:qb], dp.k[:qb], dp.v[:qb], dp.wq, dp.wk, dp.cos, dp.sin, qb, 0, cache)
+    out = ctx.prefill_append(dp.qg[qb:], dp.k[qb:], dp.v[qb:], dp.wq, dp.wk, dp.cos, dp.sin, T, qb, cache)
+    torch.cuda.synchronize()
+    got = to_bits(out)
+    ctx.close()
+    bad, frac = parity_report(got, orc.attention(win, threads=8))
+    say(f"  bad={bad} worst bound fraction={frac:.3f}")
+    assert bad == 0
+
+
 @pytest.mark.parametrize("T", [300, 2048])
 def test_all_visible_mask_equals_dense(T):
     say(f"mask all visible T={T}")
