@@ -237,35 +237,47 @@ __global__ __launch_bounds__(256) void mask_pack(MaskPackParams p)
 }
 
 // ---------------------------------------------------------------------------
-// Query prologue of one wave: loads the q half of 32 rows of head h, applies
-// (1+w) RMSNorm (sum of squares in ascending dimension order, the same chain
-// as the key prologue) and partial RoPE, and leaves the MFMA B-operand
-// fragments in qf[c]: lane (j = lane & 31, hh = lane >> 5) holds dims
-// 16c + 8hh .. +7 of query row r0 + j.  Rows at or past S are zero.
+// Query prologue of one wave for two blocks of 32 rows (block b = rows
+// r0 + 32b ..): loads the q half of the rows of head h, applies (1+w)
+// RMSNorm (sum of squares in ascending dimension order, the same chain as the
+// key prologue) and partial RoPE, and leaves the MFMA B-operand fragments in
+// qf[b][c]: lane (j = lane & 31, hh = lane >> 5) holds dims 16c + 8hh .. +7 of
+// row r0 + 32b + j.  Rows at or past S are zero.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void load_queries(const AttnParams &p, int r0, int h, int lane,
-                                             uint4 (&qf)[16])
+__device__ __forceinline__ void load_queries(const AttnParams &p, int r0, int h, int lane, uint4 (&qf)[2][16])
 {
+    constexpr int NB = 2;
     const int j = lane & 31, hh = lane >> 5;
-    const int row = r0 + j;
-    const bool ok = row < p.S;
-    const uint16_t *src = p.qg + (((size_t)(ok ? row : 0) * p.Hq + h) * 2) * D;
+    bool ok[NB];
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
-        qf[c] = *reinterpret_cast<const uint4 *>(src + 16 * c + 8 * hh);
+    for (int b = 0; b < NB; ++b) {
+        const int row = r0 + 32 * b + j;
+        ok[b] = row < p.S;
+        const uint16_t *src = p.qg + (((size_t)(ok[b] ? row : 0) * p.Hq + h) * 2) * D;
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            qf[b][c] = *reinterpret_cast<const uint4 *>(src + 16 * c + 8 * hh);
+    }
+    // Sum of squares of each row in ascending dimension order.  v_permlane32_swap
+    // exchanges the upper half-wave of its first operand with the lower
+    // half-wave of its second, so swapping block 0's word with block 1's gives
+    // the lower half-wave both halves of block 0's row and the upper half-wave
+    // both halves of block 1's: each lane runs one chain, and a final swap
+    // shares the two sums.
     float ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-        // v_permlane32_swap of a register with itself: the first result holds
-        // the lower half-wave's value (dims 16c .. 16c+7 of the row), the
-        // second the upper half-wave's (16c+8 .. 16c+15), in every lane.
-        const uint4 own = qf[c];
-        const auto sx = __builtin_amdgcn_permlane32_swap(own.x, own.x, false, false);
-        const auto sy = __builtin_amdgcn_permlane32_swap(own.y, own.y, false, false);
-        const auto sz = __builtin_amdgcn_permlane32_swap(own.z, own.z, false, false);
-        const auto sw = __builtin_amdgcn_permlane32_swap(own.w, own.w, false, false);
-        const uint4 first = make_uint4(sx[0], sy[0], sz[0], sw[0]);
-        const uint4 second = make_uint4(sx[1], sy[1], sz[1], sw[1]);
+        uint32_t a[4], bq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w0 = q == 0 ? qf[0][c].x : q == 1 ? qf[0][c].y : q == 2 ? qf[0][c].z : qf[0][c].w;
+            const uint32_t w1 = q == 0 ? qf[1][c].x : q == 1 ? qf[1][c].y : q == 2 ? qf[1][c].z : qf[1][c].w;
+            const auto r = __builtin_amdgcn_permlane32_swap(w0, w1, false, false);
+            a[q] = r[0];
+            bq[q] = r[1];
+        }
+        const uint4 first = make_uint4(a[0], a[1], a[2], a[3]);      // dims 16c .. 16c+7
+        const uint4 second = make_uint4(bq[0], bq[1], bq[2], bq[3]); // dims 16c+8 .. 16c+15
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const float x = word_f(first, t);
@@ -277,19 +289,43 @@ __device__ __forceinline__ void load_queries(const AttnParams &p, int r0, int h,
             ss += x * x;
         }
     }
-    const float rr = 1.0f / sqrtf(ss / (float)D + p.eps);
-    // Dims 0..63 (chunks 0..3) hold the rotary pairs (d, d+32) = chunks
-    // (c, c+2); the remaining chunks are only normalised.
+    float rr[NB];
     {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+        rr[0] = 1.0f / sqrtf(__uint_as_float(r[0]) / (float)D + p.eps); // block 0 (lower half-wave's sums)
+        rr[1] = 1.0f / sqrtf(__uint_as_float(r[1]) / (float)D + p.eps); // block 1 (upper half-wave's sums)
+    }
+    // Dims 64..255 (chunks 4..15) are only normalised; (1 + w) is shared by
+    // the blocks, and the bf16 pack is the norm's one rounding.
+#pragma unroll
+    for (int c = 4; c < 16; ++c) {
+        const uint4 wv = *reinterpret_cast<const uint4 *>(p.wq + 16 * c + 8 * hh);
+        float w1p[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            w1p[t] = 1.0f + word_f(wv, t);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float n[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                n[t] = (word_f(qf[b][c], t) * rr[b]) * w1p[t];
+            qf[b][c] = make_uint4(pack2(n[0], n[1]), pack2(n[2], n[3]), pack2(n[4], n[5]), pack2(n[6], n[7]));
+        }
+    }
+    // Dims 0..63 (chunks 0..3) hold the rotary pairs (d, d+32) = chunks (c, c+2).
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
         float n[4][8];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const uint4 wv = *reinterpret_cast<const uint4 *>(p.wq + 16 * c + 8 * hh);
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                n[c][t] = rbf((word_f(qf[c], t) * rr) * (1.0f + word_f(wv, t)));
+                n[c][t] = rbf((word_f(qf[b][c], t) * rr[b]) * (1.0f + word_f(wv, t)));
         }
-        const int pos = p.q_base + (ok ? row : 0);
+        const int row = r0 + 32 * b + j;
+        const int pos = p.q_base + (ok[b] ? row : 0);
         const float *ct = p.cos_tab + (size_t)pos * HALF_R;
         const float *st = p.sin_tab + (size_t)pos * HALF_R;
 #pragma unroll
@@ -303,50 +339,44 @@ __device__ __forceinline__ void load_queries(const AttnParams &p, int r0, int h,
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const float cj = rbf(cv[t]), sj = rbf(sv[t]);
-                const float a = n[c][t], bb = n[c + 2][t];
-                n[c][t] = rbf(rbf(a * cj) + rbf(-bb * sj));
-                n[c + 2][t] = rbf(rbf(bb * cj) + rbf(a * sj));
+                const float av = n[c][t], bv = n[c + 2][t];
+                n[c][t] = rbf(rbf(av * cj) + rbf(-bv * sj));
+                n[c + 2][t] = rbf(rbf(bv * cj) + rbf(av * sj));
             }
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            qf[c] = make_uint4(pack2(n[c][0], n[c][1]), pack2(n[c][2], n[c][3]),
-                               pack2(n[c][4], n[c][5]), pack2(n[c][6], n[c][7]));
-    }
+            qf[b][c] = make_uint4(pack2(n[c][0], n[c][1]), pack2(n[c][2], n[c][3]),
+                                  pack2(n[c][4], n[c][5]), pack2(n[c][6], n[c][7]));
+        if (!ok[b]) {
 #pragma unroll
-    for (int c = 4; c < 16; ++c) {
-        const uint4 wv = *reinterpret_cast<const uint4 *>(p.wq + 16 * c + 8 * hh);
-        float n[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            n[t] = rbf((word_f(qf[c], t) * rr) * (1.0f + word_f(wv, t)));
-        qf[c] = make_uint4(pack2(n[0], n[1]), pack2(n[2], n[3]), pack2(n[4], n[5]), pack2(n[6], n[7]));
-    }
-    if (!ok) {
-#pragma unroll
-        for (int c = 0; c < 16; ++c)
-            qf[c] = make_uint4(0u, 0u, 0u, 0u);
+            for (int c = 0; c < 16; ++c)
+                qf[b][c] = make_uint4(0u, 0u, 0u, 0u);
+        }
     }
 }
 
 // Debug: prepared queries in a plain [rows][Hq][D] layout.
-// grid (ceil(S/32), ceil(Hq/4)), 256 threads: wave = one head, 32 rows.
+// grid (ceil(S/64), ceil(Hq/4)), 256 threads: wave = one head, 64 rows.
 __global__ __launch_bounds__(256) void q_prologue_debug(AttnParams p, uint16_t *qp)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int h = blockIdx.y * 4 + wave;
     if (h >= p.Hq)
         return;
-    const int r0 = blockIdx.x * 32;
-    uint4 qf[16];
+    const int r0 = blockIdx.x * 64;
+    uint4 qf[2][16];
     load_queries(p, r0, h, lane, qf);
     const int j = lane & 31, hh = lane >> 5;
-    const int row = r0 + j;
-    if (row >= p.S)
-        return;
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
-        *reinterpret_cast<uint4 *>(qp + ((size_t)row * p.Hq + h) * D + 16 * c + 8 * hh) = qf[c];
+    for (int b = 0; b < 2; ++b) {
+        const int row = r0 + 32 * b + j;
+        if (row < p.S) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                *reinterpret_cast<uint4 *>(qp + ((size_t)row * p.Hq + h) * D + 16 * c + 8 * hh) = qf[b][c];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -941,8 +971,7 @@ void attn_fwd(AttnParams p)
         // Every wave prepares its queries (an idle wave's results are never
         // stored); keeping the definition unconditional keeps them in registers.
         uint4 qf[2][16];
-        load_queries(p, r0, h, lane, qf[0]);
-        load_queries(p, r0 + QB, h, lane, qf[1]);
+        load_queries(p, r0, h, lane, qf);
         const FragOffsets fo = frag_offsets(j, hh);
         // Causal visibility inside a block's diagonal tile (keys and rows both
         // start at 32 * (diag0 + b)): bit kk set iff kk <= j.
@@ -1165,7 +1194,7 @@ hipError_t launch_kp_unpack(const uint16_t *kp, int Tpad, int T, int Hkv, uint16
 
 hipError_t launch_q_prologue_debug(const AttnParams &p, uint16_t *qp, hipStream_t stream)
 {
-    hipLaunchKernelGGL(q_prologue_debug, dim3((p.S + 31) / 32, (p.Hq + 3) / 4), dim3(256), 0,
+    hipLaunchKernelGGL(q_prologue_debug, dim3((p.S + 63) / 64, (p.Hq + 3) / 4), dim3(256), 0,
                        stream, p, qp);
     return hipGetLastError();
 }
