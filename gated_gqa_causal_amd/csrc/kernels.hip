@@ -393,31 +393,29 @@ constexpr int MAX_TILES = 32768 / KT;    // tile list capacity (token cap / 32)
 constexpr int TILE_BYTES = KT * D * 2;   // one K or V^T tile: 16 KB
 constexpr int EP_STRIDE = 2 * D + 16;    // epilogue staging: bytes per row
 
-// Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane L
-// writes LDS bytes [lds + 16 L, lds + 16 L + 16) from gbase + voff.  gbase and
-// lds must be wave-uniform.  Issued through inline asm so the compiler does
-// not guard later LDS reads of *other* buffers with a wait on this load; the
-// caller orders it with an explicit s_waitcnt vmcnt before the barrier that
-// publishes the buffer.
-// M0 is reserved by the compiler: it is saved and restored around the copy.
-__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds)
+// Global -> LDS copies (global_load_lds_dwordx4 / _dword).  The instruction
+// reads gbase + voff + OFF per lane and writes LDS at M0 + OFF + 16 L (4 L for
+// the dword form) for lane L: the immediate offset applies to both addresses,
+// so the parts of one tile share M0, the base and the lane offset.  gbase and
+// m0 must be wave-uniform.  M0 is an operand, so the compiler writes it and
+// knows it is in use; a copy right after an M0 write needs one wait state,
+// which the first copy after a new M0 value (NOP) supplies.  Issued through
+// inline asm so the compiler does not guard later LDS reads of *other*
+// buffers with a wait on these loads; the caller orders them with an explicit
+// s_waitcnt vmcnt before the barrier that publishes the buffer.
+template <int OFF, bool NOP>
+__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t m0)
 {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "global_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "s"(lds), "v"(voff), "s"(gbase)
-                 : "memory");
+    if (NOP)
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%2"
+                     :: "v"(voff), "s"(gbase), "i"(OFF), "{m0}"(m0) : "memory");
+    else
+        asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2"
+                     :: "v"(voff), "s"(gbase), "i"(OFF), "{m0}"(m0) : "memory");
 }
-// Same for 4 bytes per lane (global_load_lds_dword): lane L writes lds + 4 L.
-__device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t lds)
+__device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t m0)
 {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "global_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "s"(lds), "v"(voff), "s"(gbase)
-                 : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" :: "v"(voff), "s"(gbase), "{m0}"(m0) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
@@ -491,11 +489,10 @@ __device__ __forceinline__ void acc_wait(f32x16 (&o)[8])
 // 32-cycle MFMA of its own; a step holds about that many, none depending on
 // another of the same step, so the matrix pipe does not wait on them.
 //   lane (j, hh) holds query j and keys 8g + 4hh + r of the tile (e = 4g + r).
-//   steps 0..3  : tile max (a tree of max3 on the fp32 scores; rounding is
+//   steps 0..7  : tile max (a tree of max3 on the fp32 scores, then the
+//                 partner lane's max for the tile's other 16 keys; rounding is
 //                 monotonic, so rounding the max afterwards gives the max of
-//                 the rounded scores); the scores rounded to bf16 in pairs;
-//   steps 4..7  : max with the partner lane (the tile's other 16 keys),
-//                 rounded; the rounded scores unpacked in place;
+//                 the rounded scores); the scores rounded to bf16 in place;
 //   steps 8..13 : running max (moved only past the threshold), alpha, base;
 //   steps 12..29: weights p = exp2(x log2(e)/16 - base), two per pair of
 //                 steps, packed to the bf16 MFMA operand; the row sum adds the
@@ -535,6 +532,15 @@ __device__ __forceinline__ uint32_t pack2_op(float a, float b)
     return r;
 }
 
+// x rounded to bf16 (nearest even), as an fp32 value: the packed convert with
+// a zero low half leaves bf16(x) in the high half, which is that value.
+__device__ __forceinline__ float round_op(float x)
+{
+    float r;
+    asm("v_cvt_pk_bf16_f32 %0, 0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
 {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
@@ -543,7 +549,6 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
 struct SmTmp {
     float a, b, c, d, e, f, g, mt, mt2, t1, mn, dd, bn, nb, ar, L0, L1;
     bool up, minf, same, ninf;
-    uint32_t w[8];
 };
 
 __device__ __forceinline__ void hide_step(int i, f32x16 &s, uint32_t vh)
@@ -599,19 +604,19 @@ __device__ __forceinline__ void sm_step(int i, f32x16 &s, float &m, float &l, fl
         t.d = max3f(s[9], s[10], s[11]);
     } else if (i == 1) {
         t.e = max3f(s[12], s[13], s[14]);
-        t.w[0] = pack2_op(s[0], s[1]);
-        t.w[1] = pack2_op(s[2], s[3]);
-        t.w[2] = pack2_op(s[4], s[5]);
+        s[0] = round_op(s[0]);
+        s[1] = round_op(s[1]);
+        s[2] = round_op(s[2]);
     } else if (i == 2) {
         t.f = max3f(t.a, t.b, t.c);
         t.g = max3f(t.d, t.e, s[15]);
-        t.w[3] = pack2_op(s[6], s[7]);
-        t.w[4] = pack2_op(s[8], s[9]);
+        s[3] = round_op(s[3]);
+        s[4] = round_op(s[4]);
     } else if (i == 3) {
         t.mt = max2f(t.f, t.g);
-        t.w[5] = pack2_op(s[10], s[11]);
-        t.w[6] = pack2_op(s[12], s[13]);
-        t.w[7] = pack2_op(s[14], s[15]);
+        s[5] = round_op(s[5]);
+        s[6] = round_op(s[6]);
+        s[7] = round_op(s[7]);
     } else if (i == 4) {
         // Partner lane's max: v_permlane32_swap fed the value twice leaves
         // this lane's and the partner's value in the two results.
@@ -619,31 +624,24 @@ __device__ __forceinline__ void sm_step(int i, f32x16 &s, float &m, float &l, fl
         t.mt = __uint_as_float(r[0]);
         t.mt2 = __uint_as_float(r[1]);
         t.t1 = m + TAU_X;
+        s[8] = round_op(s[8]);
     } else if (i == 5) {
         t.mt = max2f(t.mt, t.mt2);
-        s[0] = lo_f(t.w[0]);
-        s[1] = hi_f(t.w[0]);
-        s[2] = lo_f(t.w[1]);
+        s[9] = round_op(s[9]);
+        s[10] = round_op(s[10]);
+        s[11] = round_op(s[11]);
     } else if (i == 6) {
-        t.w[0] = pack2_op(t.mt, t.mt);
-        s[3] = hi_f(t.w[1]);
-        s[4] = lo_f(t.w[2]);
-        s[5] = hi_f(t.w[2]);
+        t.mt = round_op(t.mt);                  // bf16-rounded tile max
+        s[12] = round_op(s[12]);
+        s[13] = round_op(s[13]);
+        s[14] = round_op(s[14]);
     } else if (i == 7) {
-        t.mt = lo_f(t.w[0]);                    // bf16-rounded tile max
-        s[6] = lo_f(t.w[3]);
-        s[7] = hi_f(t.w[3]);
-        s[8] = lo_f(t.w[4]);
+        s[15] = round_op(s[15]);
     } else if (i == 8) {
         t.up = t.mt > t.t1;
         t.minf = (m == -INFINITY);
-        s[9] = hi_f(t.w[4]);
-        s[10] = lo_f(t.w[5]);
     } else if (i == 9) {
         t.mn = t.up ? t.mt : m;
-        s[11] = hi_f(t.w[5]);
-        s[12] = lo_f(t.w[6]);
-        s[13] = hi_f(t.w[6]);
     } else if (i == 10) {
         t.dd = m - t.mn;
         t.same = (t.mn == m);
@@ -652,8 +650,6 @@ __device__ __forceinline__ void sm_step(int i, f32x16 &s, float &m, float &l, fl
     } else if (i == 11) {
         t.dd = t.dd * SCALE_LOG2;
         t.nb = t.ninf ? 0.0f : t.bn;            // a finite base while nothing is visible
-        s[14] = lo_f(t.w[7]);
-        s[15] = hi_f(t.w[7]);
     } else if (i == 12) {
         t.ar = __builtin_amdgcn_exp2f(t.dd);
         sm_pair_F(0, s, t);
@@ -833,7 +829,7 @@ template <bool MASKED, bool BIDIR>
 __global__ __attribute__((amdgpu_flat_work_group_size(ATHREADS, ATHREADS), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd(AttnParams p)
 {
-    __shared__ __align__(16) char smem[7 * TILE_BYTES];   // K tiles 0..3, V^T tiles 4..6; epilogue staging
+    __shared__ __align__(16) char smem[8 * TILE_BYTES];   // K tiles 0..3, V^T tiles 4..7; epilogue staging
     __shared__ uint32_t bitsbuf[8][QW];
     __shared__ int tile_list[MASKED ? MAX_TILES : 1];
     __shared__ int tile_count;
@@ -896,30 +892,39 @@ void attn_fwd(AttnParams p)
             n = tile_count;
         }
         auto tile_at = [&](int u) -> int { return MASKED ? tile_list[u] : u; };
-        auto kbuf = [&](int i) { return smem + TILE_BYTES * i; };
-        auto vbuf = [&](int i) { return smem + TILE_BYTES * (4 + i); };
-
-        // Each of the 4 waves moves 4 KB of each 16 KB tile straight from global
-        // memory into LDS (global_load_lds_dwordx4: lane L of an instruction
-        // writes the 16 bytes at LDS base + 16 L, from consecutive addresses).
-        auto load_tile = [&](const uint16_t *base, int tile, char *dst) {
+        const uint32_t smem_base = lds_addr(smem);
+        const uint32_t bits_base = lds_addr(bitsbuf);
+        // Tile streams of this KV head, and this wave's quarter of a tile: the
+        // 4 waves each move 4 KB of every 16 KB tile (lane L of part i moves the
+        // 16 bytes at 4096 w + 1024 i + 16 L, into the same offset of the buffer).
+        const uint16_t *kbase = p.kp + (size_t)kvh * (p.Tpad / KT) * (KT * D);
+        const uint16_t *vbase = p.vt + (size_t)kvh * (p.Tpad / KT) * (KT * D);
+        const uint32_t voff = (uint32_t)(wave * 4096 + lane * 16);
+        auto m0_of = [&](bool is_k, int u) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane(
+                (int)(smem_base + TILE_BYTES * ((is_k ? 0 : 4) + (u & 3)) + wave * 4096));
+        };
+        auto src_of = [&](bool is_k, int tile) {
             tile = __builtin_amdgcn_readfirstlane(tile);
-            const uint16_t *src = base + ((size_t)kvh * (p.Tpad / KT) + tile) * (size_t)(KT * D);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int nn = wave * 4 + i;
-                dma16(src, (uint32_t)(nn * 1024 + lane * 16), lds_addr(dst) + nn * 1024);
-            }
+            return (is_k ? kbase : vbase) + (size_t)tile * (KT * D);
+        };
+        auto load_tile = [&](bool is_k, int tile, int u) {
+            const uint16_t *src = src_of(is_k, tile);
+            const uint32_t m0 = m0_of(is_k, u);
+            dma16<0, true>(src, voff, m0);
+            dma16<1024, false>(src, voff, m0);
+            dma16<2048, false>(src, voff, m0);
+            dma16<3072, false>(src, voff, m0);
         };
         // Masked path: the 64 rows' visibility words of a tile, next to its K
         // load; wave w moves the words of rows 16w .. 16w+15 (lanes outside that
         // range are masked off, lane L still writes word L).
-        auto load_bits = [&](int tile, uint32_t *dst) {
+        auto load_bits = [&](int tile, int slot) {
             if (MASKED) {
                 tile = __builtin_amdgcn_readfirstlane(tile);
                 if ((lane >> 4) == wave) {
                     const int row = min(r0 + lane, p.S - 1);   // rows past S read a real row
-                    dma4(p.bits, (uint32_t)(((size_t)row * p.W + tile) * 4), lds_addr(dst));
+                    dma4(p.bits, (uint32_t)(((size_t)row * p.W + tile) * 4), bits_base + (uint32_t)(slot * QW * 4));
                 }
             }
         };
@@ -932,15 +937,19 @@ void attn_fwd(AttnParams p)
         // the wave's issue for tens of cycles, which the MFMAs then cover).
         auto load_part = [&](int k, int part) {
             if (part == 4) {
-                load_bits(tile_clamped(k + 3), bitsbuf[(k + 3) & 7]);
+                load_bits(tile_clamped(k + 3), (k + 3) & 7);
                 return;
             }
             const bool is_k = part < 4;
-            const int tile = __builtin_amdgcn_readfirstlane(tile_clamped(is_k ? k + 3 : k + 1));
-            const uint16_t *src = (is_k ? p.kp : p.vt) + ((size_t)kvh * (p.Tpad / KT) + tile) * (size_t)(KT * D);
-            const char *dst = is_k ? kbuf((k + 3) & 3) : vbuf((k + 1) % 3);
-            const int nn = wave * 4 + (is_k ? part : part - 5);
-            dma16(src, (uint32_t)(nn * 1024 + lane * 16), lds_addr(dst) + nn * 1024);
+            const int u = is_k ? k + 3 : k + 1;
+            const uint16_t *src = src_of(is_k, tile_clamped(u));
+            const uint32_t m0 = m0_of(is_k, u);
+            switch (is_k ? part : part - 5) {
+            case 0: dma16<0, true>(src, voff, m0); break;
+            case 1: dma16<1024, false>(src, voff, m0); break;
+            case 2: dma16<2048, false>(src, voff, m0); break;
+            default: dma16<3072, false>(src, voff, m0); break;
+            }
         };
         auto issue_loads = [&](int k) {
             return [&, k](int slot) {
@@ -962,10 +971,10 @@ void attn_fwd(AttnParams p)
         if (n > 0) {
 #pragma unroll
             for (int u = 0; u < 3; ++u) {
-                load_tile(p.kp, tile_clamped(u), kbuf(u));
-                load_bits(tile_clamped(u), bitsbuf[u]);
+                load_tile(true, tile_clamped(u), u);
+                load_bits(tile_clamped(u), u);
             }
-            load_tile(p.vt, tile_clamped(0), vbuf(0));
+            load_tile(false, tile_clamped(0), 0);
         }
 
         // Every wave prepares its queries (an idle wave's results are never
@@ -1023,14 +1032,13 @@ void attn_fwd(AttnParams p)
         };
         // LDS addresses of this lane's fragment 0 in the K / V^T buffer of tile k
         // (kept opaque so every fragment read uses the instruction's offset field).
-        const uint32_t smem_base = lds_addr(smem);
         auto kaddr_of = [&](int k) {
             uint32_t a = smem_base + TILE_BYTES * (k & 3) + fo.k;
             asm volatile("" : "+v"(a));
             return a;
         };
         auto vaddr_of = [&](int k) {
-            uint32_t a = smem_base + TILE_BYTES * (4 + k % 3) + fo.v;
+            uint32_t a = smem_base + TILE_BYTES * (4 + (k & 3)) + fo.v;
             asm volatile("" : "+v"(a));
             return a;
         };
