@@ -356,6 +356,8 @@ __device__ __forceinline__ void load_queries(const AttnParams &p, int r0, int h,
     }
 }
 
+__device__ __forceinline__ void load_queries1(const AttnParams &p, int r0, int h, int lane, uint4 (&qf)[16]);
+
 // Debug: prepared queries in a plain [rows][Hq][D] layout.
 // grid (ceil(S/64), ceil(Hq/4)), 256 threads: wave = one head, 64 rows.
 __global__ __launch_bounds__(256) void q_prologue_debug(AttnParams p, uint16_t *qp)
@@ -367,6 +369,9 @@ __global__ __launch_bounds__(256) void q_prologue_debug(AttnParams p, uint16_t *
     const int r0 = blockIdx.x * 64;
     uint4 qf[2][16];
     load_queries(p, r0, h, lane, qf);
+    // The first 32 rows come from the one-block prologue, the next 32 from
+    // block 1 of the two-block one: both are checked.
+    load_queries1(p, r0, h, lane, qf[0]);
     const int j = lane & 31, hh = lane >> 5;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -1164,6 +1169,426 @@ void attn_fwd(AttnParams p)
 }
 
 // ---------------------------------------------------------------------------
+// Eight-wave attention for the unmasked passes (causal and bidirectional).
+//
+// The same work item (64 query rows x the 4 query heads of a head group of
+// one KV head) on 8 waves, two per SIMD: wave w owns head 4hg + (w & 3) and
+// the 32-row block w >> 2, so a SIMD holds the two blocks of one head.  A
+// wave's registers (at most 256 with two waves per SIMD) hold one block: O
+// (128 AGPRs), its query fragments (64) and the scores of one tile (16).  The
+// issue port of a SIMD is shared by its two waves, which roughly doubles the
+// instruction budget around each MFMA compared with one wave per SIMD.  The
+// two blocks run complementary phases of the same key interval:
+//   block 0, interval k: [S(k)]                 [O += V(k-1) P(k-1) | softmax k  ]
+//   block 1, interval k: [O += V(k-2) P(k-2) | softmax k-1]  [S(k)]
+// so while one wave issues the softmax's vector work the other issues a run
+// of plain MFMAs.  Each wave moves an eighth of every K and V^T tile into
+// LDS (2 KB), K three tiles ahead and V^T two ahead, four buffers
+// each (block 1 still reads V(k-2) while V(k+1) arrives).
+// ---------------------------------------------------------------------------
+constexpr int ATHREADS8 = 512;
+constexpr int SMEM8 = (8 * TILE_BYTES > 8 * QB * EP_STRIDE) ? 8 * TILE_BYTES : 8 * QB * EP_STRIDE;
+
+// Query prologue of one 32-row block (rows r0 ..): the same arithmetic as
+// load_queries; swapping each word with itself gives every lane both halves
+// of its row for the sum of squares.
+__device__ __forceinline__ void load_queries1(const AttnParams &p, int r0, int h, int lane, uint4 (&qf)[16])
+{
+    const int j = lane & 31, hh = lane >> 5;
+    const int row = r0 + j;
+    const bool ok = row < p.S;
+    const uint16_t *src = p.qg + (((size_t)(ok ? row : 0) * p.Hq + h) * 2) * D;
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        qf[c] = *reinterpret_cast<const uint4 *>(src + 16 * c + 8 * hh);
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        uint32_t a[4], bq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w = q == 0 ? qf[c].x : q == 1 ? qf[c].y : q == 2 ? qf[c].z : qf[c].w;
+            const auto r = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+            a[q] = r[0];
+            bq[q] = r[1];
+        }
+        const uint4 first = make_uint4(a[0], a[1], a[2], a[3]);      // dims 16c .. 16c+7
+        const uint4 second = make_uint4(bq[0], bq[1], bq[2], bq[3]); // dims 16c+8 .. 16c+15
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float x = word_f(first, t);
+            ss += x * x;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float x = word_f(second, t);
+            ss += x * x;
+        }
+    }
+    const float rr = 1.0f / sqrtf(ss / (float)D + p.eps);
+#pragma unroll
+    for (int c = 4; c < 16; ++c) {
+        const uint4 wv = *reinterpret_cast<const uint4 *>(p.wq + 16 * c + 8 * hh);
+        float n[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            n[t] = (word_f(qf[c], t) * rr) * (1.0f + word_f(wv, t));
+        qf[c] = make_uint4(pack2(n[0], n[1]), pack2(n[2], n[3]), pack2(n[4], n[5]), pack2(n[6], n[7]));
+    }
+    {
+        float n[4][8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint4 wv = *reinterpret_cast<const uint4 *>(p.wq + 16 * c + 8 * hh);
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                n[c][t] = rbf((word_f(qf[c], t) * rr) * (1.0f + word_f(wv, t)));
+        }
+        const int pos = p.q_base + (ok ? row : 0);
+        const float *ct = p.cos_tab + (size_t)pos * HALF_R;
+        const float *st = p.sin_tab + (size_t)pos * HALF_R;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const float4 c0 = *reinterpret_cast<const float4 *>(ct + 16 * c + 8 * hh);
+            const float4 c1 = *reinterpret_cast<const float4 *>(ct + 16 * c + 8 * hh + 4);
+            const float4 s0 = *reinterpret_cast<const float4 *>(st + 16 * c + 8 * hh);
+            const float4 s1 = *reinterpret_cast<const float4 *>(st + 16 * c + 8 * hh + 4);
+            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float cj = rbf(cv[t]), sj = rbf(sv[t]);
+                const float av = n[c][t], bv = n[c + 2][t];
+                n[c][t] = rbf(rbf(av * cj) + rbf(-bv * sj));
+                n[c + 2][t] = rbf(rbf(bv * cj) + rbf(av * sj));
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            qf[c] = make_uint4(pack2(n[c][0], n[c][1]), pack2(n[c][2], n[c][3]),
+                               pack2(n[c][4], n[c][5]), pack2(n[c][6], n[c][7]));
+    }
+    if (!ok) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            qf[c] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// Scores half (one block): S^T(k) = K(k) . Q^T, 16 MFMAs, one per slot, K
+// fragments read one ahead (the registers of a wave at two waves per SIMD
+// allow no more); issue(slot) places the copies among the MFMAs.
+template <typename Issue>
+__device__ __forceinline__ void s_half8(uint32_t kaddr, const uint4 (&qf)[16], f32x16 &s, Issue &&issue)
+{
+    bf16x8 kf[16];
+    kf[0] = lds_read16(kaddr);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        if (c + 1 < 16)
+            kf[c + 1] = lds_read16(kaddr + 1024 * (c + 1));
+        const f32x16 z = {};
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], __builtin_bit_cast(bf16x8, qf[c]), c ? s : z, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(c);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Softmax step i of the one-block program.  The packs of weight pairs 4..7
+// (the second operand word group) and the row-sum tail are left to
+// sm_tail8: the context MFMAs of the same half still read that group.
+__device__ __forceinline__ void sm_step8(int i, f32x16 &s, float &m, float &l, float &alpha, u32x4 (&pw)[2],
+                                         SmTmp &t)
+{
+    if (i >= 14 && i < 28) {
+        const int q = (i - 14) >> 1;
+        if ((i & 1) == 0) {
+            sm_pair_F(q + 1, s, t);
+            if (q < 4)
+                sm_pair_C(q, s, pw);
+        } else {
+            sm_pair_E(q + 1, s);
+            if (q < 4)
+                sm_pair_D(q, pw, t);
+        }
+    } else if (i < 14) {
+        sm_step(i, s, m, l, alpha, pw, t);
+    }
+}
+__device__ __forceinline__ void sm_tail8(f32x16 &s, float &l, float alpha, u32x4 (&pw)[2], SmTmp &t)
+{
+#pragma unroll
+    for (int q = 4; q < 8; ++q)
+        sm_pair_C(q, s, pw);
+#pragma unroll
+    for (int q = 4; q < 8; ++q)
+        sm_pair_D(q, pw, t);
+    t.L0 = t.L0 + t.L1;
+    l = __builtin_fmaf(l, alpha, t.L0);
+    pin(l);
+}
+
+// Context half (one block): O^T += V^T . P^T for the tile whose weights are
+// in pw (16 MFMAs, kc-major: the first 8 read only the first operand word
+// group; V fragments read one ahead), with the softmax of the scores s in the
+// gaps, two steps per slot from slot 1 (the last score MFMA may still be in
+// flight at slot 0).  The first word group is repacked only after the eighth
+// MFMA and the second after the last, so one weight buffer serves both tiles.
+template <bool DO_PV, bool DO_SM>
+__device__ __forceinline__ void pv_half8(uint32_t vaddr, f32x16 (&o)[8], u32x4 (&pw)[2], f32x16 &s, float &m,
+                                         float &l, float &alpha)
+{
+    SmTmp t;
+    bf16x8 vf[16];
+    if (DO_PV)
+        vf[0] = lds_read16(vaddr);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (DO_PV) {
+            if (i + 1 < 16) {
+                const int n1 = i + 1;
+                vf[n1] = lds_read16(vaddr + 8192 * (n1 >> 3) + 512 * (n1 & 7));
+            }
+            if ((i & 7) == 0)
+                mfma_o<true>(o[i & 7], vf[i], pw[i >> 3]);
+            else
+                mfma_o<false>(o[i & 7], vf[i], pw[i >> 3]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (DO_SM && i >= 1) {
+            sm_step8(2 * i - 2, s, m, l, alpha, pw, t);
+            sm_step8(2 * i - 1, s, m, l, alpha, pw, t);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (DO_SM)
+        sm_tail8(s, l, alpha, pw, t);
+}
+
+template <bool BIDIR>
+__global__ __attribute__((amdgpu_flat_work_group_size(ATHREADS8, ATHREADS8), amdgpu_waves_per_eu(2, 2)))
+void attn_fwd8(AttnParams p)
+{
+    __shared__ __align__(16) char smem[SMEM8];     // K tiles 0..3, V^T tiles 4..7; epilogue staging
+
+    const int lane_id = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hw = wave & 3;                        // head within the group of four
+    const int blk = wave >> 2;                      // 32-row block; 1 = the lagging phase
+
+    // Work items and their order as in attn_fwd.
+    const int per_rb = p.Hkv * p.n_hg;
+    const int n_items = p.nrb * per_rb;
+    const int P = (int)gridDim.x;
+#pragma clang loop unroll(disable)
+    for (int pass = 0;; ++pass) {
+        const int item = pass * P + ((pass & 1) ? P - 1 - (int)blockIdx.x : (int)blockIdx.x);
+        if (item >= n_items)
+            break;
+        if (pass > 0)
+            __syncthreads();                         // the previous item is done with LDS
+        int lane = lane_id;
+        asm volatile("" : "+v"(lane));
+        const int j = lane & 31, hh = lane >> 5;
+        const int rb = p.nrb - 1 - item / per_rb;
+        const int rem = item % per_rb;
+        const int kvh = rem / p.n_hg, hg = rem % p.n_hg;
+        const int gidx = hg * 4 + hw;
+        const bool active = gidx < p.G;
+        const int h = kvh * p.G + (active ? gidx : 0);
+        const int r0 = rb * QW;
+        const int rbase = r0 + QB * blk;                 // this wave's rows rbase .. rbase + 31
+
+        const int P0 = p.q_base + r0;
+        const int ntiles = BIDIR ? (p.T + KT - 1) / KT : min(P0 + QW - 1, p.T - 1) / KT + 1;
+        const int diag = P0 / KT + blk;                  // this block's diagonal tile
+        const int n = ntiles;                            // >= 1: row r0 sees key 0
+
+        const uint32_t smem_base = lds_addr(smem);
+        const uint16_t *kbase = p.kp + (size_t)kvh * (p.Tpad / KT) * (KT * D);
+        const uint16_t *vbase = p.vt + (size_t)kvh * (p.Tpad / KT) * (KT * D);
+        // Wave w moves bytes [2048 w, 2048 w + 2048) of every tile, in two parts.
+        const uint32_t voff = (uint32_t)(wave * 2048 + lane * 16);
+        auto m0_of = [&](bool is_k, int u) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane(
+                (int)(smem_base + TILE_BYTES * ((is_k ? 0 : 4) + (u & 3)) + wave * 2048));
+        };
+        auto src_of = [&](bool is_k, int tile) {
+            tile = __builtin_amdgcn_readfirstlane(tile);
+            return (is_k ? kbase : vbase) + (size_t)tile * (KT * D);
+        };
+        auto tile_clamped = [&](int u) { return min(u, n - 1); };
+        auto load_tile = [&](bool is_k, int u) {
+            const uint16_t *src = src_of(is_k, tile_clamped(u));
+            const uint32_t m0 = m0_of(is_k, u);
+            dma16<0, true>(src, voff, m0);
+            dma16<1024, false>(src, voff, m0);
+        };
+        // Interval k's copies (issued in the wave's scores half): K(k+3) and
+        // V(k+1), two parts each.
+        auto issue_loads = [&](int k) {
+            return [&, k](int slot) {
+                if (slot == 1 || slot == 5) {
+                    const uint16_t *src = src_of(true, tile_clamped(k + 3));
+                    const uint32_t m0 = m0_of(true, k + 3);
+                    if (slot == 1)
+                        dma16<0, true>(src, voff, m0);
+                    else
+                        dma16<1024, false>(src, voff, m0);
+                } else if (slot == 9 || slot == 13) {
+                    const uint16_t *src = src_of(false, tile_clamped(k + 1));
+                    const uint32_t m0 = m0_of(false, k + 1);
+                    if (slot == 9)
+                        dma16<0, true>(src, voff, m0);
+                    else
+                        dma16<1024, false>(src, voff, m0);
+                }
+            };
+        };
+        // Wait for the previous interval's copies (this interval's two or four
+        // stay in flight), then the barrier.
+        auto close_interval = [&]() {
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            __syncthreads();
+        };
+
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+            load_tile(true, u);
+        load_tile(false, 0);
+
+        uint4 qf[16];
+        load_queries1(p, rbase, h, lane, qf);
+        const FragOffsets fo = frag_offsets(j, hh);
+        const uint32_t diag_vis = (j == 31) ? 0xffffffffu : ((2u << j) - 1u);
+
+        f32x16 o[8];
+        {
+            const bf16x8 zero = {};
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+                asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(o[db]) : "v"(zero));
+        }
+        float m = -INFINITY, l = 0.0f, alpha = 1.0f;
+        f32x16 s;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            s[e] = 0.0f;
+        u32x4 pw[2] = {};
+
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+
+        auto causal_hide = [&](int u, f32x16 &sc) {
+            if (BIDIR) {
+                if (u == n - 1 && (p.T & (KT - 1)) != 0)
+                    hide_all(sc, ((1u << (p.T & (KT - 1))) - 1u) >> (4 * hh));
+            } else if (u >= diag) {
+                const uint32_t vis = (u == diag) ? diag_vis : 0u;
+                hide_all(sc, vis >> (4 * hh));
+            }
+        };
+        auto kaddr_of = [&](int k) {
+            uint32_t a = smem_base + TILE_BYTES * (k & 3) + fo.k;
+            asm volatile("" : "+v"(a));
+            return a;
+        };
+        auto vaddr_of = [&](int k) {
+            uint32_t a = smem_base + TILE_BYTES * (4 + (k & 3)) + fo.v;
+            asm volatile("" : "+v"(a));
+            return a;
+        };
+        const int cc = lane & 31;                       // epilogue: 16-byte chunk of a row
+        uint4 gw[16];
+        auto load_gates = [&]() {
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+                const int row = min(rbase + 2 * it + hh, p.S - 1);
+                gw[it] = *reinterpret_cast<const uint4 *>(p.qg + (((size_t)row * p.Hq + h) * 2 + 1) * D + 8 * cc);
+            }
+        };
+
+        // Epilogue: ctx = bf16(O / l), out = bf16(ctx * bf16(sigmoid(gate))),
+        // through LDS as whole 512-byte rows.
+        auto epilogue = [&]() {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();                             // all waves are done with the tile buffers
+            char *ep = smem + wave * QB * EP_STRIDE;
+            const float lt = pair_sum(l);
+            const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
+            acc_wait(o);
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d0 = 32 * db + 8 * g + 4 * hh;
+                    const uint2 cw = make_uint2(pack2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                                                pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
+                    *reinterpret_cast<uint2 *>(ep + j * EP_STRIDE + 2 * d0) = cw;
+                }
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+                const int rr = 2 * it + hh;
+                const int row = rbase + rr;
+                const uint4 cv = *reinterpret_cast<const uint4 *>(ep + rr * EP_STRIDE + 16 * cc);
+                const uint32_t cws[4] = {cv.x, cv.y, cv.z, cv.w};
+                const uint32_t gws[4] = {gw[it].x, gw[it].y, gw[it].z, gw[it].w};
+                uint32_t ow[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float ov[2];
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const float ctx = hf ? hi_f(cws[q]) : lo_f(cws[q]);
+                        const float gv = hf ? hi_f(gws[q]) : lo_f(gws[q]);
+                        const float sg = rbf(__builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * LOG2E)));
+                        ov[hf] = ctx * sg;
+                    }
+                    ow[q] = pack2(ov[0], ov[1]);
+                }
+                if (active && row < p.S)
+                    *reinterpret_cast<uint4 *>(p.out + ((size_t)row * p.Hq + h) * D + 8 * cc) =
+                        make_uint4(ow[0], ow[1], ow[2], ow[3]);
+            }
+        };
+
+        // Both phases run the same sequence S(0), softmax(0), S(1), O += V(0)P(0)
+        // and softmax(1), ...; block 0 closes each interval after its context
+        // half, block 1 after its scores half, which puts block 1 half an
+        // interval behind.  The barrier is the workgroup's: each wave arrives
+        // once per interval, from either place.
+        const bool lag = blk == 1;
+        s_half8(kaddr_of(0), qf, s, issue_loads(0));
+        if (lag)
+            close_interval();
+        causal_hide(0, s);
+        pv_half8<false, true>(0u, o, pw, s, m, l, alpha);
+        rescale(o, alpha);
+        if (!lag)
+            close_interval();
+#pragma clang loop unroll(disable)
+        for (int k = 1; k < n; ++k) {
+            s_half8(kaddr_of(k), qf, s, issue_loads(k));
+            if (lag)
+                close_interval();
+            causal_hide(k, s);
+            pv_half8<true, true>(vaddr_of(k - 1), o, pw, s, m, l, alpha);
+            rescale(o, alpha);
+            if (!lag)
+                close_interval();
+        }
+        if (lag)
+            close_interval();
+        load_gates();
+        pv_half8<true, false>(vaddr_of(n - 1), o, pw, s, m, l, alpha);
+        if (!lag)
+            close_interval();
+        epilogue();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
 hipError_t launch_kv_prologue(const KvPrologueParams &p, int ntiles, hipStream_t stream)
@@ -1186,10 +1611,10 @@ hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stre
         hipLaunchKernelGGL((attn_fwd<true, false>), dim3(nblocks), dim3(ATHREADS), 0, stream, p);
         break;
     case AttnMode::Bidirectional:
-        hipLaunchKernelGGL((attn_fwd<false, true>), dim3(nblocks), dim3(ATHREADS), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd8<true>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
         break;
     default:
-        hipLaunchKernelGGL((attn_fwd<false, false>), dim3(nblocks), dim3(ATHREADS), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd8<false>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
     }
     return hipGetLastError();
 }
