@@ -14,7 +14,13 @@ launch stream.  ``cpu_baseline`` times the CPU oracle on a bounded row sample
 of the same workload.
 
 ``--mode copy`` runs only a plain device copy of known size (used to scale the
-HBM byte counters of a ``rocprofv3 --pmc`` run).
+HBM byte counters of a ``rocprofv3 --pmc`` run).  ``--mode gemm`` times the
+vendor library's bf16 GEMM (torch.matmul, 8192^3, random N(0,1) operands) on
+the same box: the matrix-core rate a tuned library reaches under this box's
+power limit, as context for the attention kernel's ``roofline``.  ``--mode
+mfma`` runs the library's calibration kernel (back-to-back bf16 MFMAs on
+pseudo-random operands, one wave per SIMD on every compute unit) and reports
+the shader clock and matrix-core rate the device sustains under that load.
 """
 
 from __future__ import annotations
@@ -85,7 +91,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--cpu-threads", type=int, default=0)
-    ap.add_argument("--mode", choices=["attention", "copy"], default="attention")
+    ap.add_argument("--mode", choices=["attention", "copy", "gemm", "mfma"], default="attention")
     ap.add_argument("--cached", action="store_true",
                     help="prefix workloads: keys before q_base come from a prepared K/V cache "
                          "(attn_prefill_append); only the window's keys are prepared per step")
@@ -118,6 +124,34 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes_read_per_copy": nbytes,
                           "bytes_written_per_copy": nbytes, "copies": args.steps}), flush=True)
+        return
+
+    if args.mode == "mfma":
+        ga.attn_mfma_clock_probe(2000)                 # warm the clocks
+        mhz, tf = ga.attn_mfma_clock_probe(40000)
+        print(json.dumps({"mode": "mfma", "op": "v_mfma_f32_32x32x16_bf16", "operands": "uniform [-1,1) bf16",
+                          "shader_mhz": round(mhz), "tflops": round(tf, 1)}), flush=True)
+        return
+
+    if args.mode == "gemm":
+        n = 8192
+        g = torch.Generator(device=dev)
+        g.manual_seed(0)
+        a = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        b = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+        for _ in range(max(args.warmup, 1)):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"mode": "gemm", "m": n, "n": n, "k": n, "dtype": "bf16", "ms": round(ms, 5),
+                          "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}), flush=True)
         return
 
     t0 = time.perf_counter()

@@ -86,6 +86,8 @@ def _load():
         "attn_ctx_set_timing": (ctypes.c_int, [vp, ctypes.c_int]),
         "attn_ctx_read_timing": (ctypes.c_int, [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                                 ctypes.POINTER(i32)]),
+        "attn_mfma_clock_probe": (ctypes.c_int, [i32, vp, ctypes.POINTER(ctypes.c_double),
+                                                 ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -170,6 +172,17 @@ def attn_ctx_read_timing(ctx, kernel: int):
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_ctx_read_timing")
     return ms.value, n.value
+
+
+def attn_mfma_clock_probe(iters: int, stream: int = 0):
+    """(shader clock MHz, bf16 MFMA TFLOP/s) of the current device under a
+    pure matrix-core load with pseudo-random operands (blocking)."""
+    mhz = ctypes.c_double()
+    tf = ctypes.c_double()
+    rc = lib.attn_mfma_clock_probe(iters, stream, ctypes.byref(mhz), ctypes.byref(tf))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_mfma_clock_probe")
+    return mhz.value, tf.value
 
 
 # ---- tensor-level wrapper --------------------------------------------------

@@ -463,4 +463,47 @@ int attn_ctx_read_timing(attn_ctx *ctx, int kernel, double *total_ms, int32_t *l
     return ATTN_OK;
 }
 
+int attn_mfma_clock_probe(int32_t iters, void *stream, double *mhz, double *tflops)
+{
+    if (!mhz || !tflops)
+        return ATTN_ERR_NULL_ARG;
+    if (iters < 1 || iters > 10000000)
+        return ATTN_ERR_RANGE;
+    int device = 0, cus = 0;
+    if (hipGetDevice(&device) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
+        return ATTN_ERR_DEVICE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    long long *rec = nullptr;
+    float *sink = nullptr;
+    if (hipMalloc(&rec, sizeof(long long) * 2 * cus) != hipSuccess)
+        return ATTN_ERR_NOMEM;
+    if (hipMalloc(&sink, sizeof(float) * 256 * cus) != hipSuccess) {
+        (void)hipFree(rec);
+        return ATTN_ERR_NOMEM;
+    }
+    std::vector<long long> h(2 * (size_t)cus);
+    int rc = ATTN_OK;
+    if (ga::launch_mfma_clock_probe(iters, cus, rec, sink, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess ||
+        hipMemcpy(h.data(), rec, sizeof(long long) * 2 * cus, hipMemcpyDeviceToHost) != hipSuccess)
+        rc = ATTN_ERR_LAUNCH;
+    (void)hipFree(rec);
+    (void)hipFree(sink);
+    if (rc != ATTN_OK)
+        return rc;
+    double cyc = 0.0, ticks = 0.0;
+    for (int i = 0; i < cus; ++i) {
+        cyc += (double)h[2 * i];
+        ticks += (double)h[2 * i + 1];
+    }
+    cyc /= cus;
+    ticks /= cus;
+    if (ticks <= 0.0)
+        return ATTN_ERR_LAUNCH;
+    const double seconds = ticks / 100.0e6;
+    *mhz = cyc / seconds / 1.0e6;
+    *tflops = (double)cus * 4.0 * iters * 16.0 * 32768.0 / seconds / 1.0e12;
+    return ATTN_OK;
+}
+
 }  // extern "C"

@@ -1589,6 +1589,57 @@ void attn_fwd8(AttnParams p)
 }
 
 // ---------------------------------------------------------------------------
+// Calibration: the matrix-core rate this device sustains under its power
+// limit.  One workgroup per compute unit, one wave per SIMD, back-to-back
+// v_mfma_f32_32x32x16_bf16 on four independent accumulators with operands
+// drawn from a xorshift generator (uniform in [-1, 1), i.e. every bit of the
+// bf16 operands toggles like real data).  Each workgroup records its shader
+// cycles (s_memtime) and 100 MHz ticks (s_memrealtime) over the loop.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mfma_clock_probe(int iters, long long *rec, float *sink)
+{
+    f32x16 acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            acc[m][e] = 0.0f;
+    bf16x8 a[4], b[4];
+    uint32_t x = 2463534242u ^ (threadIdx.x * 7919u + blockIdx.x * 104729u);
+    auto next = [&]() {
+        x ^= x << 13;
+        x ^= x >> 17;
+        x ^= x << 5;
+        return (float)(x & 0xffffu) * (1.0f / 32768.0f) - 1.0f;
+    };
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a[m][e] = (__bf16)next();
+            b[m][e] = (__bf16)next();
+        }
+    const long long c0 = clock64(), r0 = wall_clock64();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+            acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(m >> 2) & 3], b[m & 3], acc[m & 3], 0, 0, 0);
+    }
+    const long long c1 = clock64(), r1 = wall_clock64();
+    float sum = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            sum += acc[m][e];
+    sink[blockIdx.x * 256 + threadIdx.x] = sum;
+    if (threadIdx.x == 0) {
+        rec[2 * blockIdx.x] = c1 - c0;
+        rec[2 * blockIdx.x + 1] = r1 - r0;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
 hipError_t launch_kv_prologue(const KvPrologueParams &p, int ntiles, hipStream_t stream)
@@ -1622,6 +1673,12 @@ hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stre
 hipError_t launch_kp_unpack(const uint16_t *kp, int Tpad, int T, int Hkv, uint16_t *out, hipStream_t stream)
 {
     hipLaunchKernelGGL(kp_unpack, dim3((T + KT - 1) / KT, Hkv), dim3(256), 0, stream, kp, Tpad, T, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_clock_probe(int iters, int n_wg, long long *rec, float *sink, hipStream_t stream)
+{
+    hipLaunchKernelGGL(mfma_clock_probe, dim3(n_wg), dim3(256), 0, stream, iters, rec, sink);
     return hipGetLastError();
 }
 

@@ -208,6 +208,18 @@ ATTN_EXPORT int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t
 ATTN_EXPORT int attn_ctx_set_timing(attn_ctx *ctx, int enable);
 ATTN_EXPORT int attn_ctx_read_timing(attn_ctx *ctx, int kernel, double *total_ms, int32_t *launches);
 
+/*
+ * Calibration (not part of the attention path): the bf16 matrix-core rate the
+ * current device sustains under its power limit.  Launches one workgroup per
+ * compute unit on `stream`, one wave per SIMD issuing back-to-back
+ * v_mfma_f32_32x32x16_bf16 (iters x 16 per wave) on pseudo-random operands,
+ * waits for it, and returns the mean shader clock (MHz, s_memtime cycles over
+ * s_memrealtime's 100 MHz ticks) and the MFMA rate (TFLOP/s).  Allocates and
+ * frees a few KB of device memory itself; blocking.  iters in [1, 1e7], else
+ * ATTN_ERR_RANGE.
+ */
+ATTN_EXPORT int attn_mfma_clock_probe(int32_t iters, void *stream, double *mhz, double *tflops);
+
 #ifdef __cplusplus
 }
 #endif

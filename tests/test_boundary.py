@@ -174,3 +174,11 @@ def test_kv_cache_bytes(ga):
     rc, n = ga.attn_kv_cache_bytes(_geom(ga, n_q_heads=24, n_kv_heads=5))
     assert rc == ga.ATTN_ERR_GEOMETRY and n == 0
     assert ga.lib.attn_kv_cache_bytes(g, None) == ga.ATTN_ERR_NULL_ARG
+
+
+def test_mfma_probe_refuses_bad_arguments(ga):
+    """The calibration entry checks its arguments before touching a device."""
+    mhz, tf = ctypes.c_double(), ctypes.c_double()
+    assert ga.lib.attn_mfma_clock_probe(0, None, ctypes.byref(mhz), ctypes.byref(tf)) == ga.ATTN_ERR_RANGE
+    assert ga.lib.attn_mfma_clock_probe(10 ** 8, None, ctypes.byref(mhz), ctypes.byref(tf)) == ga.ATTN_ERR_RANGE
+    assert ga.lib.attn_mfma_clock_probe(10, None, None, ctypes.byref(tf)) == ga.ATTN_ERR_NULL_ARG

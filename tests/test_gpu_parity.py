@@ -337,3 +337,17 @@ def test_timing_hooks():
     assert n == 3 and ms > 0
     ctx.set_timing(False)
     ctx.close()
+
+
+@pytest.mark.gpu
+def test_mfma_clock_probe_is_plausible():
+    """The calibration kernel runs and reports a clock and rate a gfx950 can
+    have: at most the 2.4 GHz boost clock and the matching 2.5 PFLOP/s."""
+    import gated_gqa_causal_amd as ga
+    say("mfma clock probe")
+    mhz, tf = ga.attn_mfma_clock_probe(2000)
+    assert 300.0 < mhz < 2500.0
+    assert 100.0 < tf < 2600.0
+    # rate and clock agree: 4 SIMDs x 1024 FLOP per cycle per compute unit
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert abs(tf * 1e12 / (cus * 4 * 1024 * mhz * 1e6) - 1.0) < 0.1
