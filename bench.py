@@ -13,6 +13,10 @@ dominant kernel (attention), timed with HIP events around each launch on the
 launch stream.  ``cpu_baseline`` times the CPU oracle on a bounded row sample
 of the same workload.
 
+A packed-batch workload (``--workload c6_varlen_16x128_2048``) runs its
+sequences in one ``attn_prefill_gated_batch`` call per step; its CPU baseline
+samples the longest sequence.
+
 ``--mode copy`` runs only a plain device copy of known size (used to scale the
 HBM byte counters of a ``rocprofv3 --pmc`` run).  ``--mode gemm`` times the
 vendor library's bf16 GEMM (torch.matmul, 8192^3, random N(0,1) operands) on
@@ -155,20 +159,34 @@ def main():
         return
 
     t0 = time.perf_counter()
-    p = synth.config_problem(args.workload)
-    log(f"workload {args.workload}: T={p.T} q_base={p.q_base} Hq={p.n_q_heads} Hkv={p.n_kv_heads} "
-        f"mask={'yes' if p.mask is not None else 'no'}; generated in {time.perf_counter() - t0:.1f}s")
+    batch = None
+    if args.workload in synth.BATCH_CONFIGS:
+        # A packed batch: p stands for its longest sequence where one problem is
+        # needed (shapes, the CPU baseline's sample).
+        batch = synth.config_batch(args.workload)
+        p = max(batch.seqs, key=lambda q: q.T)
+        log(f"workload {args.workload}: {len(batch.seqs)} sequences, {batch.total} tokens "
+            f"(lengths {min(batch.lens)}..{max(batch.lens)}), Hq={p.n_q_heads} Hkv={p.n_kv_heads}; "
+            f"generated in {time.perf_counter() - t0:.1f}s")
+    else:
+        p = synth.config_problem(args.workload)
+        log(f"workload {args.workload}: T={p.T} q_base={p.q_base} Hq={p.n_q_heads} Hkv={p.n_kv_heads} "
+            f"mask={'yes' if p.mask is not None else 'no'}; generated in {time.perf_counter() - t0:.1f}s")
 
     def dev_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    qg, k, v = dev_bf16(p.qg), dev_bf16(p.k), dev_bf16(p.v)
+    src = batch if batch is not None else p
+    qg, k, v = dev_bf16(src.qg), dev_bf16(src.k), dev_bf16(src.v)
     wq, wk = dev_bf16(p.q_norm_w), dev_bf16(p.k_norm_w)
     cos = torch.from_numpy(p.cos).to(dev)
     sin = torch.from_numpy(p.sin).to(dev)
     mask = None if p.mask is None else torch.from_numpy(p.mask).to(dev)
-    out = torch.empty((p.rows, p.n_q_heads * 256), dtype=torch.bfloat16, device=dev)
-    ctx = ga.Context(p.n_q_heads, p.n_kv_heads, p.T, p.rms_eps)
+    rows = batch.total if batch is not None else p.rows
+    out = torch.empty((rows, p.n_q_heads * 256), dtype=torch.bfloat16, device=dev)
+    # A batch's sequences each start on a 32-key tile of the workspace.
+    cap = sum((L + 31) // 32 * 32 for L in batch.lens) if batch is not None else p.T
+    ctx = ga.Context(p.n_q_heads, p.n_kv_heads, cap, p.rms_eps)
     stream = torch.cuda.current_stream()
 
     cache = None
@@ -184,7 +202,9 @@ def main():
         k_new, v_new = k[qb:], v[qb:]
 
     def step():
-        if cache is not None:
+        if batch is not None:
+            ctx.prefill_gated_batch(qg, k, v, wq, wk, cos, sin, batch.lens, out=out, stream=stream)
+        elif cache is not None:
             ctx.prefill_append(qg, k_new, v_new, wq, wk, cos, sin, p.T, p.q_base, cache, out=out, stream=stream)
         elif not p.causal:
             ctx.prefill_bidirectional(qg, k, v, wq, wk, cos, sin, out=out, stream=stream)
@@ -215,7 +235,7 @@ def main():
     mp_ms, mp_n = ctx.read_timing(ga.ATTN_KERNEL_MASK_PACK)
     ctx.set_timing(False)
     ms_per_step = total_ms / args.steps
-    flops = p.flops()
+    flops = batch.flops() if batch is not None else p.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     attn_avg_ms = attn_ms / max(attn_n, 1)
     achieved = flops / (attn_avg_ms * 1e-3) / 1e12
@@ -235,18 +255,22 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": p.name, "tokens": p.T, "q_base": p.q_base, "n_q_heads": p.n_q_heads,
+        "config": {"workload": args.workload, "tokens": batch.total if batch is not None else p.T,
+                   "q_base": p.q_base, "n_q_heads": p.n_q_heads,
                    "n_kv_heads": p.n_kv_heads, "head_dim": p.head_dim, "rotary_dim": p.rotary_dim,
                    "masked": p.mask is not None, "causal": p.causal, "cached_prefix": bool(args.cached),
-                   "seed": p.seed,
+                   "seed": synth.BATCH_CONFIGS[args.workload]["seed"] if batch is not None else p.seed,
                    "algorithmic_gflop": round(flops / 1e9, 3)},
         "kernels_ms": {"attention": round(attn_avg_ms, 5),
                        "kv_prologue": round(pro_ms / max(pro_n, 1), 5),
                        "mask_pack": round(mp_ms / max(mp_n, 1), 5) if mp_n else None},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(p.name)},
+                     "traffic": measured_traffic(args.workload)},
     }
+    if batch is not None:
+        rec["config"]["sequences"] = len(batch.seqs)
+        rec["config"]["seq_lens"] = batch.lens
     ctx.close()
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)

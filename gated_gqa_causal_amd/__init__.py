@@ -26,6 +26,7 @@ ATTN_ROTARY_DIM = 64
 ATTN_MAX_GROUP = 16
 ATTN_MAX_TOKENS = 32768
 ATTN_QBASE_ALIGN = 128
+ATTN_MAX_SEQS = 4096
 
 ATTN_OK = 0
 ATTN_ERR_NULL_ARG = -1
@@ -88,6 +89,10 @@ def _load():
                                                 ctypes.POINTER(i32)]),
         "attn_mfma_clock_probe": (ctypes.c_int, [i32, vp, ctypes.POINTER(ctypes.c_double),
                                                  ctypes.POINTER(ctypes.c_double)]),
+        "attn_validate_batch": (ctypes.c_int, [ctypes.POINTER(attn_geometry), ctypes.POINTER(attn_inputs), i32,
+                                               ctypes.POINTER(i32), vp]),
+        "attn_prefill_gated_batch": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, ctypes.POINTER(i32),
+                                                    vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -172,6 +177,22 @@ def attn_ctx_read_timing(ctx, kernel: int):
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_ctx_read_timing")
     return ms.value, n.value
+
+
+def _lens_array(seq_lens):
+    n = len(seq_lens)
+    return n, (ctypes.c_int32 * max(n, 1))(*[int(x) for x in seq_lens])
+
+
+def attn_validate_batch(geom: attn_geometry, inputs, seq_lens, out) -> int:
+    n, arr = _lens_array(seq_lens)
+    return lib.attn_validate_batch(ctypes.byref(geom), ctypes.byref(inputs) if inputs is not None else None, n,
+                                   arr, out)
+
+
+def attn_prefill_gated_batch(ctx, inputs: attn_inputs, seq_lens, out: int, stream: int) -> int:
+    n, arr = _lens_array(seq_lens)
+    return lib.attn_prefill_gated_batch(ctx, ctypes.byref(inputs), n, arr, out, stream)
 
 
 def attn_mfma_clock_probe(iters: int, stream: int = 0):
@@ -274,6 +295,17 @@ class Context:
         rc = attn_prefill_gated(self.handle, inp, S, out.data_ptr(), self._stream(stream))
         if rc != ATTN_OK:
             raise AttnError(rc, "attn_prefill_gated")
+        return out
+
+    def prefill_gated_batch(self, qg, k, v, q_norm_w, k_norm_w, cos, sin, seq_lens, out=None, stream=None):
+        """Packed batch: the sequences' rows back to back in qg / k / v / out, each
+        a causal pass at positions 0..len-1 (seq_lens: host list of lengths)."""
+        total = int(sum(int(x) for x in seq_lens))
+        inp = self.inputs(qg, k, v, q_norm_w, k_norm_w, cos, sin, total, total)
+        out = self._out(out, total)
+        rc = attn_prefill_gated_batch(self.handle, inp, list(seq_lens), out.data_ptr(), self._stream(stream))
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_prefill_gated_batch")
         return out
 
     def kv_cache(self):

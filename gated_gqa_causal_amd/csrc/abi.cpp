@@ -30,6 +30,14 @@ struct attn_ctx {
     uint16_t *vt = nullptr;        // transposed values, [Hkv][tpad/32] tiles of 256 x 32
     uint32_t *mask_bits = nullptr; // [max_tokens][mask_words]
     uint8_t *tile_vis = nullptr;   // [ceil(max_tokens/64)][mask_words]
+    // packed batches: the per-call sequence tables (device), staged through a
+    // pinned host buffer whose previous copy `batch_copied` must have landed
+    // before it is rewritten
+    int *batch_tab = nullptr;
+    int *batch_host = nullptr;
+    size_t batch_cap = 0;          // ints in each
+    hipEvent_t batch_copied = nullptr;
+    bool batch_pending = false;
     // timing
     bool timing = false;
     std::vector<hipEvent_t> pool;
@@ -110,6 +118,8 @@ void fill_kv_params(ga::KvPrologueParams &kp, const attn_ctx *ctx, const attn_in
     kp.tile0 = 0;
     kp.k_row0 = 0;
     kp.eps = ctx->geom.rms_eps;
+    kp.tile_seg = nullptr;
+    kp.seg = nullptr;
 }
 
 // Bytes of a caller-owned K/V cache for a geometry: prepared keys and
@@ -147,6 +157,75 @@ void fill_attn_params(ga::AttnParams &ap, const attn_ctx *ctx, const attn_inputs
     // One workgroup per compute unit at most; each walks its share of the
     // work items (see the attention kernel).
     ap.n_wg = (int)std::min<int64_t>((int64_t)ap.nrb * ap.Hkv * ap.n_hg, ctx->num_cus);
+    ap.pairs = nullptr;
+    ap.seg = nullptr;
+}
+
+// Packed batch bookkeeping: ints of the per-call table for a workspace of
+// `tpad` keys: seg {len, first row, first tile, 0} per sequence, the sequence
+// of every prepared tile, and the (sequence, row block) pairs heaviest first.
+size_t batch_table_ints(int tpad) { return 4 * (size_t)ATTN_MAX_SEQS + tpad / 32 + 2 * ((size_t)tpad / 64 + ATTN_MAX_SEQS); }
+
+struct BatchPlan {
+    int64_t total = 0, tiles = 0;
+    int max_len = 0, pairs = 0;
+};
+
+// Checks the lengths (and, with `tab`, writes the table): every length in
+// [0, max_tokens], their sum <= max_tokens, and their 32-key tiles within the
+// workspace (each sequence starts on a tile boundary).
+int plan_batch(const attn_geometry &g, int32_t n_seqs, const int32_t *lens, BatchPlan *plan, int *tab)
+{
+    if (n_seqs < 0 || n_seqs > ATTN_MAX_SEQS)
+        return ATTN_ERR_RANGE;
+    if (n_seqs > 0 && !lens)
+        return ATTN_ERR_NULL_ARG;
+    const int64_t tpad = ((int64_t)g.max_tokens + 63) / 64 * 64;
+    BatchPlan pl;
+    for (int i = 0; i < n_seqs; ++i) {
+        if (lens[i] < 0 || lens[i] > g.max_tokens)
+            return ATTN_ERR_RANGE;
+        pl.total += lens[i];
+        pl.tiles += (lens[i] + 31) / 32;
+        pl.max_len = std::max(pl.max_len, (int)lens[i]);
+    }
+    if (pl.total > g.max_tokens || pl.tiles * 32 > tpad)
+        return ATTN_ERR_RANGE;
+    struct Pair {
+        int nt, seq, rb;
+    };
+    std::vector<Pair> pairs;
+    if (tab) {
+        int *seg = tab, *tile_seg = tab + 4 * n_seqs;
+        int row = 0, tile = 0;
+        for (int i = 0; i < n_seqs; ++i) {
+            const int L = lens[i], nt = (L + 31) / 32;
+            seg[4 * i] = L;
+            seg[4 * i + 1] = row;
+            seg[4 * i + 2] = tile;
+            seg[4 * i + 3] = 0;
+            for (int t = 0; t < nt; ++t)
+                tile_seg[tile + t] = i;
+            for (int rb = 0; rb * 64 < L; ++rb)
+                pairs.push_back({std::min(rb * 64 + 63, L - 1) / 32 + 1, i, rb});
+            row += L;
+            tile += nt;
+        }
+        // Heaviest walks first (ties: sequence, then row block), as the single
+        // pass numbers its row blocks.
+        std::sort(pairs.begin(), pairs.end(), [](const Pair &a, const Pair &b) {
+            return a.nt != b.nt ? a.nt > b.nt : a.seq != b.seq ? a.seq < b.seq : a.rb < b.rb;
+        });
+        int *pr = tile_seg + pl.tiles;
+        for (size_t k = 0; k < pairs.size(); ++k) {
+            pr[2 * k] = pairs[k].seq;
+            pr[2 * k + 1] = pairs[k].rb;
+        }
+        pl.pairs = (int)pairs.size();
+    }
+    if (plan)
+        *plan = pl;
+    return ATTN_OK;
 }
 
 // kind 4: `mask` is the caller's K/V cache; the prologue writes keys
@@ -306,6 +385,10 @@ int attn_ctx_create(const attn_geometry *geom, int device, attn_ctx **out)
               hipMalloc(&ctx->vt, kv_elems * 2) == hipSuccess &&
               hipMalloc(&ctx->mask_bits, (size_t)geom->max_tokens * ctx->mask_words * 4) == hipSuccess &&
               hipMalloc(&ctx->tile_vis, nrb * ctx->mask_words) == hipSuccess;
+    ctx->batch_cap = batch_table_ints(ctx->tpad);
+    ok = ok && hipMalloc(&ctx->batch_tab, ctx->batch_cap * sizeof(int)) == hipSuccess &&
+         hipHostMalloc(&ctx->batch_host, ctx->batch_cap * sizeof(int), hipHostMallocDefault) == hipSuccess &&
+         hipEventCreateWithFlags(&ctx->batch_copied, hipEventDisableTiming) == hipSuccess;
     if (!ok) {
         (void)hipGetLastError();
         attn_ctx_destroy(ctx);
@@ -327,6 +410,11 @@ void attn_ctx_destroy(attn_ctx *ctx)
     (void)hipFree(ctx->vt);
     (void)hipFree(ctx->mask_bits);
     (void)hipFree(ctx->tile_vis);
+    (void)hipFree(ctx->batch_tab);
+    if (ctx->batch_host)
+        (void)hipHostFree(ctx->batch_host);
+    if (ctx->batch_copied)
+        (void)hipEventDestroy(ctx->batch_copied);
     for (hipEvent_t e : ctx->pool)
         (void)hipEventDestroy(e);
     if (prev >= 0 && prev != ctx->device)
@@ -372,6 +460,87 @@ int attn_prefill_append(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t
 int attn_prefill_bidirectional(attn_ctx *ctx, const attn_inputs *in, int32_t S, void *out, void *stream)
 {
     return run(ctx, in, S, 0, 3, nullptr, out, stream);
+}
+
+int attn_validate_batch(const attn_geometry *geom, const attn_inputs *in, int32_t n_seqs, const int32_t *seq_lens,
+                        const void *out)
+{
+    int rc = check_geometry(geom);
+    if (rc != ATTN_OK)
+        return rc;
+    BatchPlan pl;
+    rc = plan_batch(*geom, n_seqs, seq_lens, &pl, nullptr);
+    if (rc != ATTN_OK)
+        return rc;
+    if (pl.total == 0)
+        return ATTN_OK;             // nothing to do: pointers unused
+    if (!in || !out)
+        return ATTN_ERR_NULL_ARG;
+    if (!in->qg || !in->k || !in->v || !in->q_norm_w || !in->k_norm_w || !in->cos_tab || !in->sin_tab)
+        return ATTN_ERR_NULL_ARG;
+    if (in->n_pos < pl.max_len)
+        return ATTN_ERR_RANGE;
+    if (!aligned16(in->qg) || !aligned16(in->k) || !aligned16(in->v) || !aligned16(in->q_norm_w) ||
+        !aligned16(in->k_norm_w) || !aligned16(in->cos_tab) || !aligned16(in->sin_tab) || !aligned16(out))
+        return ATTN_ERR_ALIGN;
+    return ATTN_OK;
+}
+
+int attn_prefill_gated_batch(attn_ctx *ctx, const attn_inputs *in, int32_t n_seqs, const int32_t *seq_lens,
+                             void *out, void *stream)
+{
+    if (!ctx)
+        return ATTN_ERR_NULL_ARG;
+    int rc = attn_validate_batch(&ctx->geom, in, n_seqs, seq_lens, out);
+    if (rc != ATTN_OK)
+        return rc;
+    BatchPlan pl;
+    (void)plan_batch(ctx->geom, n_seqs, seq_lens, &pl, nullptr);
+    if (pl.total == 0)
+        return ATTN_OK;
+    rc = current_device_matches(ctx);
+    if (rc != ATTN_OK)
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    // The staging buffer is reused: the previous call's copy must have landed.
+    if (ctx->batch_pending && hipEventSynchronize(ctx->batch_copied) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+    ctx->batch_pending = false;
+    (void)plan_batch(ctx->geom, n_seqs, seq_lens, &pl, ctx->batch_host);
+    const size_t n_int = 4 * (size_t)n_seqs + (size_t)pl.tiles + 2 * (size_t)pl.pairs;
+    if (n_int > ctx->batch_cap)
+        return ATTN_ERR_RANGE;
+    if (hipMemcpyAsync(ctx->batch_tab, ctx->batch_host, n_int * sizeof(int), hipMemcpyHostToDevice, s) !=
+            hipSuccess ||
+        hipEventRecord(ctx->batch_copied, s) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+    ctx->batch_pending = true;
+    const int *seg = ctx->batch_tab, *tile_seg = seg + 4 * n_seqs, *pairs = tile_seg + pl.tiles;
+
+    ga::KvPrologueParams kvp;
+    fill_kv_params(kvp, ctx, in, pl.max_len);
+    kvp.tile_seg = tile_seg;
+    kvp.seg = seg;
+    {
+        Timer tm(ctx, s, ATTN_KERNEL_KV_PROLOGUE);
+        if (ga::launch_kv_prologue(kvp, (int)pl.tiles, s) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+        tm.stop();
+    }
+    ga::AttnParams ap;
+    fill_attn_params(ap, ctx, in, pl.max_len, 0, out);
+    ap.pairs = pairs;
+    ap.seg = seg;
+    ap.nrb = pl.pairs;
+    ap.n_wg = (int)std::min<int64_t>((int64_t)ap.nrb * ap.Hkv * ap.n_hg, ctx->num_cus);
+    {
+        Timer tm(ctx, s, ATTN_KERNEL_ATTENTION);
+        if (ga::launch_attention(ap, ga::AttnMode::Causal, s) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+        tm.stop();
+    }
+    return ATTN_OK;
 }
 
 int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, void *qp_out,

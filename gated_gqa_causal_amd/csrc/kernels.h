@@ -19,6 +19,10 @@ struct KvPrologueParams {
     int tile0;                // first tile written (grid x = tile - tile0)
     int k_row0;               // position of row 0 of k and v
     float eps;
+    // Packed batch (else null): tile_seg[x] = sequence of prepared tile x;
+    // seg[4 s ..] = {length, first row in k/v, first prepared tile, 0}.
+    const int *tile_seg;
+    const int *seg;
 };
 
 struct MaskPackParams {
@@ -43,6 +47,11 @@ struct AttnParams {
     int Hq, Hkv, G, n_hg, nrb, Tpad, W;
     int n_wg;                 // attention workgroups (<= work items)
     float eps;
+    // Packed batch (else null): pairs[2 i ..] = {sequence, row block} of the
+    // i-th (64-row block) in walk order, nrb = their count; seg as in
+    // KvPrologueParams.  Each sequence is a causal pass at positions 0..len-1.
+    const int *pairs;
+    const int *seg;
 };
 
 constexpr int kRowsPerBlock = 64;

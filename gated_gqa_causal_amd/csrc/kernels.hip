@@ -101,14 +101,22 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
     __shared__ __align__(16) uint16_t ks[KT][D + 8];
     __shared__ __align__(16) uint16_t vs[KT][D + 8];
     __shared__ float rs[KT];
+    // tile: prepared tile written; t0: position of its first key; T: keys of
+    // the sequence; raw row of position key = key + row_base.
     const int tile = p.tile0 + (int)blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
-    const int t0 = tile * KT;
+    int t0 = tile * KT, T = p.T, row_base = -p.k_row0;
+    if (p.tile_seg) {
+        const int sq = p.tile_seg[blockIdx.x];
+        T = p.seg[4 * sq];
+        row_base = p.seg[4 * sq + 1];
+        t0 = (tile - p.seg[4 * sq + 2]) * KT;
+    }
 
     for (int it = 0; it < 4; ++it) {
         const int idx = it * 256 + tid, r = idx >> 5, ch = idx & 31, key = t0 + r;
         uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-        if (key < p.T) {
-            const size_t off = ((size_t)(key - p.k_row0) * p.Hkv + c) * D + ch * 8;
+        if (key < T) {
+            const size_t off = ((size_t)(key + row_base) * p.Hkv + c) * D + ch * 8;
             kv = *reinterpret_cast<const uint4 *>(p.k + off);
             vv = *reinterpret_cast<const uint4 *>(p.v + off);
         }
@@ -138,7 +146,7 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
             const int d = sub + 8 * s;
             n[s] = rbf((bf2f(ks[r][d]) * rr) * (1.0f + bf2f(p.wk[d])));
         }
-        if (key < p.T) {
+        if (key < T) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int j = sub + 8 * s;
@@ -151,7 +159,7 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
         }
 #pragma unroll
         for (int s = 0; s < 32; ++s)
-            ks[r][sub + 8 * s] = (key < p.T) ? f2bf(n[s]) : (uint16_t)0;
+            ks[r][sub + 8 * s] = (key < T) ? f2bf(n[s]) : (uint16_t)0;
     }
     __syncthreads();
 
@@ -1368,7 +1376,7 @@ __device__ __forceinline__ void pv_half8(uint32_t vaddr, f32x16 (&o)[8], u32x4 (
 
 template <bool BIDIR>
 __global__ __attribute__((amdgpu_flat_work_group_size(ATHREADS8, ATHREADS8), amdgpu_waves_per_eu(2, 2)))
-void attn_fwd8(AttnParams p)
+void attn_fwd8(AttnParams pk)
 {
     __shared__ __align__(16) char smem[SMEM8];     // K tiles 0..3, V^T tiles 4..7; epilogue staging
 
@@ -1377,9 +1385,10 @@ void attn_fwd8(AttnParams p)
     const int hw = wave & 3;                        // head within the group of four
     const int blk = wave >> 2;                      // 32-row block; 1 = the lagging phase
 
-    // Work items and their order as in attn_fwd.
-    const int per_rb = p.Hkv * p.n_hg;
-    const int n_items = p.nrb * per_rb;
+    // Work items and their order as in attn_fwd (a packed batch lists its
+    // (sequence, row block) pairs heaviest first instead).
+    const int per_rb = pk.Hkv * pk.n_hg;
+    const int n_items = pk.nrb * per_rb;
     const int P = (int)gridDim.x;
 #pragma clang loop unroll(disable)
     for (int pass = 0;; ++pass) {
@@ -1391,7 +1400,21 @@ void attn_fwd8(AttnParams p)
         int lane = lane_id;
         asm volatile("" : "+v"(lane));
         const int j = lane & 31, hh = lane >> 5;
-        const int rb = p.nrb - 1 - item / per_rb;
+        // The item's problem: the launch's, or one sequence of a packed batch
+        // (its rows, its prepared key tiles, positions from 0).
+        AttnParams p = pk;
+        int rb, ktile0 = 0;
+        if (!BIDIR && pk.pairs) {
+            const int sq = pk.pairs[2 * (item / per_rb)];
+            rb = pk.pairs[2 * (item / per_rb) + 1];
+            p.S = p.T = pk.seg[4 * sq];
+            p.q_base = 0;
+            p.qg = pk.qg + (size_t)pk.seg[4 * sq + 1] * pk.Hq * 2 * D;
+            p.out = pk.out + (size_t)pk.seg[4 * sq + 1] * pk.Hq * D;
+            ktile0 = pk.seg[4 * sq + 2];
+        } else {
+            rb = pk.nrb - 1 - item / per_rb;
+        }
         const int rem = item % per_rb;
         const int kvh = rem / p.n_hg, hg = rem % p.n_hg;
         const int gidx = hg * 4 + hw;
@@ -1406,8 +1429,8 @@ void attn_fwd8(AttnParams p)
         const int n = ntiles;                            // >= 1: row r0 sees key 0
 
         const uint32_t smem_base = lds_addr(smem);
-        const uint16_t *kbase = p.kp + (size_t)kvh * (p.Tpad / KT) * (KT * D);
-        const uint16_t *vbase = p.vt + (size_t)kvh * (p.Tpad / KT) * (KT * D);
+        const uint16_t *kbase = p.kp + ((size_t)kvh * (p.Tpad / KT) + ktile0) * (KT * D);
+        const uint16_t *vbase = p.vt + ((size_t)kvh * (p.Tpad / KT) + ktile0) * (KT * D);
         // Wave w moves bytes [2048 w, 2048 w + 2048) of every tile, in two parts.
         const uint32_t voff = (uint32_t)(wave * 2048 + lane * 16);
         auto m0_of = [&](bool is_k, int u) {

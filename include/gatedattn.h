@@ -62,6 +62,7 @@ extern "C" {
 #define ATTN_MAX_GROUP 16         /* query heads per KV head, 1..16          */
 #define ATTN_MAX_TOKENS 32768     /* cap on T (keys); max_tokens <= this     */
 #define ATTN_QBASE_ALIGN 128      /* q_base must be a multiple of this       */
+#define ATTN_MAX_SEQS 4096        /* sequences per packed batch              */
 
 typedef enum {
     ATTN_OK = 0,
@@ -186,6 +187,31 @@ ATTN_EXPORT int attn_prefill_bidirectional(attn_ctx *ctx, const attn_inputs *in,
 ATTN_EXPORT int attn_kv_cache_bytes(const attn_geometry *geom, size_t *bytes);
 ATTN_EXPORT int attn_prefill_append(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base,
                                     void *kv_cache, void *out, void *stream);
+
+/*
+ * Packed batch of independent sequences in one launch (the serving page's
+ * batched gated attention: a pack of candidates must give each candidate the
+ * bits it gets alone, whatever its neighbours and their order).
+ * seq_lens: host int32 [n_seqs], read during the call only.  Rows of qg, k, v
+ * and out hold the sequences back to back: sequence i starts at row
+ * sum_{j<i} seq_lens[j] (qg [total][Hq][2][D], k and v [total][Hkv][D], out
+ * [total][Hq * D]).  Each sequence is a dense causal pass at positions
+ * 0..len-1 (cos/sin rows 0..len-1, so n_pos >= the longest length), sharing
+ * the norm weights; its output rows equal attn_prefill_gated on that
+ * sequence alone, bit for bit.  Limits: 0 <= n_seqs <= ATTN_MAX_SEQS, every
+ * length in [0, max_tokens], the total <= max_tokens, and the sum of the
+ * lengths rounded up to 32 <= max_tokens rounded up to 64 (each sequence's
+ * keys start on a 32-key tile of the workspace), else ATTN_ERR_RANGE.
+ * Zero-length sequences are allowed; a total of 0 is a no-op.  The call
+ * copies a small table (sequences, tiles, row blocks) to the device through
+ * the context's pinned staging buffer, waiting first for the previous batch
+ * call's copy on the context to land.  attn_validate_batch runs the same
+ * host-only checks.
+ */
+ATTN_EXPORT int attn_validate_batch(const attn_geometry *geom, const attn_inputs *in, int32_t n_seqs,
+                                    const int32_t *seq_lens, const void *out);
+ATTN_EXPORT int attn_prefill_gated_batch(attn_ctx *ctx, const attn_inputs *in, int32_t n_seqs,
+                                         const int32_t *seq_lens, void *out, void *stream);
 
 /*
  * Test hook: writes the prepared (normed, rotated) queries and keys the

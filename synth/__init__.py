@@ -234,6 +234,75 @@ def make_problem(*, T: int, n_q_heads: int = 24, n_kv_heads: int = 2, head_dim: 
                    sin=sin, mask=mask, seed=seed, causal=causal)
 
 
+@dataclasses.dataclass
+class Batch:
+    """A packed batch of independent causal sequences of one layer: every
+    sequence shares the norm weights and the rotary table (positions 0..len-1
+    each); the packed tensors are the sequences' rows back to back."""
+    name: str
+    seqs: list             # Problem per sequence (shared q_norm_w, k_norm_w, cos, sin)
+
+    @property
+    def lens(self):
+        return [p.T for p in self.seqs]
+
+    @property
+    def total(self) -> int:
+        return int(sum(self.lens))
+
+    def _cat(self, attr):
+        return np.concatenate([getattr(p, attr) for p in self.seqs], axis=0)
+
+    @property
+    def qg(self):
+        return self._cat("qg")
+
+    @property
+    def k(self):
+        return self._cat("k")
+
+    @property
+    def v(self):
+        return self._cat("v")
+
+    def flops(self) -> float:
+        return float(sum(p.flops() for p in self.seqs))
+
+
+def make_batch(lens, *, n_q_heads: int = 24, n_kv_heads: int = 2, seed: int = 0, gate_sigma: float = 1.0,
+               name: str = "batch") -> Batch:
+    """Sequence i draws its rows under seed ``seed * 1009 + 1 + i``; the shared
+    weights and table come from ``seed`` (a table of max(lens) positions)."""
+    n_pos = max([int(x) for x in lens] + [1])
+    shared = make_problem(T=1, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, seed=seed, n_pos=n_pos)
+    seqs = []
+    for i, L in enumerate(lens):
+        p = make_problem(T=int(L), n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, seed=seed * 1009 + 1 + i,
+                         gate_sigma=gate_sigma, n_pos=n_pos, name=f"{name}[{i}]")
+        seqs.append(dataclasses.replace(p, q_norm_w=shared.q_norm_w, k_norm_w=shared.k_norm_w, cos=shared.cos,
+                                        sin=shared.sin))
+    return Batch(name=name, seqs=seqs)
+
+
+def batch_lens(n: int, lo: int, hi: int, seed: int):
+    """n lengths uniform in [lo, hi] from the counter-based stream (stream 7)."""
+    u = splitmix64(seed, 7, 0, n)
+    return [int(lo + (int(x) % (hi - lo + 1))) for x in u]
+
+
+# Packed-batch workload: 16 sequences of 128..2048 tokens (lengths drawn as in
+# batch_lens), the 24/2 head geometry; stands in for a serving pack of prompts.
+BATCH_CONFIGS = {
+    "c6_varlen_16x128_2048": dict(n=16, lo=128, hi=2048, n_q_heads=24, n_kv_heads=2, seed=6),
+}
+
+
+def config_batch(name: str) -> Batch:
+    kw = dict(BATCH_CONFIGS[name])
+    lens = batch_lens(kw.pop("n"), kw.pop("lo"), kw.pop("hi"), kw["seed"])
+    return make_batch(lens, name=name, **kw)
+
+
 # The workloads: (keys, q heads, kv heads, q_base, seed, gate sigma, mask budget, causal).
 # c5 is the bidirectional pass (vision-path attention, no causal predicate) at c2's shape.
 CONFIGS = {

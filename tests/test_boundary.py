@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(ga):
 def test_header_constants_match_binding(ga):
     src = open(HEADER).read()
     for name in ["ATTN_ABI_VERSION", "ATTN_HEAD_DIM", "ATTN_ROTARY_DIM", "ATTN_MAX_GROUP",
-                 "ATTN_MAX_TOKENS", "ATTN_QBASE_ALIGN", "ATTN_KERNEL_KV_PROLOGUE",
+                 "ATTN_MAX_TOKENS", "ATTN_QBASE_ALIGN", "ATTN_MAX_SEQS", "ATTN_KERNEL_KV_PROLOGUE",
                  "ATTN_KERNEL_MASK_PACK", "ATTN_KERNEL_ATTENTION"]:
         m = re.search(rf"#define {name}\s+(\d+)", src)
         assert m and int(m.group(1)) == getattr(ga, name), name
@@ -182,3 +182,48 @@ def test_mfma_probe_refuses_bad_arguments(ga):
     assert ga.lib.attn_mfma_clock_probe(0, None, ctypes.byref(mhz), ctypes.byref(tf)) == ga.ATTN_ERR_RANGE
     assert ga.lib.attn_mfma_clock_probe(10 ** 8, None, ctypes.byref(mhz), ctypes.byref(tf)) == ga.ATTN_ERR_RANGE
     assert ga.lib.attn_mfma_clock_probe(10, None, None, ctypes.byref(tf)) == ga.ATTN_ERR_NULL_ARG
+
+
+BATCH_REFUSALS = [
+    # (geometry overrides, seq_lens, out, inputs overrides, expected)
+    ({}, [64, -1], FAKE, {}, "RANGE"),                         # negative length
+    ({}, [200, 57], FAKE, {}, "RANGE"),                        # total > max_tokens (256)
+    ({}, [257], FAKE, {}, "RANGE"),                            # one length > max_tokens
+    (dict(max_tokens=64), [1, 1, 1], FAKE, {}, "RANGE"),       # 3 tiles of 32 > 64 keys of workspace
+    ({}, [64, 100], FAKE, dict(n_pos=99), "RANGE"),            # table shorter than the longest sequence
+    ({}, [64, 100], None, {}, "NULL_ARG"),
+    ({}, [64, 100], FAKE, dict(k=0), "NULL_ARG"),
+    ({}, [64, 100], FAKE + 8, {}, "ALIGN"),
+    (dict(n_q_heads=24, n_kv_heads=5), [64], FAKE, {}, "GEOMETRY"),
+]
+
+
+@pytest.mark.parametrize("case", BATCH_REFUSALS, ids=lambda c: f"{c[-1]}")
+def test_batch_refusals(ga, case):
+    geo, lens, out, inov, want = case
+    inp = _inputs(ga, n_pos=256)
+    for k, v in inov.items():
+        setattr(inp, k, v)
+    rc = ga.attn_validate_batch(_geom(ga, **geo), inp, lens, out)
+    assert rc == getattr(ga, "ATTN_ERR_" + want), (rc, ga.attn_status_string(rc))
+
+
+def test_batch_count_limits(ga):
+    g = _geom(ga)
+    n = ctypes.c_int32(1)
+    assert ga.lib.attn_validate_batch(ctypes.byref(g), None, -1, None, None) == ga.ATTN_ERR_RANGE
+    assert ga.lib.attn_validate_batch(ctypes.byref(g), None, ga.ATTN_MAX_SEQS + 1, None, None) == ga.ATTN_ERR_RANGE
+    assert ga.lib.attn_validate_batch(ctypes.byref(g), None, 1, None, None) == ga.ATTN_ERR_NULL_ARG
+    assert ga.lib.attn_validate_batch(ctypes.byref(g), None, 1, ctypes.byref(n), None) == ga.ATTN_ERR_NULL_ARG
+    # ATTN_MAX_SEQS zero-length sequences: a no-op
+    assert ga.attn_validate_batch(g, None, [0] * ga.ATTN_MAX_SEQS, None) == ga.ATTN_OK
+
+
+def test_batch_valid_and_empty(ga):
+    g = _geom(ga)
+    assert ga.attn_validate_batch(g, None, [], None) == ga.ATTN_OK
+    assert ga.attn_validate_batch(g, None, [0, 0], None) == ga.ATTN_OK
+    assert ga.attn_validate_batch(g, _inputs(ga, n_pos=100), [64, 0, 100, 31], FAKE) == ga.ATTN_OK
+    # 8 sequences of 32 fill the 256-key workspace exactly
+    assert ga.attn_validate_batch(g, _inputs(ga, n_pos=32), [32] * 8, FAKE) == ga.ATTN_OK
+    assert ga.attn_validate_batch(g, _inputs(ga, n_pos=33), [32] * 7 + [1, 1], FAKE) == ga.ATTN_ERR_RANGE

@@ -351,3 +351,109 @@ def test_mfma_clock_probe_is_plausible():
     # rate and clock agree: 4 SIMDs x 1024 FLOP per cycle per compute unit
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert abs(tf * 1e12 / (cus * 4 * 1024 * mhz * 1e6) - 1.0) < 0.1
+
+
+# --------------------------------------------------------------------------
+# Packed batches: each sequence gets the bits it gets alone
+# --------------------------------------------------------------------------
+
+def _batch_tensors(b):
+    from gpu_util import bf16_tensor
+    s0 = b.seqs[0]
+    return dict(qg=bf16_tensor(b.qg), k=bf16_tensor(b.k), v=bf16_tensor(b.v), wq=bf16_tensor(s0.q_norm_w),
+                wk=bf16_tensor(s0.k_norm_w), cos=torch.from_numpy(np.ascontiguousarray(s0.cos)).to("cuda"),
+                sin=torch.from_numpy(np.ascontiguousarray(s0.sin)).to("cuda"))
+
+
+def _batch_call(ctx, b, t):
+    return ctx.prefill_gated_batch(t["qg"], t["k"], t["v"], t["wq"], t["wk"], t["cos"], t["sin"], b.lens)
+
+
+def _batch_out(b):
+    import gated_gqa_causal_amd as ga
+    s0 = b.seqs[0]
+    # each sequence's keys start on a 32-key tile of the workspace
+    ctx = ga.Context(s0.n_q_heads, s0.n_kv_heads, max(sum((L + 31) // 32 * 32 for L in b.lens), 1), s0.rms_eps)
+    out = _batch_call(ctx, b, _batch_tensors(b))
+    torch.cuda.synchronize()
+    res = to_bits(out)
+    ctx.close()
+    return res
+
+
+def _offsets(lens):
+    return np.concatenate([[0], np.cumsum(lens)]).astype(int)
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv", [([1, 31, 32, 33, 0, 64, 65, 200, 130], 24, 2),
+                                         ([300, 7, 128], 16, 4), ([5], 6, 1), ([0, 0, 97, 0], 2, 2)])
+def test_batch_equals_sequences_alone(lens, Hq, Hkv):
+    say(f"batch {lens} {Hq}/{Hkv}")
+    b = synth.make_batch(lens, n_q_heads=Hq, n_kv_heads=Hkv, seed=len(lens))
+    got = _batch_out(b)
+    off = _offsets(lens)
+    for i, p in enumerate(b.seqs):
+        if p.T == 0:
+            continue
+        alone = gpu_out(p)
+        assert np.array_equal(got[off[i]:off[i + 1]], alone), f"sequence {i} (len {p.T}) differs"
+
+
+def test_batch_order_does_not_matter():
+    lens = [200, 33, 0, 130, 64]
+    b = synth.make_batch(lens, n_q_heads=8, n_kv_heads=2, seed=11)
+    got = _batch_out(b)
+    perm = [3, 0, 4, 2, 1]
+    bp = synth.Batch(name="perm", seqs=[b.seqs[i] for i in perm])
+    gotp = _batch_out(bp)
+    off, offp = _offsets(lens), _offsets([lens[i] for i in perm])
+    for jp, i in enumerate(perm):
+        assert np.array_equal(got[off[i]:off[i + 1]], gotp[offp[jp]:offp[jp + 1]])
+
+
+def test_batch_vs_oracle(orc):
+    b = synth.make_batch([97, 1, 160, 33], n_q_heads=24, n_kv_heads=2, seed=21, gate_sigma=2.0)
+    got = _batch_out(b)
+    off = _offsets(b.lens)
+    for i, p in enumerate(b.seqs):
+        want = orc.attention(p, threads=8)
+        bad, frac = parity_report(got[off[i]:off[i + 1]], want)
+        say(f"  seq {i} len {p.T}: bad={bad} worst bound fraction={frac:.3f}")
+        assert bad == 0
+
+
+def test_batch_workload_sampled(orc):
+    """The packed workload at full size: three sequences against their own
+    launches bit for bit, sampled rows of three against the oracle."""
+    b = synth.config_batch("c6_varlen_16x128_2048")
+    say(f"batch workload {b.name} lens={b.lens}")
+    got = _batch_out(b)
+    off = _offsets(b.lens)
+    order = np.argsort(b.lens)
+    for i in [int(order[0]), int(order[len(order) // 2]), int(order[-1])]:
+        p = b.seqs[i]
+        assert np.array_equal(got[off[i]:off[i + 1]], gpu_out(p)), f"sequence {i}"
+        rows = sample_rows(p.rows, k=16, seed=i)
+        want = oracle_rows(orc, p, rows)
+        bad, frac = parity_report(got[off[i]:off[i + 1]][rows], want)
+        say(f"  seq {i} len {p.T}: rows={rows.size} bad={bad} worst bound fraction={frac:.3f}")
+        assert bad == 0
+    assert np.isfinite(bits_to_f32(got)).all()
+
+
+def test_batch_reuses_context_back_to_back():
+    """Two batches issued back to back on one context (the staging buffer is
+    reused) both give their sequences' bits."""
+    import gated_gqa_causal_amd as ga
+    b1 = synth.make_batch([64, 200], n_q_heads=8, n_kv_heads=2, seed=31)
+    b2 = synth.make_batch([130, 7, 96], n_q_heads=8, n_kv_heads=2, seed=32)
+    ctx = ga.Context(8, 2, 512, 1e-6)
+    o1 = _batch_call(ctx, b1, _batch_tensors(b1))
+    o2 = _batch_call(ctx, b2, _batch_tensors(b2))
+    torch.cuda.synchronize()
+    for b, o in ((b1, o1), (b2, o2)):
+        off = _offsets(b.lens)
+        got = to_bits(o)
+        for i, p in enumerate(b.seqs):
+            assert np.array_equal(got[off[i]:off[i + 1]], gpu_out(p))
+    ctx.close()

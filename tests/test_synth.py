@@ -58,3 +58,23 @@ def test_config_digest_stable(name):
     p = synth.config_problem(name)
     assert p.qg.shape == (64, 24, 2, 256) and p.k.shape == (64, 2, 256)
     assert p.digest() == synth.config_problem(name).digest()
+
+
+def test_batch_shares_weights_and_packs_rows():
+    b = synth.make_batch([0, 5, 33, 64], n_q_heads=4, n_kv_heads=2, seed=3)
+    assert b.lens == [0, 5, 33, 64] and b.total == 102
+    assert b.qg.shape == (102, 4, 2, 256) and b.k.shape == (102, 2, 256)
+    for p in b.seqs:
+        assert np.array_equal(p.q_norm_w, b.seqs[0].q_norm_w) and np.array_equal(p.k_norm_w, b.seqs[0].k_norm_w)
+        assert p.cos.shape == (64, 32) and np.array_equal(p.cos, b.seqs[0].cos)
+    # sequence i's rows sit at its offset
+    assert np.array_equal(b.qg[5:38], b.seqs[2].qg)
+    # a sequence's rows do not depend on its neighbours
+    b2 = synth.make_batch([7, 5, 33, 64], n_q_heads=4, n_kv_heads=2, seed=3)
+    assert np.array_equal(b2.seqs[2].qg, b.seqs[2].qg)
+
+
+def test_batch_lengths_are_seeded_and_in_range():
+    a = synth.batch_lens(64, 128, 2048, 6)
+    assert a == synth.batch_lens(64, 128, 2048, 6)
+    assert min(a) >= 128 and max(a) <= 2048 and len(set(a)) > 32
