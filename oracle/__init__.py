@@ -6,6 +6,9 @@ points of the reference model, every sum in ascending order) through ctypes
 and shares nothing with the HIP library except the seeded inputs from
 ``synth``.
 
+``oracle/fp8.py`` adds the fp8 (E4M3) K/V cache rows (per-row fp32 scale,
+widened to bf16) as plain numpy; its pins are in ``tests/test_fp8_pins.py``.
+
 Parity pins live in ``tests/test_oracle_pins.py``.  One part is unpinned
 (parity unpinned): absolute fidelity to the pages' own reference model, whose
 golden fixture is not available; the rotate-half pairing and the bf16 rounding
