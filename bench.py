@@ -99,6 +99,10 @@ def main():
     ap.add_argument("--cached", action="store_true",
                     help="prefix workloads: keys before q_base come from a prepared K/V cache "
                          "(attn_prefill_append); only the window's keys are prepared per step")
+    ap.add_argument("--fp8-cache", action="store_true",
+                    help="as --cached, with the fp8 (e4m3 rows, fp32 row scales) cache "
+                         "(attn_prefill_append_fp8): each step encodes the window's keys and "
+                         "widens the whole cache before the attention kernel")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -190,22 +194,24 @@ def main():
     stream = torch.cuda.current_stream()
 
     cache = None
-    if args.cached:
+    fp8 = bool(args.fp8_cache)
+    if args.cached or fp8:
         if not p.q_base or mask is not None or not p.causal:
-            raise SystemExit("--cached needs a prefix workload (q_base > 0, causal, unmasked)")
-        cache = ctx.kv_cache()
+            raise SystemExit("--cached / --fp8-cache need a prefix workload (q_base > 0, causal, unmasked)")
+        cache = ctx.kv_cache_fp8() if fp8 else ctx.kv_cache()
+        append = ctx.prefill_append_fp8 if fp8 else ctx.prefill_append
         qb = p.q_base
         # The prefix's keys, prepared once outside the timing (their query rows are
         # not part of this workload: a zero qg block stands in for them).
         zero_qg = torch.zeros((qb,) + tuple(qg.shape[1:]), dtype=torch.bfloat16, device=dev)
-        ctx.prefill_append(zero_qg, k[:qb], v[:qb], wq, wk, cos, sin, qb, 0, cache)
+        append(zero_qg, k[:qb], v[:qb], wq, wk, cos, sin, qb, 0, cache)
         k_new, v_new = k[qb:], v[qb:]
 
     def step():
         if batch is not None:
             ctx.prefill_gated_batch(qg, k, v, wq, wk, cos, sin, batch.lens, out=out, stream=stream)
         elif cache is not None:
-            ctx.prefill_append(qg, k_new, v_new, wq, wk, cos, sin, p.T, p.q_base, cache, out=out, stream=stream)
+            append(qg, k_new, v_new, wq, wk, cos, sin, p.T, p.q_base, cache, out=out, stream=stream)
         elif not p.causal:
             ctx.prefill_bidirectional(qg, k, v, wq, wk, cos, sin, out=out, stream=stream)
         elif mask is not None:
@@ -258,7 +264,8 @@ def main():
         "config": {"workload": args.workload, "tokens": batch.total if batch is not None else p.T,
                    "q_base": p.q_base, "n_q_heads": p.n_q_heads,
                    "n_kv_heads": p.n_kv_heads, "head_dim": p.head_dim, "rotary_dim": p.rotary_dim,
-                   "masked": p.mask is not None, "causal": p.causal, "cached_prefix": bool(args.cached),
+                   "masked": p.mask is not None, "causal": p.causal,
+                   "cached_prefix": bool(args.cached or args.fp8_cache), "fp8_cache": fp8,
                    "seed": synth.BATCH_CONFIGS[args.workload]["seed"] if batch is not None else p.seed,
                    "algorithmic_gflop": round(flops / 1e9, 3)},
         "kernels_ms": {"attention": round(attn_avg_ms, 5),

@@ -83,6 +83,9 @@ def _load():
         "attn_prefill_bidirectional": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, vp]),
         "attn_kv_cache_bytes": (ctypes.c_int, [ctypes.POINTER(attn_geometry), ctypes.POINTER(ctypes.c_size_t)]),
         "attn_prefill_append": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp, vp]),
+        "attn_kv_cache_fp8_bytes": (ctypes.c_int, [ctypes.POINTER(attn_geometry),
+                                                   ctypes.POINTER(ctypes.c_size_t)]),
+        "attn_prefill_append_fp8": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp, vp]),
         "attn_debug_prepare": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp, vp]),
         "attn_ctx_set_timing": (ctypes.c_int, [vp, ctypes.c_int]),
         "attn_ctx_read_timing": (ctypes.c_int, [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
@@ -160,6 +163,18 @@ def attn_kv_cache_bytes(geom: attn_geometry):
 def attn_prefill_append(ctx, inputs: attn_inputs, T: int, q_base: int, kv_cache: int, out: int,
                         stream: int) -> int:
     return lib.attn_prefill_append(ctx, ctypes.byref(inputs), T, q_base, kv_cache, out, stream)
+
+
+def attn_kv_cache_fp8_bytes(geom: attn_geometry):
+    """(status, bytes) of an fp8 K/V cache for the geometry."""
+    n = ctypes.c_size_t()
+    rc = lib.attn_kv_cache_fp8_bytes(ctypes.byref(geom), ctypes.byref(n))
+    return rc, n.value
+
+
+def attn_prefill_append_fp8(ctx, inputs: attn_inputs, T: int, q_base: int, kv_cache8: int, out: int,
+                            stream: int) -> int:
+    return lib.attn_prefill_append_fp8(ctx, ctypes.byref(inputs), T, q_base, kv_cache8, out, stream)
 
 
 def attn_debug_prepare(ctx, inputs: attn_inputs, T: int, q_base: int, qp_out, kp_out, stream) -> int:
@@ -315,6 +330,44 @@ class Context:
         if rc != ATTN_OK:
             raise AttnError(rc, "attn_kv_cache_bytes")
         return torch.zeros(n, dtype=torch.uint8, device=f"cuda:{self.device}")
+
+    def kv_cache_fp8(self):
+        """A zeroed device fp8 K/V cache for this context's geometry (uint8 tensor)."""
+        import torch
+        rc, n = attn_kv_cache_fp8_bytes(self.geom)
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_kv_cache_fp8_bytes")
+        return torch.zeros(n, dtype=torch.uint8, device=f"cuda:{self.device}")
+
+    def fp8_cache_views(self, kv_cache8):
+        """(key codes [Hkv][tpad][D], value codes, key scales [Hkv][tpad], value scales)
+        as views of an fp8 cache tensor."""
+        import torch
+        g = self.geom
+        tpad = (g.max_tokens + 63) // 64 * 64
+        rows = g.n_kv_heads * tpad
+        D = ATTN_HEAD_DIM
+        kc = kv_cache8[:rows * D].view(g.n_kv_heads, tpad, D)
+        vc = kv_cache8[rows * D:2 * rows * D].view(g.n_kv_heads, tpad, D)
+        sc = kv_cache8[2 * rows * D:].view(torch.float32)
+        return kc, vc, sc[:rows].view(g.n_kv_heads, tpad), sc[rows:].view(g.n_kv_heads, tpad)
+
+    def prefill_append_fp8(self, qg, k_new, v_new, q_norm_w, k_norm_w, cos, sin, T: int, q_base: int, kv_cache8,
+                           out=None, stream=None):
+        """As prefill_append, over an fp8 cache (e4m3 rows with fp32 row scales)."""
+        import torch
+        rows = T - q_base
+        inp = self.inputs(qg, k_new, v_new, q_norm_w, k_norm_w, cos, sin, rows, rows)
+        rc, n = attn_kv_cache_fp8_bytes(self.geom)
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_kv_cache_fp8_bytes")
+        self._check("kv_cache8", kv_cache8, torch.uint8, (n,))
+        out = self._out(out, rows)
+        rc = attn_prefill_append_fp8(self.handle, inp, T, q_base, kv_cache8.data_ptr(), out.data_ptr(),
+                                     self._stream(stream))
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_prefill_append_fp8")
+        return out
 
     def prefill_append(self, qg, k_new, v_new, q_norm_w, k_norm_w, cos, sin, T: int, q_base: int, kv_cache,
                        out=None, stream=None):

@@ -51,7 +51,8 @@ struct attn_ctx {
 
 namespace {
 
-constexpr int kKinds = 5;   // 0 gated, 1 prefix, 2 masked, 3 bidirectional, 4 append to a K/V cache
+constexpr int kKinds = 6;   // 0 gated, 1 prefix, 2 masked, 3 bidirectional, 4 append to a K/V cache,
+                            // 5 append to an fp8 K/V cache
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -120,6 +121,8 @@ void fill_kv_params(ga::KvPrologueParams &kp, const attn_ctx *ctx, const attn_in
     kp.eps = ctx->geom.rms_eps;
     kp.tile_seg = nullptr;
     kp.seg = nullptr;
+    kp.k8 = kp.v8 = nullptr;
+    kp.k8s = kp.v8s = nullptr;
 }
 
 // Bytes of a caller-owned K/V cache for a geometry: prepared keys and
@@ -128,6 +131,14 @@ size_t kv_cache_bytes(const attn_geometry &g)
 {
     const size_t tpad = ((size_t)g.max_tokens + 63) / 64 * 64;
     return 2 * (size_t)g.n_kv_heads * tpad * ATTN_HEAD_DIM * 2;
+}
+
+// Bytes of a caller-owned fp8 K/V cache: e4m3 key rows and value rows
+// [Hkv][tpad][256] each, then fp32 scales [Hkv][tpad] for keys and values.
+size_t kv_cache_fp8_bytes(const attn_geometry &g)
+{
+    const size_t tpad = ((size_t)g.max_tokens + 63) / 64 * 64;
+    return 2 * (size_t)g.n_kv_heads * tpad * ATTN_HEAD_DIM + 2 * (size_t)g.n_kv_heads * tpad * 4;
 }
 
 void fill_attn_params(ga::AttnParams &ap, const attn_ctx *ctx, const attn_inputs *in, int T, int q_base,
@@ -256,13 +267,38 @@ int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kin
     if (kind == 4) {
         kvp.kp = cache_k;
         kvp.vt = cache_v;
+    }
+    if (kind == 4 || kind == 5) {
         kvp.tile0 = q_base / ga::kKeysPerTile;
         kvp.k_row0 = q_base;
+    }
+    ga::KvWidenParams wp{};
+    if (kind == 5) {
+        // fp8 rows of the new keys into the cache, then every row 0..T-1
+        // widened into the workspace's tiles for the attention kernel.
+        const size_t rows = (size_t)ctx->geom.n_kv_heads * ctx->tpad;
+        uint8_t *c8 = const_cast<uint8_t *>(mask);
+        kvp.k8 = c8;
+        kvp.v8 = c8 + rows * ATTN_HEAD_DIM;
+        kvp.k8s = reinterpret_cast<float *>(c8 + 2 * rows * ATTN_HEAD_DIM);
+        kvp.v8s = kvp.k8s + rows;
+        wp.k8 = kvp.k8;
+        wp.v8 = kvp.v8;
+        wp.k8s = kvp.k8s;
+        wp.v8s = kvp.v8s;
+        wp.kp = ctx->kp;
+        wp.vt = ctx->vt;
+        wp.T = T;
+        wp.Tpad = ctx->tpad;
     }
     {
         Timer tm(ctx, s, ATTN_KERNEL_KV_PROLOGUE);
         const int tiles = (T + ga::kKeysPerTile - 1) / ga::kKeysPerTile - kvp.tile0;
-        if (ga::launch_kv_prologue(kvp, tiles, s) != hipSuccess)
+        if ((kind == 5 ? ga::launch_kv_prologue_fp8(kvp, tiles, s) : ga::launch_kv_prologue(kvp, tiles, s)) !=
+            hipSuccess)
+            return ATTN_ERR_LAUNCH;
+        if (kind == 5 && ga::launch_kv_widen(wp, (T + ga::kKeysPerTile - 1) / ga::kKeysPerTile,
+                                             ctx->geom.n_kv_heads, s) != hipSuccess)
             return ATTN_ERR_LAUNCH;
         tm.stop();
     }
@@ -329,7 +365,7 @@ int attn_validate(const attn_geometry *geom, const attn_inputs *in, int32_t T, i
         return ATTN_ERR_RANGE;
     if (q_base < 0 || q_base > T)
         return ATTN_ERR_RANGE;
-    if (kind != 1 && kind != 4 && q_base != 0)
+    if (kind != 1 && kind != 4 && kind != 5 && q_base != 0)
         return ATTN_ERR_RANGE;
     if (q_base % ATTN_QBASE_ALIGN != 0)
         return ATTN_ERR_ALIGN;
@@ -339,14 +375,14 @@ int attn_validate(const attn_geometry *geom, const attn_inputs *in, int32_t T, i
         return ATTN_ERR_NULL_ARG;
     if (!in->qg || !in->k || !in->v || !in->q_norm_w || !in->k_norm_w || !in->cos_tab || !in->sin_tab)
         return ATTN_ERR_NULL_ARG;
-    if ((kind == 2 || kind == 4) && !mask)
+    if ((kind == 2 || kind == 4 || kind == 5) && !mask)
         return ATTN_ERR_NULL_ARG;
     if (in->n_pos < T)
         return ATTN_ERR_RANGE;
     if (!aligned16(in->qg) || !aligned16(in->k) || !aligned16(in->v) || !aligned16(in->q_norm_w) ||
         !aligned16(in->k_norm_w) || !aligned16(in->cos_tab) || !aligned16(in->sin_tab) || !aligned16(out))
         return ATTN_ERR_ALIGN;
-    if (kind == 4 && !aligned16(mask))
+    if ((kind == 4 || kind == 5) && !aligned16(mask))
         return ATTN_ERR_ALIGN;
     return ATTN_OK;
 }
@@ -455,6 +491,24 @@ int attn_prefill_append(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t
                         void *out, void *stream)
 {
     return run(ctx, in, T, q_base, 4, static_cast<const uint8_t *>(kv_cache), out, stream);
+}
+
+int attn_kv_cache_fp8_bytes(const attn_geometry *geom, size_t *bytes)
+{
+    if (!bytes)
+        return ATTN_ERR_NULL_ARG;
+    *bytes = 0;
+    const int rc = check_geometry(geom);
+    if (rc != ATTN_OK)
+        return rc;
+    *bytes = kv_cache_fp8_bytes(*geom);
+    return ATTN_OK;
+}
+
+int attn_prefill_append_fp8(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, void *kv_cache8,
+                            void *out, void *stream)
+{
+    return run(ctx, in, T, q_base, 5, static_cast<const uint8_t *>(kv_cache8), out, stream);
 }
 
 int attn_prefill_bidirectional(attn_ctx *ctx, const attn_inputs *in, int32_t S, void *out, void *stream)

@@ -23,6 +23,17 @@ struct KvPrologueParams {
     // seg[4 s ..] = {length, first row in k/v, first prepared tile, 0}.
     const int *tile_seg;
     const int *seg;
+    // fp8 cache rows (kv_prologue<true> only): codes [Hkv][Tpad][256] and one
+    // fp32 scale per row [Hkv][Tpad], keys then values; rows = positions.
+    uint8_t *k8, *v8;
+    float *k8s, *v8s;
+};
+struct KvWidenParams {
+    const uint8_t *k8, *v8;   // fp8 cache rows [Hkv][Tpad][256]
+    const float *k8s, *v8s;   // their scales [Hkv][Tpad]
+    uint16_t *kp;             // [Hkv][Tpad/32] tiles of 32 keys, chunk-major
+    uint16_t *vt;             // [Hkv][Tpad/32] tiles of V^T, chunk-major
+    int T, Tpad;              // rows 0..T-1 are widened; tiles past them get zeros
 };
 
 struct MaskPackParams {
@@ -59,6 +70,8 @@ constexpr int kKeysPerTile = 32;
 constexpr int kHeadsPerBlock = 4;
 
 hipError_t launch_kv_prologue(const KvPrologueParams &p, int ntiles, hipStream_t stream);
+hipError_t launch_kv_prologue_fp8(const KvPrologueParams &p, int ntiles, hipStream_t stream);
+hipError_t launch_kv_widen(const KvWidenParams &p, int ntiles, int Hkv, hipStream_t stream);
 hipError_t launch_mask_pack(const MaskPackParams &p, int nrb, hipStream_t stream);
 enum class AttnMode { Causal, Masked, Bidirectional };
 hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stream);

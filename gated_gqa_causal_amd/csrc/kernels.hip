@@ -96,6 +96,74 @@ __device__ __forceinline__ int vt_key_of_pos(int pos)
     return (pos & ~15) | k16;
 }
 
+// Stores one tile: 32 prepared keys (ks) and 32 values (vs), bf16 rows, into
+// the chunk-major Kp and Vt layouts at element offset tile_off.
+__device__ __forceinline__ void write_kv_tile(const uint16_t (&ks)[KT][D + 8], const uint16_t (&vs)[KT][D + 8],
+                                              uint16_t *kp, uint16_t *vt, size_t tile_off, int tid)
+{
+    uint4 *kdst = reinterpret_cast<uint4 *>(kp + tile_off);
+    for (int it = 0; it < 4; ++it) {
+        const int piece = it * 256 + tid, ch = piece >> 5, r = piece & 31;
+        kdst[piece] = *reinterpret_cast<const uint4 *>(&ks[r][ch * 8]);
+    }
+    uint4 *vdst = reinterpret_cast<uint4 *>(vt + tile_off);
+    for (int q = 0; q < 4; ++q) {
+        const int d = tid;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t a = vs[vt_key_of_pos(8 * q + 2 * e)][d];
+            const uint32_t b = vs[vt_key_of_pos(8 * q + 2 * e + 1)][d];
+            w[e] = a | (b << 16);
+        }
+        vdst[q * 256 + d] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp8 cache rows (the long-prompt prefill page, Kernels list: e4m3 cache rows
+// with an fp32 scale each, widened to bf16).  E4M3 as the OCP 8-bit floating
+// point format defines it: sign, 4 exponent bits (bias 7), 3 mantissa bits,
+// subnormals at exponent 0, no infinities, S.1111.111 NaN, 448 the largest
+// finite magnitude.  A row's scale is amax / 448 (1 for a zero row); a value
+// is encoded from x / scale to the nearest code, ties to the even mantissa,
+// magnitudes past 448 saturated; it is widened as bf16(value(code) * scale).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t enc_e4m3(float x)
+{
+    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+    const float a = fabsf(x);
+    if (!(a == a))
+        return 0x7Fu;                                    // NaN
+    if (a >= 448.0f)
+        return sign | 0x7Eu;                             // saturate
+    if (a < 0.015625f) {                                 // below 2^-6: multiples of 2^-9
+        const uint32_t m = (uint32_t)__builtin_rintf(a * 512.0f);   // exact scaling, ties to even
+        return sign | m;                                 // m == 8 is the smallest normal, 0x08
+    }
+    const uint32_t ua = __float_as_uint(a);
+    uint32_t e = (ua >> 23) - 127u + 7u;                 // 1 .. 15
+    uint32_t keep = (ua >> 20) & 7u;
+    const uint32_t rest = ua & 0xFFFFFu;
+    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u)))
+        ++keep;
+    if (keep == 8u) {
+        keep = 0u;
+        ++e;
+    }
+    return sign | (e << 3) | keep;                       // a < 448 never reaches the NaN code
+}
+
+__device__ __forceinline__ float dec_e4m3(uint32_t c)
+{
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    float mag = (e == 0u) ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    if ((c & 0x7Fu) == 0x7Fu)
+        mag = __builtin_nanf("");
+    return (c & 0x80u) ? -mag : mag;
+}
+
+template <bool FP8>
 __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
 {
     __shared__ __align__(16) uint16_t ks[KT][D + 8];
@@ -163,25 +231,82 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
     }
     __syncthreads();
 
-    const size_t tile_off = ((size_t)c * (p.Tpad / KT) + tile) * (size_t)(KT * D);
-    uint4 *kdst = reinterpret_cast<uint4 *>(p.kp + tile_off);
-    for (int it = 0; it < 4; ++it) {
-        const int piece = it * 256 + tid, ch = piece >> 5, r = piece & 31;
-        kdst[piece] = *reinterpret_cast<const uint4 *>(&ks[r][ch * 8]);
+    if (!FP8) {
+        write_kv_tile(ks, vs, p.kp, p.vt, ((size_t)c * (p.Tpad / KT) + tile) * (size_t)(KT * D), tid);
+        return;
     }
-
-    uint4 *vdst = reinterpret_cast<uint4 *>(p.vt + tile_off);
-    for (int q = 0; q < 4; ++q) {
-        const int d = tid;
-        uint32_t w[4];
+    // fp8 cache rows.  Row scales: thread (key r, sub) takes the largest
+    // magnitude of its 32 dims; three xor shuffles inside the key's 8 lanes
+    // give the row's.
+    __shared__ float sk[KT], sv[KT];
+    {
+        const int r = tid >> 3, sub = tid & 7;
+        float ak = 0.0f, av = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t a = vs[vt_key_of_pos(8 * q + 2 * e)][d];
-            const uint32_t b = vs[vt_key_of_pos(8 * q + 2 * e + 1)][d];
-            w[e] = a | (b << 16);
+        for (int s = 0; s < 32; ++s) {
+            ak = fmaxf(ak, fabsf(bf2f(ks[r][sub + 8 * s])));
+            av = fmaxf(av, fabsf(bf2f(vs[r][sub + 8 * s])));
         }
-        vdst[q * 256 + d] = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+            ak = fmaxf(ak, __shfl_xor(ak, o));
+            av = fmaxf(av, __shfl_xor(av, o));
+        }
+        if (sub == 0) {
+            sk[r] = (ak > 0.0f) ? ak / 448.0f : 1.0f;
+            sv[r] = (av > 0.0f) ? av / 448.0f : 1.0f;
+        }
     }
+    __syncthreads();
+    // Codes: 32 key rows and 32 value rows of 256 bytes, 16 bytes per step.
+    for (int it = 0; it < 4; ++it) {
+        const int idx = it * 256 + tid, isv = idx >> 9, r = (idx >> 4) & 31, ch = idx & 15;
+        const int key = t0 + r;
+        if (key < T) {
+            const uint16_t *src = isv ? &vs[r][16 * ch] : &ks[r][16 * ch];
+            const float sc = isv ? sv[r] : sk[r];
+            uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                w[e >> 2] |= enc_e4m3(bf2f(src[e]) / sc) << (8 * (e & 3));
+            uint8_t *dst = (isv ? p.v8 : p.k8) + ((size_t)c * p.Tpad + key) * D + 16 * ch;
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+    if (tid < 2 * KT) {
+        const int r = tid & 31, key = t0 + r;
+        if (key < T)
+            ((tid < KT) ? p.k8s : p.v8s)[(size_t)c * p.Tpad + key] = (tid < KT) ? sk[r] : sv[r];
+    }
+}
+
+// Widens fp8 cache rows 0..T-1 into the Kp / Vt tiles.  grid (tiles, Hkv).
+__global__ __launch_bounds__(256) void kv_widen(KvWidenParams p)
+{
+    __shared__ __align__(16) uint16_t ks[KT][D + 8];
+    __shared__ __align__(16) uint16_t vs[KT][D + 8];
+    const int tile = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, t0 = tile * KT;
+    for (int it = 0; it < 4; ++it) {
+        const int idx = it * 256 + tid, isv = idx >> 9, r = (idx >> 4) & 31, ch = idx & 15;
+        const int key = t0 + r;
+        uint32_t o[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        if (key < p.T) {
+            const size_t row = (size_t)c * p.Tpad + key;
+            const uint4 cw = *reinterpret_cast<const uint4 *>((isv ? p.v8 : p.k8) + row * D + 16 * ch);
+            const float sc = (isv ? p.v8s : p.k8s)[row];
+            const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t code = (words[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+                o[e >> 1] |= (uint32_t)f2bf(dec_e4m3(code) * sc) << (16 * (e & 1));
+            }
+        }
+        uint16_t *dst = isv ? &vs[r][16 * ch] : &ks[r][16 * ch];
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4 *>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+    __syncthreads();
+    write_kv_tile(ks, vs, p.kp, p.vt, ((size_t)c * (p.Tpad / KT) + tile) * (size_t)(KT * D), tid);
 }
 
 // Debug: prepared keys from the tiled layout back to plain [Hkv][T][D].
@@ -1667,7 +1792,19 @@ __global__ __launch_bounds__(256) void mfma_clock_probe(int iters, long long *re
 // ---------------------------------------------------------------------------
 hipError_t launch_kv_prologue(const KvPrologueParams &p, int ntiles, hipStream_t stream)
 {
-    hipLaunchKernelGGL(kv_prologue, dim3(ntiles, p.Hkv), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(kv_prologue<false>, dim3(ntiles, p.Hkv), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_prologue_fp8(const KvPrologueParams &p, int ntiles, hipStream_t stream)
+{
+    hipLaunchKernelGGL(kv_prologue<true>, dim3(ntiles, p.Hkv), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_widen(const KvWidenParams &p, int ntiles, int Hkv, hipStream_t stream)
+{
+    hipLaunchKernelGGL(kv_widen, dim3(ntiles, Hkv), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -111,7 +111,8 @@ ATTN_EXPORT const char *attn_status_string(int status);
  * kind: 0 = gated full pass (q_base must be 0), 1 = prefix window,
  * 2 = masked (q_base must be 0, mask required), 3 = bidirectional full pass
  * (q_base must be 0), 4 = append to a K/V cache (`mask` is then the cache
- * pointer: required, 16-byte aligned; k and v hold the T - q_base new rows).
+ * pointer: required, 16-byte aligned; k and v hold the T - q_base new rows),
+ * 5 = append to an fp8 K/V cache (as 4, with the fp8 cache).
  * T keys, query rows T - q_base.  Touches no device; usable without a GPU.
  */
 ATTN_EXPORT int attn_validate(const attn_geometry *geom, const attn_inputs *in, int32_t T, int32_t q_base,
@@ -187,6 +188,29 @@ ATTN_EXPORT int attn_prefill_bidirectional(attn_ctx *ctx, const attn_inputs *in,
 ATTN_EXPORT int attn_kv_cache_bytes(const attn_geometry *geom, size_t *bytes);
 ATTN_EXPORT int attn_prefill_append(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base,
                                     void *kv_cache, void *out, void *stream);
+
+/*
+ * fp8 K/V cache (the long-prompt prefill page, Kernels list: e4m3 cache rows
+ * with an fp32 scale each, widened to bf16 for the attention products).
+ * Layout of the caller-owned buffer (attn_kv_cache_fp8_bytes bytes, 16-byte
+ * aligned), with tpad = max_tokens rounded up to 64 and rows = positions:
+ *   uint8 key rows   [Hkv][tpad][256]   prepared (normed, rotated) keys, e4m3
+ *   uint8 value rows [Hkv][tpad][256]   raw values, e4m3
+ *   fp32 key scales  [Hkv][tpad]        one per key row
+ *   fp32 value scales[Hkv][tpad]        one per value row
+ * E4M3 is the OCP 8-bit floating point format (bias 7, no infinities, 448
+ * the largest finite magnitude).  A row's scale is amax / 448 (1 for an all
+ * zero row); each value is encoded from value / scale to the nearest code,
+ * ties to the even mantissa, magnitudes past 448 saturated; the attention
+ * uses bf16(code value * scale).  attn_prefill_append_fp8 works as
+ * attn_prefill_append (same arguments, alignment and limits): it encodes the
+ * rows of positions q_base..T-1 into the cache, widens rows 0..T-1 into the
+ * context's workspace, and runs the window's rows over keys 0..T-1.  Chunked
+ * appends give the single call's output bit for bit.
+ */
+ATTN_EXPORT int attn_kv_cache_fp8_bytes(const attn_geometry *geom, size_t *bytes);
+ATTN_EXPORT int attn_prefill_append_fp8(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base,
+                                        void *kv_cache8, void *out, void *stream);
 
 /*
  * Packed batch of independent sequences in one launch (the serving page's

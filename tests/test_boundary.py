@@ -82,7 +82,10 @@ REFUSALS = [
     ({}, 200, 256, 1, None, FAKE, {}, "RANGE"),                    # q_base > T
     ({}, 200, 64, 1, None, FAKE, {}, "ALIGN"),                     # q_base % 128
     ({}, 200, 128, 0, None, FAKE, {}, "RANGE"),                    # q_base on the full pass
-    ({}, 200, 0, 5, None, FAKE, {}, "RANGE"),                      # bad kind
+    ({}, 200, 0, 6, None, FAKE, {}, "RANGE"),                      # bad kind
+    ({}, 200, 128, 5, None, FAKE, dict(n_pos=256), "NULL_ARG"),    # fp8 append without a cache
+    ({}, 200, 128, 5, FAKE + 4, FAKE, dict(n_pos=256), "ALIGN"),   # misaligned fp8 cache
+    ({}, 200, 64, 5, FAKE, FAKE, dict(n_pos=256), "ALIGN"),        # fp8 append q_base % 128
     ({}, 200, 0, -1, None, FAKE, {}, "RANGE"),                     # negative kind
     ({}, 200, -128, 1, None, FAKE, {}, "RANGE"),                   # negative q_base
     ({}, 200, 128, 3, None, FAKE, {}, "RANGE"),                    # q_base on the bidirectional pass
@@ -122,7 +125,7 @@ def test_null_geometry(ga):
 
 
 @pytest.mark.parametrize("T,qb,kind", [(0, 0, 0), (0, 0, 2), (256, 256, 1), (128, 128, 1), (0, 0, 3),
-                                       (128, 128, 4)])
+                                       (128, 128, 4), (256, 256, 5)])
 def test_empty_launch_is_ok_without_pointers(ga, T, qb, kind):
     # Zero query rows: a no-op, even with every pointer NULL (torch gives 0 for empty tensors).
     assert ga.attn_validate(_geom(ga), None, T, qb, kind, None, None) == ga.ATTN_OK
@@ -135,6 +138,7 @@ def test_valid_calls_pass(ga):
     assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 0, 3, None, FAKE) == ga.ATTN_OK
     assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 128, 4, FAKE, FAKE) == ga.ATTN_OK
     assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 0, 4, FAKE, FAKE) == ga.ATTN_OK
+    assert ga.attn_validate(_geom(ga), _inputs(ga, 256), 256, 128, 5, FAKE, FAKE) == ga.ATTN_OK
     for G in [1, 2, 3, 12, 16]:
         assert ga.attn_validate(_geom(ga, n_q_heads=2 * G), _inputs(ga), 64, 0, 0, None, FAKE) == 0
 
@@ -227,3 +231,12 @@ def test_batch_valid_and_empty(ga):
     # 8 sequences of 32 fill the 256-key workspace exactly
     assert ga.attn_validate_batch(g, _inputs(ga, n_pos=32), [32] * 8, FAKE) == ga.ATTN_OK
     assert ga.attn_validate_batch(g, _inputs(ga, n_pos=33), [32] * 7 + [1, 1], FAKE) == ga.ATTN_ERR_RANGE
+
+
+def test_kv_cache_fp8_bytes(ga):
+    g = _geom(ga, n_q_heads=24, n_kv_heads=2, max_tokens=200)     # tpad 256
+    rc, n = ga.attn_kv_cache_fp8_bytes(g)
+    assert rc == ga.ATTN_OK and n == 2 * 2 * 256 * 256 + 2 * 2 * 256 * 4
+    rc, n = ga.attn_kv_cache_fp8_bytes(_geom(ga, n_q_heads=24, n_kv_heads=5))
+    assert rc == ga.ATTN_ERR_GEOMETRY and n == 0
+    assert ga.lib.attn_kv_cache_fp8_bytes(ctypes.byref(g), None) == ga.ATTN_ERR_NULL_ARG

@@ -457,3 +457,84 @@ def test_batch_reuses_context_back_to_back():
         for i, p in enumerate(b.seqs):
             assert np.array_equal(got[off[i]:off[i + 1]], gpu_out(p))
     ctx.close()
+
+
+# --------------------------------------------------------------------------
+# fp8 (e4m3) K/V cache rows
+# --------------------------------------------------------------------------
+
+def _fp8_run(p, chunks, ctx=None):
+    """Appends p's keys (p.q_base == 0: qg holds every row) in chunks ending at
+    the listed positions to a fresh fp8 cache; returns (each chunk's output
+    rows, the cache tensor, the context)."""
+    import gated_gqa_causal_amd as ga
+    dp = DevProblem(p)
+    ctx = ctx or ga.Context(p.n_q_heads, p.n_kv_heads, p.T, p.rms_eps)
+    cache = ctx.kv_cache_fp8()
+    outs = []
+    for a, b in zip([0] + chunks[:-1], chunks):
+        outs.append(ctx.prefill_append_fp8(dp.qg[a:b], dp.k[a:b], dp.v[a:b], dp.wq, dp.wk, dp.cos, dp.sin,
+                                           b, a, cache))
+    torch.cuda.synchronize()
+    return outs, cache, ctx
+
+
+def _fp8_outputs(p, chunks):
+    """Stacked outputs of the chunks (query rows 0..T-1; p.q_base must be 0)."""
+    outs, cache, ctx = _fp8_run(p, chunks)
+    got = to_bits(torch.cat(outs))
+    return got, cache, ctx
+
+
+@pytest.mark.parametrize("T,Hq,Hkv", [(300, 24, 2), (129, 16, 4)])
+def test_fp8_cache_rows_bit_exact(orc, T, Hq, Hkv):
+    """The cache the GPU writes holds exactly the oracle's e4m3 codes and scales."""
+    from oracle import fp8
+    say(f"fp8 cache rows T={T} {Hq}/{Hkv}")
+    p = synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=T + 1)
+    _, cache, ctx = _fp8_outputs(p, [T])
+    kc, vc, ks, vs = ctx.fp8_cache_views(cache)
+    want = fp8.fp8_cache_kv(orc, p)
+    assert np.array_equal(kc[:, :T].cpu().numpy(), want["k_codes"]), "key codes"
+    assert np.array_equal(vc[:, :T].cpu().numpy(), want["v_codes"]), "value codes"
+    assert np.array_equal(ks[:, :T].cpu().numpy().view(np.uint32), want["k_scales"].view(np.uint32)), "key scales"
+    assert np.array_equal(vs[:, :T].cpu().numpy().view(np.uint32), want["v_scales"].view(np.uint32)), "value scales"
+    ctx.close()
+
+
+def test_fp8_append_vs_oracle(orc):
+    from oracle import fp8
+    p = synth.make_problem(T=333, n_q_heads=24, n_kv_heads=2, seed=41, gate_sigma=2.0)
+    got, _, ctx = _fp8_outputs(p, [128, 333])
+    want = fp8.attention_fp8(orc, p, threads=8)
+    bad, frac = parity_report(got, want)
+    say(f"  fp8 append: bad={bad} worst bound fraction={frac:.3f}")
+    assert bad == 0
+    ctx.close()
+
+
+@pytest.mark.parametrize("T,chunks,Hq,Hkv", [(700, [128, 384, 700], 24, 2), (2048, [1024, 1152, 2048], 16, 4)])
+def test_fp8_chunks_equal_single_append(T, chunks, Hq, Hkv):
+    p = synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=T + 3)
+    one, _, c1 = _fp8_outputs(p, [T])
+    many, _, c2 = _fp8_outputs(p, chunks)
+    assert np.array_equal(one, many)
+    c1.close()
+    c2.close()
+
+
+def test_fp8_prefix_workload_sampled(orc):
+    """c3's shape over an fp8 cache: keys 0..1023 appended first, then the
+    window 1024..8191; sampled window rows against the oracle."""
+    from oracle import fp8
+    p = synth.config_problem("c3_prefix_t8192_qb1024")
+    full = synth.make_problem(T=p.T, n_q_heads=p.n_q_heads, n_kv_heads=p.n_kv_heads, seed=p.seed)
+    say("fp8 c3 window")
+    outs, _, ctx = _fp8_run(full, [p.q_base, p.T])
+    got = to_bits(outs[1])
+    rows = sample_rows(p.rows, k=16, seed=3)
+    want = fp8.attention_fp8(orc, full, rows=rows + p.q_base, threads=8)
+    bad, frac = parity_report(got[rows], want)
+    say(f"  rows={rows.size} bad={bad} worst bound fraction={frac:.3f}")
+    assert bad == 0
+    ctx.close()
