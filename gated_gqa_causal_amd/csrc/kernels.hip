@@ -1,6 +1,6 @@
 // kernels.hip -- gfx950 (CDNA4) kernels for gated GQA causal attention prefill.
 //
-// Three kernels run on the caller's stream:
+// The kernels of a call run on the caller's stream:
 //   kv_prologue  : (1+w) RMSNorm + partial RoPE of every key once per KV head
 //                  (the QSA kernel page, "What changed": all query heads of a
 //                  KV head read the same prepared key), and V transposed into
@@ -8,8 +8,9 @@
 //   mask_pack    : masked path only.  uint8 [S][S] visibility -> one bit per
 //                  (row, key) with causality folded in, plus a per (64-row
 //                  block, 32-key tile) flag used to skip fully hidden tiles.
-//   attn_fwd     : one workgroup = 4 waves = 64 query rows x up to 4 query
-//                  heads of one KV head.  Each wave owns 64 rows of one head:
+//   kv_widen     : fp8 cache only.  e4m3 key / value rows -> the bf16 tiles.
+//   attn_fwd8    : one workgroup = 8 waves = 64 query rows x up to 4 query
+//                  heads of one KV head.  Each wave owns 32 rows of one head:
 //                  it norms and rotates its own queries, walks the key tiles
 //                  0..diagonal in ascending order (online softmax, the
 //                  attention-tile page's "Kernel change" recurrence), and
@@ -369,126 +370,6 @@ __global__ __launch_bounds__(256) void mask_pack(MaskPackParams p)
     p.tilevis[(size_t)rb * p.W + w] = any ? 1 : 0;
 }
 
-// ---------------------------------------------------------------------------
-// Query prologue of one wave for two blocks of 32 rows (block b = rows
-// r0 + 32b ..): loads the q half of the rows of head h, applies (1+w)
-// RMSNorm (sum of squares in ascending dimension order, the same chain as the
-// key prologue) and partial RoPE, and leaves the MFMA B-operand fragments in
-// qf[b][c]: lane (j = lane & 31, hh = lane >> 5) holds dims 16c + 8hh .. +7 of
-// row r0 + 32b + j.  Rows at or past S are zero.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void load_queries(const AttnParams &p, int r0, int h, int lane, uint4 (&qf)[2][16])
-{
-    constexpr int NB = 2;
-    const int j = lane & 31, hh = lane >> 5;
-    bool ok[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const int row = r0 + 32 * b + j;
-        ok[b] = row < p.S;
-        const uint16_t *src = p.qg + (((size_t)(ok[b] ? row : 0) * p.Hq + h) * 2) * D;
-#pragma unroll
-        for (int c = 0; c < 16; ++c)
-            qf[b][c] = *reinterpret_cast<const uint4 *>(src + 16 * c + 8 * hh);
-    }
-    // Sum of squares of each row in ascending dimension order.  v_permlane32_swap
-    // exchanges the upper half-wave of its first operand with the lower
-    // half-wave of its second, so swapping block 0's word with block 1's gives
-    // the lower half-wave both halves of block 0's row and the upper half-wave
-    // both halves of block 1's: each lane runs one chain, and a final swap
-    // shares the two sums.
-    float ss = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        uint32_t a[4], bq[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t w0 = q == 0 ? qf[0][c].x : q == 1 ? qf[0][c].y : q == 2 ? qf[0][c].z : qf[0][c].w;
-            const uint32_t w1 = q == 0 ? qf[1][c].x : q == 1 ? qf[1][c].y : q == 2 ? qf[1][c].z : qf[1][c].w;
-            const auto r = __builtin_amdgcn_permlane32_swap(w0, w1, false, false);
-            a[q] = r[0];
-            bq[q] = r[1];
-        }
-        const uint4 first = make_uint4(a[0], a[1], a[2], a[3]);      // dims 16c .. 16c+7
-        const uint4 second = make_uint4(bq[0], bq[1], bq[2], bq[3]); // dims 16c+8 .. 16c+15
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float x = word_f(first, t);
-            ss += x * x;
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float x = word_f(second, t);
-            ss += x * x;
-        }
-    }
-    float rr[NB];
-    {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
-        rr[0] = 1.0f / sqrtf(__uint_as_float(r[0]) / (float)D + p.eps); // block 0 (lower half-wave's sums)
-        rr[1] = 1.0f / sqrtf(__uint_as_float(r[1]) / (float)D + p.eps); // block 1 (upper half-wave's sums)
-    }
-    // Dims 64..255 (chunks 4..15) are only normalised; (1 + w) is shared by
-    // the blocks, and the bf16 pack is the norm's one rounding.
-#pragma unroll
-    for (int c = 4; c < 16; ++c) {
-        const uint4 wv = *reinterpret_cast<const uint4 *>(p.wq + 16 * c + 8 * hh);
-        float w1p[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            w1p[t] = 1.0f + word_f(wv, t);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            float n[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                n[t] = (word_f(qf[b][c], t) * rr[b]) * w1p[t];
-            qf[b][c] = make_uint4(pack2(n[0], n[1]), pack2(n[2], n[3]), pack2(n[4], n[5]), pack2(n[6], n[7]));
-        }
-    }
-    // Dims 0..63 (chunks 0..3) hold the rotary pairs (d, d+32) = chunks (c, c+2).
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        float n[4][8];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint4 wv = *reinterpret_cast<const uint4 *>(p.wq + 16 * c + 8 * hh);
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                n[c][t] = rbf((word_f(qf[b][c], t) * rr[b]) * (1.0f + word_f(wv, t)));
-        }
-        const int row = r0 + 32 * b + j;
-        const int pos = p.q_base + (ok[b] ? row : 0);
-        const float *ct = p.cos_tab + (size_t)pos * HALF_R;
-        const float *st = p.sin_tab + (size_t)pos * HALF_R;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const float4 c0 = *reinterpret_cast<const float4 *>(ct + 16 * c + 8 * hh);
-            const float4 c1 = *reinterpret_cast<const float4 *>(ct + 16 * c + 8 * hh + 4);
-            const float4 s0 = *reinterpret_cast<const float4 *>(st + 16 * c + 8 * hh);
-            const float4 s1 = *reinterpret_cast<const float4 *>(st + 16 * c + 8 * hh + 4);
-            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float cj = rbf(cv[t]), sj = rbf(sv[t]);
-                const float av = n[c][t], bv = n[c + 2][t];
-                n[c][t] = rbf(rbf(av * cj) + rbf(-bv * sj));
-                n[c + 2][t] = rbf(rbf(bv * cj) + rbf(av * sj));
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            qf[b][c] = make_uint4(pack2(n[c][0], n[c][1]), pack2(n[c][2], n[c][3]),
-                                  pack2(n[c][4], n[c][5]), pack2(n[c][6], n[c][7]));
-        if (!ok[b]) {
-#pragma unroll
-            for (int c = 0; c < 16; ++c)
-                qf[b][c] = make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
-}
-
 __device__ __forceinline__ void load_queries1(const AttnParams &p, int r0, int h, int lane, uint4 (&qf)[16]);
 
 // Debug: prepared queries in a plain [rows][Hq][D] layout.
@@ -501,10 +382,8 @@ __global__ __launch_bounds__(256) void q_prologue_debug(AttnParams p, uint16_t *
         return;
     const int r0 = blockIdx.x * 64;
     uint4 qf[2][16];
-    load_queries(p, r0, h, lane, qf);
-    // The first 32 rows come from the one-block prologue, the next 32 from
-    // block 1 of the two-block one: both are checked.
     load_queries1(p, r0, h, lane, qf[0]);
+    load_queries1(p, r0 + 32, h, lane, qf[1]);
     const int j = lane & 31, hh = lane >> 5;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -518,15 +397,12 @@ __global__ __launch_bounds__(256) void q_prologue_debug(AttnParams p, uint16_t *
 }
 
 // ---------------------------------------------------------------------------
-// Attention.  Workgroup = 8 waves = 64 query rows x 4 query heads of one KV
-// head; wave w owns head (w & 3) and rows r0 + 32 * (w >> 2) .. +31.
+// Attention helpers.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int AW = 4;                    // waves per attention workgroup (one per SIMD)
-constexpr int ATHREADS = 64 * AW;
-constexpr int QB = 32;                   // query rows per MFMA block; a wave owns two
+constexpr int QB = 32;                   // query rows per MFMA block (one per wave)
 constexpr int MAX_TILES = 32768 / KT;    // tile list capacity (token cap / 32)
 constexpr int TILE_BYTES = KT * D * 2;   // one K or V^T tile: 16 KB
 constexpr int EP_STRIDE = 2 * D + 16;    // epilogue staging: bytes per row
@@ -592,9 +468,9 @@ __device__ __forceinline__ FragOffsets frag_offsets(int j, int hh)
 }
 
 // ---------------------------------------------------------------------------
-// Context accumulators.  O^T of a wave's two 32-row blocks is 2 x 8 groups of
-// (32 dims x 32 queries) fp32 = exactly the 256 AGPRs; the VGPRs hold the
-// queries, scores and weights.  The context MFMAs are inline asm with AGPR
+// Context accumulators.  O^T of a wave's 32-row block is 8 groups of (32 dims
+// x 32 queries) fp32 = the wave's 128 AGPRs; the VGPRs hold the queries,
+// scores and weights.  The context MFMAs are inline asm with AGPR
 // accumulators.  The compiler does not track their latency, so the software
 // wait states the ISA requires around them are inserted here: VALU access to
 // an accumulator waits (up to 19 states) for the last MFMA on it, and each
@@ -622,10 +498,9 @@ __device__ __forceinline__ void acc_wait(f32x16 (&o)[8])
 
 
 // ---------------------------------------------------------------------------
-// Online softmax of one block's tile as a program of 32 steps, one per MFMA
-// slot.  A wave issues about four VALU instructions in the shadow of each
-// 32-cycle MFMA of its own; a step holds about that many, none depending on
-// another of the same step, so the matrix pipe does not wait on them.
+// Online softmax of one block's tile as a program of 32 steps placed between
+// MFMAs.  A step holds a few VALU instructions, none depending on another of
+// the same step, so the matrix pipe does not wait on them.
 //   lane (j, hh) holds query j and keys 8g + 4hh + r of the tile (e = 4g + r).
 //   steps 0..7  : tile max (a tree of max3 on the fp32 scores, then the
 //                 partner lane's max for the tile's other 16 keys; rounding is
@@ -638,7 +513,6 @@ __device__ __forceinline__ void acc_wait(f32x16 (&o)[8])
 //   steps 30, 31: l = l alpha + sum.
 // Masked path: 8 steps before these hide the scores of invisible keys.
 // ---------------------------------------------------------------------------
-constexpr int SM_STEPS = 32;
 constexpr int HIDE_STEPS = 8;
 constexpr uint32_t BF16_ONES = 0x3f803f80u;     // (1.0, 1.0) as packed bf16
 
@@ -819,116 +693,9 @@ __device__ __forceinline__ void sm_step(int i, f32x16 &s, float &m, float &l, fl
     }
 }
 
-// One softmax step per MFMA slot, starting at slot `first`; with MASKED the
-// hide steps come first (vh = this lane's visibility bits >> 4hh).
-template <bool MASKED>
-__device__ __forceinline__ void sm_slot(int slot, int first, f32x16 &s, uint32_t vh, float &m, float &l,
-                                        float &alpha, u32x4 (&pw)[2], SmTmp &t)
-{
-    int i = slot - first;
-    if (i < 0)
-        return;
-    if (MASKED) {
-        if (i < HIDE_STEPS) {
-            hide_step(i, s, vh);
-            return;
-        }
-        i -= HIDE_STEPS;
-    }
-    if (i < SM_STEPS)
-        sm_step(i, s, m, l, alpha, pw, t);
-}
-
-template <bool MASKED>
-constexpr int sm_slots()
-{
-    return (MASKED ? HIDE_STEPS : 0) + SM_STEPS;
-}
-
 __device__ __forceinline__ bf16x8 lds_read16(uint32_t addr)
 {
     return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>((uintptr_t)addr);
-}
-
-// Scores half of an interval: S^T = K . Q^T for both blocks of one tile (every
-// K fragment read from LDS feeds two MFMAs), with the softmax of block 1's
-// previous tile in the gaps.  kaddr = LDS address of this lane's fragment 0;
-// kpre holds fragments 0 and 1, read ahead.  Near its end the half reads the
-// first two V^T fragments of the context half (vaddr_next) into vpre.
-// issue(slot) places the interval's global->LDS copies among the MFMAs.
-template <bool MASKED, bool DO_S, bool DO_SM, typename Issue>
-__device__ __forceinline__ void scores_half(uint32_t kaddr, const bf16x8 (&kpre)[2], uint32_t vaddr_next,
-                                            bf16x8 (&vpre)[2], const uint4 (&qf)[2][16], f32x16 (&s)[2],
-                                            f32x16 &sp, uint32_t vh, float &m, float &l, float &alpha,
-                                            u32x4 (&pw)[2], Issue &&issue)
-{
-    SmTmp t;
-    bf16x8 kf[16];
-    kf[0] = kpre[0];
-    kf[1] = kpre[1];
-    constexpr int NSLOT = DO_SM ? (sm_slots<MASKED>() > 32 ? sm_slots<MASKED>() : 32) : 32;
-#pragma clang loop unroll(full)
-    for (int slot = 0; slot < NSLOT; ++slot) {
-        const int c = slot >> 1, b = slot & 1;
-        if (DO_S && c < 16) {
-            if (b == 0 && c + 2 < 16)
-                kf[c + 2] = lds_read16(kaddr + 1024 * (c + 2));
-            const f32x16 z = {};
-            s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], __builtin_bit_cast(bf16x8, qf[b][c]),
-                                                           c ? s[b] : z, 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);     // the MFMA leads its slot
-        }
-        if (slot == 28) {
-            vpre[0] = lds_read16(vaddr_next);
-            vpre[1] = lds_read16(vaddr_next + 512);
-        }
-        issue(slot);
-        if (DO_SM)
-            sm_slot<MASKED>(slot, 0, sp, vh, m, l, alpha, pw, t);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// Context half of an interval: O^T += V^T . P^T for both blocks of the
-// previous tile (every V fragment feeds two MFMAs), with the softmax of block
-// 0's current tile in the gaps; its first step waits one slot for the last
-// score MFMAs.  vaddr = LDS address of this lane's fragment (kc 0, db 0);
-// vpre holds fragments 0 and 1.  Near its end the half reads the first two K
-// fragments of the next interval (kaddr_next) into kpre.
-template <bool MASKED, bool DO_PV, bool DO_SM>
-__device__ __forceinline__ void context_half(uint32_t vaddr, const bf16x8 (&vpre)[2], uint32_t kaddr_next,
-                                             bf16x8 (&kpre)[2], const u32x4 (&w0)[2], const u32x4 (&w1)[2],
-                                             f32x16 (&o)[2][8], f32x16 &s, uint32_t vh, float &m, float &l,
-                                             float &alpha, u32x4 (&pw)[2])
-{
-    SmTmp t;
-    bf16x8 vf[16];
-    constexpr int FIRST = 1;
-    vf[0] = vpre[0];
-    vf[1] = vpre[1];
-    constexpr int NSLOT =
-        DO_SM ? (FIRST + sm_slots<MASKED>() > 32 ? FIRST + sm_slots<MASKED>() : 32) : 32;
-#pragma clang loop unroll(full)
-    for (int slot = 0; slot < NSLOT; ++slot) {
-        const int i = slot >> 1, b = slot & 1;     // fragment i: kc = i / 8, db = i % 8
-        if (DO_PV && i < 16) {
-            if (b == 0 && i + 2 < 16) {
-                const int n2 = i + 2;
-                vf[n2] = lds_read16(vaddr + 8192 * (n2 >> 3) + 512 * (n2 & 7));
-            }
-            if ((i & 7) == 0)
-                mfma_o<true>(o[b][i & 7], vf[i], b ? w1[i >> 3] : w0[i >> 3]);
-            else
-                mfma_o<false>(o[b][i & 7], vf[i], b ? w1[i >> 3] : w0[i >> 3]);
-        }
-        if (slot == 28) {
-            kpre[0] = lds_read16(kaddr_next);
-            kpre[1] = lds_read16(kaddr_next + 1024);
-        }
-        if (DO_SM)
-            sm_slot<MASKED>(slot, FIRST, s, vh, m, l, alpha, pw, t);
-        __builtin_amdgcn_sched_barrier(0);
-    }
 }
 
 __device__ __forceinline__ void rescale(f32x16 (&o)[8], float alpha)
@@ -952,360 +719,10 @@ __device__ __forceinline__ void rescale(f32x16 (&o)[8], float alpha)
     }
 }
 
-// Key walk.  Interval k (between two workgroup barriers) reads K(k) and
-// V(k-1) from LDS while K(k+3) and V(k+1) load (four K and three V^T
-// buffers: K runs three intervals ahead, so the next tile's first K
-// fragments can be read during this interval).  In interval k each wave runs
-//   scores half : S(k) for both blocks           | softmax of block 1, tile k-1
-//   context half: O += V(k-1) P(k-1), both blocks | softmax of block 0, tile k
-// so each half pairs 32 MFMAs with one block's softmax.  A block's O is
-// rescaled (rarely) between its last product with the old running max and its
-// first with the new one.
-// MASKED: per-row visibility bits ANDed with causality.  BIDIR: no causal
-// predicate (every row walks all key tiles; only keys past T are hidden).
-template <bool MASKED, bool BIDIR>
-__global__ __attribute__((amdgpu_flat_work_group_size(ATHREADS, ATHREADS), amdgpu_waves_per_eu(1, 1)))
-void attn_fwd(AttnParams p)
-{
-    __shared__ __align__(16) char smem[8 * TILE_BYTES];   // K tiles 0..3, V^T tiles 4..7; epilogue staging
-    __shared__ uint32_t bitsbuf[8][QW];
-    __shared__ int tile_list[MASKED ? MAX_TILES : 1];
-    __shared__ int tile_count;
-
-    const int lane_id = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-    // Work items (64-row block, KV head, head group) are numbered heaviest row
-    // block first (longest key walk).  The launch has at most one workgroup
-    // per compute unit; workgroup b of P takes items in a snake order,
-    // b, 2P-1-b, 2P+b, 4P-1-b, ..., so that each pass pairs the heavy end of
-    // the list with the light end and the workgroups' totals stay level.
-    const int per_rb = p.Hkv * p.n_hg;
-    const int n_items = p.nrb * per_rb;
-    const int P = (int)gridDim.x;
-#pragma clang loop unroll(disable)
-    for (int pass = 0;; ++pass) {
-        const int item = pass * P + ((pass & 1) ? P - 1 - (int)blockIdx.x : (int)blockIdx.x);
-        if (item >= n_items)
-            break;
-        if (pass > 0)
-            __syncthreads();                         // the previous item is done with LDS
-        // Lane-derived values are recomputed per item from an opaque copy of
-        // the lane id (hoisted out of this loop they would stay live across
-        // the key walk and crowd its registers).
-        int lane = lane_id;
-        asm volatile("" : "+v"(lane));
-        const int j = lane & 31, hh = lane >> 5;
-        const int rb = p.nrb - 1 - item / per_rb;
-        const int rem = item % per_rb;
-        const int kvh = rem / p.n_hg, hg = rem % p.n_hg;
-        const int gidx = hg * 4 + wave;
-        const bool active = gidx < p.G;
-        const int h = kvh * p.G + (active ? gidx : 0);
-        const int r0 = rb * QW;                          // the wave's rows r0 .. r0 + 63
-
-        const int P0 = p.q_base + r0;                    // first absolute position (a multiple of 64)
-        const int ntiles = BIDIR ? (p.T + KT - 1) / KT : min(P0 + QW - 1, p.T - 1) / KT + 1;
-        const int diag0 = P0 / KT;                       // block b's diagonal tile is diag0 + b
-
-        // The workgroup's tile sequence: every tile up to the diagonal, or (masked)
-        // the tiles with a visible key for some row of the block, ascending.
-        int n = ntiles;
-        if (MASKED) {
-            if (wave == 0) {
-                int cnt = 0;
-                for (int t0 = 0; t0 < ntiles; t0 += 64) {
-                    const int t = t0 + lane;
-                    const bool on = t < ntiles && p.tilevis[(size_t)rb * p.W + t] != 0;
-                    const uint64_t bal = __ballot(on);
-                    const int at = cnt + __popcll(bal & ((1ull << lane) - 1ull));
-                    if (on)
-                        tile_list[at] = t;
-                    cnt += __popcll(bal);
-                }
-                if (lane == 0)
-                    tile_count = cnt;
-            }
-            __syncthreads();
-            n = tile_count;
-        }
-        auto tile_at = [&](int u) -> int { return MASKED ? tile_list[u] : u; };
-        const uint32_t smem_base = lds_addr(smem);
-        const uint32_t bits_base = lds_addr(bitsbuf);
-        // Tile streams of this KV head, and this wave's quarter of a tile: the
-        // 4 waves each move 4 KB of every 16 KB tile (lane L of part i moves the
-        // 16 bytes at 4096 w + 1024 i + 16 L, into the same offset of the buffer).
-        const uint16_t *kbase = p.kp + (size_t)kvh * (p.Tpad / KT) * (KT * D);
-        const uint16_t *vbase = p.vt + (size_t)kvh * (p.Tpad / KT) * (KT * D);
-        const uint32_t voff = (uint32_t)(wave * 4096 + lane * 16);
-        auto m0_of = [&](bool is_k, int u) {
-            return (uint32_t)__builtin_amdgcn_readfirstlane(
-                (int)(smem_base + TILE_BYTES * ((is_k ? 0 : 4) + (u & 3)) + wave * 4096));
-        };
-        auto src_of = [&](bool is_k, int tile) {
-            tile = __builtin_amdgcn_readfirstlane(tile);
-            return (is_k ? kbase : vbase) + (size_t)tile * (KT * D);
-        };
-        auto load_tile = [&](bool is_k, int tile, int u) {
-            const uint16_t *src = src_of(is_k, tile);
-            const uint32_t m0 = m0_of(is_k, u);
-            dma16<0, true>(src, voff, m0);
-            dma16<1024, false>(src, voff, m0);
-            dma16<2048, false>(src, voff, m0);
-            dma16<3072, false>(src, voff, m0);
-        };
-        // Masked path: the 64 rows' visibility words of a tile, next to its K
-        // load; wave w moves the words of rows 16w .. 16w+15 (lanes outside that
-        // range are masked off, lane L still writes word L).
-        auto load_bits = [&](int tile, int slot) {
-            if (MASKED) {
-                tile = __builtin_amdgcn_readfirstlane(tile);
-                if ((lane >> 4) == wave) {
-                    const int row = min(r0 + lane, p.S - 1);   // rows past S read a real row
-                    dma4(p.bits, (uint32_t)(((size_t)row * p.W + tile) * 4), bits_base + (uint32_t)(slot * QW * 4));
-                }
-            }
-        };
-        // Every interval issues the same loads per wave (tiles past the end are
-        // clamped to the last one and land in a buffer nobody reads), so the
-        // wait for the previous interval's loads is one fixed count.
-        auto tile_clamped = [&](int u) { return tile_at(min(u, n - 1)); };
-        // Interval k's copies, one per issue slot: K(k+3) in 4 parts, its mask
-        // words, V(k+1) in 4 parts (spread over the scores half: a copy occupies
-        // the wave's issue for tens of cycles, which the MFMAs then cover).
-        auto load_part = [&](int k, int part) {
-            if (part == 4) {
-                load_bits(tile_clamped(k + 3), (k + 3) & 7);
-                return;
-            }
-            const bool is_k = part < 4;
-            const int u = is_k ? k + 3 : k + 1;
-            const uint16_t *src = src_of(is_k, tile_clamped(u));
-            const uint32_t m0 = m0_of(is_k, u);
-            switch (is_k ? part : part - 5) {
-            case 0: dma16<0, true>(src, voff, m0); break;
-            case 1: dma16<1024, false>(src, voff, m0); break;
-            case 2: dma16<2048, false>(src, voff, m0); break;
-            default: dma16<3072, false>(src, voff, m0); break;
-            }
-        };
-        auto issue_loads = [&](int k) {
-            return [&, k](int slot) {
-                if (slot % 3 == 1 && slot / 3 < 9)
-                    load_part(k, slot / 3);
-            };
-        };
-        auto no_issue = [](int) {};
-        // Wait for the previous interval's loads (this interval's stay in flight:
-        // 8 per wave, 9 with the mask words), then the barrier.
-        auto close_interval = [&]() {
-            if (MASKED)
-                asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-            __syncthreads();
-        };
-
-        if (n > 0) {
-#pragma unroll
-            for (int u = 0; u < 3; ++u) {
-                load_tile(true, tile_clamped(u), u);
-                load_bits(tile_clamped(u), u);
-            }
-            load_tile(false, tile_clamped(0), 0);
-        }
-
-        // Every wave prepares its queries (an idle wave's results are never
-        // stored); keeping the definition unconditional keeps them in registers.
-        uint4 qf[2][16];
-        load_queries(p, r0, h, lane, qf);
-        const FragOffsets fo = frag_offsets(j, hh);
-        // Causal visibility inside a block's diagonal tile (keys and rows both
-        // start at 32 * (diag0 + b)): bit kk set iff kk <= j.
-        const uint32_t diag_vis = (j == 31) ? 0xffffffffu : ((2u << j) - 1u);
-
-        // The accumulators start as AGPR values (written by an MFMA of zeros), so
-        // that no path into the key walk carries them in VGPRs.
-        f32x16 o[2][8];
-        {
-            const bf16x8 zero = {};
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int db = 0; db < 8; ++db)
-                    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(o[b][db]) : "v"(zero));
-        }
-        float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f}, alpha[2] = {1.0f, 1.0f};
-        f32x16 s[2];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            s[0][e] = 0.0f;
-            s[1][e] = 0.0f;
-        }
-        // Weights of each block's latest tile, as the two MFMA operand words.
-        u32x4 pw0[2] = {}, pw1[2] = {};
-
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-
-        // Visibility of tile u (walk index) for block b, as this lane's bits >> 4hh.
-        // Unmasked: applied only on tiles at or past the block's diagonal (a
-        // uniform branch before the half); masked: always, inside the half.
-        auto masked_vh = [&](int u, int b) -> uint32_t {
-            return MASKED ? (bitsbuf[u & 7][QB * b + j] >> (4 * hh)) : 0u;
-        };
-        auto causal_hide = [&](int u, int b, f32x16 &sc) {
-            if (BIDIR) {
-                // Only the last tile can hold keys past T (zero-padded): hide them.
-                if (u == ntiles - 1 && (p.T & (KT - 1)) != 0)
-                    hide_all(sc, ((1u << (p.T & (KT - 1))) - 1u) >> (4 * hh));
-            } else if (!MASKED) {
-                const int t = u;                       // unmasked: walk index = tile index
-                const int dg = diag0 + b;
-                if (t >= dg) {
-                    const uint32_t vis = (t == dg) ? diag_vis : 0u;
-                    hide_all(sc, vis >> (4 * hh));
-                }
-            }
-        };
-        // LDS addresses of this lane's fragment 0 in the K / V^T buffer of tile k
-        // (kept opaque so every fragment read uses the instruction's offset field).
-        auto kaddr_of = [&](int k) {
-            uint32_t a = smem_base + TILE_BYTES * (k & 3) + fo.k;
-            asm volatile("" : "+v"(a));
-            return a;
-        };
-        auto vaddr_of = [&](int k) {
-            uint32_t a = smem_base + TILE_BYTES * (4 + (k & 3)) + fo.v;
-            asm volatile("" : "+v"(a));
-            return a;
-        };
-
-        const int cc = lane & 31;                       // epilogue: 16-byte chunk of a row (dims 8cc .. 8cc+7)
-        uint4 gw[2][16];
-        auto load_gates = [&](int b) {
-#pragma unroll
-            for (int it = 0; it < 16; ++it) {
-                const int row = min(r0 + QB * b + 2 * it + hh, p.S - 1);
-                gw[b][it] = *reinterpret_cast<const uint4 *>(p.qg + (((size_t)row * p.Hq + h) * 2 + 1) * D + 8 * cc);
-            }
-        };
-        // The unmasked walk always has a tile (row r0 < S sees key 0).
-        if (!MASKED || n > 0) {
-            bf16x8 kpre[2], vpre[2];
-            {
-                const uint32_t a0 = kaddr_of(0);
-                kpre[0] = lds_read16(a0);
-                kpre[1] = lds_read16(a0 + 1024);
-            }
-            // Interval 0: S(0); softmax of block 0 on tile 0.
-            {
-                f32x16 unused = s[1];
-                scores_half<MASKED, true, false>(kaddr_of(0), kpre, vaddr_of(0), vpre, qf, s, unused, 0u, m[1], l[1],
-                                                 alpha[1], pw1, issue_loads(0));
-            }
-            causal_hide(0, 0, s[0]);
-            {
-                const u32x4 w0[2] = {pw0[0], pw0[1]}, w1[2] = {pw1[0], pw1[1]};
-                context_half<MASKED, false, true>(vaddr_of(0), vpre, kaddr_of(1), kpre, w0, w1, o, s[0],
-                                                  masked_vh(0, 0), m[0], l[0], alpha[0], pw0);
-            }
-            rescale(o[0], alpha[0]);
-            close_interval();
-#pragma clang loop unroll(disable)
-            for (int k = 1; k < n; ++k) {
-                f32x16 s1p = s[1];
-                causal_hide(k - 1, 1, s1p);
-                scores_half<MASKED, true, true>(kaddr_of(k), kpre, vaddr_of(k - 1), vpre, qf, s, s1p,
-                                                masked_vh(k - 1, 1), m[1], l[1], alpha[1], pw1, issue_loads(k));
-                rescale(o[1], alpha[1]);
-                causal_hide(k, 0, s[0]);
-                const u32x4 w0[2] = {pw0[0], pw0[1]}, w1[2] = {pw1[0], pw1[1]};
-                context_half<MASKED, true, true>(vaddr_of(k - 1), vpre, kaddr_of(k + 1), kpre, w0, w1, o, s[0],
-                                                 masked_vh(k, 0), m[0], l[0], alpha[0], pw0);
-                rescale(o[0], alpha[0]);
-                close_interval();
-            }
-            // Unmasked: block 0's gate rows load now (the query registers are
-            // free, and the last interval covers the latency).  The masked walk
-            // has no registers to spare for them here.
-            if (!MASKED)
-                load_gates(0);
-            // Interval n: softmax of block 1 on tile n-1; O += V(n-1) P(n-1).
-            {
-                f32x16 s1p = s[1];
-                causal_hide(n - 1, 1, s1p);
-                scores_half<MASKED, false, true>(kaddr_of(n), kpre, vaddr_of(n - 1), vpre, qf, s, s1p,
-                                                 masked_vh(n - 1, 1), m[1], l[1], alpha[1], pw1, no_issue);
-            }
-            rescale(o[1], alpha[1]);
-            {
-                f32x16 unused = s[0];
-                u32x4 pw_unused[2] = {};
-                const u32x4 w0[2] = {pw0[0], pw0[1]}, w1[2] = {pw1[0], pw1[1]};
-                context_half<MASKED, true, false>(vaddr_of(n - 1), vpre, kaddr_of(n + 1), kpre, w0, w1, o, unused, 0u,
-                                                  m[0], l[0], alpha[0], pw_unused);
-            }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();                                 // all waves are done with the tile buffers
-
-        // Epilogue: ctx = bf16(O / l), out = bf16(ctx * bf16(sigmoid(gate))).
-        // The context goes through LDS (row-major, one 528-byte row per query) so
-        // that the gate reads and output writes are whole 512-byte rows.
-        char *ep = smem + wave * QB * EP_STRIDE;
-        if (MASKED)
-            load_gates(0);
-        load_gates(1);                               // covered by block 0's epilogue
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const float lt = pair_sum(l[b]);
-            const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
-            acc_wait(o[b]);
-#pragma unroll
-            for (int db = 0; db < 8; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int d0 = 32 * db + 8 * g + 4 * hh;
-                    const uint2 cw = make_uint2(pack2(o[b][db][4 * g] * inv, o[b][db][4 * g + 1] * inv),
-                                                pack2(o[b][db][4 * g + 2] * inv, o[b][db][4 * g + 3] * inv));
-                    *reinterpret_cast<uint2 *>(ep + j * EP_STRIDE + 2 * d0) = cw;
-                }
-#pragma unroll
-            for (int it = 0; it < 16; ++it) {
-                const int rr = 2 * it + hh;
-                const int row = r0 + QB * b + rr;
-                const uint4 cv = *reinterpret_cast<const uint4 *>(ep + rr * EP_STRIDE + 16 * cc);
-                const uint32_t cws[4] = {cv.x, cv.y, cv.z, cv.w};
-                const uint32_t gws[4] = {gw[b][it].x, gw[b][it].y, gw[b][it].z, gw[b][it].w};
-                uint32_t ow[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float ov[2];
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const float ctx = hf ? hi_f(cws[q]) : lo_f(cws[q]);
-                        const float gv = hf ? hi_f(gws[q]) : lo_f(gws[q]);
-                        // Hardware reciprocal (exact at 1 and 2: a saturated logit
-                        // gives exactly 1, a zero logit exactly 1/2).
-                        const float sg = rbf(__builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * LOG2E)));
-                        ov[hf] = ctx * sg;
-                    }
-                    ow[q] = pack2(ov[0], ov[1]);
-                }
-                if (active && row < p.S)
-                    *reinterpret_cast<uint4 *>(p.out + ((size_t)row * p.Hq + h) * D + 8 * cc) =
-                        make_uint4(ow[0], ow[1], ow[2], ow[3]);
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Eight-wave attention for the unmasked passes (causal and bidirectional).
-//
-// The same work item (64 query rows x the 4 query heads of a head group of
-// one KV head) on 8 waves, two per SIMD: wave w owns head 4hg + (w & 3) and
+// Attention.  A work item is 64 query rows x the 4 query heads of a head
+// group of one KV head (the K/V tiles it stages serve all four heads), on 8
+// waves, two per SIMD: wave w owns head 4hg + (w & 3) and
 // the 32-row block w >> 2, so a SIMD holds the two blocks of one head.  A
 // wave's registers (at most 256 with two waves per SIMD) hold one block: O
 // (128 AGPRs), its query fragments (64) and the scores of one tile (16).  The
@@ -1318,12 +735,21 @@ void attn_fwd(AttnParams p)
 // of plain MFMAs.  Each wave moves an eighth of every K and V^T tile into
 // LDS (2 KB), K three tiles ahead and V^T two ahead, four buffers
 // each (block 1 still reads V(k-2) while V(k+1) arrives).
+// MASKED: the walk follows the tiles with a visible key for some row of the
+// 64 (from mask_pack's flags); each tile's 64 visibility words are copied to
+// LDS next to its K tile, and the softmax program starts with 8 steps that
+// hide invisible keys.  BIDIR: no causal predicate (every row walks all key
+// tiles; only keys past T are hidden).
 // ---------------------------------------------------------------------------
 constexpr int ATHREADS8 = 512;
 constexpr int SMEM8 = (8 * TILE_BYTES > 8 * QB * EP_STRIDE) ? 8 * TILE_BYTES : 8 * QB * EP_STRIDE;
 
-// Query prologue of one 32-row block (rows r0 ..): the same arithmetic as
-// load_queries; swapping each word with itself gives every lane both halves
+// Query prologue of one 32-row block (rows r0 .. r0+31) of head h: loads the
+// q half of the rows, applies (1+w) RMSNorm (sum of squares in ascending
+// dimension order, the same chain as the key prologue) and partial RoPE, and
+// leaves the MFMA B-operand fragments in qf[c]: lane (j = lane & 31, hh =
+// lane >> 5) holds dims 16c + 8hh .. +7 of row r0 + j.  Rows at or past S are
+// zero.  v_permlane32_swap of a word with itself gives every lane both halves
 // of its row for the sum of squares.
 __device__ __forceinline__ void load_queries1(const AttnParams &p, int r0, int h, int lane, uint4 (&qf)[16])
 {
@@ -1468,17 +894,30 @@ __device__ __forceinline__ void sm_tail8(f32x16 &s, float &l, float alpha, u32x4
 // gaps, two steps per slot from slot 1 (the last score MFMA may still be in
 // flight at slot 0).  The first word group is repacked only after the eighth
 // MFMA and the second after the last, so one weight buffer serves both tiles.
-template <bool DO_PV, bool DO_SM>
+template <bool MASKED, bool DO_PV, bool DO_SM>
 __device__ __forceinline__ void pv_half8(uint32_t vaddr, f32x16 (&o)[8], u32x4 (&pw)[2], f32x16 &s, float &m,
-                                         float &l, float &alpha)
+                                         float &l, float &alpha, uint32_t vh)
 {
     SmTmp t;
     bf16x8 vf[16];
     if (DO_PV)
         vf[0] = lds_read16(vaddr);
+    // Masked: the 8 hide steps come first; the program then runs past the
+    // 16 MFMA slots (the other wave of the SIMD keeps the matrix pipe busy).
+    constexpr int NSLOT = (DO_SM && MASKED) ? 19 : 16;
+    auto step = [&](int x) {
+        if (MASKED) {
+            if (x < HIDE_STEPS)
+                hide_step(x, s, vh);
+            else
+                sm_step8(x - HIDE_STEPS, s, m, l, alpha, pw, t);
+        } else {
+            sm_step8(x, s, m, l, alpha, pw, t);
+        }
+    };
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        if (DO_PV) {
+    for (int i = 0; i < NSLOT; ++i) {
+        if (DO_PV && i < 16) {
             if (i + 1 < 16) {
                 const int n1 = i + 1;
                 vf[n1] = lds_read16(vaddr + 8192 * (n1 >> 3) + 512 * (n1 & 7));
@@ -1490,8 +929,8 @@ __device__ __forceinline__ void pv_half8(uint32_t vaddr, f32x16 (&o)[8], u32x4 (
             __builtin_amdgcn_sched_barrier(0);
         }
         if (DO_SM && i >= 1) {
-            sm_step8(2 * i - 2, s, m, l, alpha, pw, t);
-            sm_step8(2 * i - 1, s, m, l, alpha, pw, t);
+            step(2 * i - 2);
+            step(2 * i - 1);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -1499,19 +938,26 @@ __device__ __forceinline__ void pv_half8(uint32_t vaddr, f32x16 (&o)[8], u32x4 (
         sm_tail8(s, l, alpha, pw, t);
 }
 
-template <bool BIDIR>
+template <bool MASKED, bool BIDIR>
 __global__ __attribute__((amdgpu_flat_work_group_size(ATHREADS8, ATHREADS8), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd8(AttnParams pk)
 {
     __shared__ __align__(16) char smem[SMEM8];     // K tiles 0..3, V^T tiles 4..7; epilogue staging
+    __shared__ uint32_t bitsbuf[MASKED ? 8 : 1][QW];
+    __shared__ int tile_list[MASKED ? MAX_TILES : 1];
+    __shared__ int tile_count;
 
     const int lane_id = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hw = wave & 3;                        // head within the group of four
     const int blk = wave >> 2;                      // 32-row block; 1 = the lagging phase
 
-    // Work items and their order as in attn_fwd (a packed batch lists its
-    // (sequence, row block) pairs heaviest first instead).
+    // Work items (64-row block, KV head, head group) are numbered heaviest row
+    // block first (longest key walk; a packed batch lists its (sequence, row
+    // block) pairs in that order).  The launch has at most one workgroup per
+    // compute unit; workgroup b of P takes items in a snake order, b,
+    // 2P-1-b, 2P+b, 4P-1-b, ..., so that each pass pairs the heavy end of the
+    // list with the light end and the workgroups' totals stay level.
     const int per_rb = pk.Hkv * pk.n_hg;
     const int n_items = pk.nrb * per_rb;
     const int P = (int)gridDim.x;
@@ -1529,7 +975,7 @@ void attn_fwd8(AttnParams pk)
         // (its rows, its prepared key tiles, positions from 0).
         AttnParams p = pk;
         int rb, ktile0 = 0;
-        if (!BIDIR && pk.pairs) {
+        if (!BIDIR && !MASKED && pk.pairs) {
             const int sq = pk.pairs[2 * (item / per_rb)];
             rb = pk.pairs[2 * (item / per_rb) + 1];
             p.S = p.T = pk.seg[4 * sq];
@@ -1551,7 +997,29 @@ void attn_fwd8(AttnParams pk)
         const int P0 = p.q_base + r0;
         const int ntiles = BIDIR ? (p.T + KT - 1) / KT : min(P0 + QW - 1, p.T - 1) / KT + 1;
         const int diag = P0 / KT + blk;                  // this block's diagonal tile
-        const int n = ntiles;                            // >= 1: row r0 sees key 0
+
+        // The walk: every tile up to the diagonal (>= 1: row r0 sees key 0), or
+        // (masked) the tiles with a visible key for some row of the 64, ascending.
+        int n = ntiles;
+        if (MASKED) {
+            if (wave == 0) {
+                int cnt = 0;
+                for (int t0 = 0; t0 < ntiles; t0 += 64) {
+                    const int t = t0 + lane;
+                    const bool on = t < ntiles && p.tilevis[(size_t)rb * p.W + t] != 0;
+                    const uint64_t bal = __ballot(on);
+                    const int at = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+                    if (on)
+                        tile_list[at] = t;
+                    cnt += __popcll(bal);
+                }
+                if (lane == 0)
+                    tile_count = cnt;
+            }
+            __syncthreads();
+            n = tile_count;
+        }
+        auto tile_at = [&](int u) -> int { return MASKED ? tile_list[u] : u; };
 
         const uint32_t smem_base = lds_addr(smem);
         const uint16_t *kbase = p.kp + ((size_t)kvh * (p.Tpad / KT) + ktile0) * (KT * D);
@@ -1566,7 +1034,19 @@ void attn_fwd8(AttnParams pk)
             tile = __builtin_amdgcn_readfirstlane(tile);
             return (is_k ? kbase : vbase) + (size_t)tile * (KT * D);
         };
-        auto tile_clamped = [&](int u) { return min(u, n - 1); };
+        auto tile_clamped = [&](int u) { return tile_at(min(u, n - 1)); };
+        // Masked: the 64 rows' visibility words of a tile, next to its K copy;
+        // wave w moves the words of rows 8w .. 8w+7 (lane L writes word L).
+        const uint32_t bits_base = lds_addr(bitsbuf);
+        auto load_bits = [&](int tile, int slot) {
+            if (MASKED) {
+                tile = __builtin_amdgcn_readfirstlane(tile);
+                if ((lane >> 3) == wave) {
+                    const int row = min(r0 + lane, p.S - 1);   // rows past S read a real row
+                    dma4(p.bits, (uint32_t)(((size_t)row * p.W + tile) * 4), bits_base + (uint32_t)(slot * QW * 4));
+                }
+            }
+        };
         auto load_tile = [&](bool is_k, int u) {
             const uint16_t *src = src_of(is_k, tile_clamped(u));
             const uint32_t m0 = m0_of(is_k, u);
@@ -1591,20 +1071,29 @@ void attn_fwd8(AttnParams pk)
                         dma16<0, true>(src, voff, m0);
                     else
                         dma16<1024, false>(src, voff, m0);
+                } else if (MASKED && slot == 3) {
+                    load_bits(tile_clamped(k + 3), (k + 3) & 7);
                 }
             };
         };
-        // Wait for the previous interval's copies (this interval's two or four
-        // stay in flight), then the barrier.
+        // Wait for the previous interval's copies (this interval's four, five
+        // with the mask words, stay in flight), then the barrier.
         auto close_interval = [&]() {
-            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            if (MASKED)
+                asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
             __syncthreads();
         };
 
+        if (!MASKED || n > 0) {
 #pragma unroll
-        for (int u = 0; u < 3; ++u)
-            load_tile(true, u);
-        load_tile(false, 0);
+            for (int u = 0; u < 3; ++u) {
+                load_tile(true, u);
+                load_bits(tile_clamped(u), u);
+            }
+            load_tile(false, 0);
+        }
 
         uint4 qf[16];
         load_queries1(p, rbase, h, lane, qf);
@@ -1628,8 +1117,14 @@ void attn_fwd8(AttnParams pk)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 
+        // Visibility of walk tile u for this block, as this lane's bits >> 4hh.
+        auto masked_vh = [&](int u) -> uint32_t {
+            return MASKED ? (bitsbuf[u & 7][QB * blk + j] >> (4 * hh)) : 0u;
+        };
         auto causal_hide = [&](int u, f32x16 &sc) {
-            if (BIDIR) {
+            if (MASKED) {
+                // causality is folded into the mask words
+            } else if (BIDIR) {
                 if (u == n - 1 && (p.T & (KT - 1)) != 0)
                     hide_all(sc, ((1u << (p.T & (KT - 1))) - 1u) >> (4 * hh));
             } else if (u >= diag) {
@@ -1707,31 +1202,36 @@ void attn_fwd8(AttnParams pk)
         // interval behind.  The barrier is the workgroup's: each wave arrives
         // once per interval, from either place.
         const bool lag = blk == 1;
-        s_half8(kaddr_of(0), qf, s, issue_loads(0));
-        if (lag)
-            close_interval();
-        causal_hide(0, s);
-        pv_half8<false, true>(0u, o, pw, s, m, l, alpha);
-        rescale(o, alpha);
-        if (!lag)
-            close_interval();
-#pragma clang loop unroll(disable)
-        for (int k = 1; k < n; ++k) {
-            s_half8(kaddr_of(k), qf, s, issue_loads(k));
+        if (!MASKED || n > 0) {
+            s_half8(kaddr_of(0), qf, s, issue_loads(0));
             if (lag)
                 close_interval();
-            causal_hide(k, s);
-            pv_half8<true, true>(vaddr_of(k - 1), o, pw, s, m, l, alpha);
+            causal_hide(0, s);
+            pv_half8<MASKED, false, true>(0u, o, pw, s, m, l, alpha, masked_vh(0));
             rescale(o, alpha);
             if (!lag)
                 close_interval();
+#pragma clang loop unroll(disable)
+            for (int k = 1; k < n; ++k) {
+                s_half8(kaddr_of(k), qf, s, issue_loads(k));
+                if (lag)
+                    close_interval();
+                causal_hide(k, s);
+                pv_half8<MASKED, true, true>(vaddr_of(k - 1), o, pw, s, m, l, alpha, masked_vh(k));
+                rescale(o, alpha);
+                if (!lag)
+                    close_interval();
+            }
+            if (lag)
+                close_interval();
+            if (!MASKED)
+                load_gates();                            // the last context half covers the latency
+            pv_half8<MASKED, true, false>(vaddr_of(n - 1), o, pw, s, m, l, alpha, 0u);
+            if (!lag)
+                close_interval();
         }
-        if (lag)
-            close_interval();
-        load_gates();
-        pv_half8<true, false>(vaddr_of(n - 1), o, pw, s, m, l, alpha);
-        if (!lag)
-            close_interval();
+        if (MASKED)
+            load_gates();                                // (with nothing visible O and l stay zero)
         epilogue();
     }
 }
@@ -1819,13 +1319,13 @@ hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stre
     const int nblocks = p.n_wg;
     switch (mode) {
     case AttnMode::Masked:
-        hipLaunchKernelGGL((attn_fwd<true, false>), dim3(nblocks), dim3(ATHREADS), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd8<true, false>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
         break;
     case AttnMode::Bidirectional:
-        hipLaunchKernelGGL((attn_fwd8<true>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd8<false, true>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
         break;
     default:
-        hipLaunchKernelGGL((attn_fwd8<false>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd8<false, false>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
     }
     return hipGetLastError();
 }
