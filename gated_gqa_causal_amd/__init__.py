@@ -40,6 +40,7 @@ ATTN_ERR_LAUNCH = -7
 ATTN_KERNEL_KV_PROLOGUE = 0
 ATTN_KERNEL_MASK_PACK = 1
 ATTN_KERNEL_ATTENTION = 2
+ATTN_KERNEL_WEIGHTS = 3
 
 KIND_GATED, KIND_PREFIX, KIND_MASKED = 0, 1, 2
 
@@ -81,6 +82,9 @@ def _load():
         "attn_prefill_prefix": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp]),
         "attn_prefill_masked": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, vp, vp]),
         "attn_prefill_bidirectional": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, vp]),
+        "attn_validate_weights": (ctypes.c_int, [ctypes.POINTER(attn_geometry), ctypes.POINTER(attn_inputs),
+                                                 i32, i32, i32, vp, vp, vp]),
+        "attn_prefill_weights": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, i32, vp, vp, vp, vp]),
         "attn_kv_cache_bytes": (ctypes.c_int, [ctypes.POINTER(attn_geometry), ctypes.POINTER(ctypes.c_size_t)]),
         "attn_prefill_append": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp, vp]),
         "attn_kv_cache_fp8_bytes": (ctypes.c_int, [ctypes.POINTER(attn_geometry),
@@ -151,6 +155,17 @@ def attn_prefill_masked(ctx, inputs: attn_inputs, S: int, mask: int, out: int, s
 
 def attn_prefill_bidirectional(ctx, inputs: attn_inputs, S: int, out: int, stream: int) -> int:
     return lib.attn_prefill_bidirectional(ctx, ctypes.byref(inputs), S, out, stream)
+
+
+def attn_validate_weights(geom: attn_geometry, inputs: Optional[attn_inputs], T: int, q_base: int, kind: int,
+                          mask: Optional[int], out: Optional[int], weights: Optional[int]) -> int:
+    return lib.attn_validate_weights(ctypes.byref(geom), None if inputs is None else ctypes.byref(inputs),
+                                     T, q_base, kind, mask, out, weights)
+
+
+def attn_prefill_weights(ctx, inputs: attn_inputs, T: int, q_base: int, kind: int, mask: Optional[int], out: int,
+                         weights: int, stream: int) -> int:
+    return lib.attn_prefill_weights(ctx, ctypes.byref(inputs), T, q_base, kind, mask, out, weights, stream)
 
 
 def attn_kv_cache_bytes(geom: attn_geometry):
@@ -416,6 +431,29 @@ class Context:
         if rc != ATTN_OK:
             raise AttnError(rc, "attn_prefill_masked")
         return out
+
+    def prefill_weights(self, qg, k, v, q_norm_w, k_norm_w, cos, sin, kind: int = 0, q_base: int = 0, mask=None,
+                        out=None, weights=None, stream=None):
+        """The pass of `kind` (0 gated, 1 prefix window at q_base, 2 masked, 3
+        bidirectional) plus its normalised bf16 weights [rows][Hq][T].
+        Returns (out, weights)."""
+        import torch
+        g = self.geom
+        T = k.shape[0]
+        rows = T - q_base
+        inp = self.inputs(qg, k, v, q_norm_w, k_norm_w, cos, sin, rows, T)
+        if mask is not None:
+            self._check("mask", mask, torch.uint8, (T, T))
+        out = self._out(out, rows)
+        shape = (rows, g.n_q_heads, T)
+        if weights is None:
+            weights = torch.empty(shape, dtype=torch.bfloat16, device=f"cuda:{self.device}")
+        self._check("weights", weights, torch.bfloat16, shape)
+        rc = attn_prefill_weights(self.handle, inp, T, q_base, kind, None if mask is None else mask.data_ptr(),
+                                  out.data_ptr(), weights.data_ptr(), self._stream(stream))
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_prefill_weights")
+        return out, weights
 
     def debug_prepare(self, qg, k, v, q_norm_w, k_norm_w, cos, sin, q_base: int = 0, stream=None):
         """Prepared queries [rows][Hq][D] and keys [Hkv][T][D] as the kernels see them."""

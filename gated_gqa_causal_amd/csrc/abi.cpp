@@ -30,6 +30,7 @@ struct attn_ctx {
     uint16_t *vt = nullptr;        // transposed values, [Hkv][tpad/32] tiles of 256 x 32
     uint32_t *mask_bits = nullptr; // [max_tokens][mask_words]
     uint8_t *tile_vis = nullptr;   // [ceil(max_tokens/64)][mask_words]
+    float *row_stats = nullptr;    // [max_tokens][Hq][2]: softmax max and sum (weights calls)
     // packed batches: the per-call sequence tables (device), staged through a
     // pinned host buffer whose previous copy `batch_copied` must have landed
     // before it is rewritten
@@ -170,6 +171,7 @@ void fill_attn_params(ga::AttnParams &ap, const attn_ctx *ctx, const attn_inputs
     ap.n_wg = (int)std::min<int64_t>((int64_t)ap.nrb * ap.Hkv * ap.n_hg, ctx->num_cus);
     ap.pairs = nullptr;
     ap.seg = nullptr;
+    ap.ml = nullptr;
 }
 
 // Packed batch bookkeeping: ints of the per-call table for a workspace of
@@ -242,7 +244,7 @@ int plan_batch(const attn_geometry &g, int32_t n_seqs, const int32_t *lens, Batc
 // kind 4: `mask` is the caller's K/V cache; the prologue writes keys
 // q_base..T-1 into it (k and v hold only those rows) and attention reads it.
 int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kind, const uint8_t *mask,
-        void *out, void *stream)
+        void *out, void *stream, void *weights = nullptr)
 {
     if (!ctx)
         return ATTN_ERR_NULL_ARG;
@@ -321,11 +323,19 @@ int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kin
             return ATTN_ERR_LAUNCH;
         tm.stop();
     }
+    const ga::AttnMode mode = kind == 2 ? ga::AttnMode::Masked
+                              : kind == 3 ? ga::AttnMode::Bidirectional : ga::AttnMode::Causal;
+    if (weights)
+        ap.ml = ctx->row_stats;
     {
         Timer tm(ctx, s, ATTN_KERNEL_ATTENTION);
-        if (ga::launch_attention(ap, kind == 2 ? ga::AttnMode::Masked
-                                     : kind == 3 ? ga::AttnMode::Bidirectional : ga::AttnMode::Causal,
-                                 s) != hipSuccess)
+        if (ga::launch_attention(ap, mode, s) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+        tm.stop();
+    }
+    if (weights) {
+        Timer tm(ctx, s, ATTN_KERNEL_WEIGHTS);
+        if (ga::launch_attn_weights(ap, mode, static_cast<uint16_t *>(weights), s) != hipSuccess)
             return ATTN_ERR_LAUNCH;
         tm.stop();
     }
@@ -420,7 +430,9 @@ int attn_ctx_create(const attn_geometry *geom, int device, attn_ctx **out)
     bool ok = hipMalloc(&ctx->kp, kv_elems * 2) == hipSuccess &&
               hipMalloc(&ctx->vt, kv_elems * 2) == hipSuccess &&
               hipMalloc(&ctx->mask_bits, (size_t)geom->max_tokens * ctx->mask_words * 4) == hipSuccess &&
-              hipMalloc(&ctx->tile_vis, nrb * ctx->mask_words) == hipSuccess;
+              hipMalloc(&ctx->tile_vis, nrb * ctx->mask_words) == hipSuccess &&
+              hipMalloc(&ctx->row_stats, (size_t)geom->max_tokens * geom->n_q_heads * 2 * sizeof(float)) ==
+                  hipSuccess;
     ctx->batch_cap = batch_table_ints(ctx->tpad);
     ok = ok && hipMalloc(&ctx->batch_tab, ctx->batch_cap * sizeof(int)) == hipSuccess &&
          hipHostMalloc(&ctx->batch_host, ctx->batch_cap * sizeof(int), hipHostMallocDefault) == hipSuccess &&
@@ -446,6 +458,7 @@ void attn_ctx_destroy(attn_ctx *ctx)
     (void)hipFree(ctx->vt);
     (void)hipFree(ctx->mask_bits);
     (void)hipFree(ctx->tile_vis);
+    (void)hipFree(ctx->row_stats);
     (void)hipFree(ctx->batch_tab);
     if (ctx->batch_host)
         (void)hipHostFree(ctx->batch_host);
@@ -473,6 +486,34 @@ int attn_prefill_masked(attn_ctx *ctx, const attn_inputs *in, int32_t S, const u
                         void *stream)
 {
     return run(ctx, in, S, 0, 2, mask, out, stream);
+}
+
+int attn_validate_weights(const attn_geometry *geom, const attn_inputs *in, int32_t T, int32_t q_base,
+                          int32_t kind, const void *mask, const void *out, const void *weights)
+{
+    if (!geom)
+        return ATTN_ERR_NULL_ARG;
+    if (kind < 0 || kind > 3)
+        return ATTN_ERR_RANGE;   // the cache kinds have no weights variant
+    int rc = attn_validate(geom, in, T, q_base, kind, mask, out);
+    if (rc != ATTN_OK || T - q_base == 0)
+        return rc;
+    if (!weights)
+        return ATTN_ERR_NULL_ARG;
+    if (!aligned16(weights))
+        return ATTN_ERR_ALIGN;
+    return ATTN_OK;
+}
+
+int attn_prefill_weights(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int32_t kind,
+                         const uint8_t *mask, void *out, void *weights, void *stream)
+{
+    if (!ctx)
+        return ATTN_ERR_NULL_ARG;
+    int rc = attn_validate_weights(&ctx->geom, in, T, q_base, kind, mask, out, weights);
+    if (rc != ATTN_OK)
+        return rc;
+    return run(ctx, in, T, q_base, kind, kind == 2 ? mask : nullptr, out, stream, weights);
 }
 
 int attn_kv_cache_bytes(const attn_geometry *geom, size_t *bytes)
@@ -658,7 +699,7 @@ int attn_ctx_read_timing(attn_ctx *ctx, int kernel, double *total_ms, int32_t *l
 {
     if (!ctx || !total_ms || !launches)
         return ATTN_ERR_NULL_ARG;
-    if (kernel < 0 || kernel > ATTN_KERNEL_ATTENTION)
+    if (kernel < 0 || kernel > ATTN_KERNEL_WEIGHTS)
         return ATTN_ERR_RANGE;
     if (current_device_matches(ctx) != ATTN_OK)
         return ATTN_ERR_DEVICE;

@@ -63,6 +63,9 @@ struct AttnParams {
     // KvPrologueParams.  Each sequence is a causal pass at positions 0..len-1.
     const int *pairs;
     const int *seg;
+    // Optional (else null): per (row, query head) the softmax's final
+    // reference max (raw score units) and row sum, [S][Hq][2] fp32.
+    float *ml;
 };
 
 constexpr int kRowsPerBlock = 64;
@@ -75,6 +78,7 @@ hipError_t launch_kv_widen(const KvWidenParams &p, int ntiles, int Hkv, hipStrea
 hipError_t launch_mask_pack(const MaskPackParams &p, int nrb, hipStream_t stream);
 enum class AttnMode { Causal, Masked, Bidirectional };
 hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stream);
+hipError_t launch_attn_weights(const AttnParams &p, AttnMode mode, uint16_t *weights, hipStream_t stream);
 hipError_t launch_kp_unpack(const uint16_t *kp, int Tpad, int T, int Hkv, uint16_t *out, hipStream_t stream);
 hipError_t launch_mfma_clock_probe(int iters, int n_wg, long long *rec, float *sink, hipStream_t stream);
 hipError_t launch_q_prologue_debug(const AttnParams &p, uint16_t *qp, hipStream_t stream);

@@ -1159,6 +1159,10 @@ void attn_fwd8(AttnParams pk)
             __syncthreads();                             // all waves are done with the tile buffers
             char *ep = smem + wave * QB * EP_STRIDE;
             const float lt = pair_sum(l);
+            if (p.ml && hh == 0 && active && rbase + j < p.S) {
+                p.ml[((size_t)(rbase + j) * p.Hq + h) * 2] = m;
+                p.ml[((size_t)(rbase + j) * p.Hq + h) * 2 + 1] = lt;
+            }
             const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
             acc_wait(o);
 #pragma unroll
@@ -1233,6 +1237,88 @@ void attn_fwd8(AttnParams pk)
         if (MASKED)
             load_gates();                                // (with nothing visible O and l stay zero)
         epilogue();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Attention weights: bf16 [S][Hq][T], weight[i][h][j] = bf16(exp2((s_ij -
+// m_ih) log2(e)/16) / l_ih) with s the bf16-rounded score and (m, l) the
+// reference max and row sum the attention pass recorded; hidden keys give 0.
+// Every element is written (zeros for tiles past a row block's diagonal and
+// for tiles the mask hides from the whole block).  grid (ceil(S/32),
+// ceil(Hq/4)), 256 threads: wave w takes query head 4y + w, rows 32x ..
+// 32x+31.  K fragments are read straight from the prepared tiles in HBM
+// (their layout is the LDS layout of the attention kernel); the weight
+// stores bound the kernel.
+// ---------------------------------------------------------------------------
+template <int MODE>   // 0 causal, 1 masked (causal and mask), 2 bidirectional
+__global__ __launch_bounds__(256) void attn_weights(AttnParams p, uint16_t *wout)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int h = blockIdx.y * 4 + wave;
+    if (h >= p.Hq)
+        return;                                          // no barriers below
+    const int j = lane & 31, hh = lane >> 5;
+    const int r0 = blockIdx.x * 32, row = r0 + j;
+    const int kvh = h / p.G;
+    uint4 qf[16];
+    load_queries1(p, r0, h, lane, qf);
+    const int rc = min(row, p.S - 1);
+    const float m = p.ml[((size_t)rc * p.Hq + h) * 2];
+    const float lsum = p.ml[((size_t)rc * p.Hq + h) * 2 + 1];
+    const float nb = (m == -INFINITY) ? 0.0f : m * -SCALE_LOG2;
+    const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
+    const int pos0 = p.q_base + r0;                      // a multiple of 32
+    const int nvis = (MODE == 2 ? p.T - 1 : min(pos0 + 31, p.T - 1)) / KT + 1;
+    const int ntiles = (p.T + KT - 1) / KT;
+    const int diag = pos0 / KT;
+    const uint32_t diag_vis = (j == 31) ? 0xffffffffu : ((2u << j) - 1u);
+    const FragOffsets fo = frag_offsets(j, hh);
+    const bool vec = (p.T & 3) == 0;                     // 8-byte stores stay aligned
+    uint16_t *dst_row = wout + ((size_t)rc * p.Hq + h) * p.T + 4 * hh;
+    for (int t = 0; t < ntiles; ++t) {
+        uint32_t w[16];
+        if (t < nvis && (MODE != 1 || p.tilevis[(size_t)(r0 / QW) * p.W + t] != 0)) {
+            const char *kt = reinterpret_cast<const char *>(p.kp + ((size_t)kvh * (p.Tpad / KT) + t) * (KT * D));
+            f32x16 s;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kt + fo.k + 1024 * c);
+                const f32x16 z = {};
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8, qf[c]), c ? s : z, 0,
+                                                            0, 0);
+            }
+            if (MODE == 1)
+                hide_all(s, p.bits[(size_t)rc * p.W + t] >> (4 * hh));
+            else if (MODE == 0 && t >= diag)
+                hide_all(s, (t == diag ? diag_vis : 0u) >> (4 * hh));
+            // rbf, not the inline-asm round_op: the scores come from the MFMA
+            // builtin, and only a read the compiler sees gets the wait states
+            // that reading a matrix-core result requires.
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                w[e] = f2bf(__builtin_amdgcn_exp2f(__builtin_fmaf(rbf(s[e]), SCALE_LOG2, nb)) * inv);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                w[e] = 0u;
+        }
+        if (row >= p.S)
+            continue;
+        uint16_t *dst = dst_row + (size_t)t * KT;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int key = t * KT + 8 * g + 4 * hh;
+            if (vec && key + 3 < p.T) {
+                *reinterpret_cast<uint2 *>(dst + 8 * g) =
+                    make_uint2(w[4 * g] | (w[4 * g + 1] << 16), w[4 * g + 2] | (w[4 * g + 3] << 16));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (key + r < p.T)
+                        dst[8 * g + r] = (uint16_t)w[4 * g + r];
+            }
+        }
     }
 }
 
@@ -1327,6 +1413,18 @@ hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stre
     default:
         hipLaunchKernelGGL((attn_fwd8<false, false>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_weights(const AttnParams &p, AttnMode mode, uint16_t *weights, hipStream_t stream)
+{
+    const dim3 grid((p.S + 31) / 32, (p.Hq + 3) / 4);
+    if (mode == AttnMode::Masked)
+        hipLaunchKernelGGL(attn_weights<1>, grid, dim3(256), 0, stream, p, weights);
+    else if (mode == AttnMode::Bidirectional)
+        hipLaunchKernelGGL(attn_weights<2>, grid, dim3(256), 0, stream, p, weights);
+    else
+        hipLaunchKernelGGL(attn_weights<0>, grid, dim3(256), 0, stream, p, weights);
     return hipGetLastError();
 }
 

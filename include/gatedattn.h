@@ -121,7 +121,8 @@ ATTN_EXPORT int attn_validate(const attn_geometry *geom, const attn_inputs *in, 
 /*
  * Creates a context on `device` for `geom`, allocating its workspace (about
  * 2 * Hkv * max_tokens * D * 2 bytes for prepared keys and values, plus
- * max_tokens^2 / 8 bytes of packed mask bits).  The device becomes current
+ * max_tokens^2 / 8 bytes of packed mask bits and max_tokens * Hq * 8 bytes
+ * of softmax row statistics).  The device becomes current
  * on the calling thread.  On success *out holds the context; on failure
  * *out is NULL and nothing stays allocated.
  */
@@ -167,6 +168,33 @@ ATTN_EXPORT int attn_prefill_masked(attn_ctx *ctx, const attn_inputs *in, int32_
  */
 ATTN_EXPORT int attn_prefill_bidirectional(attn_ctx *ctx, const attn_inputs *in, int32_t S, void *out,
                                            void *stream);
+
+/*
+ * Attention weights (the QSA kernel page, "What changed" and its timing
+ * table: the kernel also writes the normalised weights, bf16 [rows][heads]
+ * [tokens], which its golden checks).  Runs the pass of `kind` (0 gated,
+ * 1 prefix window, 2 masked with `mask`, 3 bidirectional; the K/V cache kinds
+ * are refused with ATTN_ERR_RANGE) exactly as its own entry point does (same
+ * arguments, limits and `out`, bit for bit), then writes
+ *   weights[i][h][j] = bf16(exp(s_ij - m_ih) / l_ih)
+ * into the caller's device buffer `weights`, bf16 [T - q_base][Hq][T],
+ * 16-byte aligned: s_ij = bf16(q_i . k_j) / 16 is row i's rounded score,
+ * m_ih and l_ih the reference max and the sum of the bf16 weight numerators
+ * the pass's online softmax ended with, so that out's context is
+ * sum_j weight * v_j up to the rounding of the weights.  Hidden keys (causal,
+ * masked, or a row with no visible key) give 0; every element is written.
+ * Row statistics live in the context's workspace (max_tokens * Hq * 8
+ * bytes), so calls on one context must be stream-ordered.
+ * attn_validate_weights runs the host-only checks: attn_validate's, then
+ * weights non-NULL (ATTN_ERR_NULL_ARG) and 16-byte aligned (ATTN_ERR_ALIGN);
+ * an empty window is a no-op and skips them.
+ */
+ATTN_EXPORT int attn_validate_weights(const attn_geometry *geom, const attn_inputs *in, int32_t T,
+                                      int32_t q_base, int32_t kind, const void *mask, const void *out,
+                                      const void *weights);
+ATTN_EXPORT int attn_prefill_weights(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base,
+                                     int32_t kind, const uint8_t *mask, void *out, void *weights,
+                                     void *stream);
 
 /*
  * Cached prefix continuation (the prefix state of the system1-omni
@@ -255,6 +283,7 @@ ATTN_EXPORT int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t
 #define ATTN_KERNEL_KV_PROLOGUE 0
 #define ATTN_KERNEL_MASK_PACK 1
 #define ATTN_KERNEL_ATTENTION 2
+#define ATTN_KERNEL_WEIGHTS 3
 ATTN_EXPORT int attn_ctx_set_timing(attn_ctx *ctx, int enable);
 ATTN_EXPORT int attn_ctx_read_timing(attn_ctx *ctx, int kernel, double *total_ms, int32_t *launches);
 

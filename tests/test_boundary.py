@@ -40,7 +40,7 @@ def test_header_constants_match_binding(ga):
     src = open(HEADER).read()
     for name in ["ATTN_ABI_VERSION", "ATTN_HEAD_DIM", "ATTN_ROTARY_DIM", "ATTN_MAX_GROUP",
                  "ATTN_MAX_TOKENS", "ATTN_QBASE_ALIGN", "ATTN_MAX_SEQS", "ATTN_KERNEL_KV_PROLOGUE",
-                 "ATTN_KERNEL_MASK_PACK", "ATTN_KERNEL_ATTENTION"]:
+                 "ATTN_KERNEL_MASK_PACK", "ATTN_KERNEL_ATTENTION", "ATTN_KERNEL_WEIGHTS"]:
         m = re.search(rf"#define {name}\s+(\d+)", src)
         assert m and int(m.group(1)) == getattr(ga, name), name
     for name in ["ATTN_OK", "ATTN_ERR_NULL_ARG", "ATTN_ERR_GEOMETRY", "ATTN_ERR_RANGE",
@@ -240,3 +240,36 @@ def test_kv_cache_fp8_bytes(ga):
     rc, n = ga.attn_kv_cache_fp8_bytes(_geom(ga, n_q_heads=24, n_kv_heads=5))
     assert rc == ga.ATTN_ERR_GEOMETRY and n == 0
     assert ga.lib.attn_kv_cache_fp8_bytes(ctypes.byref(g), None) == ga.ATTN_ERR_NULL_ARG
+
+
+WEIGHT_REFUSALS = [
+    # (T, q_base, kind, mask, out, weights, expected)
+    (64, 0, 4, FAKE, FAKE, FAKE, "RANGE"),         # cache kinds have no weights variant
+    (256, 128, 5, FAKE, FAKE, FAKE, "RANGE"),
+    (64, 0, 7, None, FAKE, FAKE, "RANGE"),
+    (64, 0, -1, None, FAKE, FAKE, "RANGE"),
+    (64, 0, 0, None, FAKE, None, "NULL_ARG"),      # weights missing
+    (64, 0, 0, None, FAKE, FAKE + 8, "ALIGN"),     # weights misaligned
+    (64, 0, 2, None, FAKE, FAKE, "NULL_ARG"),      # masked without a mask
+    (64, 0, 0, None, None, FAKE, "NULL_ARG"),      # out missing
+    (300, 0, 0, None, FAKE, FAKE, "RANGE"),        # T > max_tokens
+    (200, 64, 1, None, FAKE, FAKE, "ALIGN"),       # q_base % 128
+]
+
+
+@pytest.mark.parametrize("case", WEIGHT_REFUSALS, ids=lambda c: f"{c[-1]}")
+def test_weights_refusals(ga, case):
+    T, qb, kind, mask, out, w, want = case
+    rc = ga.attn_validate_weights(_geom(ga), _inputs(ga, 256), T, qb, kind, mask, out, w)
+    assert rc == getattr(ga, "ATTN_ERR_" + want), (rc, ga.attn_status_string(rc))
+
+
+def test_weights_valid_and_empty(ga):
+    g, inp = _geom(ga), _inputs(ga, 256)
+    for T, qb, kind, mask in [(256, 0, 0, None), (256, 128, 1, None), (256, 0, 2, FAKE + 3), (100, 0, 3, None)]:
+        assert ga.attn_validate_weights(g, inp, T, qb, kind, mask, FAKE, FAKE) == ga.ATTN_OK
+    # an empty window needs no pointers at all
+    assert ga.attn_validate_weights(g, None, 0, 0, 0, None, None, None) == ga.ATTN_OK
+    assert ga.attn_validate_weights(g, None, 128, 128, 1, None, None, None) == ga.ATTN_OK
+    assert ga.lib.attn_validate_weights(None, None, 0, 0, 0, None, None, None) == ga.ATTN_ERR_NULL_ARG
+    assert ga.attn_prefill_weights(None, inp, 64, 0, 0, None, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG

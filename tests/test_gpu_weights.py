@@ -1,0 +1,157 @@
+"""GPU parity of the attention-weights entry point (the QSA kernel page,
+"What changed": the kernel also writes the normalised bf16 weights, which its
+golden checks) against the oracle's weights.
+
+Per element |gpu - oracle| <= 1e-2 + 1e-2 |oracle| (the output tolerance);
+the visibility pattern is bit-exact: every hidden key's weight is exactly 0.
+The pass's own output must equal the plain entry point's, bit for bit.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from gpu_util import DevProblem, bits_to_f32, make_ctx, run, to_bits  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_gqa_causal_amd  # noqa: F401
+    yield
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _kind(p):
+    if p.mask is not None:
+        return 2
+    if not p.causal:
+        return 3
+    return 1 if p.q_base else 0
+
+
+def _visible(p, rows):
+    """[n][T] visibility of the listed window rows, from its definition."""
+    j = np.arange(p.T)[None, :]
+    pos = (p.q_base + np.asarray(rows))[:, None]
+    vis = np.ones((len(rows), p.T), dtype=bool)
+    if p.causal:
+        vis &= j <= pos
+    if p.mask is not None:
+        vis &= np.asarray(p.mask)[np.asarray(rows)] != 0
+    return vis
+
+
+def _weights(ctx, p, rows=None):
+    """(out bits, the plain entry point's out bits, fp32 weights of `rows`)."""
+    dp = DevProblem(p)
+    out, w = ctx.prefill_weights(*dp.args(), kind=_kind(p), q_base=p.q_base, mask=dp.mask)
+    plain = run(ctx, dp)
+    torch.cuda.synchronize()
+    if rows is not None:
+        w = w[torch.as_tensor(np.asarray(rows, dtype=np.int64), device=w.device)]
+    return to_bits(out), to_bits(plain), bits_to_f32(to_bits(w))
+
+
+def _check(p, rows, got_w, want, label):
+    vis = _visible(p, rows)
+    ref = want["weights"]
+    assert got_w.shape == ref.shape
+    hidden = ~vis[:, None, :].repeat(p.n_q_heads, axis=1)
+    assert np.all(got_w[hidden] == 0.0), "a hidden key has a non-zero weight"
+    err = np.abs(got_w.astype(np.float64) - ref)
+    bound = 1e-2 + 1e-2 * np.abs(ref)
+    bad = int((~(err <= bound)).sum())
+    pos = ref > 1e-3
+    rel = float(np.max(err[pos] / ref[pos])) if pos.any() else 0.0
+    sums = got_w.astype(np.float64).sum(axis=2)
+    any_vis = vis.any(axis=1)
+    say(f"  {label}: bad={bad} of {ref.size}  worst rel (w>1e-3)={rel:.4f}  "
+        f"identical={np.mean(got_w == ref):.4f}  max |row sum - 1|="
+        f"{np.max(np.abs(sums[any_vis] - 1.0)) if any_vis.any() else 0.0:.4f}")
+    assert bad == 0
+    assert np.all(np.abs(sums[any_vis] - 1.0) <= 1e-2)
+    assert np.all(sums[~any_vis] == 0.0)
+
+
+CASES = [
+    ("s64", dict(T=64, n_q_heads=24, n_kv_heads=2, seed=20)),
+    ("s1", dict(T=1, n_q_heads=4, n_kv_heads=2, seed=21)),
+    ("s200_ragged", dict(T=200, n_q_heads=24, n_kv_heads=2, seed=22)),
+    ("s131_g4_odd", dict(T=131, n_q_heads=16, n_kv_heads=4, seed=23)),    # T % 4 != 0: 2-byte stores
+    ("prefix_t300_qb128", dict(T=300, n_q_heads=8, n_kv_heads=2, q_base=128, seed=24)),
+    ("masked_s300_b40", dict(T=300, n_q_heads=24, n_kv_heads=2, seed=25, mask_budget=40)),
+    ("masked_s257_b3", dict(T=257, n_q_heads=8, n_kv_heads=2, seed=26, mask_budget=3)),
+    ("bidir_s200", dict(T=200, n_q_heads=16, n_kv_heads=4, seed=27, causal=False)),
+    ("bidir_s97_g6", dict(T=97, n_q_heads=6, n_kv_heads=1, seed=28, causal=False)),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_weights_vs_oracle(orc, name, kw):
+    say(f"weights {name} {kw}")
+    p = synth.make_problem(name=name, **kw)
+    ctx = make_ctx(p)
+    out, plain, got_w = _weights(ctx, p)
+    ctx.close()
+    assert np.array_equal(out, plain), "the weights call changed the pass's output"
+    rows = np.arange(p.rows, dtype=np.int32)
+    want = orc.attention(p, rows=rows, want_weights=True, threads=8)
+    _check(p, rows, got_w, want, name)
+
+
+def test_weights_rows_with_no_visible_key(orc):
+    # A mask that hides every key from some rows: those rows' weights are all 0.
+    p = synth.make_problem(name="masked_empty_rows", T=160, n_q_heads=8, n_kv_heads=2, seed=29, mask_budget=16)
+    mask = np.array(p.mask, copy=True)
+    mask[5] = 0
+    mask[64:96] = 0
+    p.mask = mask
+    ctx = make_ctx(p)
+    out, plain, got_w = _weights(ctx, p)
+    ctx.close()
+    assert np.array_equal(out, plain)
+    assert np.all(got_w[5] == 0.0) and np.all(got_w[64:96] == 0.0)
+    want = orc.attention(p, rows=np.arange(p.rows, dtype=np.int32), want_weights=True, threads=8)
+    _check(p, np.arange(p.rows), got_w, want, "masked_empty_rows")
+
+
+@pytest.mark.parametrize("name", ["c1_dense_s2048", "c2_dense_s8192_g4"])
+def test_weights_workload_sampled(orc, name):
+    # The full-size workloads; the oracle computes sampled rows one by one.
+    say(f"weights workload {name}")
+    p = synth.config_problem(name)
+    r = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, p.rows - 1],
+                                     r.integers(0, p.rows, size=12)])).astype(np.int32)
+    ctx = make_ctx(p)
+    out, plain, got_w = _weights(ctx, p, rows)
+    ctx.close()
+    assert np.array_equal(out, plain)
+    want = orc.attention(p, rows=rows, want_weights=True, threads=8)
+    _check(p, rows, got_w, want, name)
+
+
+def test_weights_reuse_context_smaller_call(orc):
+    # Two calls on one context, the second smaller: nothing of the first leaks.
+    big = synth.make_problem(name="w_big", T=300, n_q_heads=8, n_kv_heads=2, seed=30)
+    small = synth.make_problem(name="w_small", T=70, n_q_heads=8, n_kv_heads=2, seed=31)
+    ctx = make_ctx(big)
+    _weights(ctx, big)
+    out, plain, got_w = _weights(ctx, small)
+    ctx.close()
+    assert np.array_equal(out, plain)
+    want = orc.attention(small, rows=np.arange(small.rows, dtype=np.int32), want_weights=True, threads=8)
+    _check(small, np.arange(small.rows), got_w, want, "reuse_small")
