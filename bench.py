@@ -103,6 +103,9 @@ def main():
                     help="as --cached, with the fp8 (e4m3 rows, fp32 row scales) cache "
                          "(attn_prefill_append_fp8): each step encodes the window's keys and "
                          "widens the whole cache before the attention kernel")
+    ap.add_argument("--weights", action="store_true",
+                    help="each step also writes the normalised bf16 attention weights [rows][Hq][T] "
+                         "(attn_prefill_weights)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -207,8 +210,18 @@ def main():
         append(zero_qg, k[:qb], v[:qb], wq, wk, cos, sin, qb, 0, cache)
         k_new, v_new = k[qb:], v[qb:]
 
+    wbuf = None
+    if args.weights:
+        if batch is not None or cache is not None:
+            raise SystemExit("--weights covers the single-sequence passes (gated, prefix, masked, bidirectional)")
+        wbuf = torch.empty((rows, p.n_q_heads, p.T), dtype=torch.bfloat16, device=dev)
+        wkind = 2 if mask is not None else 3 if not p.causal else 1 if p.q_base else 0
+
     def step():
-        if batch is not None:
+        if wbuf is not None:
+            ctx.prefill_weights(qg, k, v, wq, wk, cos, sin, kind=wkind, q_base=p.q_base, mask=mask, out=out,
+                                weights=wbuf, stream=stream)
+        elif batch is not None:
             ctx.prefill_gated_batch(qg, k, v, wq, wk, cos, sin, batch.lens, out=out, stream=stream)
         elif cache is not None:
             append(qg, k_new, v_new, wq, wk, cos, sin, p.T, p.q_base, cache, out=out, stream=stream)
@@ -239,6 +252,7 @@ def main():
     attn_ms, attn_n = ctx.read_timing(ga.ATTN_KERNEL_ATTENTION)
     pro_ms, pro_n = ctx.read_timing(ga.ATTN_KERNEL_KV_PROLOGUE)
     mp_ms, mp_n = ctx.read_timing(ga.ATTN_KERNEL_MASK_PACK)
+    w_ms, w_n = ctx.read_timing(ga.ATTN_KERNEL_WEIGHTS)
     ctx.set_timing(False)
     ms_per_step = total_ms / args.steps
     flops = batch.flops() if batch is not None else p.flops()
@@ -246,7 +260,8 @@ def main():
     attn_avg_ms = attn_ms / max(attn_n, 1)
     achieved = flops / (attn_avg_ms * 1e-3) / 1e12
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; attention {attn_avg_ms:.4f} ms, "
-        f"kv prologue {pro_ms / max(pro_n, 1):.4f} ms, mask pack {mp_ms / max(mp_n, 1):.4f} ms")
+        f"kv prologue {pro_ms / max(pro_n, 1):.4f} ms, mask pack {mp_ms / max(mp_n, 1):.4f} ms"
+        + (f", weights {w_ms / max(w_n, 1):.4f} ms" if w_n else ""))
 
     rec = {
         "metric": "gated causal attention prefill TFLOP/s and ms at S=8192, D=256 bf16",
@@ -266,15 +281,26 @@ def main():
                    "n_kv_heads": p.n_kv_heads, "head_dim": p.head_dim, "rotary_dim": p.rotary_dim,
                    "masked": p.mask is not None, "causal": p.causal,
                    "cached_prefix": bool(args.cached or args.fp8_cache), "fp8_cache": fp8,
+                   "weights": bool(args.weights),
                    "seed": synth.BATCH_CONFIGS[args.workload]["seed"] if batch is not None else p.seed,
                    "algorithmic_gflop": round(flops / 1e9, 3)},
         "kernels_ms": {"attention": round(attn_avg_ms, 5),
                        "kv_prologue": round(pro_ms / max(pro_n, 1), 5),
-                       "mask_pack": round(mp_ms / max(mp_n, 1), 5) if mp_n else None},
+                       "mask_pack": round(mp_ms / max(mp_n, 1), 5) if mp_n else None,
+                       "weights": round(w_ms / max(w_n, 1), 5) if w_n else None},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(args.workload)},
     }
+    if w_n:
+        # Weights kernel: bf16 weights written, plus the queries, keys and row
+        # statistics it reads once.
+        wbytes = (rows * p.n_q_heads * p.T * 2 + rows * p.n_q_heads * 256 * 2
+                  + p.n_kv_heads * p.T * 256 * 2 + rows * p.n_q_heads * 8)
+        w_gbs = wbytes / (w_ms / w_n * 1e-3) / 1e9
+        rec["weights_roofline"] = {"bound": "hbm", "achieved": round(w_gbs, 1), "peak": PEAK_HBM_GBS,
+                                   "unit": "GB/s", "frac": round(w_gbs / PEAK_HBM_GBS, 4),
+                                   "bytes_per_launch": wbytes}
     if batch is not None:
         rec["config"]["sequences"] = len(batch.seqs)
         rec["config"]["seq_lens"] = batch.lens

@@ -1245,78 +1245,133 @@ void attn_fwd8(AttnParams pk)
 // m_ih) log2(e)/16) / l_ih) with s the bf16-rounded score and (m, l) the
 // reference max and row sum the attention pass recorded; hidden keys give 0.
 // Every element is written (zeros for tiles past a row block's diagonal and
-// for tiles the mask hides from the whole block).  grid (ceil(S/32),
-// ceil(Hq/4)), 256 threads: wave w takes query head 4y + w, rows 32x ..
-// 32x+31.  K fragments are read straight from the prepared tiles in HBM
-// (their layout is the LDS layout of the attention kernel); the weight
-// stores bound the kernel.
+// for tiles the mask hides from the whole block).
+// grid (ceil(S/64), Hkv * n_hg), 512 threads, the attention kernel's work
+// split: wave w takes query head 4 hg + (w & 3) of the block's KV head (idle
+// past the group) and rows r0 + 32 (w >> 2) .. +31.  The eight waves stage
+// each key tile once in LDS (the prepared tiles already have the LDS layout;
+// the next tile's bytes wait in registers while the current one is used).
+// The weight stores bound the kernel: each wave stages WT_GROUP tiles of its
+// 32 rows and writes them as whole 128-byte row segments.
 // ---------------------------------------------------------------------------
+constexpr int WT_GROUP = 2;                          // tiles per staged group
+constexpr int WT_ROW = WT_GROUP * KT * 2 + 16;       // staging bytes per row (padded)
+constexpr int WT_SMEM = 2 * TILE_BYTES + 8 * 32 * WT_ROW;
+
 template <int MODE>   // 0 causal, 1 masked (causal and mask), 2 bidirectional
-__global__ __launch_bounds__(256) void attn_weights(AttnParams p, uint16_t *wout)
+__global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int h = blockIdx.y * 4 + wave;
-    if (h >= p.Hq)
-        return;                                          // no barriers below
+    __shared__ __attribute__((aligned(16))) char smem[WT_SMEM];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hw = wave & 3, blk = wave >> 2;
+    const int kvh = blockIdx.y / p.n_hg, hg = blockIdx.y - kvh * p.n_hg;
+    const int hq = 4 * hg + hw;                          // head within the KV group
+    const bool active = hq < p.G;
+    const int h = kvh * p.G + (active ? hq : 0);
     const int j = lane & 31, hh = lane >> 5;
-    const int r0 = blockIdx.x * 32, row = r0 + j;
-    const int kvh = h / p.G;
+    const int R0 = blockIdx.x * QW;                      // the block's first row
+    const int r0 = R0 + QB * blk;                        // this wave's rows r0 .. r0 + 31
+    char *stage = smem + 2 * TILE_BYTES + wave * 32 * WT_ROW;
+
     uint4 qf[16];
     load_queries1(p, r0, h, lane, qf);
-    const int rc = min(row, p.S - 1);
+    const int rc = min(r0 + j, p.S - 1);
     const float m = p.ml[((size_t)rc * p.Hq + h) * 2];
     const float lsum = p.ml[((size_t)rc * p.Hq + h) * 2 + 1];
     const float nb = (m == -INFINITY) ? 0.0f : m * -SCALE_LOG2;
     const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
-    const int pos0 = p.q_base + r0;                      // a multiple of 32
-    const int nvis = (MODE == 2 ? p.T - 1 : min(pos0 + 31, p.T - 1)) / KT + 1;
+    const int P0 = p.q_base + R0;                        // a multiple of 64
     const int ntiles = (p.T + KT - 1) / KT;
-    const int diag = pos0 / KT;
+    const int nvis = (MODE == 2 ? p.T - 1 : min(P0 + QW - 1, p.T - 1)) / KT + 1;   // the block's tiles
+    const int diag = (P0 + QB * blk) / KT;               // this wave's diagonal tile
     const uint32_t diag_vis = (j == 31) ? 0xffffffffu : ((2u << j) - 1u);
     const FragOffsets fo = frag_offsets(j, hh);
-    const bool vec = (p.T & 3) == 0;                     // 8-byte stores stay aligned
-    uint16_t *dst_row = wout + ((size_t)rc * p.Hq + h) * p.T + 4 * hh;
-    for (int t = 0; t < ntiles; ++t) {
-        uint32_t w[16];
-        if (t < nvis && (MODE != 1 || p.tilevis[(size_t)(r0 / QW) * p.W + t] != 0)) {
-            const char *kt = reinterpret_cast<const char *>(p.kp + ((size_t)kvh * (p.Tpad / KT) + t) * (KT * D));
-            f32x16 s;
+    const bool vec = (p.T & 7) == 0;                     // 16-byte stores stay aligned
+    const char *ktiles = reinterpret_cast<const char *>(p.kp + (size_t)kvh * (p.Tpad / KT) * (KT * D));
+
+    // Tiles the block computes: up to its diagonal, and (masked) visible to some row.
+    auto computed = [&](int t) {
+        return t < nvis && (MODE != 1 || p.tilevis[(size_t)(R0 / QW) * p.W + t] != 0);
+    };
+    auto next_computed = [&](int t) {
+        for (++t; t < nvis; ++t)
+            if (computed(t))
+                return t;
+        return ntiles;
+    };
+    uint4 k0 = {}, k1 = {};
+    int tnext = computed(0) ? 0 : next_computed(0);
+    if (tnext < ntiles) {
+        k0 = *reinterpret_cast<const uint4 *>(ktiles + (size_t)tnext * TILE_BYTES + 16 * tid);
+        k1 = *reinterpret_cast<const uint4 *>(ktiles + (size_t)tnext * TILE_BYTES + 8192 + 16 * tid);
+    }
+    int nbuf = 0;
+    // Write-out lane map: 8 lanes per row, 16 bytes (8 keys) each.
+    const int wr = lane >> 3, wc = lane & 7;
+    for (int t0 = 0; t0 < ntiles; t0 += WT_GROUP) {
 #pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kt + fo.k + 1024 * c);
-                const f32x16 z = {};
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8, qf[c]), c ? s : z, 0,
-                                                            0, 0);
-            }
-            if (MODE == 1)
-                hide_all(s, p.bits[(size_t)rc * p.W + t] >> (4 * hh));
-            else if (MODE == 0 && t >= diag)
-                hide_all(s, (t == diag ? diag_vis : 0u) >> (4 * hh));
-            // rbf, not the inline-asm round_op: the scores come from the MFMA
-            // builtin, and only a read the compiler sees gets the wait states
-            // that reading a matrix-core result requires.
+        for (int tl = 0; tl < WT_GROUP; ++tl) {
+            const int t = t0 + tl;
+            uint32_t w[16];
+            if (t == tnext) {                            // block-uniform
+                char *kb = smem + TILE_BYTES * nbuf;
+                *reinterpret_cast<uint4 *>(kb + 16 * tid) = k0;
+                *reinterpret_cast<uint4 *>(kb + 8192 + 16 * tid) = k1;
+                __syncthreads();                         // the tile is in place; the other buffer is free
+                tnext = next_computed(t);
+                if (tnext < ntiles) {
+                    k0 = *reinterpret_cast<const uint4 *>(ktiles + (size_t)tnext * TILE_BYTES + 16 * tid);
+                    k1 = *reinterpret_cast<const uint4 *>(ktiles + (size_t)tnext * TILE_BYTES + 8192 + 16 * tid);
+                }
+                f32x16 s;
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                w[e] = f2bf(__builtin_amdgcn_exp2f(__builtin_fmaf(rbf(s[e]), SCALE_LOG2, nb)) * inv);
-        } else {
+                for (int c = 0; c < 16; ++c) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + fo.k + 1024 * c);
+                    const f32x16 z = {};
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8, qf[c]), c ? s : z,
+                                                                0, 0, 0);
+                }
+                nbuf ^= 1;
+                if (MODE == 1)
+                    hide_all(s, p.bits[(size_t)rc * p.W + t] >> (4 * hh));
+                else if (MODE == 0 && t >= diag)
+                    hide_all(s, (t == diag ? diag_vis : 0u) >> (4 * hh));
+                // rbf, not the inline-asm round_op: the scores come from the
+                // MFMA builtin, and only a read the compiler sees gets the wait
+                // states that reading a matrix-core result requires.
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                w[e] = 0u;
-        }
-        if (row >= p.S)
-            continue;
-        uint16_t *dst = dst_row + (size_t)t * KT;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int key = t * KT + 8 * g + 4 * hh;
-            if (vec && key + 3 < p.T) {
-                *reinterpret_cast<uint2 *>(dst + 8 * g) =
-                    make_uint2(w[4 * g] | (w[4 * g + 1] << 16), w[4 * g + 2] | (w[4 * g + 3] << 16));
+                for (int e = 0; e < 16; ++e)
+                    w[e] = f2bf(__builtin_amdgcn_exp2f(__builtin_fmaf(rbf(s[e]), SCALE_LOG2, nb)) * inv);
             } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (key + r < p.T)
-                        dst[8 * g + r] = (uint16_t)w[4 * g + r];
+                for (int e = 0; e < 16; ++e)
+                    w[e] = 0u;
+            }
+            // Lane (j, hh) holds keys 8g + 4hh + r of row j: 8 bytes per g.
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<uint2 *>(stage + j * WT_ROW + (tl * KT + 8 * g + 4 * hh) * 2) =
+                    make_uint2(w[4 * g] | (w[4 * g + 1] << 16), w[4 * g + 2] | (w[4 * g + 3] << 16));
+        }
+        // The wave reads back only what it wrote: its own LDS accesses stay in
+        // order, and the compiler waits for the writes before these reads.
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int rr = 8 * it + wr;
+            const int row = r0 + rr;
+            const int key = t0 * KT + 8 * wc;
+            const uint4 v = *reinterpret_cast<const uint4 *>(stage + rr * WT_ROW + 16 * wc);
+            if (!active || row >= p.S || key >= p.T)
+                continue;
+            uint16_t *dst = wout + ((size_t)row * p.Hq + h) * p.T + key;
+            if (vec) {
+                *reinterpret_cast<uint4 *>(dst) = v;
+            } else {
+                const uint32_t words[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (key + q < p.T)
+                        dst[q] = (uint16_t)(words[q >> 1] >> (16 * (q & 1)));
             }
         }
     }
@@ -1418,13 +1473,13 @@ hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stre
 
 hipError_t launch_attn_weights(const AttnParams &p, AttnMode mode, uint16_t *weights, hipStream_t stream)
 {
-    const dim3 grid((p.S + 31) / 32, (p.Hq + 3) / 4);
+    const dim3 grid((p.S + QW - 1) / QW, p.Hkv * p.n_hg);
     if (mode == AttnMode::Masked)
-        hipLaunchKernelGGL(attn_weights<1>, grid, dim3(256), 0, stream, p, weights);
+        hipLaunchKernelGGL(attn_weights<1>, grid, dim3(512), 0, stream, p, weights);
     else if (mode == AttnMode::Bidirectional)
-        hipLaunchKernelGGL(attn_weights<2>, grid, dim3(256), 0, stream, p, weights);
+        hipLaunchKernelGGL(attn_weights<2>, grid, dim3(512), 0, stream, p, weights);
     else
-        hipLaunchKernelGGL(attn_weights<0>, grid, dim3(256), 0, stream, p, weights);
+        hipLaunchKernelGGL(attn_weights<0>, grid, dim3(512), 0, stream, p, weights);
     return hipGetLastError();
 }
 

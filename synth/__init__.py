@@ -313,6 +313,7 @@ CONFIGS = {
     "c4_masked_s8192": dict(T=8192, n_q_heads=24, n_kv_heads=2, q_base=0, seed=4, mask_budget=2048),
     "c5_bidir_s8192_g4": dict(T=8192, n_q_heads=16, n_kv_heads=4, q_base=0, seed=5, gate_sigma=2.0,
                               causal=False),
+    "c7_bidir_s2048": dict(T=2048, n_q_heads=24, n_kv_heads=2, q_base=0, seed=7, causal=False),
 }
 
 

@@ -128,7 +128,7 @@ def test_weights_rows_with_no_visible_key(orc):
     _check(p, np.arange(p.rows), got_w, want, "masked_empty_rows")
 
 
-@pytest.mark.parametrize("name", ["c1_dense_s2048", "c2_dense_s8192_g4"])
+@pytest.mark.parametrize("name", ["c1_dense_s2048", "c2_dense_s8192_g4", "c7_bidir_s2048"])
 def test_weights_workload_sampled(orc, name):
     # The full-size workloads; the oracle computes sampled rows one by one.
     say(f"weights workload {name}")
