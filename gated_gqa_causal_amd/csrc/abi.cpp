@@ -335,7 +335,7 @@ int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kin
     }
     if (weights) {
         Timer tm(ctx, s, ATTN_KERNEL_WEIGHTS);
-        if (ga::launch_attn_weights(ap, mode, static_cast<uint16_t *>(weights), s) != hipSuccess)
+        if (ga::launch_attn_weights(ap, mode, static_cast<uint16_t *>(weights), ctx->num_cus, s) != hipSuccess)
             return ATTN_ERR_LAUNCH;
         tm.stop();
     }

@@ -78,7 +78,8 @@ hipError_t launch_kv_widen(const KvWidenParams &p, int ntiles, int Hkv, hipStrea
 hipError_t launch_mask_pack(const MaskPackParams &p, int nrb, hipStream_t stream);
 enum class AttnMode { Causal, Masked, Bidirectional };
 hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stream);
-hipError_t launch_attn_weights(const AttnParams &p, AttnMode mode, uint16_t *weights, hipStream_t stream);
+hipError_t launch_attn_weights(const AttnParams &p, AttnMode mode, uint16_t *weights, int num_cus,
+                               hipStream_t stream);
 hipError_t launch_kp_unpack(const uint16_t *kp, int Tpad, int T, int Hkv, uint16_t *out, hipStream_t stream);
 hipError_t launch_mfma_clock_probe(int iters, int n_wg, long long *rec, float *sink, hipStream_t stream);
 hipError_t launch_q_prologue_debug(const AttnParams &p, uint16_t *qp, hipStream_t stream);

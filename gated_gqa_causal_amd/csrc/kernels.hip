@@ -36,6 +36,7 @@
 // [0..3, 8..11, 4..7, 12..15], matching the accumulator rows a lane holds.
 
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stdint.h>
 
 #include "kernels.h"
@@ -1246,7 +1247,7 @@ void attn_fwd8(AttnParams pk)
 // reference max and row sum the attention pass recorded; hidden keys give 0.
 // Every element is written (zeros for tiles past a row block's diagonal and
 // for tiles the mask hides from the whole block).
-// grid (ceil(S/64), Hkv * n_hg), 512 threads, the attention kernel's work
+// grid (ceil(S/64), Hkv * n_hg, key splits), 512 threads, the attention kernel's work
 // split: wave w takes query head 4 hg + (w & 3) of the block's KV head (idle
 // past the group) and rows r0 + 32 (w >> 2) .. +31.  The eight waves stage
 // each key tile once in LDS (the prepared tiles already have the LDS layout;
@@ -1257,6 +1258,9 @@ void attn_fwd8(AttnParams pk)
 constexpr int WT_GROUP = 2;                          // tiles per staged group
 constexpr int WT_ROW = WT_GROUP * KT * 2 + 16;       // staging bytes per row (padded)
 constexpr int WT_SMEM = 2 * TILE_BYTES + 8 * 32 * WT_ROW;
+#ifndef WT_ROTATE
+#define WT_ROTATE 1
+#endif
 
 template <int MODE>   // 0 causal, 1 masked (causal and mask), 2 bidirectional
 __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout)
@@ -1289,39 +1293,57 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
     const bool vec = (p.T & 7) == 0;                     // 16-byte stores stay aligned
     const char *ktiles = reinterpret_cast<const char *>(p.kp + (size_t)kvh * (p.Tpad / KT) * (KT * D));
 
+    // Key range: blockIdx.z takes groups [g_begin, g_begin + ng) of WT_GROUP
+    // tiles, walked from a block-dependent starting group so that blocks
+    // writing at the same time spread over the address space.
+    const int ngroups_all = (ntiles + WT_GROUP - 1) / WT_GROUP;
+    const int gper = (ngroups_all + gridDim.z - 1) / gridDim.z;
+    const int g_begin = blockIdx.z * gper;
+    const int ng = max(min(gper, ngroups_all - g_begin), 0);
+    const int rot = (WT_ROTATE && ng > 0) ? (int)((blockIdx.x * 5u + blockIdx.y * 3u) % (unsigned)ng) : 0;
+    const int nq = ng * WT_GROUP;                        // walk positions
+    auto tile_of = [&](int q) {
+        int gg = q / WT_GROUP + rot;
+        gg = gg >= ng ? gg - ng : gg;
+        return (g_begin + gg) * WT_GROUP + q % WT_GROUP;
+    };
     // Tiles the block computes: up to its diagonal, and (masked) visible to some row.
     auto computed = [&](int t) {
         return t < nvis && (MODE != 1 || p.tilevis[(size_t)(R0 / QW) * p.W + t] != 0);
     };
-    auto next_computed = [&](int t) {
-        for (++t; t < nvis; ++t)
-            if (computed(t))
-                return t;
-        return ntiles;
+    auto next_computed = [&](int q) {
+        for (++q; q < nq; ++q)
+            if (computed(tile_of(q)))
+                return q;
+        return nq;
     };
     uint4 k0 = {}, k1 = {};
-    int tnext = computed(0) ? 0 : next_computed(0);
-    if (tnext < ntiles) {
-        k0 = *reinterpret_cast<const uint4 *>(ktiles + (size_t)tnext * TILE_BYTES + 16 * tid);
-        k1 = *reinterpret_cast<const uint4 *>(ktiles + (size_t)tnext * TILE_BYTES + 8192 + 16 * tid);
+    int qnext = next_computed(-1);
+    if (qnext < nq) {
+        const char *src = ktiles + (size_t)tile_of(qnext) * TILE_BYTES;
+        k0 = *reinterpret_cast<const uint4 *>(src + 16 * tid);
+        k1 = *reinterpret_cast<const uint4 *>(src + 8192 + 16 * tid);
     }
     int nbuf = 0;
     // Write-out lane map: 8 lanes per row, 16 bytes (8 keys) each.
     const int wr = lane >> 3, wc = lane & 7;
-    for (int t0 = 0; t0 < ntiles; t0 += WT_GROUP) {
+    for (int gq = 0; gq < ng; ++gq) {
+        const int t0 = tile_of(gq * WT_GROUP);
 #pragma unroll
         for (int tl = 0; tl < WT_GROUP; ++tl) {
+            const int q = gq * WT_GROUP + tl;
             const int t = t0 + tl;
             uint32_t w[16];
-            if (t == tnext) {                            // block-uniform
+            if (q == qnext) {                            // block-uniform
                 char *kb = smem + TILE_BYTES * nbuf;
                 *reinterpret_cast<uint4 *>(kb + 16 * tid) = k0;
                 *reinterpret_cast<uint4 *>(kb + 8192 + 16 * tid) = k1;
                 __syncthreads();                         // the tile is in place; the other buffer is free
-                tnext = next_computed(t);
-                if (tnext < ntiles) {
-                    k0 = *reinterpret_cast<const uint4 *>(ktiles + (size_t)tnext * TILE_BYTES + 16 * tid);
-                    k1 = *reinterpret_cast<const uint4 *>(ktiles + (size_t)tnext * TILE_BYTES + 8192 + 16 * tid);
+                qnext = next_computed(q);
+                if (qnext < nq) {
+                    const char *src = ktiles + (size_t)tile_of(qnext) * TILE_BYTES;
+                    k0 = *reinterpret_cast<const uint4 *>(src + 16 * tid);
+                    k1 = *reinterpret_cast<const uint4 *>(src + 8192 + 16 * tid);
                 }
                 f32x16 s;
 #pragma unroll
@@ -1471,9 +1493,16 @@ hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stre
     return hipGetLastError();
 }
 
-hipError_t launch_attn_weights(const AttnParams &p, AttnMode mode, uint16_t *weights, hipStream_t stream)
+hipError_t launch_attn_weights(const AttnParams &p, AttnMode mode, uint16_t *weights, int num_cus,
+                               hipStream_t stream)
 {
-    const dim3 grid((p.S + QW - 1) / QW, p.Hkv * p.n_hg);
+    // Split the keys over blockIdx.z until there are about two workgroups per
+    // compute unit (two fit its LDS), keeping at least 16 tiles per split.
+    const int blocks = ((p.S + QW - 1) / QW) * p.Hkv * p.n_hg;
+    const int groups = ((p.T + KT - 1) / KT + WT_GROUP - 1) / WT_GROUP;
+    int nz = (2 * num_cus + blocks - 1) / blocks;
+    nz = std::max(1, std::min(nz, groups / (16 / WT_GROUP)));
+    const dim3 grid((p.S + QW - 1) / QW, p.Hkv * p.n_hg, nz);
     if (mode == AttnMode::Masked)
         hipLaunchKernelGGL(attn_weights<1>, grid, dim3(512), 0, stream, p, weights);
     else if (mode == AttnMode::Bidirectional)
