@@ -177,6 +177,44 @@ def test_append_chunks_equal_full_pass(T, chunks, Hq, Hkv):
     assert np.array_equal(got, want)
 
 
+def test_branches_continue_a_shared_prefix_cache():
+    """Branches continued from one prefix cache (each call prepares its own new
+    keys over the previous branch's) give, bit for bit, one pass over prefix +
+    branch, in any order and repeated; bf16 and fp8 caches."""
+    P, lens, Hq, Hkv = 256, [1, 200, 37, 128], 16, 4
+    Tmax = P + max(lens)
+    say(f"shared prefix P={P} branches {lens}")
+    A = synth.make_problem(T=Tmax, n_q_heads=Hq, n_kv_heads=Hkv, seed=50)
+    da = DevProblem(A)
+    dbs = [DevProblem(synth.make_problem(T=Tmax, n_q_heads=Hq, n_kv_heads=Hkv, seed=60 + i))
+           for i in range(len(lens))]
+    ctx = make_ctx(A)
+
+    def tokens(i):
+        T = P + lens[i]
+        cat = lambda x, y: torch.cat([x[:P], y[P:T]]).contiguous()
+        return cat(da.qg, dbs[i].qg), cat(da.k, dbs[i].k), cat(da.v, dbs[i].v), T
+
+    for fp8 in (False, True):
+        want = []
+        for i in range(len(lens)):
+            qg, k, v, T = tokens(i)
+            if fp8:
+                fresh = ctx.kv_cache_fp8()
+                full = ctx.prefill_append_fp8(qg, k, v, da.wq, da.wk, da.cos, da.sin, T, 0, fresh)
+            else:
+                full = ctx.prefill_gated(qg, k, v, da.wq, da.wk, da.cos, da.sin)
+            want.append(to_bits(full)[P:])
+        cache = ctx.kv_cache_fp8() if fp8 else ctx.kv_cache()
+        append = ctx.prefill_append_fp8 if fp8 else ctx.prefill_append
+        append(da.qg[:P], da.k[:P], da.v[:P], da.wq, da.wk, da.cos, da.sin, P, 0, cache)
+        for i in [2, 0, 3, 1, 2, 0]:
+            qg, k, v, T = tokens(i)
+            got = to_bits(append(qg[P:], k[P:], v[P:], da.wq, da.wk, da.cos, da.sin, T, P, cache))
+            assert np.array_equal(got, want[i]), f"branch {i} (fp8={fp8})"
+    ctx.close()
+
+
 def test_append_window_vs_oracle(orc):
     """The last appended chunk against the oracle's prefix window."""
     say("append window vs oracle")
