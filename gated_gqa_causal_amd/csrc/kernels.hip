@@ -1255,7 +1255,10 @@ void attn_fwd8(AttnParams pk)
 // The weight stores bound the kernel: each wave stages WT_GROUP tiles of its
 // 32 rows and writes them as whole 128-byte row segments.
 // ---------------------------------------------------------------------------
-constexpr int WT_GROUP = 2;                          // tiles per staged group
+#ifndef WT_GROUP_TILES
+#define WT_GROUP_TILES 2
+#endif
+constexpr int WT_GROUP = WT_GROUP_TILES;             // tiles per staged group
 constexpr int WT_ROW = WT_GROUP * KT * 2 + 16;       // staging bytes per row (padded)
 constexpr int WT_SMEM = 2 * TILE_BYTES + 8 * 32 * WT_ROW;
 #ifndef WT_ROTATE
@@ -1325,8 +1328,9 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
         k1 = *reinterpret_cast<const uint4 *>(src + 8192 + 16 * tid);
     }
     int nbuf = 0;
-    // Write-out lane map: 8 lanes per row, 16 bytes (8 keys) each.
-    const int wr = lane >> 3, wc = lane & 7;
+    // Write-out lane map: WT_LPR lanes per row, 16 bytes (8 keys) each.
+    constexpr int WT_LPR = WT_GROUP * KT * 2 / 16, WT_RPI = 64 / WT_LPR;
+    const int wr = lane / WT_LPR, wc = lane % WT_LPR;
     for (int gq = 0; gq < ng; ++gq) {
         const int t0 = tile_of(gq * WT_GROUP);
 #pragma unroll
@@ -1378,8 +1382,8 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
         // The wave reads back only what it wrote: its own LDS accesses stay in
         // order, and the compiler waits for the writes before these reads.
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int rr = 8 * it + wr;
+        for (int it = 0; it < 32 / WT_RPI; ++it) {
+            const int rr = WT_RPI * it + wr;
             const int row = r0 + rr;
             const int key = t0 * KT + 8 * wc;
             const uint4 v = *reinterpret_cast<const uint4 *>(stage + rr * WT_ROW + 16 * wc);
