@@ -43,6 +43,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0         # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attention.json")
+TRAFFIC_WEIGHTS_FILE = os.path.join(ROOT, "profiles", "traffic_weights.json")
 KERNEL_SOURCE = os.path.join(ROOT, "gated_gqa_causal_amd", "csrc", "kernels.hip")
 
 
@@ -55,11 +56,12 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed PMC summary, or None
-    when the kernel source changed since the counters were taken."""
+def measured_traffic(workload: str, path: str = TRAFFIC_FILE):
+    """HBM bytes per launch of a kernel (the attention kernel, or the weights
+    kernel) from a committed PMC summary, or None when the kernel source changed
+    since the counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -300,6 +302,7 @@ def main():
         w_gbs = wbytes / (w_ms / w_n * 1e-3) / 1e9
         rec["weights_roofline"] = {"bound": "hbm", "achieved": round(w_gbs, 1), "peak": PEAK_HBM_GBS,
                                    "unit": "GB/s", "frac": round(w_gbs / PEAK_HBM_GBS, 4),
+                                   "traffic": measured_traffic(args.workload, TRAFFIC_WEIGHTS_FILE),
                                    "bytes_per_launch": wbytes}
     if batch is not None:
         rec["config"]["sequences"] = len(batch.seqs)

@@ -1261,6 +1261,12 @@ void attn_fwd8(AttnParams pk)
 constexpr int WT_GROUP = WT_GROUP_TILES;             // tiles per staged group
 constexpr int WT_ROW = WT_GROUP * KT * 2 + 16;       // staging bytes per row (padded)
 constexpr int WT_SMEM = 2 * TILE_BYTES + 8 * 32 * WT_ROW;
+#ifndef WT_XCD
+#define WT_XCD 1
+#endif
+#ifndef WT_NT
+#define WT_NT 1
+#endif
 #ifndef WT_ROTATE
 #define WT_ROTATE 1
 #endif
@@ -1271,12 +1277,24 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
     __shared__ __attribute__((aligned(16))) char smem[WT_SMEM];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hw = wave & 3, blk = wave >> 2;
-    const int kvh = blockIdx.y / p.n_hg, hg = blockIdx.y - kvh * p.n_hg;
+    // Workgroups go to the eight XCDs in turn (linear id mod 8), each XCD with
+    // its own L2.  Renumber so that XCD x takes the x-th eighth of the work,
+    // ordered row block fastest: its blocks share a KV head and so its key tiles.
+    int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+    if (WT_XCD) {
+        const unsigned nb = gridDim.x * gridDim.y * gridDim.z, per = nb / 8;
+        const unsigned b = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+        const unsigned wk = (b < per * 8) ? (b % 8) * per + b / 8 : b;
+        bx = (int)(wk % gridDim.x);
+        by = (int)((wk / gridDim.x) % gridDim.y);
+        bz = (int)(wk / (gridDim.x * gridDim.y));
+    }
+    const int kvh = by / p.n_hg, hg = by - kvh * p.n_hg;
     const int hq = 4 * hg + hw;                          // head within the KV group
     const bool active = hq < p.G;
     const int h = kvh * p.G + (active ? hq : 0);
     const int j = lane & 31, hh = lane >> 5;
-    const int R0 = blockIdx.x * QW;                      // the block's first row
+    const int R0 = bx * QW;                              // the block's first row
     const int r0 = R0 + QB * blk;                        // this wave's rows r0 .. r0 + 31
     char *stage = smem + 2 * TILE_BYTES + wave * 32 * WT_ROW;
 
@@ -1301,9 +1319,9 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
     // writing at the same time spread over the address space.
     const int ngroups_all = (ntiles + WT_GROUP - 1) / WT_GROUP;
     const int gper = (ngroups_all + gridDim.z - 1) / gridDim.z;
-    const int g_begin = blockIdx.z * gper;
+    const int g_begin = bz * gper;
     const int ng = max(min(gper, ngroups_all - g_begin), 0);
-    const int rot = (WT_ROTATE && ng > 0) ? (int)((blockIdx.x * 5u + blockIdx.y * 3u) % (unsigned)ng) : 0;
+    const int rot = (WT_ROTATE && ng > 0) ? (int)(((unsigned)bx * 5u + (unsigned)by * 3u) % (unsigned)ng) : 0;
     const int nq = ng * WT_GROUP;                        // walk positions
     auto tile_of = [&](int q) {
         int gg = q / WT_GROUP + rot;
@@ -1391,7 +1409,13 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
                 continue;
             uint16_t *dst = wout + ((size_t)row * p.Hq + h) * p.T + key;
             if (vec) {
+#if WT_NT
+                // Streaming store: the weights are not read again, and kept out
+                // of L2 they leave it to the key tiles the other blocks reuse.
+                __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(dst));
+#else
                 *reinterpret_cast<uint4 *>(dst) = v;
+#endif
             } else {
                 const uint32_t words[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
