@@ -77,15 +77,34 @@ def cpu_baseline(p, rows_target: int, threads: int):
     stride = max(1, p.rows // rows_target)
     rows = np.arange(p.rows - 1, -1, -stride, dtype=np.int32)[::-1].copy()
     kp = orc.prepare_keys(p)
+
+    def pair_flops(rr):
+        # 4 D FLOPs per visible (row, key, query head), as in the GPU's figure.
+        pos = p.q_base + rr.astype(np.int64)
+        if p.mask is not None:
+            m = np.asarray(p.mask)[rr] != 0
+            vis = (m & (np.arange(p.T)[None, :] <= pos[:, None])).sum()
+        elif not p.causal:
+            vis = rr.size * p.T
+        else:
+            vis = (pos + 1).sum()
+        return 4.0 * p.head_dim * p.n_q_heads * float(vis)
+
     t0 = time.perf_counter()
     orc.attention(p, rows=rows, kp=kp, threads=threads)
     dt = time.perf_counter() - t0
-    pos = p.q_base + rows.astype(np.int64)
-    flops = 4.0 * p.head_dim * p.n_q_heads * float((pos + 1).sum())
+    flops = pair_flops(rows)
+    # One thread over a fixed subset (the last 64 rows, all heads).
+    last = np.arange(max(0, p.rows - 64), p.rows, dtype=np.int32)
+    t1 = time.perf_counter()
+    orc.attention(p, rows=last, kp=kp, threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows.size} query rows (every {stride}th, ending at the last row) x "
                       f"{p.n_q_heads} heads of {p.name}; keys prepared outside the timing; "
-                      f"{dt:.2f} s wall, {flops / 1e9:.1f} GFLOP"}
+                      f"{dt:.2f} s wall, {flops / 1e9:.1f} GFLOP",
+            "one_thread": {"value": pair_flops(last) / dt1 / 1e12, "unit": "TFLOP/s",
+                           "sample": f"the last {last.size} rows x {p.n_q_heads} heads, {dt1:.2f} s wall"}}
 
 
 def main():
@@ -108,6 +127,8 @@ def main():
     ap.add_argument("--weights", action="store_true",
                     help="each step also writes the normalised bf16 attention weights [rows][Hq][T] "
                          "(attn_prefill_weights)")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MiB scrub buffer between timed steps (outside each step's events)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -242,15 +263,30 @@ def main():
     log(f"warmup {args.warmup} done")
 
     ctx.set_timing(True)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    # One event between consecutive steps (per-step spread); with --cold a
+    # 512 MiB scrub write runs between steps, outside each step's event pair.
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
+    if scrub is None:
+        marks = [ev() for _ in range(args.steps + 1)]
+        marks[0].record(stream)
+        for i in range(args.steps):
+            step()
+            marks[i + 1].record(stream)
+        torch.cuda.synchronize()
+        total_ms = marks[0].elapsed_time(marks[-1])
+        step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+    else:
+        pairs = [(ev(), ev()) for _ in range(args.steps)]
+        for i in range(args.steps):
+            scrub.fill_(i & 255)
+            pairs[i][0].record(stream)
+            step()
+            pairs[i][1].record(stream)
+        torch.cuda.synchronize()
+        step_ms = [a.elapsed_time(b) for a, b in pairs]
+        total_ms = sum(step_ms)
     attn_ms, attn_n = ctx.read_timing(ga.ATTN_KERNEL_ATTENTION)
     pro_ms, pro_n = ctx.read_timing(ga.ATTN_KERNEL_KV_PROLOGUE)
     mp_ms, mp_n = ctx.read_timing(ga.ATTN_KERNEL_MASK_PACK)
@@ -286,6 +322,10 @@ def main():
                    "weights": bool(args.weights),
                    "seed": synth.BATCH_CONFIGS[args.workload]["seed"] if batch is not None else p.seed,
                    "algorithmic_gflop": round(flops / 1e9, 3)},
+        "step_ms": {"median": round(float(np.median(step_ms)), 5),
+                    "p10": round(float(np.percentile(step_ms, 10)), 5),
+                    "p90": round(float(np.percentile(step_ms, 90)), 5),
+                    "caches": "cold (512 MiB scrub between steps)" if args.cold else "warm"},
         "kernels_ms": {"attention": round(attn_avg_ms, 5),
                        "kv_prologue": round(pro_ms / max(pro_n, 1), 5),
                        "mask_pack": round(mp_ms / max(mp_n, 1), 5) if mp_n else None,
