@@ -96,6 +96,8 @@ CASES = [
     ("masked_s257_b3", dict(T=257, n_q_heads=8, n_kv_heads=2, seed=26, mask_budget=3)),
     ("bidir_s200", dict(T=200, n_q_heads=16, n_kv_heads=4, seed=27, causal=False)),
     ("bidir_s97_g6", dict(T=97, n_q_heads=6, n_kv_heads=1, seed=28, causal=False)),
+    ("prefix_t301_qb128_g1", dict(T=301, n_q_heads=2, n_kv_heads=2, q_base=128, seed=32)),   # ragged T
+    ("s100_g16", dict(T=100, n_q_heads=32, n_kv_heads=2, seed=33)),
 ]
 
 
