@@ -68,6 +68,12 @@ def _load():
     if not os.path.exists(LIBPATH):
         raise ImportError(f"{LIBPATH} is not built; run __graft_entry__.build() "
                           "(the HIP library is required, there is no fallback)")
+    # torch first: its HIP runtime (loaded under the unversioned file name)
+    # then satisfies the library's libamdhip64.so.7 dependency by soname.
+    # Loaded the other way round, the process would hold two HIP runtimes, and
+    # the library's device calls would go to one that does not own torch's
+    # device memory and streams (ctx creation then fails on a GPU).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIBPATH)
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
     sig = {

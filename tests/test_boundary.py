@@ -273,3 +273,20 @@ def test_weights_valid_and_empty(ga):
     assert ga.attn_validate_weights(g, None, 128, 128, 1, None, None, None) == ga.ATTN_OK
     assert ga.lib.attn_validate_weights(None, None, 0, 0, 0, None, None, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_prefill_weights(None, inp, 64, 0, 0, None, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
+
+
+def test_one_hip_runtime_in_the_process():
+    """Importing the binding (before anything else imports torch) leaves one
+    HIP runtime mapped: the library must share torch's, whose device memory
+    and streams it is handed.  Two runtimes in one process make the library's
+    device calls fail on a GPU."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import gated_gqa_causal_amd\n"
+            "import torch\n"
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(paths)); print(sorted(paths))\n") % ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.splitlines()[0] == "1", r.stdout
