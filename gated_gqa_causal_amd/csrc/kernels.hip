@@ -371,20 +371,32 @@ __global__ __launch_bounds__(256) void mask_pack(MaskPackParams p)
     p.tilevis[(size_t)rb * p.W + w] = any ? 1 : 0;
 }
 
-__device__ __forceinline__ void load_queries1(const AttnParams &p, int r0, int h, int lane, uint4 (&qf)[16]);
+__device__ __forceinline__ void load_queries1(const AttnParams &p, int r0, int h, int lane, uint4 (&qf)[16],
+                                              const float *wq1);
+
+// (1 + w_q) in fp32 for the query prologue, in LDS; the caller's barrier
+// publishes it.  Needs at least D threads.
+__device__ __forceinline__ void fill_wq1(float *wq1, const uint16_t *wq)
+{
+    if (threadIdx.x < D)
+        wq1[threadIdx.x] = 1.0f + bf2f(wq[threadIdx.x]);
+}
 
 // Debug: prepared queries in a plain [rows][Hq][D] layout.
 // grid (ceil(S/64), ceil(Hq/4)), 256 threads: wave = one head, 64 rows.
 __global__ __launch_bounds__(256) void q_prologue_debug(AttnParams p, uint16_t *qp)
 {
+    __shared__ __align__(16) float wq1[D];
+    fill_wq1(wq1, p.wq);
+    __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int h = blockIdx.y * 4 + wave;
     if (h >= p.Hq)
         return;
     const int r0 = blockIdx.x * 64;
     uint4 qf[2][16];
-    load_queries1(p, r0, h, lane, qf[0]);
-    load_queries1(p, r0 + 32, h, lane, qf[1]);
+    load_queries1(p, r0, h, lane, qf[0], wq1);
+    load_queries1(p, r0 + 32, h, lane, qf[1], wq1);
     const int j = lane & 31, hh = lane >> 5;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -750,9 +762,16 @@ constexpr int SMEM8 = (8 * TILE_BYTES > 8 * QB * EP_STRIDE) ? 8 * TILE_BYTES : 8
 // dimension order, the same chain as the key prologue) and partial RoPE, and
 // leaves the MFMA B-operand fragments in qf[c]: lane (j = lane & 31, hh =
 // lane >> 5) holds dims 16c + 8hh .. +7 of row r0 + j.  Rows at or past S are
-// zero.  v_permlane32_swap of a word with itself gives every lane both halves
-// of its row for the sum of squares.
-__device__ __forceinline__ void load_queries1(const AttnParams &p, int r0, int h, int lane, uint4 (&qf)[16])
+// zero.  wq1 is (1 + w_q) in fp32, in LDS (the same fp32 sum the plain
+// definition forms per element).
+// The sum of squares runs on the lanes that hold the first 8 dims of each
+// 16-dim chunk (hh = 0): each takes its partner lane's 8 (lane ^ 32, through
+// ds_bpermute, which leaves the fragments in place) and chains the 16 in
+// dimension order.  The hh = 1 lanes run the same instructions on the two
+// halves swapped and then take their partner's sum, so both lanes of a row
+// hold the one ascending chain.
+__device__ __forceinline__ void load_queries1(const AttnParams &p, int r0, int h, int lane, uint4 (&qf)[16],
+                                              const float *wq1)
 {
     const int j = lane & 31, hh = lane >> 5;
     const int row = r0 + j;
@@ -761,72 +780,104 @@ __device__ __forceinline__ void load_queries1(const AttnParams &p, int r0, int h
 #pragma unroll
     for (int c = 0; c < 16; ++c)
         qf[c] = *reinterpret_cast<const uint4 *>(src + 16 * c + 8 * hh);
+    const int partner = (lane ^ 32) << 2;
+    auto one = [&](uint32_t w) { return (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)w); };
+    auto from_partner = [&](const uint4 &u) { return make_uint4(one(u.x), one(u.y), one(u.z), one(u.w)); };
     float ss = 0.0f;
+    // The partner's words are fetched one chunk ahead (the fences keep the
+    // compiler from fetching them all up front, which would hold 64 more
+    // registers).
+    uint4 other = from_partner(qf[0]);
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-        uint32_t a[4], bq[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t w = q == 0 ? qf[c].x : q == 1 ? qf[c].y : q == 2 ? qf[c].z : qf[c].w;
-            const auto r = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-            a[q] = r[0];
-            bq[q] = r[1];
-        }
-        const uint4 first = make_uint4(a[0], a[1], a[2], a[3]);      // dims 16c .. 16c+7
-        const uint4 second = make_uint4(bq[0], bq[1], bq[2], bq[3]); // dims 16c+8 .. 16c+15
+        uint4 next = other;
+        if (c + 1 < 16)
+            next = from_partner(qf[c + 1]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const float x = word_f(first, t);
+            const float x = word_f(qf[c], t);
             ss += x * x;
         }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const float x = word_f(second, t);
+            const float x = word_f(other, t);
             ss += x * x;
         }
+        __builtin_amdgcn_sched_barrier(0);
+        other = next;
+    }
+    {
+        // lanes hh = 1 take the chain of lane (j, 0): the first result of a
+        // swap fed the same value twice is the lower-half lane's value.
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+        ss = __uint_as_float(r[0]);
     }
     const float rr = 1.0f / sqrtf(ss / (float)D + p.eps);
+    // (1 + w) of a chunk's 8 dims, read one chunk ahead (fenced like the
+    // partner words above).
+    struct W8 {
+        float4 a, b;
+        __device__ float operator[](int t) const
+        {
+            return t == 0 ? a.x : t == 1 ? a.y : t == 2 ? a.z : t == 3 ? a.w
+                 : t == 4 ? b.x : t == 5 ? b.y : t == 6 ? b.z : b.w;
+        }
+    };
+    auto w_of = [&](int c) {
+        return W8{*reinterpret_cast<const float4 *>(wq1 + 16 * c + 8 * hh),
+                  *reinterpret_cast<const float4 *>(wq1 + 16 * c + 8 * hh + 4)};
+    };
+    // The norm unpacks the fragment words again: hidden from the compiler,
+    // which would otherwise keep the chain's 128 unpacked values alive until
+    // here (more registers than a wave has).
+    auto fresh = [](const uint4 &u) {
+        u32x4 v = {u.x, u.y, u.z, u.w};
+        asm volatile("" : "+v"(v));
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    };
+    W8 wv = w_of(4);
 #pragma unroll
     for (int c = 4; c < 16; ++c) {
-        const uint4 wv = *reinterpret_cast<const uint4 *>(p.wq + 16 * c + 8 * hh);
+        const W8 wn = w_of(c + 1 < 16 ? c + 1 : 0);
+        const uint4 qv = fresh(qf[c]);
         float n[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-            n[t] = (word_f(qf[c], t) * rr) * (1.0f + word_f(wv, t));
+            n[t] = (word_f(qv, t) * rr) * wv[t];
         qf[c] = make_uint4(pack2(n[0], n[1]), pack2(n[2], n[3]), pack2(n[4], n[5]), pack2(n[6], n[7]));
+        __builtin_amdgcn_sched_barrier(0);
+        wv = wn;
     }
-    {
-        float n[4][8];
+    // Rotary dims 0..63: chunks c and c + 2 hold the pairs (d, d + 32).
+    const int pos = p.q_base + (ok ? row : 0);
+    const float *ct = p.cos_tab + (size_t)pos * HALF_R;
+    const float *st = p.sin_tab + (size_t)pos * HALF_R;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint4 wv = *reinterpret_cast<const uint4 *>(p.wq + 16 * c + 8 * hh);
+    for (int c = 0; c < 2; ++c) {
+        const float4 c0 = *reinterpret_cast<const float4 *>(ct + 16 * c + 8 * hh);
+        const float4 c1 = *reinterpret_cast<const float4 *>(ct + 16 * c + 8 * hh + 4);
+        const float4 s0 = *reinterpret_cast<const float4 *>(st + 16 * c + 8 * hh);
+        const float4 s1 = *reinterpret_cast<const float4 *>(st + 16 * c + 8 * hh + 4);
+        const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const W8 wa = w_of(c), wb = w_of(c + 2);
+        const uint4 qa = fresh(qf[c]), qb = fresh(qf[c + 2]);
+        float a[8], b[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
-                n[c][t] = rbf((word_f(qf[c], t) * rr) * (1.0f + word_f(wv, t)));
-        }
-        const int pos = p.q_base + (ok ? row : 0);
-        const float *ct = p.cos_tab + (size_t)pos * HALF_R;
-        const float *st = p.sin_tab + (size_t)pos * HALF_R;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const float4 c0 = *reinterpret_cast<const float4 *>(ct + 16 * c + 8 * hh);
-            const float4 c1 = *reinterpret_cast<const float4 *>(ct + 16 * c + 8 * hh + 4);
-            const float4 s0 = *reinterpret_cast<const float4 *>(st + 16 * c + 8 * hh);
-            const float4 s1 = *reinterpret_cast<const float4 *>(st + 16 * c + 8 * hh + 4);
-            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float cj = rbf(cv[t]), sj = rbf(sv[t]);
-                const float av = n[c][t], bv = n[c + 2][t];
-                n[c][t] = rbf(rbf(av * cj) + rbf(-bv * sj));
-                n[c + 2][t] = rbf(rbf(bv * cj) + rbf(av * sj));
-            }
+        for (int t = 0; t < 8; ++t) {
+            a[t] = round_op((word_f(qa, t) * rr) * wa[t]);
+            b[t] = round_op((word_f(qb, t) * rr) * wb[t]);
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            qf[c] = make_uint4(pack2(n[c][0], n[c][1]), pack2(n[c][2], n[c][3]),
-                               pack2(n[c][4], n[c][5]), pack2(n[c][6], n[c][7]));
+        for (int t = 0; t < 8; ++t) {
+            const float cj = round_op(cv[t]), sj = round_op(sv[t]);
+            const float av = a[t], bv = b[t];
+            a[t] = round_op(round_op(av * cj) + round_op(-bv * sj));
+            b[t] = round_op(round_op(bv * cj) + round_op(av * sj));
+        }
+        qf[c] = make_uint4(pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(a[4], a[5]), pack2(a[6], a[7]));
+        qf[c + 2] = make_uint4(pack2(b[0], b[1]), pack2(b[2], b[3]), pack2(b[4], b[5]), pack2(b[6], b[7]));
+        __builtin_amdgcn_sched_barrier(0);
     }
     if (!ok) {
 #pragma unroll
@@ -947,6 +998,7 @@ void attn_fwd8(AttnParams pk)
     __shared__ uint32_t bitsbuf[MASKED ? 8 : 1][QW];
     __shared__ int tile_list[MASKED ? MAX_TILES : 1];
     __shared__ int tile_count;
+    __shared__ __align__(16) float wq1[D];
 
     const int lane_id = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -962,6 +1014,8 @@ void attn_fwd8(AttnParams pk)
     const int per_rb = pk.Hkv * pk.n_hg;
     const int n_items = pk.nrb * per_rb;
     const int P = (int)gridDim.x;
+    fill_wq1(wq1, pk.wq);
+    __syncthreads();
 #pragma clang loop unroll(disable)
     for (int pass = 0;; ++pass) {
         const int item = pass * P + ((pass & 1) ? P - 1 - (int)blockIdx.x : (int)blockIdx.x);
@@ -969,8 +1023,11 @@ void attn_fwd8(AttnParams pk)
             break;
         if (pass > 0)
             __syncthreads();                         // the previous item is done with LDS
-        int lane = lane_id;
-        asm volatile("" : "+v"(lane));
+        // The lane index, rebuilt every pass by instructions the compiler
+        // cannot hoist (kept across the whole loop it would hold a register
+        // through the key walk, and the walk has none to spare).
+        int lane;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
         const int j = lane & 31, hh = lane >> 5;
         // The item's problem: the launch's, or one sequence of a packed batch
         // (its rows, its prepared key tiles, positions from 0).
@@ -1097,13 +1154,15 @@ void attn_fwd8(AttnParams pk)
         }
 
         uint4 qf[16];
-        load_queries1(p, rbase, h, lane, qf);
+        load_queries1(p, rbase, h, lane, qf, wq1);
         const FragOffsets fo = frag_offsets(j, hh);
         const uint32_t diag_vis = (j == 31) ? 0xffffffffu : ((2u << j) - 1u);
 
         f32x16 o[8];
         {
-            const bf16x8 zero = {};
+            uint32_t z;
+            asm volatile("v_mov_b32 %0, 0" : "=v"(z));    // built here, not kept across passes
+            const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{z, z, z, z});
 #pragma unroll
             for (int db = 0; db < 8; ++db)
                 asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(o[db]) : "v"(zero));
@@ -1175,11 +1234,15 @@ void attn_fwd8(AttnParams pk)
                                                 pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
                     *reinterpret_cast<uint2 *>(ep + j * EP_STRIDE + 2 * d0) = cw;
                 }
+            // Row rbase + 2 it + hh of the block: its staged context and its
+            // output row, stepped by two rows per iteration.
+            const char *crow = ep + hh * EP_STRIDE + 16 * cc;
+            uint16_t *orow = p.out + ((size_t)(rbase + hh) * p.Hq + h) * D + 8 * cc;
+            const size_t ostep = (size_t)2 * p.Hq * D;
+            const int rows_left = active ? p.S - rbase - hh : 0;   // this lane stores iterations it < ceil(rows_left / 2)
 #pragma unroll
             for (int it = 0; it < 16; ++it) {
-                const int rr = 2 * it + hh;
-                const int row = rbase + rr;
-                const uint4 cv = *reinterpret_cast<const uint4 *>(ep + rr * EP_STRIDE + 16 * cc);
+                const uint4 cv = *reinterpret_cast<const uint4 *>(crow + 2 * it * EP_STRIDE);
                 const uint32_t cws[4] = {cv.x, cv.y, cv.z, cv.w};
                 const uint32_t gws[4] = {gw[it].x, gw[it].y, gw[it].z, gw[it].w};
                 uint32_t ow[4];
@@ -1190,14 +1253,14 @@ void attn_fwd8(AttnParams pk)
                     for (int hf = 0; hf < 2; ++hf) {
                         const float ctx = hf ? hi_f(cws[q]) : lo_f(cws[q]);
                         const float gv = hf ? hi_f(gws[q]) : lo_f(gws[q]);
-                        const float sg = rbf(__builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * LOG2E)));
+                        const float sg = round_op(__builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * LOG2E)));
                         ov[hf] = ctx * sg;
                     }
                     ow[q] = pack2(ov[0], ov[1]);
                 }
-                if (active && row < p.S)
-                    *reinterpret_cast<uint4 *>(p.out + ((size_t)row * p.Hq + h) * D + 8 * cc) =
-                        make_uint4(ow[0], ow[1], ow[2], ow[3]);
+                if (2 * it < rows_left)
+                    *reinterpret_cast<uint4 *>(orow) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+                orow += ostep;
             }
         };
 
@@ -1275,6 +1338,9 @@ template <int MODE>   // 0 causal, 1 masked (causal and mask), 2 bidirectional
 __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout)
 {
     __shared__ __attribute__((aligned(16))) char smem[WT_SMEM];
+    __shared__ __align__(16) float wq1[D];
+    fill_wq1(wq1, p.wq);
+    __syncthreads();
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hw = wave & 3, blk = wave >> 2;
     // Workgroups go to the eight XCDs in turn (linear id mod 8), each XCD with
@@ -1299,7 +1365,7 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
     char *stage = smem + 2 * TILE_BYTES + wave * 32 * WT_ROW;
 
     uint4 qf[16];
-    load_queries1(p, r0, h, lane, qf);
+    load_queries1(p, r0, h, lane, qf, wq1);
     const int rc = min(r0 + j, p.S - 1);
     const float m = p.ml[((size_t)rc * p.Hq + h) * 2];
     const float lsum = p.ml[((size_t)rc * p.Hq + h) * 2 + 1];
