@@ -71,6 +71,14 @@ __device__ __forceinline__ uint32_t pack2(float a, float b)
 }
 __device__ __forceinline__ uint16_t f2bf(float a) { return __builtin_bit_cast(uint16_t, (__bf16)a); }
 __device__ __forceinline__ float rbf(float a) { return bf2f(f2bf(a)); }
+// x rounded to bf16 (nearest even), as an fp32 value: the packed convert with
+// a zero low half leaves bf16(x) in the high half, which is that value.
+__device__ __forceinline__ float round_op(float x)
+{
+    float r;
+    asm("v_cvt_pk_bf16_f32 %0, 0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
 
 __device__ __forceinline__ float word_f(const uint4 &u, int t)
 {
@@ -98,19 +106,25 @@ __device__ __forceinline__ int vt_key_of_pos(int pos)
     return (pos & ~15) | k16;
 }
 
-// Stores one tile: 32 prepared keys (ks) and 32 values (vs), bf16 rows, into
-// the chunk-major Kp and Vt layouts at element offset tile_off.
-__device__ __forceinline__ void write_kv_tile(const uint16_t (&ks)[KT][D + 8], const uint16_t (&vs)[KT][D + 8],
-                                              uint16_t *kp, uint16_t *vt, size_t tile_off, int tid)
+// Stores 32 prepared keys (ks, bf16 rows) as one chunk-major Kp tile at kdst
+// (256 threads).
+__device__ __forceinline__ void write_k_tile(const uint16_t (&ks)[KT][D + 8], uint16_t *kdst, int tid)
 {
-    uint4 *kdst = reinterpret_cast<uint4 *>(kp + tile_off);
+    uint4 *dst = reinterpret_cast<uint4 *>(kdst);
     for (int it = 0; it < 4; ++it) {
         const int piece = it * 256 + tid, ch = piece >> 5, r = piece & 31;
-        kdst[piece] = *reinterpret_cast<const uint4 *>(&ks[r][ch * 8]);
+        dst[piece] = *reinterpret_cast<const uint4 *>(&ks[r][ch * 8]);
     }
-    uint4 *vdst = reinterpret_cast<uint4 *>(vt + tile_off);
-    for (int q = 0; q < 4; ++q) {
-        const int d = tid;
+}
+
+// Stores 32 values (vs, bf16 rows) as one chunk-major Vt tile at vdst: its
+// 1024 16-byte pieces (q, d) = (piece / 256, piece % 256), taken by threads t
+// of nthreads in steps of nthreads.
+__device__ __forceinline__ void write_vt_tile(const uint16_t (&vs)[KT][D + 8], uint16_t *vdst, int t, int nthreads)
+{
+    uint4 *dst = reinterpret_cast<uint4 *>(vdst);
+    for (int piece = t; piece < 4 * D; piece += nthreads) {
+        const int q = piece >> 8, d = piece & (D - 1);
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -118,8 +132,17 @@ __device__ __forceinline__ void write_kv_tile(const uint16_t (&ks)[KT][D + 8], c
             const uint32_t b = vs[vt_key_of_pos(8 * q + 2 * e + 1)][d];
             w[e] = a | (b << 16);
         }
-        vdst[q * 256 + d] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[piece] = make_uint4(w[0], w[1], w[2], w[3]);
     }
+}
+
+// Stores one tile: 32 prepared keys (ks) and 32 values (vs), bf16 rows, into
+// the chunk-major Kp and Vt layouts at element offset tile_off (256 threads).
+__device__ __forceinline__ void write_kv_tile(const uint16_t (&ks)[KT][D + 8], const uint16_t (&vs)[KT][D + 8],
+                                              uint16_t *kp, uint16_t *vt, size_t tile_off, int tid)
+{
+    write_k_tile(ks, kp + tile_off, tid);
+    write_vt_tile(vs, vt + tile_off, tid, 256);
 }
 
 // ---------------------------------------------------------------------------
@@ -171,6 +194,7 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
     __shared__ __align__(16) uint16_t ks[KT][D + 8];
     __shared__ __align__(16) uint16_t vs[KT][D + 8];
     __shared__ float rs[KT];
+    __shared__ float wk1[D];                     // 1 + w_k in fp32
     // tile: prepared tile written; t0: position of its first key; T: keys of
     // the sequence; raw row of position key = key + row_base.
     const int tile = p.tile0 + (int)blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
@@ -181,7 +205,9 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
         row_base = p.seg[4 * sq + 1];
         t0 = (tile - p.seg[4 * sq + 2]) * KT;
     }
+    const size_t tile_off = ((size_t)c * (p.Tpad / KT) + tile) * (size_t)(KT * D);
 
+    wk1[tid] = 1.0f + bf2f(p.wk[tid]);
     for (int it = 0; it < 4; ++it) {
         const int idx = it * 256 + tid, r = idx >> 5, ch = idx & 31, key = t0 + r;
         uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
@@ -195,14 +221,30 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
     }
     __syncthreads();
 
-    // Sum of squares in ascending dimension order, one thread per key.
     if (tid < KT) {
+        // Sum of squares of key row tid in ascending dimension order; the
+        // row's 16-byte chunks are read from LDS eight ahead of the chain.
+        const uint4 *row = reinterpret_cast<const uint4 *>(&ks[tid][0]);
+        uint4 buf[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            buf[i] = row[i];
         float ss = 0.0f;
-        for (int d = 0; d < D; ++d) {
-            const float x = bf2f(ks[tid][d]);
-            ss += x * x;
+#pragma unroll
+        for (int ch = 0; ch < D / 8; ++ch) {
+            const uint4 u = buf[ch & 7];
+            if (ch + 8 < D / 8)
+                buf[ch & 7] = row[ch + 8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float x = word_f(u, t);
+                ss += x * x;
+            }
         }
         rs[tid] = 1.0f / sqrtf(ss / (float)D + p.eps);
+    } else if (!FP8 && tid >= 64) {
+        // Meanwhile waves 1..3 store the transposed value tile.
+        write_vt_tile(vs, p.vt + tile_off, tid - 64, 192);
     }
     __syncthreads();
 
@@ -214,17 +256,17 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
 #pragma unroll
         for (int s = 0; s < 32; ++s) {
             const int d = sub + 8 * s;
-            n[s] = rbf((bf2f(ks[r][d]) * rr) * (1.0f + bf2f(p.wk[d])));
+            n[s] = round_op((bf2f(ks[r][d]) * rr) * wk1[d]);
         }
         if (key < T) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int j = sub + 8 * s;
-                const float cj = rbf(p.cos_tab[(size_t)key * HALF_R + j]);
-                const float sj = rbf(p.sin_tab[(size_t)key * HALF_R + j]);
+                const float cj = round_op(p.cos_tab[(size_t)key * HALF_R + j]);
+                const float sj = round_op(p.sin_tab[(size_t)key * HALF_R + j]);
                 const float a = n[s], b = n[s + 4];
-                n[s] = rbf(rbf(a * cj) + rbf(-b * sj));
-                n[s + 4] = rbf(rbf(b * cj) + rbf(a * sj));
+                n[s] = round_op(round_op(a * cj) + round_op(-b * sj));
+                n[s + 4] = round_op(round_op(b * cj) + round_op(a * sj));
             }
         }
 #pragma unroll
@@ -234,7 +276,7 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
     __syncthreads();
 
     if (!FP8) {
-        write_kv_tile(ks, vs, p.kp, p.vt, ((size_t)c * (p.Tpad / KT) + tile) * (size_t)(KT * D), tid);
+        write_k_tile(ks, p.kp + tile_off, tid);
         return;
     }
     // fp8 cache rows.  Row scales: thread (key r, sub) takes the largest
@@ -325,7 +367,7 @@ __global__ __launch_bounds__(256) void kp_unpack(const uint16_t *kp, int Tpad, i
 }
 
 // ---------------------------------------------------------------------------
-// Mask packing.  grid (ceil(W/256), nrb), 256 threads; thread = (row block, word).
+// Mask packing (launch shape below).
 // bits[row][w] bit b = mask[row][32w+b] != 0 && 32w+b <= row && 32w+b < S.
 // tilevis[rb][w] = any bit of the 64 x 32 block.
 // ---------------------------------------------------------------------------
@@ -335,40 +377,72 @@ __device__ __forceinline__ uint32_t nz_bits4(uint32_t u)
            ((u & 0x00ff0000u) ? 4u : 0u) | ((u & 0xff000000u) ? 8u : 0u);
 }
 
+// grid (ceil(W / 32), row blocks of 64), 256 threads: thread t takes key
+// word w0 + (t & 31) of the 8 rows 8 (t >> 5) .. +7 of the block, all eight
+// rows' loads in flight at once; the 8 row groups' OR of the words gives the
+// tile flag (through LDS).
 __global__ __launch_bounds__(256) void mask_pack(MaskPackParams p)
 {
-    const int w = blockIdx.x * 256 + threadIdx.x;
+    __shared__ uint32_t anyw[8][32];
+    const int tid = threadIdx.x, wl = tid & 31, rg = tid >> 5;
+    const int w = blockIdx.x * 32 + wl;
     const int rb = blockIdx.y;
-    if (w >= p.W)
-        return;
     const int key0 = 32 * w;
-    uint32_t any = 0;
-    for (int r = 0; r < QW; ++r) {
-        const int row = rb * QW + r;
-        if (row >= p.S)
-            break;
-        uint32_t word = 0;
-        if (key0 <= row) {
-            const uint8_t *src = p.mask + (size_t)row * p.S + key0;
-            if (p.vec16 && key0 + 32 <= p.S) {
-                const uint4 a = *reinterpret_cast<const uint4 *>(src);
-                const uint4 b = *reinterpret_cast<const uint4 *>(src + 16);
-                word = nz_bits4(a.x) | (nz_bits4(a.y) << 4) | (nz_bits4(a.z) << 8) |
-                       (nz_bits4(a.w) << 12) | (nz_bits4(b.x) << 16) | (nz_bits4(b.y) << 20) |
-                       (nz_bits4(b.z) << 24) | (nz_bits4(b.w) << 28);
-            } else {
-                for (int b = 0; b < 32; ++b)
-                    if (key0 + b < p.S && src[b] != 0)
-                        word |= 1u << b;
+    const int row0 = rb * QW + 8 * rg;
+    uint32_t words[8];
+    if (w < p.W && p.vec16 && key0 + 32 <= p.S) {
+        uint4 a[8], b[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int row = row0 + r;
+            a[r] = b[r] = make_uint4(0u, 0u, 0u, 0u);
+            if (row < p.S && key0 <= row) {
+                const uint8_t *src = p.mask + (size_t)row * p.S + key0;
+                a[r] = *reinterpret_cast<const uint4 *>(src);
+                b[r] = *reinterpret_cast<const uint4 *>(src + 16);
             }
-            const int last = row - key0;               // keys key0..row are causal
-            if (last < 31)
-                word &= (2u << last) - 1u;
         }
-        p.bits[(size_t)row * p.W + w] = word;
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            words[r] = nz_bits4(a[r].x) | (nz_bits4(a[r].y) << 4) | (nz_bits4(a[r].z) << 8) |
+                       (nz_bits4(a[r].w) << 12) | (nz_bits4(b[r].x) << 16) | (nz_bits4(b[r].y) << 20) |
+                       (nz_bits4(b[r].z) << 24) | (nz_bits4(b[r].w) << 28);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int row = row0 + r;
+            uint32_t word = 0;
+            if (w < p.W && row < p.S && key0 <= row) {
+                const uint8_t *src = p.mask + (size_t)row * p.S + key0;
+                for (int bit = 0; bit < 32; ++bit)
+                    if (key0 + bit < p.S && src[bit] != 0)
+                        word |= 1u << bit;
+            }
+            words[r] = word;
+        }
+    }
+    uint32_t any = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int row = row0 + r;
+        uint32_t word = words[r];
+        const int last = row - key0;                   // keys key0..row are causal
+        if (last < 0)
+            word = 0;
+        else if (last < 31)
+            word &= (2u << last) - 1u;
+        if (w < p.W && row < p.S)
+            p.bits[(size_t)row * p.W + w] = word;
         any |= word;
     }
-    p.tilevis[(size_t)rb * p.W + w] = any ? 1 : 0;
+    anyw[rg][wl] = any;
+    __syncthreads();
+    if (rg == 0 && w < p.W) {
+#pragma unroll
+        for (int g = 1; g < 8; ++g)
+            any |= anyw[g][wl];
+        p.tilevis[(size_t)rb * p.W + w] = any ? 1 : 0;
+    }
 }
 
 __device__ __forceinline__ void load_queries1(const AttnParams &p, int r0, int h, int lane, uint4 (&qf)[16],
@@ -557,14 +631,6 @@ __device__ __forceinline__ uint32_t pack2_op(float a, float b)
     return r;
 }
 
-// x rounded to bf16 (nearest even), as an fp32 value: the packed convert with
-// a zero low half leaves bf16(x) in the high half, which is that value.
-__device__ __forceinline__ float round_op(float x)
-{
-    float r;
-    asm("v_cvt_pk_bf16_f32 %0, 0, %1" : "=v"(r) : "v"(x));
-    return r;
-}
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
 {
@@ -1168,11 +1234,11 @@ void attn_fwd8(AttnParams pk)
                 asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(o[db]) : "v"(zero));
         }
         float m = -INFINITY, l = 0.0f, alpha = 1.0f;
+        // Scores and weights need no initial value: the first score MFMA of
+        // a tile takes a zero accumulator, and the first tile's softmax writes
+        // all eight weight words before a context MFMA reads them.
         f32x16 s;
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            s[e] = 0.0f;
-        u32x4 pw[2] = {};
+        u32x4 pw[2];
 
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -1567,7 +1633,7 @@ hipError_t launch_kv_widen(const KvWidenParams &p, int ntiles, int Hkv, hipStrea
 
 hipError_t launch_mask_pack(const MaskPackParams &p, int nrb, hipStream_t stream)
 {
-    hipLaunchKernelGGL(mask_pack, dim3((p.W + 255) / 256, nrb), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(mask_pack, dim3((p.W + 31) / 32, nrb), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
