@@ -58,16 +58,57 @@ def kernel_source_hash() -> str:
 
 def measured_traffic(workload: str, path: str = TRAFFIC_FILE):
     """HBM bytes per launch of a kernel (the attention kernel, or the weights
-    kernel) from a committed PMC summary, or None when the kernel source changed
-    since the counters were taken."""
+    kernel) on a workload, from a committed PMC summary ({"workloads": {key:
+    {"kernel_source_sha256_16": ..., "bytes_per_launch": ...}}}, the key being
+    the workload name and the flags that change what runs, e.g.
+    "c3_prefix_t8192_qb1024 --cached"), or None when there is no record or
+    the kernel source changed since its counters were taken."""
     try:
         with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            rec = json.load(f).get("workloads", {}).get(workload)
+    except (OSError, ValueError, AttributeError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("workload") != workload:
+    if not rec or rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def kernel_algorithmic(p, rows: int, keys: int, new_keys: int, flops: float, weights: bool,
+                       fp8_cache: bool = False) -> dict:
+    """Algorithmic work of one launch of each kernel of a step: FLOPs for the
+    attention kernel, bytes that must cross HBM at least once for every kernel.
+
+    rows: query rows of the step; keys: keys the attention walks (T, or a
+    packed batch's total); new_keys: keys the key prologue prepares (all of
+    them, or the window's when the prefix comes from a cache); flops: the
+    step's algorithmic FLOPs (4 D per visible (row, key, query head));
+    fp8_cache: the key prologue writes e4m3 cache rows with one fp32 scale
+    each, and kv_widen turns the cache's keys 0..keys-1 into bf16 tiles."""
+    Hq, Hkv, D = p.n_q_heads, p.n_kv_heads, p.head_dim
+    half_rot = p.rotary_dim // 2
+    out_b = rows * Hq * D * 2
+    att_read = (rows * Hq * 2 * D * 2                  # q|gate rows
+                + 2 * Hkv * keys * D * 2               # prepared keys and transposed values
+                + 2 * rows * half_rot * 4)             # cos/sin rows of the query positions
+    rec = {"attention": {"flop": flops, "read_bytes": att_read, "write_bytes": out_b},
+           "kv_prologue": {"read_bytes": 2 * new_keys * Hkv * D * 2 + 2 * new_keys * half_rot * 4 + D * 2,
+                           "write_bytes": 2 * new_keys * Hkv * D * 2}}
+    if fp8_cache:
+        rec["kv_prologue"]["write_bytes"] = 2 * new_keys * Hkv * (D + 4)
+        rec["kv_widen"] = {"read_bytes": 2 * keys * Hkv * (D + 4), "write_bytes": 2 * keys * Hkv * D * 2}
+    if p.mask is not None:
+        S = p.rows
+        W = (S + 31) // 32
+        # The causal part of each row, in whole 32-key words: mask_pack reads
+        # those bytes and writes a bit word for every key word plus one flag per
+        # (64-row block, key word); the attention kernel reads the causal words.
+        causal_words = sum(i // 32 + 1 for i in range(S))
+        rec["mask_pack"] = {"read_bytes": 32 * causal_words, "write_bytes": S * W * 4 + ((S + 63) // 64) * W}
+        rec["attention"]["read_bytes"] += 4 * causal_words
+    if weights:
+        rec["weights"] = {"read_bytes": rows * Hq * D * 2 + Hkv * keys * D * 2 + rows * Hq * 8,
+                          "write_bytes": rows * Hq * keys * 2}
+    return rec
 
 
 def cpu_baseline(p, rows_target: int, threads: int):
@@ -293,6 +334,9 @@ def main():
     w_ms, w_n = ctx.read_timing(ga.ATTN_KERNEL_WEIGHTS)
     ctx.set_timing(False)
     ms_per_step = total_ms / args.steps
+    traffic_key = " ".join([args.workload] + [f for f, on in (("--cached", args.cached),
+                                                              ("--fp8-cache", args.fp8_cache),
+                                                              ("--weights", args.weights)) if on])
     flops = batch.flops() if batch is not None else p.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     attn_avg_ms = attn_ms / max(attn_n, 1)
@@ -332,7 +376,7 @@ def main():
                        "weights": round(w_ms / max(w_n, 1), 5) if w_n else None},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(args.workload)},
+                     "traffic": measured_traffic(traffic_key)},
     }
     if w_n:
         # Weights kernel: bf16 weights written, plus the queries, keys and row
@@ -342,8 +386,11 @@ def main():
         w_gbs = wbytes / (w_ms / w_n * 1e-3) / 1e9
         rec["weights_roofline"] = {"bound": "hbm", "achieved": round(w_gbs, 1), "peak": PEAK_HBM_GBS,
                                    "unit": "GB/s", "frac": round(w_gbs / PEAK_HBM_GBS, 4),
-                                   "traffic": measured_traffic(args.workload, TRAFFIC_WEIGHTS_FILE),
+                                   "traffic": measured_traffic(traffic_key, TRAFFIC_WEIGHTS_FILE),
                                    "bytes_per_launch": wbytes}
+    keys = batch.total if batch is not None else p.T
+    new_keys = keys - p.q_base if cache is not None else keys
+    rec["kernels_algorithmic"] = kernel_algorithmic(p, rows, keys, new_keys, flops, bool(w_n), fp8)
     if batch is not None:
         rec["config"]["sequences"] = len(batch.seqs)
         rec["config"]["seq_lens"] = batch.lens
