@@ -8,9 +8,12 @@ seeded synthetic tensors resident in HBM before the timed region.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 Prints one JSON line.  ``value`` is algorithmic TFLOP/s of the whole step
-(4*D FLOPs per visible (row, key, query head) triple).  ``roofline`` is for the
-dominant kernel (attention), timed with HIP events around each launch on the
-launch stream.  ``cpu_baseline`` times the CPU oracle on a bounded row sample
+(4*D FLOPs per visible (row, key, query head) triple), from one event pair
+around the K steps.  ``roofline`` is for the dominant kernel (attention),
+timed with the library's HIP events around each of its launches on the launch
+stream; the other kernels get events only with ``--time-all-kernels`` and the
+steps one each only with ``--step-spread``, since every event costs the stream
+a few microseconds.  ``cpu_baseline`` times the CPU oracle on a bounded row sample
 of the same workload.
 
 A packed-batch workload (``--workload c6_varlen_16x128_2048``) runs its
@@ -168,6 +171,12 @@ def main():
     ap.add_argument("--weights", action="store_true",
                     help="each step also writes the normalised bf16 attention weights [rows][Hq][T] "
                          "(attn_prefill_weights)")
+    ap.add_argument("--step-spread", action="store_true",
+                    help="record an event between consecutive steps and report the per-step median/p10/p90 "
+                         "(each event costs the stream a few microseconds)")
+    ap.add_argument("--time-all-kernels", action="store_true",
+                    help="library events around every kernel (kv prologue, mask pack too), not only the "
+                         "attention (and weights) kernel")
     ap.add_argument("--cold", action="store_true",
                     help="write a 512 MiB scrub buffer between timed steps (outside each step's events)")
     args = ap.parse_args()
@@ -303,21 +312,31 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
 
-    ctx.set_timing(True)
-    # One event between consecutive steps (per-step spread); with --cold a
-    # 512 MiB scrub write runs between steps, outside each step's event pair.
+    # Library events (a few microseconds of stream time each) only around the
+    # kernels the JSON line needs: the attention kernel for `roofline`, the
+    # weights kernel for `weights_roofline`; --time-all-kernels adds the rest.
+    timed = [ga.ATTN_KERNEL_ATTENTION] + ([ga.ATTN_KERNEL_WEIGHTS] if args.weights else [])
+    ctx.set_timing(True, kernels=None if args.time_all_kernels else timed)
+    # One event pair around the K steps; --step-spread adds one event between
+    # consecutive steps (per-step median/p10/p90); with --cold a 512 MiB scrub
+    # write runs between steps, outside each step's event pair.
     ev = lambda: torch.cuda.Event(enable_timing=True)
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+    step_ms = None
     torch.cuda.synchronize()
     if scrub is None:
-        marks = [ev() for _ in range(args.steps + 1)]
+        marks = [ev() for _ in range(args.steps + 1 if args.step_spread else 2)]
         marks[0].record(stream)
         for i in range(args.steps):
             step()
-            marks[i + 1].record(stream)
+            if args.step_spread:
+                marks[i + 1].record(stream)
+        if not args.step_spread:
+            marks[1].record(stream)
         torch.cuda.synchronize()
         total_ms = marks[0].elapsed_time(marks[-1])
-        step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+        if args.step_spread:
+            step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     else:
         pairs = [(ev(), ev()) for _ in range(args.steps)]
         for i in range(args.steps):
@@ -341,8 +360,9 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     attn_avg_ms = attn_ms / max(attn_n, 1)
     achieved = flops / (attn_avg_ms * 1e-3) / 1e12
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; attention {attn_avg_ms:.4f} ms, "
-        f"kv prologue {pro_ms / max(pro_n, 1):.4f} ms, mask pack {mp_ms / max(mp_n, 1):.4f} ms"
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step; attention {attn_avg_ms:.4f} ms"
+        + (f", kv prologue {pro_ms / pro_n:.4f} ms" if pro_n else "")
+        + (f", mask pack {mp_ms / mp_n:.4f} ms" if mp_n else "")
         + (f", weights {w_ms / max(w_n, 1):.4f} ms" if w_n else ""))
 
     rec = {
@@ -366,12 +386,16 @@ def main():
                    "weights": bool(args.weights),
                    "seed": synth.BATCH_CONFIGS[args.workload]["seed"] if batch is not None else p.seed,
                    "algorithmic_gflop": round(flops / 1e9, 3)},
-        "step_ms": {"median": round(float(np.median(step_ms)), 5),
-                    "p10": round(float(np.percentile(step_ms, 10)), 5),
-                    "p90": round(float(np.percentile(step_ms, 90)), 5),
-                    "caches": "cold (512 MiB scrub between steps)" if args.cold else "warm"},
+        "step_ms": None if step_ms is None else {
+            "median": round(float(np.median(step_ms)), 5),
+            "p10": round(float(np.percentile(step_ms, 10)), 5),
+            "p90": round(float(np.percentile(step_ms, 90)), 5),
+            "caches": "cold (512 MiB scrub between steps)" if args.cold else "warm"},
+        "timing_events": "library events around " + ("every kernel" if args.time_all_kernels else
+                                                     " and ".join(["attention"] + (["weights"] if args.weights else [])))
+                         + (", one bench event per step" if step_ms is not None else ", one pair around the steps"),
         "kernels_ms": {"attention": round(attn_avg_ms, 5),
-                       "kv_prologue": round(pro_ms / max(pro_n, 1), 5),
+                       "kv_prologue": round(pro_ms / pro_n, 5) if pro_n else None,
                        "mask_pack": round(mp_ms / max(mp_n, 1), 5) if mp_n else None,
                        "weights": round(w_ms / max(w_n, 1), 5) if w_n else None},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,

@@ -41,6 +41,7 @@ ATTN_KERNEL_KV_PROLOGUE = 0
 ATTN_KERNEL_MASK_PACK = 1
 ATTN_KERNEL_ATTENTION = 2
 ATTN_KERNEL_WEIGHTS = 3
+ATTN_TIMING_ALL = 15
 
 KIND_GATED, KIND_PREFIX, KIND_MASKED = 0, 1, 2
 
@@ -98,6 +99,7 @@ def _load():
         "attn_prefill_append_fp8": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp, vp]),
         "attn_debug_prepare": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp, vp]),
         "attn_ctx_set_timing": (ctypes.c_int, [vp, ctypes.c_int]),
+        "attn_ctx_set_timing_mask": (ctypes.c_int, [vp, ctypes.c_int]),
         "attn_ctx_read_timing": (ctypes.c_int, [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                                 ctypes.POINTER(i32)]),
         "attn_mfma_clock_probe": (ctypes.c_int, [i32, vp, ctypes.POINTER(ctypes.c_double),
@@ -204,6 +206,10 @@ def attn_debug_prepare(ctx, inputs: attn_inputs, T: int, q_base: int, qp_out, kp
 
 def attn_ctx_set_timing(ctx, enable: bool) -> int:
     return lib.attn_ctx_set_timing(ctx, 1 if enable else 0)
+
+
+def attn_ctx_set_timing_mask(ctx, kernel_mask: int) -> int:
+    return lib.attn_ctx_set_timing_mask(ctx, kernel_mask)
 
 
 def attn_ctx_read_timing(ctx, kernel: int):
@@ -477,8 +483,13 @@ class Context:
             raise AttnError(rc, "attn_debug_prepare")
         return qp, kp
 
-    def set_timing(self, enable: bool):
-        rc = attn_ctx_set_timing(self.handle, enable)
+    def set_timing(self, enable: bool, kernels=None):
+        """Events around every launch (kernels None) or around the launches of
+        the listed ATTN_KERNEL_* ids only; enable False stops."""
+        if kernels is None:
+            rc = attn_ctx_set_timing(self.handle, enable)
+        else:
+            rc = attn_ctx_set_timing_mask(self.handle, sum(1 << k for k in set(kernels)) if enable else 0)
         if rc != ATTN_OK:
             raise AttnError(rc, "attn_ctx_set_timing")
 

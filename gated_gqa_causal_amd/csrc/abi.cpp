@@ -40,7 +40,7 @@ struct attn_ctx {
     hipEvent_t batch_copied = nullptr;
     bool batch_pending = false;
     // timing
-    bool timing = false;
+    int timing = 0;                // bit (1 << ATTN_KERNEL_*) per timed kernel
     std::vector<hipEvent_t> pool;
     size_t pool_used = 0;
     struct Rec {
@@ -82,7 +82,7 @@ struct Timer {
     hipEvent_t a = nullptr, b = nullptr;
     Timer(attn_ctx *c, hipStream_t s, int k) : ctx(c), stream(s), kernel(k)
     {
-        if (ctx->timing && ctx->pool_used + 2 <= ctx->pool.size()) {
+        if ((ctx->timing >> kernel & 1) && ctx->pool_used + 2 <= ctx->pool.size()) {
             a = ctx->pool[ctx->pool_used++];
             b = ctx->pool[ctx->pool_used++];
             (void)hipEventRecord(a, stream);
@@ -675,13 +675,15 @@ int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t 
     return ATTN_OK;
 }
 
-int attn_ctx_set_timing(attn_ctx *ctx, int enable)
+int attn_ctx_set_timing_mask(attn_ctx *ctx, int kernel_mask)
 {
     if (!ctx)
         return ATTN_ERR_NULL_ARG;
+    if (kernel_mask & ~ATTN_TIMING_ALL)
+        return ATTN_ERR_RANGE;
     if (current_device_matches(ctx) != ATTN_OK)
         return ATTN_ERR_DEVICE;
-    if (enable && ctx->pool.empty()) {
+    if (kernel_mask && ctx->pool.empty()) {
         for (int i = 0; i < 8192; ++i) {
             hipEvent_t e;
             if (hipEventCreate(&e) != hipSuccess)
@@ -689,10 +691,15 @@ int attn_ctx_set_timing(attn_ctx *ctx, int enable)
             ctx->pool.push_back(e);
         }
     }
-    ctx->timing = enable != 0;
+    ctx->timing = kernel_mask;
     ctx->pool_used = 0;
     ctx->recs.clear();
     return ATTN_OK;
+}
+
+int attn_ctx_set_timing(attn_ctx *ctx, int enable)
+{
+    return attn_ctx_set_timing_mask(ctx, enable ? ATTN_TIMING_ALL : 0);
 }
 
 int attn_ctx_read_timing(attn_ctx *ctx, int kernel, double *total_ms, int32_t *launches)

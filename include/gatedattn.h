@@ -276,15 +276,23 @@ ATTN_EXPORT int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t
 /*
  * Per-kernel timing with HIP events recorded on the call's stream around
  * each launch.  enable != 0 creates an event pool (outside any timed
- * region) and starts recording; 0 stops.  attn_ctx_read_timing waits for the
- * recorded events, returns the summed duration (ms) and launch count of one
- * kernel since the last read, and clears them.  kernel: ATTN_KERNEL_*.
+ * region) and starts recording for every kernel; 0 stops.
+ * attn_ctx_set_timing_mask does the same for the kernels whose bits
+ * (1 << ATTN_KERNEL_*) are set in kernel_mask (0 stops; bits outside
+ * ATTN_TIMING_ALL: ATTN_ERR_RANGE): each recorded event costs the stream a
+ * few microseconds, so a caller timing whole calls records only the kernels
+ * it needs.  attn_ctx_read_timing waits for the recorded events, returns the
+ * summed duration (ms) and launch count of one kernel since the last read,
+ * and clears them.  kernel: ATTN_KERNEL_*.  Errors: ATTN_ERR_NULL_ARG,
+ * ATTN_ERR_DEVICE (another device current), ATTN_ERR_NOMEM (event pool).
  */
 #define ATTN_KERNEL_KV_PROLOGUE 0
 #define ATTN_KERNEL_MASK_PACK 1
 #define ATTN_KERNEL_ATTENTION 2
 #define ATTN_KERNEL_WEIGHTS 3
+#define ATTN_TIMING_ALL 15                /* the four kernels above */
 ATTN_EXPORT int attn_ctx_set_timing(attn_ctx *ctx, int enable);
+ATTN_EXPORT int attn_ctx_set_timing_mask(attn_ctx *ctx, int kernel_mask);
 ATTN_EXPORT int attn_ctx_read_timing(attn_ctx *ctx, int kernel, double *total_ms, int32_t *launches);
 
 /*

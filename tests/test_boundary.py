@@ -40,7 +40,7 @@ def test_header_constants_match_binding(ga):
     src = open(HEADER).read()
     for name in ["ATTN_ABI_VERSION", "ATTN_HEAD_DIM", "ATTN_ROTARY_DIM", "ATTN_MAX_GROUP",
                  "ATTN_MAX_TOKENS", "ATTN_QBASE_ALIGN", "ATTN_MAX_SEQS", "ATTN_KERNEL_KV_PROLOGUE",
-                 "ATTN_KERNEL_MASK_PACK", "ATTN_KERNEL_ATTENTION", "ATTN_KERNEL_WEIGHTS"]:
+                 "ATTN_KERNEL_MASK_PACK", "ATTN_KERNEL_ATTENTION", "ATTN_KERNEL_WEIGHTS", "ATTN_TIMING_ALL"]:
         m = re.search(rf"#define {name}\s+(\d+)", src)
         assert m and int(m.group(1)) == getattr(ga, name), name
     for name in ["ATTN_OK", "ATTN_ERR_NULL_ARG", "ATTN_ERR_GEOMETRY", "ATTN_ERR_RANGE",
@@ -152,6 +152,7 @@ def test_null_context_refused(ga):
     assert ga.attn_prefill_append(None, inp, 256, 128, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_debug_prepare(None, inp, 64, 0, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_ctx_set_timing(None, 1) == ga.ATTN_ERR_NULL_ARG
+    assert ga.attn_ctx_set_timing_mask(None, 1 << ga.ATTN_KERNEL_ATTENTION) == ga.ATTN_ERR_NULL_ARG
     ga.attn_ctx_destroy(None)      # no-op
 
 

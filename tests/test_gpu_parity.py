@@ -373,6 +373,14 @@ def test_timing_hooks():
     assert n == 3 and ms > 0
     ms, n = ctx.read_timing(ga.ATTN_KERNEL_KV_PROLOGUE)
     assert n == 3 and ms > 0
+    # Only the attention kernel's launches.
+    ctx.set_timing(True, kernels=[ga.ATTN_KERNEL_ATTENTION])
+    for _ in range(2):
+        run(ctx, dp)
+    assert ctx.read_timing(ga.ATTN_KERNEL_KV_PROLOGUE) == (0.0, 0)
+    ms, n = ctx.read_timing(ga.ATTN_KERNEL_ATTENTION)
+    assert n == 2 and ms > 0
+    assert ga.attn_ctx_set_timing_mask(ctx.handle, ga.ATTN_TIMING_ALL + 1) == ga.ATTN_ERR_RANGE
     ctx.set_timing(False)
     ctx.close()
 
