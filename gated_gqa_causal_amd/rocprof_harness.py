@@ -348,7 +348,7 @@ def markdown(s: dict) -> str:
 
 
 def cmd_run(a) -> int:
-    out_dir = os.path.abspath(a.out or os.path.join(ROOT, "gpurun_out", f"prof_{a.workload}"))
+    out_dir = os.path.abspath(a.out or os.path.join("rocprof_out", a.workload))
     os.makedirs(out_dir, exist_ok=True)
     extra = shlex.split(a.bench_args)
     base = ["--workload", a.workload, "--no-cpu-baseline"] + extra
@@ -418,7 +418,7 @@ def main() -> int:
     r = sub.add_parser("run")
     r.add_argument("--workload", default="c2_dense_s8192_g4")
     r.add_argument("--bench-args", default="", help="extra bench.py flags, e.g. \"--weights\"")
-    r.add_argument("--out", default=None)
+    r.add_argument("--out", default=None, help="output folder (default rocprof_out/<workload>)")
     r.add_argument("--calibration", default=None, help="summary.json (or calibration JSON) of an earlier run")
     r.add_argument("--steps", type=int, default=20)
     r.add_argument("--warmup", type=int, default=3)

@@ -215,7 +215,7 @@ def pin_attention_vs_sdpa(o):
 
 
 def pin_bidirectional_vs_sdpa(o):
-    """Bidirectional pass (no causal predicate; the survey's vision-path variant):
+    """Bidirectional pass (no causal predicate; the vision-path variant of the attention-tile page):
     ungated context against float64 attention over every key, same bound as above."""
     for n, (T, Hq, Hkv) in enumerate([(1, 2, 1), (5, 4, 2), (37, 6, 2), (70, 8, 2)]):
         p = _problem(T, Hq, Hkv, seed=140 + n, causal=False)
