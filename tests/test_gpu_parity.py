@@ -318,6 +318,28 @@ def test_row_sums_at_max_tokens():
     assert np.all(np.abs(got - 1.0) <= 2e-3 * 4 + 2 ** -8), np.abs(got - 1).max()
 
 
+def test_library_max_tokens(orc):
+    """At the library's token cap: sampled rows against the oracle (row and key
+    offsets at their largest), and the last 1024 rows as a prefix window equal
+    to the full pass's rows bit for bit."""
+    import gated_gqa_causal_amd as ga
+    T = ga.ATTN_MAX_TOKENS
+    say(f"library max tokens T={T}, 4/1 heads")
+    p = synth.make_problem(T=T, n_q_heads=4, n_kv_heads=1, seed=41)
+    ctx = ga.Context(4, 1, T)
+    got = gpu_out(p, ctx)
+    rows = sample_rows(p.rows, k=16, seed=3)
+    want = oracle_rows(orc, p, rows)
+    bad, frac = parity_report(got[rows], want)
+    say(f"  rows={rows.size} bad={bad} worst bound fraction={frac:.3f}")
+    assert bad == 0
+    assert np.isfinite(bits_to_f32(got)).all()
+    pw = synth.make_problem(T=T, n_q_heads=4, n_kv_heads=1, seed=41, q_base=T - 1024)
+    win = gpu_out(pw, ctx)
+    ctx.close()
+    assert np.array_equal(win, got[T - 1024:])
+
+
 # --------------------------------------------------------------------------
 # Negative controls: the gate is not vacuous
 # --------------------------------------------------------------------------
