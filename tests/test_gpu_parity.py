@@ -340,6 +340,29 @@ def test_library_max_tokens(orc):
     assert np.array_equal(win, got[T - 1024:])
 
 
+def test_masked_library_max_tokens(orc):
+    """Masked pass at the token cap: a [32768][32768] u8 mask (each key visible
+    with probability 1/4, causality ANDed by the pass), so the longest row
+    block's tile list holds every one of its 1024 key tiles; sampled rows
+    against the oracle."""
+    import gated_gqa_causal_amd as ga
+    T = ga.ATTN_MAX_TOKENS
+    say(f"masked library max tokens T={T}, 4/1 heads")
+    p = synth.make_problem(T=T, n_q_heads=4, n_kv_heads=1, seed=42)
+    rng = np.random.default_rng(42)
+    mask = np.empty((T, T), dtype=np.uint8)
+    for r0 in range(0, T, 2048):
+        mask[r0:r0 + 2048] = rng.integers(0, 4, size=(2048, T), dtype=np.uint8) == 0
+    pm = synth.Problem(**{**p.__dict__, "mask": mask})
+    got = gpu_out(pm)
+    rows = sample_rows(pm.rows, k=16, seed=4)
+    want = oracle_rows(orc, pm, rows)
+    bad, frac = parity_report(got[rows], want)
+    say(f"  rows={rows.size} bad={bad} worst bound fraction={frac:.3f}")
+    assert bad == 0
+    assert np.isfinite(bits_to_f32(got)).all()
+
+
 # --------------------------------------------------------------------------
 # Negative controls: the gate is not vacuous
 # --------------------------------------------------------------------------
