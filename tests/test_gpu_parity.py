@@ -513,6 +513,28 @@ def test_batch_vs_oracle(orc):
         assert bad == 0
 
 
+def test_batch_at_the_token_cap(orc):
+    """The largest packed batch the cap admits: 1024 sequences of 1..32 tokens
+    (each starts on a 32-key tile, 1024 x 32 = 32768 keys), 1024 row blocks
+    in one launch, every sequence against the oracle."""
+    import gated_gqa_causal_amd as ga
+    rng = np.random.default_rng(5)
+    lens = [int(x) for x in rng.integers(1, 33, size=ga.ATTN_MAX_TOKENS // 32)]
+    lens[0], lens[-1] = 32, 1
+    b = synth.make_batch(lens, n_q_heads=4, n_kv_heads=1, seed=23)
+    say(f"batch at the cap: {len(lens)} sequences, {b.total} tokens")
+    got = _batch_out(b)
+    off = _offsets(b.lens)
+    worst, bad = 0.0, 0
+    for i, p in enumerate(b.seqs):
+        n, frac = parity_report(got[off[i]:off[i + 1]], orc.attention(p, threads=1))
+        bad += n
+        worst = max(worst, frac)
+    say(f"  bad={bad} worst bound fraction={worst:.3f}")
+    assert bad == 0
+    assert np.isfinite(bits_to_f32(got)).all()
+
+
 def test_batch_workload_sampled(orc):
     """The packed workload at full size: three sequences against their own
     launches bit for bit, sampled rows of three against the oracle."""
