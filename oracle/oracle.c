@@ -159,10 +159,21 @@ int oracle_prepare_keys(const oracle_problem *p, bf16_t *kp)
     if (p->n_pos < p->T)
         return -1;
     for (int32_t c = 0; c < Hkv; ++c)
-        for (int32_t j = 0; j < p->T; ++j)
-            oracle_norm_rope(p->k + ((size_t)j * Hkv + c) * D, p->k_norm_w,
-                             p->cos_tab + (size_t)j * (R / 2), p->sin_tab + (size_t)j * (R / 2),
+        for (int32_t j = 0; j < p->T; ++j) {
+#if ORACLE_MUTATION == 15
+            const int32_t pos = 0;                        /* key position ignored */
+#else
+            const int32_t pos = j;
+#endif
+#if ORACLE_MUTATION == 16
+            const int32_t src = 0;                        /* every KV head reads head 0's keys */
+#else
+            const int32_t src = c;
+#endif
+            oracle_norm_rope(p->k + ((size_t)j * Hkv + src) * D, p->k_norm_w,
+                             p->cos_tab + (size_t)pos * (R / 2), p->sin_tab + (size_t)pos * (R / 2),
                              D, R, p->rms_eps, kp + ((size_t)c * p->T + j) * D);
+        }
     return 0;
 }
 

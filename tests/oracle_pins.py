@@ -177,6 +177,79 @@ def pin_rope_relative_position(o):
         assert abs(vals[0] - want) <= tol, f"rotary score {vals[0]} vs float64 {want}"
 
 
+def _prologue_err(n, rotary_dim=64):
+    """Per-element bound on |prepared - exact| for a vector whose exact (float64)
+    normed value is n: the norm's one rounding (plus fp32 noise) on every dim,
+    and on the rotary pairs the roundings of cos/sin, of both products and of
+    the sum (relative to |a| + |b| of the pair)."""
+    half = rotary_dim // 2
+    e = 2 * U * np.abs(n)
+    ab = np.abs(n[..., :half]) + np.abs(n[..., half:rotary_dim])
+    e[..., :half] = 5 * U * ab
+    e[..., half:rotary_dim] = 5 * U * ab
+    return e + 1e-30
+
+
+def pin_prepare_keys_f64(o):
+    """Each prepared key is the float64 (1+w) RMSNorm of its own raw row, rotated at
+    the key's own position, for its own KV head: positions and heads come from the
+    raw inputs here, not from the oracle (the QSA kernel page, "Semantics": every
+    key is normed and partially rotated once per KV head at its position)."""
+    for T, Hkv, seed in [(300, 3, 19), (70, 2, 20)]:
+        p = _problem(T, 2 * Hkv, Hkv, seed=seed)
+        got = bf(o.prepare_keys(p))                          # [Hkv][T][D]
+        n = rmsnorm_f64(bf(p.k), bf(p.k_norm_w), 1e-6)       # [T][Hkv][D]
+        want = rope_f64(n, np.arange(T)[:, None]).transpose(1, 0, 2)
+        tol = _prologue_err(n).transpose(1, 0, 2)
+        bad = np.abs(got - want) > tol
+        assert not bad.any(), (f"prepared keys vs float64 norm + rotation at the key's position and head: "
+                               f"{bad.sum()} of {bad.size} (T={T}, Hkv={Hkv})")
+
+
+def pin_prepare_queries_f64(o):
+    """Each prepared query is the float64 (1+w) RMSNorm of the q half of its own head's
+    slice of the fused row, rotated at absolute position q_base + i."""
+    for T, Hq, Hkv, qb, seed in [(90, 6, 2, 0, 21), (300, 4, 2, 128, 22)]:
+        p = _problem(T, Hq, Hkv, q_base=qb, seed=seed)
+        got = bf(o.prepare_queries(p))                       # [rows][Hq][D]
+        n = rmsnorm_f64(bf(p.qg[:, :, 0, :]), bf(p.q_norm_w), 1e-6)
+        want = rope_f64(n, (qb + np.arange(p.rows))[:, None])
+        bad = np.abs(got - want) > _prologue_err(n)
+        assert not bad.any(), f"prepared queries vs float64 (q_base={qb}): {bad.sum()} of {bad.size}"
+
+
+def pin_attention_from_raw_vs_sdpa(o):
+    """Whole path from the raw inputs: float64 norm + rotation of raw q and k at
+    absolute positions, then float64 scaled-dot-product attention (torch, its own
+    GQA mapping and mask), against the oracle's ungated context.  Bound: the three
+    roundings after the scores (as in pin_attention_vs_sdpa) plus the prologue's:
+    a score moves by at most ds = sum_d (eq|k| + |q|ek + eq ek) / 16, which moves a
+    weight by a factor within exp(+-2 max ds)."""
+    for n_, (T, Hq, Hkv, qb, mb) in enumerate(_GEOMS):
+        p = _problem(T, Hq, Hkv, q_base=qb, seed=200 + n_, mask_budget=mb)
+        r = o.attention(p, want_ctx=True)
+        nq = rmsnorm_f64(bf(p.qg[:, :, 0, :]), bf(p.q_norm_w), 1e-6)          # [rows][Hq][D]
+        nk = rmsnorm_f64(bf(p.k), bf(p.k_norm_w), 1e-6)                       # [T][Hkv][D]
+        q64 = rope_f64(nq, (qb + np.arange(p.rows))[:, None])
+        k64 = rope_f64(nk, np.arange(T)[:, None]).transpose(1, 0, 2)          # [Hkv][T][D]
+        eq, ek = _prologue_err(nq), _prologue_err(nk).transpose(1, 0, 2)
+        v = bf(p.v)
+        want = sdpa_f64(q64, k64, v, qb, p.mask)
+        absv = sdpa_f64(q64, k64, np.abs(v), qb, p.mask)
+        smax = score_max_f64(q64, k64, qb, p.mask)
+        G = Hq // Hkv
+        kk, ekk = np.repeat(k64, G, axis=0), np.repeat(ek, G, axis=0)         # [Hq][T][D]
+        ds = (np.einsum("rhd,htd->rht", eq, np.abs(kk)) + np.einsum("rhd,htd->rht", np.abs(q64), ekk)
+              + np.einsum("rhd,htd->rht", eq, ekk)) / 16.0
+        dmax = ds.max(axis=-1)                                                # over keys (a bound)
+        got = bf(r["ctx"]).reshape(want.shape)
+        tol = (1.5 * (U * np.abs(want) + U * (1.0 + 2.0 * smax[..., None]) * absv)
+               + 1.1 * np.expm1(2.0 * dmax)[..., None] * absv + 1e-7)
+        bad = np.abs(got - want) > tol
+        assert not bad.any(), (f"context from raw inputs vs float64 attention, geometry {n_}: "
+                               f"{bad.sum()} of {bad.size}")
+
+
 # --------------------------------------------------------------------------
 # Attention core and gate
 # --------------------------------------------------------------------------
@@ -194,7 +267,8 @@ _GEOMS = [
 
 def pin_attention_vs_sdpa(o):
     """Ungated context against float64 scaled-dot-product attention on the oracle's
-    own prepared q/k (library routine with its own GQA mapping and mask handling).
+    own prepared q/k (library routine with its own GQA mapping and mask handling);
+    the prepared q/k themselves are pinned from the raw inputs above.
 
     First-order bound from the three remaining bf16 roundings: score (perturbs the
     weights by at most 2*U*max|s|), weight (U), context (U)."""

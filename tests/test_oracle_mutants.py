@@ -29,6 +29,8 @@ MUTANTS = {
     12: "last visible key dropped from the context",
     13: "K read in place of V",
     14: "causal predicate kept in the bidirectional pass",
+    15: "keys rotated at position 0 (key position ignored)",
+    16: "every KV head's prepared keys taken from KV head 0",
 }
 
 
