@@ -3,6 +3,9 @@ run it through the library's C ABI (via the thin Python binding)."""
 
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -79,3 +82,97 @@ def parity_report(got_bits: np.ndarray, ref_bits: np.ndarray):
     err = np.abs(g - r)
     bad = ~(err <= bound)          # NaN counts as bad
     return int(bad.sum()), float(np.nanmax(err / bound)) if err.size else 0.0
+
+
+# --------------------------------------------------------------------------
+# Deviation in row-scale bf16 quanta
+# --------------------------------------------------------------------------
+# The contract bound above has an absolute floor of 1e-2, which at long
+# sequences is as large as the outputs themselves (the late rows of an
+# 8192-token pass have a median |out| near 0.005), so it cannot see a wrong
+# late row.  The scale that can: the bf16 spacing at the root-mean-square of
+# the row-head's 256 oracle outputs, q = 2^(floor(log2 rms) - 7).  The GPU
+# rounds the unnormalised weight exp2(y - m) and divides by the row sum at the
+# end, where the oracle rounds the normalised weight: each weight differs by at
+# most two bf16 roundings, errors of random sign over the keys, so the
+# context's deviation has an rms of about u sqrt(sum w^2 v^2), under one or two
+# quanta of the row's scale (a numpy model of the two rounding schemes gives
+# at most 1.06 over rows of the 8192-token workload; the GPU at most 1.43 over
+# every workload and edge case).  A 10% error in a row is at least 12.8 quanta
+# rms, a 6% one (one 32-key tile dropped from a late row) at least 7.7, so the
+# rms bound sits at 3.  A single element may be off by a bf16 step of its own
+# value (a score rounding that flips, summed in another order); an element at
+# 8-16x the row's rms has a step of 8-16 quanta, so the element bound is
+# max(16 quanta, two steps of the element).
+QUANTA_RMS_MAX = 3.0       # per row-head rms of the deviation
+QUANTA_ELEM_MAX = 16.0     # any single element (or two bf16 steps of it, if larger)
+
+
+def row_scale_quanta(got_bits: np.ndarray, ref_bits: np.ndarray, n_heads: int):
+    """Deviations in quanta of each row-head's scale.
+
+    Returns (per-element quanta [rows][Hq][D], per row-head rms quanta
+    [rows][Hq], mask of row-heads whose oracle outputs are all zero)."""
+    g = bits_to_f32(got_bits).astype(np.float64).reshape(got_bits.shape[0], n_heads, -1)
+    r = bits_to_f32(ref_bits).astype(np.float64).reshape(ref_bits.shape[0], n_heads, -1)
+    rms = np.sqrt(np.mean(r * r, axis=-1))
+    zero = rms == 0.0
+    q = np.where(zero, 1.0, 2.0 ** (np.floor(np.log2(np.where(zero, 1.0, rms))) - 7))
+    d = np.abs(g - r) / q[..., None]
+    d = np.where(np.isnan(d), np.inf, d)
+    return d, np.sqrt(np.mean(d * d, axis=-1)), zero
+
+
+def quanta_histogram(d: np.ndarray):
+    """Counts of element deviations (row-scale quanta) in the bins 0, (0,1], (1,2], (2,4], (4,8], (8,16], >16."""
+    edges = [0.0, 1.0, 2.0, 4.0, 8.0, 16.0]
+    h = {"0": int((d == 0).sum())}
+    lo = 0.0
+    for e in edges[1:]:
+        h[f"<={e:g}"] = int(((d > lo) & (d <= e)).sum())
+        lo = e
+    h[">16"] = int((d > 16.0).sum())
+    return h
+
+
+def parity_record(label: str, got_bits: np.ndarray, ref_bits: np.ndarray, n_heads: int, rows=None):
+    """Contract bound + row-scale quanta of one comparison; appends the record to
+    the file named by ATTN_PARITY_LOG (one JSON object per line) when set, and
+    returns it.  The caller asserts on it with check_parity."""
+    bad, frac = parity_report(got_bits, ref_bits)
+    d, rq, zero = row_scale_quanta(got_bits, ref_bits, n_heads)
+    g = got_bits.reshape(got_bits.shape[0], n_heads, -1)
+    r = bits_to_f32(ref_bits).astype(np.float64).reshape(d.shape)
+    ar = np.abs(r)
+    step = np.where(ar > 0, 2.0 ** (np.floor(np.log2(np.where(ar > 0, ar, 1.0))) - 7), 0.0)
+    q = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
+    q = np.where(q > 0, 2.0 ** (np.floor(np.log2(np.where(q > 0, q, 1.0))) - 7), 1.0)
+    outliers = int((d[~zero] * q[~zero] > np.maximum(QUANTA_ELEM_MAX * q[~zero], 2.0 * step[~zero])).sum())
+    rec = {
+        "case": label, "rows": int(got_bits.shape[0]), "elements": int(got_bits.size),
+        "bound_violations": bad, "worst_bound_frac": round(frac, 4),
+        "rms_quanta_max": round(float(rq[~zero].max()) if (~zero).any() else 0.0, 3),
+        "rms_quanta_median": round(float(np.median(rq[~zero])) if (~zero).any() else 0.0, 3),
+        "elem_quanta_max": round(float(d[~zero].max()) if (~zero).any() else 0.0, 2),
+        "elem_outliers": outliers,
+        "hist": quanta_histogram(d[~zero]),
+        "zero_rows_nonzero": int((g[zero] != 0).sum()),
+        "identical": round(float(np.mean(got_bits == ref_bits)), 4),
+    }
+    if rows is not None:
+        rec["first_rows"] = [int(x) for x in np.asarray(rows)[:4]]
+    path = os.environ.get("ATTN_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+    return rec
+
+
+def check_parity(rec):
+    """The contract bound on every element, the row-scale quanta bounds (rms per
+    row-head, and each element within max(16 quanta, two bf16 steps of itself)),
+    and exact zeros where the oracle's row-head is all zero (no visible key)."""
+    assert rec["bound_violations"] == 0, rec
+    assert rec["zero_rows_nonzero"] == 0, rec
+    assert rec["rms_quanta_max"] <= QUANTA_RMS_MAX, rec
+    assert rec["elem_outliers"] == 0, rec

@@ -2,11 +2,20 @@
 "What changed": the kernel also writes the normalised bf16 weights, which its
 golden checks) against the oracle's weights.
 
-Per element |gpu - oracle| <= 1e-2 + 1e-2 |oracle| (the output tolerance);
-the visibility pattern is bit-exact: every hidden key's weight is exactly 0.
+Per visible key |gpu - oracle| <= 0.07 |oracle|: both are one bf16 rounding of
+the same normalised weight (two roundings apart at most, 2 x 2^-7), computed
+from scores that agree unless the fp32 dot product, summed in another order,
+lands on the other side of a bf16 rounding boundary (one bf16 step of the dot,
+at most 1/32 in the score for |q.k| < 128, a factor exp(1/32) on the weight).
+The visibility pattern is bit-exact: every hidden key's weight is exactly +0,
+every visible key's positive.  Row sums (fp32 over the bf16 weights) are 1
+within 2u (the two roundings of each weight on the GPU's side, u = 2^-8), and
+within 2e-3 for rows with at least 1024 visible keys (the QSA kernel page's
+review, item F2: row sums at the token cap), including every row at the cap.
 The pass's own output must equal the plain entry point's, bit for bit.
 """
 
+import os
 import sys
 
 import numpy as np
@@ -24,8 +33,10 @@ from gpu_util import DevProblem, bits_to_f32, make_ctx, run, to_bits  # noqa: E4
 @pytest.fixture(scope="module", autouse=True)
 def gpu():
     if not torch.cuda.is_available():
+        if os.environ.get("ATTN_REQUIRE_GPU") == "1":
+            pytest.fail("ATTN_REQUIRE_GPU=1 but no GPU is visible")
         pytest.skip("no GPU")
-    import gated_gqa_causal_amd  # noqa: F401
+    import gated_gqa_causal_amd  # noqa: F401  (fails loudly if the library is missing)
     yield
 
 
@@ -65,24 +76,36 @@ def _weights(ctx, p, rows=None):
     return to_bits(out), to_bits(plain), bits_to_f32(to_bits(w))
 
 
+U = 2.0 ** -8
+WEIGHT_REL = 0.07
+
+
 def _check(p, rows, got_w, want, label):
     vis = _visible(p, rows)
     ref = want["weights"]
     assert got_w.shape == ref.shape
-    hidden = ~vis[:, None, :].repeat(p.n_q_heads, axis=1)
-    assert np.all(got_w[hidden] == 0.0), "a hidden key has a non-zero weight"
+    visb = np.broadcast_to(vis[:, None, :], got_w.shape)
+    assert np.all(got_w[~visb] == 0.0), "a hidden key has a non-zero weight"
+    assert not np.signbit(got_w).any(), "a negative weight or -0"
+    assert np.all(got_w[visb] > 0.0), "a visible key has a zero weight"
     err = np.abs(got_w.astype(np.float64) - ref)
     bound = 1e-2 + 1e-2 * np.abs(ref)
     bad = int((~(err <= bound)).sum())
-    pos = ref > 1e-3
-    rel = float(np.max(err[pos] / ref[pos])) if pos.any() else 0.0
+    rel = err[visb] / ref[visb] if visb.any() else np.zeros(1)
+    ulps = err[visb] / (2.0 ** (np.floor(np.log2(ref[visb])) - 7)) if visb.any() else np.zeros(1)
     sums = got_w.astype(np.float64).sum(axis=2)
-    any_vis = vis.any(axis=1)
-    say(f"  {label}: bad={bad} of {ref.size}  worst rel (w>1e-3)={rel:.4f}  "
+    nvis = vis.sum(axis=1)
+    any_vis = nvis > 0
+    dev = np.abs(sums - 1.0)
+    say(f"  {label}: bad={bad} of {ref.size}  worst rel={float(rel.max()):.4f}  "
+        f"within 1 / 2 bf16 steps: {np.mean(ulps <= 1):.5f} / {np.mean(ulps <= 2):.5f}  "
         f"identical={np.mean(got_w == ref):.4f}  max |row sum - 1|="
-        f"{np.max(np.abs(sums[any_vis] - 1.0)) if any_vis.any() else 0.0:.4f}")
+        f"{float(dev[any_vis].max()) if any_vis.any() else 0.0:.2e}")
     assert bad == 0
-    assert np.all(np.abs(sums[any_vis] - 1.0) <= 1e-2)
+    assert float(rel.max()) <= WEIGHT_REL, f"worst relative weight error {rel.max()}"
+    assert np.all(dev[any_vis] <= 2 * U + 1e-5)
+    long_rows = nvis >= 1024
+    assert np.all(dev[long_rows] <= 2e-3), float(dev[long_rows].max())
     assert np.all(sums[~any_vis] == 0.0)
 
 
@@ -157,3 +180,38 @@ def test_weights_reuse_context_smaller_call(orc):
     assert np.array_equal(out, plain)
     want = orc.attention(small, rows=np.arange(small.rows, dtype=np.int32), want_weights=True, threads=8)
     _check(small, np.arange(small.rows), got_w, want, "reuse_small")
+
+
+def test_weights_at_the_token_cap(orc):
+    """The weights of a causal pass at the library's token cap (32768 keys, 2 query
+    heads on one KV head: 4 GiB of weights): every row sums to 1 within 2e-3 (the
+    QSA kernel page's review, item F2), every key past its row is exactly 0, and
+    sampled rows match the oracle's weights."""
+    import gated_gqa_causal_amd as ga
+    T = ga.ATTN_MAX_TOKENS
+    say(f"weights at the token cap T={T}")
+    p = synth.make_problem(name="weights_cap", T=T, n_q_heads=2, n_kv_heads=1, seed=34)
+    ctx = ga.Context(2, 1, T)
+    dp = DevProblem(p)
+    out, w = ctx.prefill_weights(*dp.args(), kind=0)
+    torch.cuda.synchronize()
+    worst, future_nz, visible_zero = 0.0, 0, 0
+    keys = torch.arange(T, device="cuda")
+    for r0 in range(0, T, 2048):
+        rows = torch.arange(r0, r0 + 2048, device="cuda")
+        chunk = w[r0:r0 + 2048]
+        sums = chunk.float().sum(dim=2)
+        worst = max(worst, float((sums - 1.0).abs().max()))
+        future = (keys[None, :] > rows[:, None])[:, None, :]
+        nz = chunk != 0
+        future_nz += int((nz & future).sum())
+        visible_zero += int((~nz & ~future).sum())
+    say(f"  max |row sum - 1| = {worst:.3g}; keys past their row with a non-zero weight: {future_nz}; "
+        f"visible keys at zero: {visible_zero}")
+    assert worst <= 2e-3
+    assert future_nz == 0 and visible_zero == 0
+    rows = np.array([0, 1, 31, 32, 4095, 16383, 16384, 32766, 32767], dtype=np.int32)
+    got_w = bits_to_f32(to_bits(w[torch.as_tensor(rows.astype(np.int64), device="cuda")]))
+    ctx.close()
+    want = orc.attention(p, rows=rows, want_weights=True, threads=len(rows))
+    _check(p, rows, got_w, want, "cap")
