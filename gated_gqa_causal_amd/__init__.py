@@ -27,6 +27,7 @@ ATTN_MAX_GROUP = 16
 ATTN_MAX_TOKENS = 32768
 ATTN_QBASE_ALIGN = 128
 ATTN_MAX_SEQS = 4096
+ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 ATTN_OK = 0
 ATTN_ERR_NULL_ARG = -1
@@ -86,6 +87,8 @@ def _load():
                                            ctypes.POINTER(vp)]),
         "attn_ctx_destroy": (None, [vp]),
         "attn_prefill_gated": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, vp]),
+        "attn_prefill_gated_noalloc": (ctypes.c_int, [ctypes.POINTER(attn_geometry), ctypes.POINTER(attn_inputs),
+                                                      i32, vp, vp]),
         "attn_prefill_prefix": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp]),
         "attn_prefill_masked": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, vp, vp]),
         "attn_prefill_bidirectional": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, vp]),
@@ -151,6 +154,12 @@ def attn_ctx_destroy(ctx: Optional[int]) -> None:
 
 def attn_prefill_gated(ctx, inputs: attn_inputs, S: int, out: int, stream: int) -> int:
     return lib.attn_prefill_gated(ctx, ctypes.byref(inputs), S, out, stream)
+
+
+def attn_prefill_gated_noalloc(geom: attn_geometry, inputs: Optional[attn_inputs], S: int, out: Optional[int],
+                               stream: Optional[int]) -> int:
+    return lib.attn_prefill_gated_noalloc(ctypes.byref(geom), None if inputs is None else ctypes.byref(inputs),
+                                          S, out, stream)
 
 
 def attn_prefill_prefix(ctx, inputs: attn_inputs, T: int, q_base: int, out: int, stream: int) -> int:

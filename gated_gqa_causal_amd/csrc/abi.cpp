@@ -105,25 +105,32 @@ int current_device_matches(const attn_ctx *ctx)
     return ATTN_OK;
 }
 
-void fill_kv_params(ga::KvPrologueParams &kp, const attn_ctx *ctx, const attn_inputs *in, int T)
+// Prepared keys / transposed values of Hkv x tpad keys at kp_ws / vt_ws.
+void fill_kv_params_ws(ga::KvPrologueParams &kp, const attn_geometry &g, uint16_t *kp_ws, uint16_t *vt_ws,
+                       int tpad, const attn_inputs *in, int T)
 {
     kp.k = static_cast<const uint16_t *>(in->k);
     kp.v = static_cast<const uint16_t *>(in->v);
     kp.wk = static_cast<const uint16_t *>(in->k_norm_w);
     kp.cos_tab = in->cos_tab;
     kp.sin_tab = in->sin_tab;
-    kp.kp = ctx->kp;
-    kp.vt = ctx->vt;
+    kp.kp = kp_ws;
+    kp.vt = vt_ws;
     kp.T = T;
-    kp.Hkv = ctx->geom.n_kv_heads;
-    kp.Tpad = ctx->tpad;
+    kp.Hkv = g.n_kv_heads;
+    kp.Tpad = tpad;
     kp.tile0 = 0;
     kp.k_row0 = 0;
-    kp.eps = ctx->geom.rms_eps;
+    kp.eps = g.rms_eps;
     kp.tile_seg = nullptr;
     kp.seg = nullptr;
     kp.k8 = kp.v8 = nullptr;
     kp.k8s = kp.v8s = nullptr;
+}
+
+void fill_kv_params(ga::KvPrologueParams &kp, const attn_ctx *ctx, const attn_inputs *in, int T)
+{
+    fill_kv_params_ws(kp, ctx->geom, ctx->kp, ctx->vt, ctx->tpad, in, T);
 }
 
 // Bytes of a caller-owned K/V cache for a geometry: prepared keys and
@@ -142,18 +149,17 @@ size_t kv_cache_fp8_bytes(const attn_geometry &g)
     return 2 * (size_t)g.n_kv_heads * tpad * ATTN_HEAD_DIM + 2 * (size_t)g.n_kv_heads * tpad * 4;
 }
 
-void fill_attn_params(ga::AttnParams &ap, const attn_ctx *ctx, const attn_inputs *in, int T, int q_base,
-                      void *out)
+void fill_attn_params_ws(ga::AttnParams &ap, const attn_geometry &g, const uint16_t *kp_ws, const uint16_t *vt_ws,
+                         int tpad, int num_cus, const attn_inputs *in, int T, int q_base, void *out)
 {
-    const attn_geometry &g = ctx->geom;
     ap.qg = static_cast<const uint16_t *>(in->qg);
-    ap.kp = ctx->kp;
-    ap.vt = ctx->vt;
+    ap.kp = kp_ws;
+    ap.vt = vt_ws;
     ap.wq = static_cast<const uint16_t *>(in->q_norm_w);
     ap.cos_tab = in->cos_tab;
     ap.sin_tab = in->sin_tab;
-    ap.bits = ctx->mask_bits;
-    ap.tilevis = ctx->tile_vis;
+    ap.bits = nullptr;
+    ap.tilevis = nullptr;
     ap.out = static_cast<uint16_t *>(out);
     ap.S = T - q_base;
     ap.T = T;
@@ -163,15 +169,30 @@ void fill_attn_params(ga::AttnParams &ap, const attn_ctx *ctx, const attn_inputs
     ap.G = g.n_q_heads / g.n_kv_heads;
     ap.n_hg = (ap.G + ga::kHeadsPerBlock - 1) / ga::kHeadsPerBlock;
     ap.nrb = (ap.S + ga::kRowsPerBlock - 1) / ga::kRowsPerBlock;
-    ap.Tpad = ctx->tpad;
+    ap.Tpad = tpad;
     ap.W = (T + 31) / 32;
     ap.eps = g.rms_eps;
     // One workgroup per compute unit at most; each walks its share of the
     // work items (see the attention kernel).
-    ap.n_wg = (int)std::min<int64_t>((int64_t)ap.nrb * ap.Hkv * ap.n_hg, ctx->num_cus);
+    ap.n_wg = (int)std::min<int64_t>((int64_t)ap.nrb * ap.Hkv * ap.n_hg, num_cus);
     ap.pairs = nullptr;
     ap.seg = nullptr;
     ap.ml = nullptr;
+}
+
+void fill_attn_params(ga::AttnParams &ap, const attn_ctx *ctx, const attn_inputs *in, int T, int q_base,
+                      void *out)
+{
+    fill_attn_params_ws(ap, ctx->geom, ctx->kp, ctx->vt, ctx->tpad, ctx->num_cus, in, T, q_base, out);
+    ap.bits = ctx->mask_bits;
+    ap.tilevis = ctx->tile_vis;
+}
+
+// Scratch bytes the allocation-free pass over S tokens needs.
+size_t noalloc_bytes(const attn_geometry &g, int S)
+{
+    const size_t tpad = ((size_t)S + 63) / 64 * 64;
+    return 2 * (size_t)g.n_kv_heads * tpad * ATTN_HEAD_DIM * 2;
 }
 
 // Packed batch bookkeeping: ints of the per-call table for a workspace of
@@ -474,6 +495,46 @@ void attn_ctx_destroy(attn_ctx *ctx)
 int attn_prefill_gated(attn_ctx *ctx, const attn_inputs *in, int32_t S, void *out, void *stream)
 {
     return run(ctx, in, S, 0, 0, nullptr, out, stream);
+}
+
+int attn_prefill_gated_noalloc(const attn_geometry *geom, const attn_inputs *in, int32_t S, void *out,
+                               void *stream)
+{
+    static_assert(ga::kNoallocScratchBytes == ATTN_NOALLOC_SCRATCH_BYTES, "scratch size");
+    int rc = attn_validate(geom, in, S, 0, 0, nullptr, out);
+    if (rc != ATTN_OK)
+        return rc;
+    if (S == 0)
+        return ATTN_OK;
+    if (noalloc_bytes(*geom, S) > ga::kNoallocScratchBytes)
+        return ATTN_ERR_RANGE;
+    int device = -1, num_cus = 0;
+    if (hipGetDevice(&device) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+        num_cus <= 0) {
+        (void)hipGetLastError();
+        return ATTN_ERR_DEVICE;
+    }
+    uint16_t *scr = nullptr;
+    if (ga::noalloc_scratch(device, &scr) != hipSuccess) {
+        (void)hipGetLastError();
+        return ATTN_ERR_DEVICE;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    // The scratch holds this call's prepared keys, then its transposed values;
+    // every tile the attention reads is written by this call's prologue first.
+    const int tpad = (S + 63) / 64 * 64;
+    uint16_t *kp_ws = scr, *vt_ws = scr + (size_t)geom->n_kv_heads * tpad * ATTN_HEAD_DIM;
+    ga::KvPrologueParams kvp;
+    fill_kv_params_ws(kvp, *geom, kp_ws, vt_ws, tpad, in, S);
+    if (ga::launch_kv_prologue(kvp, (S + ga::kKeysPerTile - 1) / ga::kKeysPerTile, s) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+    ga::AttnParams ap;
+    fill_attn_params_ws(ap, *geom, kp_ws, vt_ws, tpad, num_cus, in, S, 0, out);
+    if (ga::launch_attention(ap, ga::AttnMode::Causal, s) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+    return ATTN_OK;
 }
 
 int attn_prefill_prefix(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, void *out,

@@ -72,6 +72,15 @@ constexpr int kRowsPerBlock = 64;
 constexpr int kKeysPerTile = 32;
 constexpr int kHeadsPerBlock = 4;
 
+// Scratch of the allocation-free entry point: prepared keys and transposed
+// values of one call (2 x Hkv x round_up(S, 64) x 256 bf16), one fixed array
+// per device (kernels.hip).
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+constexpr int kNoallocMaxDevices = 64;
+// The device address of this device's scratch array (the current device must
+// be `device`); looked up once per device with hipGetSymbolAddress.
+hipError_t noalloc_scratch(int device, uint16_t **ptr);
+
 hipError_t launch_kv_prologue(const KvPrologueParams &p, int ntiles, hipStream_t stream);
 hipError_t launch_kv_prologue_fp8(const KvPrologueParams &p, int ntiles, hipStream_t stream);
 hipError_t launch_kv_widen(const KvWidenParams &p, int ntiles, int Hkv, hipStream_t stream);

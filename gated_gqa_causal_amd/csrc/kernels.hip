@@ -37,6 +37,7 @@
 
 #include <hip/hip_runtime.h>
 #include <algorithm>
+#include <mutex>
 #include <stdint.h>
 
 #include "kernels.h"
@@ -1608,6 +1609,33 @@ __global__ __launch_bounds__(256) void mfma_clock_probe(int iters, long long *re
         rec[2 * blockIdx.x] = c1 - c0;
         rec[2 * blockIdx.x + 1] = r1 - r0;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: the prepared keys and
+// transposed values of one call, in the workspace's tile layout.  Every device
+// the library runs on holds its own copy until the process ends.  On the host
+// the array's name is only a stand-in for the symbol, never a device address:
+// host code uses the per-device address noalloc_scratch() returns.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint16_t scratch[kNoallocScratchBytes / sizeof(uint16_t)];
+
+hipError_t noalloc_scratch(int device, uint16_t **ptr)
+{
+    static std::mutex mu;
+    static uint16_t *addr[kNoallocMaxDevices] = {};
+    if (device < 0 || device >= kNoallocMaxDevices || !ptr)
+        return hipErrorInvalidValue;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        void *a = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !a)
+            return e != hipSuccess ? e : hipErrorInvalidSymbol;
+        addr[device] = static_cast<uint16_t *>(a);
+    }
+    *ptr = addr[device];
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

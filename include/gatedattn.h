@@ -140,6 +140,27 @@ ATTN_EXPORT void attn_ctx_destroy(attn_ctx *ctx);
 ATTN_EXPORT int attn_prefill_gated(attn_ctx *ctx, const attn_inputs *in, int32_t S, void *out, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the dense
+ * causal full pass of attn_prefill_gated without a context.  Same inputs,
+ * layouts and output, bit for bit; geom describes the call (S <= max_tokens).
+ * The prepared keys and transposed values go to a fixed scratch array in the
+ * library's device code, ATTN_NOALLOC_SCRATCH_BYTES per device, held by every
+ * device the library runs on until the process ends; the first call on a
+ * device looks its address up once (with that device current).  The call
+ * allocates nothing.  Limit: 2 * n_kv_heads * round_up(S, 64) * 256 * 2 bytes
+ * <= ATTN_NOALLOC_SCRATCH_BYTES (n_kv_heads * round_up(S, 64) <= 32768, e.g.
+ * 4 KV heads at 8192 tokens), else ATTN_ERR_RANGE before any device work.
+ * Errors as attn_prefill_gated, plus ATTN_ERR_DEVICE if the current device
+ * cannot be queried.  Every call on one device shares that device's scratch:
+ * calls that overlap on one device (other streams, other threads) race and
+ * must be ordered by the caller.  S == 0 is a no-op.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+ATTN_EXPORT int attn_prefill_gated_noalloc(const attn_geometry *geom, const attn_inputs *in, int32_t S, void *out,
+                                           void *stream);
+
+/*
  * Prefix-continuation window: keys at positions 0..T-1, query rows at
  * positions q_base..T-1 (qg holds T - q_base rows; out is device bf16
  * [T - q_base][Hq * D]).  q_base must be a multiple of ATTN_QBASE_ALIGN and

@@ -291,3 +291,19 @@ def test_one_hip_runtime_in_the_process():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
     assert r.stdout.splitlines()[0] == "1", r.stdout
+
+
+def test_noalloc_refusals_before_device_work(ga):
+    """The allocation-free entry point refuses on the host, before any device
+    call: past its scratch (n_kv_heads * round_up(S, 64) > 32768), past the
+    geometry's max_tokens, bad geometry, null pointers; S == 0 is a no-op."""
+    inp = _inputs(ga, n_pos=32768)
+    g = _geom(ga, n_q_heads=16, n_kv_heads=4, max_tokens=32768)
+    assert ga.attn_prefill_gated_noalloc(g, inp, 8193, FAKE, None) == ga.ATTN_ERR_RANGE
+    g2 = _geom(ga, n_q_heads=8, n_kv_heads=8, max_tokens=32768)
+    assert ga.attn_prefill_gated_noalloc(g2, inp, 4097, FAKE, None) == ga.ATTN_ERR_RANGE
+    assert ga.attn_prefill_gated_noalloc(_geom(ga, max_tokens=256), inp, 257, FAKE, None) == ga.ATTN_ERR_RANGE
+    assert ga.attn_prefill_gated_noalloc(_geom(ga, n_kv_heads=5), inp, 64, FAKE, None) == ga.ATTN_ERR_GEOMETRY
+    assert ga.attn_prefill_gated_noalloc(_geom(ga), None, 64, FAKE, None) == ga.ATTN_ERR_NULL_ARG
+    assert ga.attn_prefill_gated_noalloc(_geom(ga), inp, 64, None, None) == ga.ATTN_ERR_NULL_ARG
+    assert ga.attn_prefill_gated_noalloc(_geom(ga), inp, 0, None, None) == ga.ATTN_OK
