@@ -41,6 +41,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "schedule.h"
 
 namespace ga {
 
@@ -1072,21 +1073,17 @@ void attn_fwd8(AttnParams pk)
     const int hw = wave & 3;                        // head within the group of four
     const int blk = wave >> 2;                      // 32-row block; 1 = the lagging phase
 
-    // Work items (64-row block, KV head, head group) are numbered heaviest row
-    // block first (longest key walk; a packed batch lists its (sequence, row
-    // block) pairs in that order).  The launch has at most one workgroup per
-    // compute unit; workgroup b of P takes items in a snake order, b,
-    // 2P-1-b, 2P+b, 4P-1-b, ..., so that each pass pairs the heavy end of the
-    // list with the light end and the workgroups' totals stay level.
-    const int per_rb = pk.Hkv * pk.n_hg;
-    const int n_items = pk.nrb * per_rb;
+    // Work items (64-row block, KV head, head group), row blocks heaviest
+    // first (longest key walk; a packed batch lists its (sequence, row block)
+    // pairs in that order), are dealt to at most one workgroup per compute
+    // unit by sched_item: a snake order, KV heads kept to their own XCDs.
     const int P = (int)gridDim.x;
     fill_wq1(wq1, pk.wq);
     __syncthreads();
 #pragma clang loop unroll(disable)
     for (int pass = 0;; ++pass) {
-        const int item = pass * P + ((pass & 1) ? P - 1 - (int)blockIdx.x : (int)blockIdx.x);
-        if (item >= n_items)
+        SchedItem si;
+        if (!sched_item((int)blockIdx.x, P, pass, pk.nrb, pk.Hkv, pk.n_hg, si))
             break;
         if (pass > 0)
             __syncthreads();                         // the previous item is done with LDS
@@ -1101,18 +1098,17 @@ void attn_fwd8(AttnParams pk)
         AttnParams p = pk;
         int rb, ktile0 = 0;
         if (!BIDIR && !MASKED && pk.pairs) {
-            const int sq = pk.pairs[2 * (item / per_rb)];
-            rb = pk.pairs[2 * (item / per_rb) + 1];
+            const int sq = pk.pairs[2 * si.rbi];
+            rb = pk.pairs[2 * si.rbi + 1];
             p.S = p.T = pk.seg[4 * sq];
             p.q_base = 0;
             p.qg = pk.qg + (size_t)pk.seg[4 * sq + 1] * pk.Hq * 2 * D;
             p.out = pk.out + (size_t)pk.seg[4 * sq + 1] * pk.Hq * D;
             ktile0 = pk.seg[4 * sq + 2];
         } else {
-            rb = pk.nrb - 1 - item / per_rb;
+            rb = pk.nrb - 1 - si.rbi;
         }
-        const int rem = item % per_rb;
-        const int kvh = rem / p.n_hg, hg = rem % p.n_hg;
+        const int kvh = si.kvh, hg = si.hg;
         const int gidx = hg * 4 + hw;
         const bool active = gidx < p.G;
         const int h = kvh * p.G + (active ? gidx : 0);
