@@ -114,13 +114,34 @@ def kernel_algorithmic(p, rows: int, keys: int, new_keys: int, flops: float, wei
     return rec
 
 
+def cpu_info():
+    """(CPU model name, logical CPUs this process may run on)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    return model, avail
+
+
 def cpu_baseline(p, rows_target: int, threads: int):
+    """The oracle on a bounded row sample of the workload: its key prologue
+    (every key, all KV heads) and the attention of every `stride`-th row
+    ending at the last, all heads, spread over `threads` host threads.
+    Returns (the cpu_baseline record, the sampled rows, their oracle outputs)."""
     import numpy as np
     import oracle
     orc = oracle.get()
     stride = max(1, p.rows // rows_target)
     rows = np.arange(p.rows - 1, -1, -stride, dtype=np.int32)[::-1].copy()
-    kp = orc.prepare_keys(p)
 
     def pair_flops(rr):
         # 4 D FLOPs per visible (row, key, query head), as in the GPU's figure.
@@ -135,7 +156,9 @@ def cpu_baseline(p, rows_target: int, threads: int):
         return 4.0 * p.head_dim * p.n_q_heads * float(vis)
 
     t0 = time.perf_counter()
-    orc.attention(p, rows=rows, kp=kp, threads=threads)
+    kp = orc.prepare_keys(p)
+    t_keys = time.perf_counter() - t0
+    want = orc.attention(p, rows=rows, kp=kp, threads=threads)
     dt = time.perf_counter() - t0
     flops = pair_flops(rows)
     # One thread over a fixed subset (the last 64 rows, all heads).
@@ -143,12 +166,74 @@ def cpu_baseline(p, rows_target: int, threads: int):
     t1 = time.perf_counter()
     orc.attention(p, rows=last, kp=kp, threads=1)
     dt1 = time.perf_counter() - t1
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows.size} query rows (every {stride}th, ending at the last row) x "
-                      f"{p.n_q_heads} heads of {p.name}; keys prepared outside the timing; "
-                      f"{dt:.2f} s wall, {flops / 1e9:.1f} GFLOP",
-            "one_thread": {"value": pair_flops(last) / dt1 / 1e12, "unit": "TFLOP/s",
-                           "sample": f"the last {last.size} rows x {p.n_q_heads} heads, {dt1:.2f} s wall"}}
+    model, avail = cpu_info()
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "cores_available": avail, "cpu_model": model,
+           "cores_note": "the oracle's rows spread over at most 16 threads, the host share of one GPU",
+           "sample": f"{rows.size} query rows (every {stride}th, ending at the last row) x "
+                     f"{p.n_q_heads} heads of {p.name}, after the key prologue over all {p.T} keys "
+                     f"({t_keys:.2f} s, single-threaded, inside the timing); {dt:.2f} s wall, "
+                     f"{flops / 1e9:.1f} GFLOP",
+           "one_thread": {"value": pair_flops(last) / dt1 / 1e12, "unit": "TFLOP/s",
+                          "sample": f"the last {last.size} rows x {p.n_q_heads} heads (keys prepared "
+                                    f"beforehand), {dt1:.2f} s wall"}}
+    return rec, rows, want
+
+
+class TimingEvents:
+    """HIP events created with hipEventDisableSystemFence, through the HIP
+    runtime torch loaded: timing-only events whose recording neither writes
+    back nor invalidates the caches (torch's events carry a system-scope
+    fence, which at this step size adds tens of microseconds to each step)."""
+
+    def __init__(self, n: int):
+        import ctypes
+        import torch
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(0x20000000)) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e)
+
+    def record(self, i: int, stream):
+        if self.hip.hipEventRecord(self.ev[i], self.ct.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed(self, i: int, j: int) -> float:
+        ms = self.ct.c_float(0.0)
+        if self.hip.hipEventSynchronize(self.ev[j]) != 0 or \
+                self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
+def device_peak():
+    """Compute units and peak shader clock the device reports, and the dense
+    bf16 MFMA rate they give (4 SIMDs x 1024 FLOP per clock per compute unit)."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    mhz = None
+    try:
+        import ctypes
+        # The HIP runtime torch loaded (a second runtime in the process would
+        # not share its device state); hipDeviceAttributeClockRate = 5, kHz.
+        hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        val = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, 0) == 0 and val.value > 0:
+            mhz = val.value / 1000.0
+    except (OSError, AttributeError):
+        pass
+    return {"compute_units": cus, "peak_sclk_mhz": mhz,
+            "tflops": None if mhz is None else round(cus * 4 * 1024 * mhz * 1e6 / 1e12, 1)}
 
 
 def main():
@@ -177,6 +262,11 @@ def main():
     ap.add_argument("--time-all-kernels", action="store_true",
                     help="library events around every kernel (kv prologue, mask pack too), not only the "
                          "attention (and weights) kernel")
+    ap.add_argument("--preheat-ms", type=float, default=250.0,
+                    help="after the W warmup steps, run untimed steps until this much time has passed "
+                         "since the first one: the GPU takes 30-60 ms of load to leave its idle clocks")
+    ap.add_argument("--no-spread", action="store_true",
+                    help="skip the second run of K steps that gives the per-step median/p10/p90")
     ap.add_argument("--cold", action="store_true",
                     help="write a 512 MiB scrub buffer between timed steps (outside each step's events)")
     args = ap.parse_args()
@@ -307,10 +397,22 @@ def main():
         else:
             ctx.prefill_gated(qg, k, v, wq, wk, cos, sin, out=out, stream=stream)
 
+    tw = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} done")
+    # Pre-heat: from idle the shader clock ramps up over 30-60 ms of load (c2:
+    # 0.49 ms per step in the first 20 steps after the warmup, 0.458 from the
+    # 60th on), so untimed steps run on until preheat_ms have passed; the
+    # timed steps then measure the steady state.
+    pre_steps = 0
+    while (time.perf_counter() - tw) * 1e3 < args.preheat_ms:
+        for _ in range(10):
+            step()
+        pre_steps += 10
+        torch.cuda.synchronize()
+    preheat = {"steps": pre_steps, "ms": round((time.perf_counter() - tw) * 1e3, 1)}
+    log(f"warmup {args.warmup} done, pre-heat {pre_steps} more steps ({preheat['ms']} ms since the first)")
 
     # Library events (a few microseconds of stream time each) only around the
     # kernels the JSON line needs: the attention kernel for `roofline`, the
@@ -352,6 +454,33 @@ def main():
     mp_ms, mp_n = ctx.read_timing(ga.ATTN_KERNEL_MASK_PACK)
     w_ms, w_n = ctx.read_timing(ga.ATTN_KERNEL_WEIGHTS)
     ctx.set_timing(False)
+    spread = None
+    if step_ms is None and not args.no_spread:
+        # The per-step spread from a second run of K steps with a timing-only
+        # event between consecutive steps (so these steps are not the ones
+        # `value` is computed from), straight after the timed steps, before
+        # any host work lets the GPU idle and its clock drop.
+        te = TimingEvents(args.steps + 1)
+        te.record(0, stream)
+        for i in range(args.steps):
+            step()
+            te.record(i + 1, stream)
+        torch.cuda.synchronize()
+        sp = [te.elapsed(i, i + 1) for i in range(args.steps)]
+        te.close()
+        spread = {"median": round(float(np.median(sp)), 5), "p10": round(float(np.percentile(sp, 10)), 5),
+                  "p90": round(float(np.percentile(sp, 90)), 5),
+                  "from": "a second run of K steps, a timing-only event between consecutive steps"}
+    out_bits = out.view(torch.int16).cpu().numpy().view(np.uint16) if batch is None else None
+    bit_exact = None
+    if batch is None and cache is None and wbuf is None and mask is None and p.causal and p.rows >= 2048:
+        # The bit-exact index check on the benchmark's own inputs: a prefix
+        # window over the last rows (q_base a multiple of 128) equals the same
+        # rows of the timed pass.
+        qb = p.q_base + (p.rows // 2) // 128 * 128
+        win = ctx.prefill_prefix(qg[qb - p.q_base:], k, v, wq, wk, cos, sin, qb, stream=stream)
+        torch.cuda.synchronize()
+        bit_exact = {f"prefix_window_from_{qb}_equals_the_pass": bool(torch.equal(win, out[qb - p.q_base:]))}
     ms_per_step = total_ms / args.steps
     traffic_key = " ".join([args.workload] + [f for f, on in (("--cached", args.cached),
                                                               ("--fp8-cache", args.fp8_cache),
@@ -401,7 +530,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(traffic_key)},
+        "peak_from_device": device_peak(),
+        "warmup_preheat": preheat,
     }
+    if spread is not None:
+        rec["step_ms"] = spread
     if w_n:
         # Weights kernel: bf16 weights written, plus the queries, keys and row
         # statistics it reads once.
@@ -419,10 +552,24 @@ def main():
         rec["config"]["sequences"] = len(batch.seqs)
         rec["config"]["seq_lens"] = batch.lens
     ctx.close()
+    rec["parity"] = None
     if not args.no_cpu_baseline:
-        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        threads = args.cpu_threads or min(16, cpu_info()[1])
         log(f"cpu baseline: oracle on {args.cpu_rows} rows, {threads} threads")
-        rec["cpu_baseline"] = cpu_baseline(p, args.cpu_rows, threads)
+        rec["cpu_baseline"], rows_s, want = cpu_baseline(p, args.cpu_rows, threads)
+        if out_bits is not None:
+            # The timed pass's output on the oracle's sampled rows: the contract
+            # bound and the deviation in quanta of each row-head's scale.
+            sys.path.insert(0, os.path.join(ROOT, "tests"))
+            from gpu_util import QUANTA_RMS_MAX, parity_record
+            pr = parity_record(p.name, out_bits[rows_s], want, p.n_q_heads)
+            rec["parity"] = {"rows_vs_oracle": int(rows_s.size), "elements": pr["elements"],
+                             "contract_bound_violations": pr["bound_violations"],
+                             "worst_bound_frac": pr["worst_bound_frac"],
+                             "row_quanta_rms_max": pr["rms_quanta_max"], "row_quanta_rms_limit": QUANTA_RMS_MAX,
+                             "elem_quanta_max": pr["elem_quanta_max"], "elem_outliers": pr["elem_outliers"],
+                             "quanta_hist": pr["hist"], "identical": pr["identical"],
+                             "bit_exact": bit_exact}
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

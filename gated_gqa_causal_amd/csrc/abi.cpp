@@ -745,9 +745,12 @@ int attn_ctx_set_timing_mask(attn_ctx *ctx, int kernel_mask)
     if (current_device_matches(ctx) != ATTN_OK)
         return ATTN_ERR_DEVICE;
     if (kernel_mask && ctx->pool.empty()) {
+        // Timing-only events: no system-scope fence when they are recorded,
+        // so recording one neither writes back and invalidates the caches
+        // around the timed kernel nor slows the work that follows it.
         for (int i = 0; i < 8192; ++i) {
             hipEvent_t e;
-            if (hipEventCreate(&e) != hipSuccess)
+            if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess)
                 return ATTN_ERR_NOMEM;
             ctx->pool.push_back(e);
         }
