@@ -100,7 +100,6 @@ def _load():
         "attn_kv_cache_fp8_bytes": (ctypes.c_int, [ctypes.POINTER(attn_geometry),
                                                    ctypes.POINTER(ctypes.c_size_t)]),
         "attn_prefill_append_fp8": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp, vp]),
-        "attn_debug_prepare": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, i32, vp, vp, vp]),
         "attn_ctx_set_timing": (ctypes.c_int, [vp, ctypes.c_int]),
         "attn_ctx_set_timing_mask": (ctypes.c_int, [vp, ctypes.c_int]),
         "attn_ctx_read_timing": (ctypes.c_int, [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
@@ -207,10 +206,6 @@ def attn_kv_cache_fp8_bytes(geom: attn_geometry):
 def attn_prefill_append_fp8(ctx, inputs: attn_inputs, T: int, q_base: int, kv_cache8: int, out: int,
                             stream: int) -> int:
     return lib.attn_prefill_append_fp8(ctx, ctypes.byref(inputs), T, q_base, kv_cache8, out, stream)
-
-
-def attn_debug_prepare(ctx, inputs: attn_inputs, T: int, q_base: int, qp_out, kp_out, stream) -> int:
-    return lib.attn_debug_prepare(ctx, ctypes.byref(inputs), T, q_base, qp_out, kp_out, stream)
 
 
 def attn_ctx_set_timing(ctx, enable: bool) -> int:
@@ -475,22 +470,6 @@ class Context:
         if rc != ATTN_OK:
             raise AttnError(rc, "attn_prefill_weights")
         return out, weights
-
-    def debug_prepare(self, qg, k, v, q_norm_w, k_norm_w, cos, sin, q_base: int = 0, stream=None):
-        """Prepared queries [rows][Hq][D] and keys [Hkv][T][D] as the kernels see them."""
-        import torch
-        g = self.geom
-        T = k.shape[0]
-        rows = T - q_base
-        inp = self.inputs(qg, k, v, q_norm_w, k_norm_w, cos, sin, rows, T)
-        dev = f"cuda:{self.device}"
-        qp = torch.empty((rows, g.n_q_heads, ATTN_HEAD_DIM), dtype=torch.bfloat16, device=dev)
-        kp = torch.empty((g.n_kv_heads, T, ATTN_HEAD_DIM), dtype=torch.bfloat16, device=dev)
-        rc = attn_debug_prepare(self.handle, inp, T, q_base, qp.data_ptr() if rows else None,
-                                kp.data_ptr() if T else None, self._stream(stream))
-        if rc != ATTN_OK:
-            raise AttnError(rc, "attn_debug_prepare")
-        return qp, kp
 
     def set_timing(self, enable: bool, kernels=None):
         """Events around every launch (kernels None) or around the launches of

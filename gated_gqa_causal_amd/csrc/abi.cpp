@@ -19,6 +19,9 @@
 
 #include "gatedattn.h"
 #include "kernels.h"
+#ifdef ATTN_TEST_HOOKS
+#include "test_hooks.h"
+#endif
 
 struct attn_ctx {
     int device = -1;
@@ -699,6 +702,7 @@ int attn_prefill_gated_batch(attn_ctx *ctx, const attn_inputs *in, int32_t n_seq
     return ATTN_OK;
 }
 
+#ifdef ATTN_TEST_HOOKS
 int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, void *qp_out,
                        void *kp_out, void *stream)
 {
@@ -735,6 +739,7 @@ int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t 
     }
     return ATTN_OK;
 }
+#endif  // ATTN_TEST_HOOKS
 
 int attn_ctx_set_timing_mask(attn_ctx *ctx, int kernel_mask)
 {

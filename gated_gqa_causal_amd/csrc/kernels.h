@@ -89,8 +89,11 @@ enum class AttnMode { Causal, Masked, Bidirectional };
 hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stream);
 hipError_t launch_attn_weights(const AttnParams &p, AttnMode mode, uint16_t *weights, int num_cus,
                                hipStream_t stream);
-hipError_t launch_kp_unpack(const uint16_t *kp, int Tpad, int T, int Hkv, uint16_t *out, hipStream_t stream);
 hipError_t launch_mfma_clock_probe(int iters, int n_wg, long long *rec, float *sink, hipStream_t stream);
+#ifdef ATTN_TEST_HOOKS
+// Test build only: prepared keys / queries back in plain layouts.
+hipError_t launch_kp_unpack(const uint16_t *kp, int Tpad, int T, int Hkv, uint16_t *out, hipStream_t stream);
 hipError_t launch_q_prologue_debug(const AttnParams &p, uint16_t *qp, hipStream_t stream);
+#endif
 
 }  // namespace ga

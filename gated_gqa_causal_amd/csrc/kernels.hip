@@ -2,9 +2,10 @@
 //
 // The kernels of a call run on the caller's stream:
 //   kv_prologue  : (1+w) RMSNorm + partial RoPE of every key once per KV head
-//                  (the QSA kernel page, "What changed": all query heads of a
-//                  KV head read the same prepared key), and V transposed into
-//                  MFMA-ready key tiles.  Writes the context's workspace.
+//                  (the QSA kernel page, "What changed": a key is prepared a
+//                  single time and then shared by every query head of its KV
+//                  group), and V transposed into MFMA-ready key tiles.  Writes
+//                  the context's workspace.
 //   mask_pack    : masked path only.  uint8 [S][S] visibility -> one bit per
 //                  (row, key) with causality folded in, plus a per (64-row
 //                  block, 32-key tile) flag used to skip fully hidden tiles.
@@ -17,8 +18,9 @@
 //                  applies the sigmoid gate in the epilogue.
 //
 // Rounding points follow the QSA kernel page ("Semantics"; final commit
-// message): norms cast once, cos/sin cast to bf16 and the rotation done in
-// bf16, the score rounded to bf16 before the exact 1/16 scale, the weights
+// message): each normalised vector rounded to bf16 a single time, cos/sin
+// rounded to bf16 and the rotation done in bf16 arithmetic, the score
+// rounded to bf16 before the exact 1/16 scale, the weights
 // rounded to bf16 before the context product, the context rounded, the
 // sigmoid rounded before the final product.  The GPU's online softmax rounds
 // the unnormalised weight exp2(y - m) and divides by the fp32 row sum at the
@@ -355,6 +357,7 @@ __global__ __launch_bounds__(256) void kv_widen(KvWidenParams p)
     write_kv_tile(ks, vs, p.kp, p.vt, ((size_t)c * (p.Tpad / KT) + tile) * (size_t)(KT * D), tid);
 }
 
+#ifdef ATTN_TEST_HOOKS
 // Debug: prepared keys from the tiled layout back to plain [Hkv][T][D].
 // grid (ceil(T/32), Hkv), 256 threads.
 __global__ __launch_bounds__(256) void kp_unpack(const uint16_t *kp, int Tpad, int T, uint16_t *out)
@@ -367,6 +370,7 @@ __global__ __launch_bounds__(256) void kp_unpack(const uint16_t *kp, int Tpad, i
             *reinterpret_cast<uint4 *>(out + ((size_t)c * T + key) * D + ch * 8) = src[piece];
     }
 }
+#endif  // ATTN_TEST_HOOKS
 
 // ---------------------------------------------------------------------------
 // Mask packing (launch shape below).
@@ -458,6 +462,7 @@ __device__ __forceinline__ void fill_wq1(float *wq1, const uint16_t *wq)
         wq1[threadIdx.x] = 1.0f + bf2f(wq[threadIdx.x]);
 }
 
+#ifdef ATTN_TEST_HOOKS
 // Debug: prepared queries in a plain [rows][Hq][D] layout.
 // grid (ceil(S/64), ceil(Hq/4)), 256 threads: wave = one head, 64 rows.
 __global__ __launch_bounds__(256) void q_prologue_debug(AttnParams p, uint16_t *qp)
@@ -484,6 +489,7 @@ __global__ __launch_bounds__(256) void q_prologue_debug(AttnParams p, uint16_t *
         }
     }
 }
+#endif  // ATTN_TEST_HOOKS
 
 // ---------------------------------------------------------------------------
 // Attention helpers.
@@ -1381,21 +1387,9 @@ void attn_fwd8(AttnParams pk)
 // The weight stores bound the kernel: each wave stages WT_GROUP tiles of its
 // 32 rows and writes them as whole 128-byte row segments.
 // ---------------------------------------------------------------------------
-#ifndef WT_GROUP_TILES
-#define WT_GROUP_TILES 2
-#endif
-constexpr int WT_GROUP = WT_GROUP_TILES;             // tiles per staged group
+constexpr int WT_GROUP = 2;                         // tiles per staged group
 constexpr int WT_ROW = WT_GROUP * KT * 2 + 16;       // staging bytes per row (padded)
 constexpr int WT_SMEM = 2 * TILE_BYTES + 8 * 32 * WT_ROW;
-#ifndef WT_XCD
-#define WT_XCD 1
-#endif
-#ifndef WT_NT
-#define WT_NT 1
-#endif
-#ifndef WT_ROTATE
-#define WT_ROTATE 1
-#endif
 
 template <int MODE>   // 0 causal, 1 masked (causal and mask), 2 bidirectional
 __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout)
@@ -1409,8 +1403,8 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
     // Workgroups go to the eight XCDs in turn (linear id mod 8), each XCD with
     // its own L2.  Renumber so that XCD x takes the x-th eighth of the work,
     // ordered row block fastest: its blocks share a KV head and so its key tiles.
-    int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
-    if (WT_XCD) {
+    int bx, by, bz;
+    {
         const unsigned nb = gridDim.x * gridDim.y * gridDim.z, per = nb / 8;
         const unsigned b = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
         const unsigned wk = (b < per * 8) ? (b % 8) * per + b / 8 : b;
@@ -1450,7 +1444,7 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
     const int gper = (ngroups_all + gridDim.z - 1) / gridDim.z;
     const int g_begin = bz * gper;
     const int ng = max(min(gper, ngroups_all - g_begin), 0);
-    const int rot = (WT_ROTATE && ng > 0) ? (int)(((unsigned)bx * 5u + (unsigned)by * 3u) % (unsigned)ng) : 0;
+    const int rot = (ng > 0) ? (int)(((unsigned)bx * 5u + (unsigned)by * 3u) % (unsigned)ng) : 0;
     const int nq = ng * WT_GROUP;                        // walk positions
     auto tile_of = [&](int q) {
         int gg = q / WT_GROUP + rot;
@@ -1538,13 +1532,9 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
                 continue;
             uint16_t *dst = wout + ((size_t)row * p.Hq + h) * p.T + key;
             if (vec) {
-#if WT_NT
                 // Streaming store: the weights are not read again, and kept out
                 // of L2 they leave it to the key tiles the other blocks reuse.
                 __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(dst));
-#else
-                *reinterpret_cast<uint4 *>(dst) = v;
-#endif
             } else {
                 const uint32_t words[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -1696,15 +1686,16 @@ hipError_t launch_attn_weights(const AttnParams &p, AttnMode mode, uint16_t *wei
     return hipGetLastError();
 }
 
-hipError_t launch_kp_unpack(const uint16_t *kp, int Tpad, int T, int Hkv, uint16_t *out, hipStream_t stream)
-{
-    hipLaunchKernelGGL(kp_unpack, dim3((T + KT - 1) / KT, Hkv), dim3(256), 0, stream, kp, Tpad, T, out);
-    return hipGetLastError();
-}
-
 hipError_t launch_mfma_clock_probe(int iters, int n_wg, long long *rec, float *sink, hipStream_t stream)
 {
     hipLaunchKernelGGL(mfma_clock_probe, dim3(n_wg), dim3(256), 0, stream, iters, rec, sink);
+    return hipGetLastError();
+}
+
+#ifdef ATTN_TEST_HOOKS
+hipError_t launch_kp_unpack(const uint16_t *kp, int Tpad, int T, int Hkv, uint16_t *out, hipStream_t stream)
+{
+    hipLaunchKernelGGL(kp_unpack, dim3((T + KT - 1) / KT, Hkv), dim3(256), 0, stream, kp, Tpad, T, out);
     return hipGetLastError();
 }
 
@@ -1714,5 +1705,6 @@ hipError_t launch_q_prologue_debug(const AttnParams &p, uint16_t *qp, hipStream_
                        stream, p, qp);
     return hipGetLastError();
 }
+#endif  // ATTN_TEST_HOOKS
 
 }  // namespace ga

@@ -287,14 +287,6 @@ ATTN_EXPORT int attn_prefill_gated_batch(attn_ctx *ctx, const attn_inputs *in, i
                                          const int32_t *seq_lens, void *out, void *stream);
 
 /*
- * Test hook: writes the prepared (normed, rotated) queries and keys the
- * kernels use, in plain layouts.  qp_out: device bf16 [T - q_base][Hq][D]
- * (may be NULL); kp_out: device bf16 [Hkv][T][D] (may be NULL).
- */
-ATTN_EXPORT int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base,
-                       void *qp_out, void *kp_out, void *stream);
-
-/*
  * Per-kernel timing with HIP events recorded on the call's stream around
  * each launch.  enable != 0 creates an event pool (outside any timed
  * region) and starts recording for every kernel; 0 stops.

@@ -16,7 +16,7 @@
  *   2. (1+w) RMSNorm, fp32 throughout, one cast to bf16 at the end.
  *   3. Partial RoPE on the first R of D dims, rotate-half pairs (j, j+R/2),
  *      cos/sin taken from the shared fp32 table and cast to bf16, each
- *      product and the sum rounded to bf16 ("rotate in bf16").
+ *      product and the sum rounded to bf16 (the rotation is bf16 arithmetic).
  *   4. Score = bf16(q . k) then times 1/sqrt(D) (exact for D = 256).
  *   5. fp32 softmax over the rounded scores of the visible keys; the
  *      normalised weights are rounded to bf16 before the context reduction.
@@ -104,7 +104,8 @@ void oracle_bf16_round(const float *in, bf16_t *out, int64_t n)
  * (1+w) RMSNorm then partial RoPE of one head vector x[D] at table row
  * cos_row/sin_row (QSA kernel page, "Semantics": (1+w) RMSNorm at the model's
  * eps and 64-of-256 partial RoPE from the shared table; final commit message:
- * the norms cast once, cos/sin cast to bf16 and rotated in bf16).
+ * the normalised vector is rounded to bf16 a single time, the table's cos and
+ * sin are rounded to bf16, and the rotation's products and sums are bf16).
  */
 void oracle_norm_rope(const bf16_t *x, const bf16_t *w, const float *cos_row,
                       const float *sin_row, int32_t D, int32_t R, float eps, bf16_t *out)

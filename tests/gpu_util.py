@@ -41,6 +41,52 @@ class DevProblem:
         return (self.qg, self.k, self.v, self.wq, self.wk, self.cos, self.sin)
 
 
+_TEST_LIB = None
+
+
+def test_lib():
+    """The test build of the library (libgatedattn_test.so: the full C ABI plus
+    the test hooks), loaded beside the product library; its contexts are its
+    own.  Built by build() next to the product library."""
+    global _TEST_LIB
+    if _TEST_LIB is None:
+        import ctypes
+        import gated_gqa_causal_amd as ga      # torch first, then the HIP runtime it loaded
+        lib = ctypes.CDLL(ga.LIBPATH.replace("libgatedattn.so", "libgatedattn_test.so"))
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        lib.attn_ctx_create.argtypes = [ctypes.POINTER(ga.attn_geometry), ctypes.c_int, ctypes.POINTER(vp)]
+        lib.attn_ctx_create.restype = ctypes.c_int
+        lib.attn_ctx_destroy.argtypes = [vp]
+        lib.attn_ctx_destroy.restype = None
+        lib.attn_debug_prepare.argtypes = [vp, ctypes.POINTER(ga.attn_inputs), i32, i32, vp, vp, vp]
+        lib.attn_debug_prepare.restype = ctypes.c_int
+        _TEST_LIB = lib
+    return _TEST_LIB
+
+
+def debug_prepare(dp: "DevProblem", q_base: int = 0):
+    """Prepared queries [rows][Hq][D] and keys [Hkv][T][D] (bf16 tensors) as the
+    kernels compute them, through the test build's attn_debug_prepare."""
+    import ctypes
+    import gated_gqa_causal_amd as ga
+    p = dp.p
+    lib = test_lib()
+    geom = ga.geometry(p.n_q_heads, p.n_kv_heads, max(p.T, 1), p.rms_eps)
+    h = ctypes.c_void_p()
+    rc = lib.attn_ctx_create(ctypes.byref(geom), torch.cuda.current_device(), ctypes.byref(h))
+    assert rc == ga.ATTN_OK, rc
+    inp = ga.attn_inputs(dp.qg.data_ptr(), dp.k.data_ptr(), dp.v.data_ptr(), dp.wq.data_ptr(), dp.wk.data_ptr(),
+                         dp.cos.data_ptr(), dp.sin.data_ptr(), dp.cos.shape[0])
+    qp = torch.empty((p.T - q_base, p.n_q_heads, 256), dtype=torch.bfloat16, device="cuda")
+    kp = torch.empty((p.n_kv_heads, p.T, 256), dtype=torch.bfloat16, device="cuda")
+    rc = lib.attn_debug_prepare(h, ctypes.byref(inp), p.T, q_base, qp.data_ptr(), kp.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    lib.attn_ctx_destroy(h)
+    assert rc == ga.ATTN_OK, rc
+    return qp, kp
+
+
 def make_ctx(p: synth.Problem, max_tokens=None):
     import gated_gqa_causal_amd as ga
     return ga.Context(p.n_q_heads, p.n_kv_heads, max_tokens or max(p.T, 1), p.rms_eps)

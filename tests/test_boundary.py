@@ -150,7 +150,6 @@ def test_null_context_refused(ga):
     assert ga.attn_prefill_masked(None, inp, 64, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_prefill_bidirectional(None, inp, 64, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_prefill_append(None, inp, 256, 128, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
-    assert ga.attn_debug_prepare(None, inp, 64, 0, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_ctx_set_timing(None, 1) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_ctx_set_timing_mask(None, 1 << ga.ATTN_KERNEL_ATTENTION) == ga.ATTN_ERR_NULL_ARG
     ga.attn_ctx_destroy(None)      # no-op
@@ -307,3 +306,21 @@ def test_noalloc_refusals_before_device_work(ga):
     assert ga.attn_prefill_gated_noalloc(_geom(ga), None, 64, FAKE, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_prefill_gated_noalloc(_geom(ga), inp, 64, None, None) == ga.ATTN_ERR_NULL_ARG
     assert ga.attn_prefill_gated_noalloc(_geom(ga), inp, 0, None, None) == ga.ATTN_OK
+
+
+def test_test_hooks_only_in_the_test_build(ga):
+    """The test hooks (csrc/test_hooks.h) are exported by the test build alone;
+    the product library has none of them."""
+    import ctypes
+    prod = ctypes.CDLL(ga.LIBPATH)
+    assert not hasattr(prod, "attn_debug_prepare")
+    test = ctypes.CDLL(ga.LIBPATH.replace("libgatedattn.so", "libgatedattn_test.so"))
+    src = open(os.path.join(ROOT, "gated_gqa_causal_amd", "csrc", "test_hooks.h")).read()
+    hooks = sorted(set(re.findall(r"ATTN_EXPORT\s+[\w\s\*]*?\b(attn_\w+)\s*\(", src)))
+    assert hooks == ["attn_debug_prepare"]
+    for n in declared_functions() + hooks:
+        assert hasattr(test, n), f"{n} not exported by the test build"
+    f = test.attn_debug_prepare
+    f.argtypes = [ctypes.c_void_p, ctypes.POINTER(ga.attn_inputs), ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, ctypes.byref(_inputs(ga)), 64, 0, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG

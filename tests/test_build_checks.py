@@ -120,3 +120,21 @@ def test_register_operand_parser():
     assert b._regs("v9") == {9}
     assert b._regs("a[0:15]") == set()
     assert b._regs("s0") == set()
+
+
+# ---- packed fp32 arithmetic ----------------------------------------------------
+
+def test_packed_fp32_arithmetic_is_refused():
+    bad = _lines("""
+    v_pk_mul_f32 v[0:1], v[2:3], v[4:5]
+    v_pk_fma_f32 v[6:7], v[2:3], v[4:5], v[6:7]
+    v_pk_add_f32 v[8:9], v[2:3], v[4:5] op_sel_hi:[1,1]
+    """)
+    assert len(b._check_no_packed_fp32("k", bad)) == 3
+    ok = _lines("""
+    v_pk_mov_b32 v[0:1], v[2:3], v[4:5] op_sel:[0,1]
+    v_pk_add_f16 v0, v1, v2
+    v_cvt_pk_bf16_f32 v3, v4, v5
+    v_mul_f32_e32 v6, v7, v8
+    """)
+    assert b._check_no_packed_fp32("k", ok) == []

@@ -39,8 +39,8 @@ def gpu():
     yield
 
 
-from gpu_util import (DevProblem, bits_to_f32, check_parity, gpu_out, make_ctx, parity_record,  # noqa: E402
-                      parity_report, run, to_bits)
+from gpu_util import (DevProblem, bits_to_f32, check_parity, debug_prepare, gpu_out, make_ctx,  # noqa: E402
+                      parity_record, parity_report, run, to_bits)
 
 _CFG = {}
 
@@ -72,20 +72,16 @@ def sample_rows(n_rows, k=48, seed=0):
 
 
 # --------------------------------------------------------------------------
-# Prologue: bit-exact prepared queries and keys
+# Prologue: bit-exact prepared queries and keys (through the test build's hook)
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,Hq,Hkv,qb", [(64, 24, 2, 0), (200, 16, 4, 0), (300, 4, 2, 128), (33, 2, 1, 0)])
 def test_prologue_bit_exact(orc, T, Hq, Hkv, qb):
     say(f"prologue T={T} Hq={Hq} Hkv={Hkv} q_base={qb}")
     p = synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, q_base=qb, seed=T)
-    ctx = make_ctx(p)
-    dp = DevProblem(p)
-    qp, kp = ctx.debug_prepare(*dp.args(), q_base=qb)
-    torch.cuda.synchronize()
+    qp, kp = debug_prepare(DevProblem(p), q_base=qb)
     assert np.array_equal(to_bits(kp), orc.prepare_keys(p)), "prepared keys differ"
     assert np.array_equal(to_bits(qp), orc.prepare_queries(p)), "prepared queries differ"
-    ctx.close()
 
 
 # --------------------------------------------------------------------------
