@@ -55,8 +55,13 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 prefix of the kernels' sources (kernels.hip and the headers it
+    builds from: the parameter blocks and the work schedule)."""
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "kernels.h", "schedule.h"):
+        with open(os.path.join(os.path.dirname(KERNEL_SOURCE), name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, path: str = TRAFFIC_FILE):
@@ -473,7 +478,8 @@ def main():
                   "from": "a second run of K steps, a timing-only event between consecutive steps"}
     out_bits = out.view(torch.int16).cpu().numpy().view(np.uint16) if batch is None else None
     bit_exact = None
-    if batch is None and cache is None and wbuf is None and mask is None and p.causal and p.rows >= 2048:
+    if (not args.no_cpu_baseline and batch is None and cache is None and wbuf is None and mask is None
+            and p.causal and p.rows >= 2048):
         # The bit-exact index check on the benchmark's own inputs: a prefix
         # window over the last rows (q_base a multiple of 128) equals the same
         # rows of the timed pass.

@@ -77,8 +77,13 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 prefix of the kernels' sources (kernels.hip and the headers it
+    builds from: the parameter blocks and the work schedule)."""
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "kernels.h", "schedule.h"):
+        with open(os.path.join(os.path.dirname(KERNEL_SOURCE), name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def kernel_key(name: str):
@@ -361,12 +366,16 @@ def cmd_run(a) -> int:
     else:
         cal = calibrate(out_dir, a.pmc_timeout)
     cmds = []
+    # (no second spread run: the summary takes the last `steps` launches)
     trace = run_pass("trace", ["--kernel-trace", "--stats"],
-                     base + ["--steps", str(a.steps), "--warmup", str(a.warmup)], out_dir, a.trace_timeout)
+                     base + ["--steps", str(a.steps), "--warmup", str(a.warmup), "--no-spread"], out_dir,
+                     a.trace_timeout)
     cmds.append(trace["cmd"])
     counters = {}
     for name, ctrs in PASSES.items():
-        r = run_pass(name, ["--pmc"] + ctrs, base + ["--steps", str(a.pmc_steps), "--warmup", "1"],
+        # Counts do not depend on the clock: no pre-heat under the counters.
+        r = run_pass(name, ["--pmc"] + ctrs, base + ["--steps", str(a.pmc_steps), "--warmup", "1",
+                                                     "--preheat-ms", "0", "--no-spread"],
                      out_dir, a.pmc_timeout)
         counters[name] = read_counters(r["dir"], last=a.pmc_steps)
         cmds.append(r["cmd"])
