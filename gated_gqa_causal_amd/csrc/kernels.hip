@@ -1146,7 +1146,18 @@ void attn_fwd8(AttnParams pk)
             __syncthreads();
             n = tile_count;
         }
-        auto tile_at = [&](int u) -> int { return MASKED ? tile_list[u] : u; };
+        // Masked: 64 consecutive walk entries from entry wbase on (clamped to
+        // the last), one per lane; the walk takes its tile numbers from this
+        // register by lane index rather than through an LDS read and wait.
+        // In interval k the walk needs entries k+1 .. k+3, and wbase is moved
+        // to k+1 whenever k+1 is a multiple of 32, so they stay inside it.
+        int walk_win = 0, wbase = 0;
+        auto walk_window = [&](int base) {
+            if (MASKED) {
+                wbase = base;
+                walk_win = tile_list[min(base + lane, n - 1)];
+            }
+        };
 
         const uint32_t smem_base = lds_addr(smem);
         const uint16_t *kbase = p.kp + ((size_t)kvh * (p.Tpad / KT) + ktile0) * (KT * D);
@@ -1161,7 +1172,9 @@ void attn_fwd8(AttnParams pk)
             tile = __builtin_amdgcn_readfirstlane(tile);
             return (is_k ? kbase : vbase) + (size_t)tile * (KT * D);
         };
-        auto tile_clamped = [&](int u) { return tile_at(min(u, n - 1)); };
+        auto tile_clamped = [&](int u) -> int {
+            return MASKED ? __builtin_amdgcn_readlane(walk_win, u - wbase) : min(u, n - 1);
+        };
         // Masked: the 64 rows' visibility words of a tile, next to its K copy;
         // wave w moves the words of rows 8w .. 8w+7 (lane L writes word L).
         const uint32_t bits_base = lds_addr(bitsbuf);
@@ -1178,7 +1191,7 @@ void attn_fwd8(AttnParams pk)
             const uint16_t *src = src_of(is_k, tile_clamped(u));
             const uint32_t m0 = m0_of(is_k, u);
             dma16<0, true>(src, voff, m0);
-            dma16<1024, false>(src, voff, m0);
+            dma16<1024, MASKED>(src, voff, m0);
         };
         // Interval k's copies (issued in the wave's scores half): K(k+3) and
         // V(k+1), two parts each.
@@ -1190,14 +1203,14 @@ void attn_fwd8(AttnParams pk)
                     if (slot == 1)
                         dma16<0, true>(src, voff, m0);
                     else
-                        dma16<1024, false>(src, voff, m0);
+                        dma16<1024, MASKED>(src, voff, m0);
                 } else if (slot == 9 || slot == 13) {
                     const uint16_t *src = src_of(false, tile_clamped(k + 1));
                     const uint32_t m0 = m0_of(false, k + 1);
                     if (slot == 9)
                         dma16<0, true>(src, voff, m0);
                     else
-                        dma16<1024, false>(src, voff, m0);
+                        dma16<1024, MASKED>(src, voff, m0);
                 } else if (MASKED && slot == 3) {
                     load_bits(tile_clamped(k + 3), (k + 3) & 7);
                 }
@@ -1214,6 +1227,7 @@ void attn_fwd8(AttnParams pk)
         };
 
         if (!MASKED || n > 0) {
+            walk_window(0);
 #pragma unroll
             for (int u = 0; u < 3; ++u) {
                 load_tile(true, u);
@@ -1350,6 +1364,8 @@ void attn_fwd8(AttnParams pk)
                 close_interval();
 #pragma clang loop unroll(disable)
             for (int k = 1; k < n; ++k) {
+                if (MASKED && ((k + 1) & 31) == 0)
+                    walk_window(k + 1);
                 s_half8(kaddr_of(k), qf, s, issue_loads(k));
                 if (lag)
                     close_interval();
@@ -1361,15 +1377,14 @@ void attn_fwd8(AttnParams pk)
             }
             if (lag)
                 close_interval();
-            if (!MASKED)
-                load_gates();                            // the last context half covers the latency
+        }
+        load_gates();                                    // the last context half covers the latency
+        if (!MASKED || n > 0) {
             pv_half8<MASKED, true, false>(vaddr_of(n - 1), o, pw, s, m, l, alpha, 0u);
             if (!lag)
                 close_interval();
         }
-        if (MASKED)
-            load_gates();                                // (with nothing visible O and l stay zero)
-        epilogue();
+        epilogue();                                      // (masked, nothing visible: O and l stay zero)
     }
 }
 
