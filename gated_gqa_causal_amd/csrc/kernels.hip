@@ -1055,6 +1055,14 @@ __device__ __forceinline__ void pv_half8(uint32_t vaddr, f32x16 (&o)[8], u32x4 (
             __builtin_amdgcn_sched_barrier(0);
         }
         if (DO_SM && i >= 1) {
+            // The softmax reads s first through inline asm, for which the
+            // compiler inserts no wait states after the last score MFMA (the
+            // compiler's own); these complete the count on every path into
+            // this slot (the first tile has no context MFMAs before it).
+            if (i == 1 && DO_PV)
+                asm volatile("s_nop 4");
+            else if (i == 1)
+                asm volatile("s_nop 7\n\ts_nop 7");
             step(2 * i - 2);
             step(2 * i - 1);
         }

@@ -79,6 +79,72 @@ def test_scan_continues_through_a_label():
     assert len(b._check_asm_reads_of_mfma_results("k", asm)) == 1
 
 
+def test_short_path_through_a_taken_branch_is_refused():
+    # The fall-through is long enough; the branch target is reached after
+    # three wait states and reads the result at once.
+    asm = _lines("""
+    v_mfma_f32_32x32x16_bf16 v[0:15], v[20:23], v[24:27], v[0:15]
+    s_and_b64 vcc, exec, s[4:5]
+    s_cbranch_vccnz .LBB0_7
+    s_nop 7
+    s_nop 7
+    s_nop 7
+.LBB0_7:
+    ;;#ASMSTART
+    v_max3_f32 v30, v0, v1, v2
+    ;;#ASMEND
+    """)
+    probs = b._check_asm_reads_of_mfma_results("k", asm)
+    assert len(probs) == 1 and "after 2 wait states" in probs[0]
+    # The same through an unconditional branch to a label further down.
+    jump = _lines("""
+    v_mfma_f32_32x32x16_bf16 v[0:15], v[20:23], v[24:27], v[0:15]
+    s_branch .LBB0_9
+    s_nop 7
+    s_nop 7
+    s_nop 7
+.LBB0_9:
+    ;;#ASMSTART
+    v_max3_f32 v30, v0, v1, v2
+    ;;#ASMEND
+    """)
+    assert len(b._check_asm_reads_of_mfma_results("k", jump)) == 1
+
+
+def test_taken_branch_with_enough_wait_states_passes():
+    asm = _lines("""
+    v_mfma_f32_32x32x16_bf16 v[0:15], v[20:23], v[24:27], v[0:15]
+    s_cbranch_vccnz .LBB0_7
+    s_waitcnt vmcnt(4)
+    s_barrier
+.LBB0_7:
+    s_nop 7
+    s_nop 7
+    s_nop 4
+    ;;#ASMSTART
+    v_max3_f32 v30, v0, v1, v2
+    ;;#ASMEND
+    """)
+    assert b._check_asm_reads_of_mfma_results("k", asm) == []
+
+
+def test_a_later_mfma_of_the_chain_takes_over_the_count():
+    # The read is far from the chain's first MFMA and close to its last: one
+    # finding, against the last.
+    asm = _lines("""
+    v_mfma_f32_32x32x16_bf16 v[0:15], v[20:23], v[24:27], 0
+    s_nop 7
+    s_nop 7
+    s_nop 7
+    v_mfma_f32_32x32x16_bf16 v[0:15], v[28:31], v[32:35], v[0:15]
+    ;;#ASMSTART
+    v_max3_f32 v30, v0, v1, v2
+    ;;#ASMEND
+    """)
+    probs = b._check_asm_reads_of_mfma_results("k", asm)
+    assert len(probs) == 1 and "v[28:31]" in probs[0] and "after 0 wait states" in probs[0]
+
+
 # ---- a VALU result feeding an inline-asm MFMA operand ------------------------
 
 def test_valu_result_into_inline_mfma_operand():
