@@ -31,7 +31,7 @@ struct attn_ctx {
     int mask_words = 0;            // 32-key words per mask row at max_tokens
     uint16_t *kp = nullptr;        // prepared keys, [Hkv][tpad/32] tiles of 32 x 256
     uint16_t *vt = nullptr;        // transposed values, [Hkv][tpad/32] tiles of 256 x 32
-    uint32_t *mask_bits = nullptr; // [max_tokens][mask_words]
+    uint32_t *mask_bits = nullptr; // [mask_words][tpad]: key word major
     uint8_t *tile_vis = nullptr;   // [ceil(max_tokens/64)][mask_words]
     float *row_stats = nullptr;    // [max_tokens][Hq][2]: softmax max and sum (weights calls)
     // packed batches: the per-call sequence tables (device), staged through a
@@ -174,6 +174,7 @@ void fill_attn_params_ws(ga::AttnParams &ap, const attn_geometry &g, const uint1
     ap.nrb = (ap.S + ga::kRowsPerBlock - 1) / ga::kRowsPerBlock;
     ap.Tpad = tpad;
     ap.W = (T + 31) / 32;
+    ap.bstride = (ap.S + ga::kRowsPerBlock - 1) / ga::kRowsPerBlock * ga::kRowsPerBlock;
     ap.eps = g.rms_eps;
     // One workgroup per compute unit at most; each walks its share of the
     // work items (see the attention kernel).
@@ -341,6 +342,7 @@ int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kin
         mp.tilevis = ctx->tile_vis;
         mp.S = T;
         mp.W = ap.W;
+        mp.bstride = ap.bstride;
         mp.vec16 = (T % 16 == 0) && aligned16(mask);
         Timer tm(ctx, s, ATTN_KERNEL_MASK_PACK);
         if (ga::launch_mask_pack(mp, ap.nrb, s) != hipSuccess)
@@ -453,7 +455,7 @@ int attn_ctx_create(const attn_geometry *geom, int device, attn_ctx **out)
     const size_t nrb = (size_t)(geom->max_tokens + 63) / 64;
     bool ok = hipMalloc(&ctx->kp, kv_elems * 2) == hipSuccess &&
               hipMalloc(&ctx->vt, kv_elems * 2) == hipSuccess &&
-              hipMalloc(&ctx->mask_bits, (size_t)geom->max_tokens * ctx->mask_words * 4) == hipSuccess &&
+              hipMalloc(&ctx->mask_bits, (size_t)ctx->tpad * ctx->mask_words * 4) == hipSuccess &&
               hipMalloc(&ctx->tile_vis, nrb * ctx->mask_words) == hipSuccess &&
               hipMalloc(&ctx->row_stats, (size_t)geom->max_tokens * geom->n_q_heads * 2 * sizeof(float)) ==
                   hipSuccess;

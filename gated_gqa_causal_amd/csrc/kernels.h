@@ -38,9 +38,10 @@ struct KvWidenParams {
 
 struct MaskPackParams {
     const uint8_t *mask;      // [S][S]
-    uint32_t *bits;           // [S][W]
+    uint32_t *bits;           // [W][bstride]: key word major, rows contiguous
     uint8_t *tilevis;         // [nrb][W]
     int S, W;
+    int bstride;              // rows per key word: S rounded up to 64 (pad rows 0)
     int vec16;                // mask rows may be read 16 bytes at a time
 };
 
@@ -51,11 +52,12 @@ struct AttnParams {
     const uint16_t *wq;       // [256]
     const float *cos_tab;     // [n_pos][32]
     const float *sin_tab;     // [n_pos][32]
-    const uint32_t *bits;     // [S][W] (masked only)
+    const uint32_t *bits;     // [W][bstride] (masked only; MaskPackParams)
     const uint8_t *tilevis;   // [nrb][W] (masked only)
     uint16_t *out;            // [S][Hq][256]
     int S, T, q_base;
     int Hq, Hkv, G, n_hg, nrb, Tpad, W;
+    int bstride;              // masked only: rows per key word of bits
     int n_wg;                 // attention workgroups (<= work items)
     float eps;
     // Packed batch (else null): pairs[2 i ..] = {sequence, row block} of the

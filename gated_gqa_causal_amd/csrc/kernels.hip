@@ -374,7 +374,9 @@ __global__ __launch_bounds__(256) void kp_unpack(const uint16_t *kp, int Tpad, i
 
 // ---------------------------------------------------------------------------
 // Mask packing (launch shape below).
-// bits[row][w] bit b = mask[row][32w+b] != 0 && 32w+b <= row && 32w+b < S.
+// bits[w][row] bit b = mask[row][32w+b] != 0 && 32w+b <= row && 32w+b < S
+// (key word major: a tile's words of consecutive rows are adjacent; rows
+// S .. bstride-1 get zero words).
 // tilevis[rb][w] = any bit of the 64 x 32 block.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t nz_bits4(uint32_t u)
@@ -431,15 +433,18 @@ __global__ __launch_bounds__(256) void mask_pack(MaskPackParams p)
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const int row = row0 + r;
-        uint32_t word = words[r];
         const int last = row - key0;                   // keys key0..row are causal
         if (last < 0)
-            word = 0;
+            words[r] = 0;
         else if (last < 31)
-            word &= (2u << last) - 1u;
-        if (w < p.W && row < p.S)
-            p.bits[(size_t)row * p.W + w] = word;
-        any |= word;
+            words[r] &= (2u << last) - 1u;
+        any |= words[r];
+    }
+    // The 8 rows' words are adjacent in bits (row0 + 7 < bstride, 32-byte aligned).
+    if (w < p.W) {
+        uint4 *dst = reinterpret_cast<uint4 *>(p.bits + (size_t)w * p.bstride + row0);
+        dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
+        dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
     }
     anyw[rg][wl] = any;
     __syncthreads();
@@ -1184,14 +1189,15 @@ void attn_fwd8(AttnParams pk)
             return MASKED ? __builtin_amdgcn_readlane(walk_win, u - wbase) : min(u, n - 1);
         };
         // Masked: the 64 rows' visibility words of a tile, next to its K copy;
-        // wave w moves the words of rows 8w .. 8w+7 (lane L writes word L).
+        // wave w moves the words of rows 8w .. 8w+7 (lane L writes word L),
+        // 32 adjacent bytes of the key-word-major bits.
         const uint32_t bits_base = lds_addr(bitsbuf);
         auto load_bits = [&](int tile, int slot) {
             if (MASKED) {
                 tile = __builtin_amdgcn_readfirstlane(tile);
                 if ((lane >> 3) == wave) {
-                    const int row = min(r0 + lane, p.S - 1);   // rows past S read a real row
-                    dma4(p.bits, (uint32_t)(((size_t)row * p.W + tile) * 4), bits_base + (uint32_t)(slot * QW * 4));
+                    const int row = r0 + lane;                  // < bstride (pad rows hold zero words)
+                    dma4(p.bits, (uint32_t)(((size_t)tile * p.bstride + row) * 4), bits_base + (uint32_t)(slot * QW * 4));
                 }
             }
         };
@@ -1523,7 +1529,7 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
                 }
                 nbuf ^= 1;
                 if (MODE == 1)
-                    hide_all(s, p.bits[(size_t)rc * p.W + t] >> (4 * hh));
+                    hide_all(s, p.bits[(size_t)t * p.bstride + rc] >> (4 * hh));
                 else if (MODE == 0 && t >= diag)
                     hide_all(s, (t == diag ? diag_vis : 0u) >> (4 * hh));
                 // rbf, not the inline-asm round_op: the scores come from the
