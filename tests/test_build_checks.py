@@ -204,3 +204,42 @@ def test_packed_fp32_arithmetic_is_refused():
     v_mul_f32_e32 v6, v7, v8
     """)
     assert b._check_no_packed_fp32("k", ok) == []
+
+
+# ---- a VALU-written SGPR address read by an LDS copy --------------------------
+
+def test_lds_copy_right_after_readfirstlane_of_its_address_is_refused():
+    asm = _lines("""
+    v_readfirstlane_b32 s8, v3
+    s_mov_b32 m0, s20
+    ;;#ASMSTART
+    s_nop 0
+    global_load_lds_dwordx4 v97, s[8:9] offset:0
+    ;;#ASMEND
+    """)
+    probs = b._check_vmem_sgpr_after_valu("k", asm)
+    assert len(probs) == 1 and "2 wait states" in probs[0]
+
+
+def test_lds_copy_after_salu_address_or_enough_wait_states_passes():
+    salu = _lines("""
+    v_readfirstlane_b32 s8, v3
+    s_lshl_b32 s10, s8, 14
+    s_add_u32 s12, s4, s10
+    s_addc_u32 s13, s5, 0
+    global_load_lds_dwordx4 v97, s[12:13] offset:0
+    """)
+    # The copy reads s[12:13], written by SALU instructions only.
+    assert b._check_vmem_sgpr_after_valu("k", salu) == []
+    padded = _lines("""
+    v_readlane_b32 s8, v3, 5
+    s_nop 4
+    global_load_lds_dwordx4 v97, s[8:9] offset:0x400
+    """)
+    assert b._check_vmem_sgpr_after_valu("k", padded) == []
+    label = _lines("""
+.LBB0_4:
+    global_load_lds_dword v97, s[8:9]
+    """)
+    assert len(b._check_vmem_sgpr_after_valu("k", label)) == 1
+
