@@ -119,6 +119,31 @@ def test_parity_full(orc, name, kw):
     check_parity(rec)
 
 
+def test_parity_full_block_sparse_mask(orc):
+    """Every row of a masked pass whose mask hides whole (64-row block, 32-key
+    tile) pairs: about 30% of each block's causal tiles, plus a quarter of the
+    remaining keys.  The walks (up to about 100 tiles) skip tiles and run past
+    the 32- and 64-entry boundaries of the tile list; all rows against the
+    oracle (a row whose keys are all hidden gives zeros)."""
+    T = 4096
+    say(f"parity_full block-sparse mask T={T}")
+    p = synth.make_problem(name="blocksparse", T=T, n_q_heads=8, n_kv_heads=2, seed=43)
+    rng = np.random.default_rng(43)
+    mask = (rng.random((T, T)) >= 0.25).astype(np.uint8)
+    nrb, ntile = (T + 63) // 64, (T + 31) // 32
+    off = rng.random((nrb, ntile)) < 0.3
+    off[:, 0] = False                                # row 0 keeps key 0 (no empty row block)
+    for rb in range(nrb):
+        for t in np.nonzero(off[rb])[0]:
+            mask[64 * rb:64 * rb + 64, 32 * t:32 * t + 32] = 0
+    pm = synth.Problem(**{**p.__dict__, "mask": mask})
+    got = gpu_out(pm)
+    want = orc.attention(pm, threads=8)
+    rec = parity_record("full block-sparse", got, want, pm.n_q_heads)
+    say(f"  {rec}")
+    check_parity(rec)
+
+
 # --------------------------------------------------------------------------
 # The workloads at full size, in the benchmark's launch configuration,
 # on sampled rows the oracle computes one by one
@@ -406,13 +431,15 @@ def test_hidden_keys_perturbation_invariance_per_row(name, rows):
     ctx.close()
 
 
-def test_hidden_keys_perturbation_invariance_per_block():
+def test_hidden_keys_perturbation_invariance_per_block(orc):
     """Per 64-row block of the masked workload: with the block's mask rows cleared on
     a random half of its 32-key tiles and a random quarter of the other keys, the
     keys hidden from all 64 rows (those, plus the block's causal future) are
     randomised in K and V; the block's 64 rows stay bit-identical.  The cleared
     tiles are skipped by the walk (no copy, no product), so this covers the
-    tile-skip path as well as the per-key hide."""
+    tile-skip path as well as the per-key hide; sampled rows of each block also
+    match the oracle (a walk over the wrong visible tiles would be invariant
+    too, but not equal to it)."""
     p = cfg("c4_masked_s8192")
     say("perturbation invariance per block, c4 with cleared tiles")
     rng = np.random.default_rng(7)
@@ -429,6 +456,10 @@ def test_hidden_keys_perturbation_invariance_per_block():
     dp = DevProblem(pm)
     ctx = make_ctx(pm)
     base = run(ctx, dp).clone()
+    rows = np.array([64 * rb + r for rb in blocks for r in (0, 17, 40, 63)], dtype=np.int32)
+    rec = parity_record("c4 cleared tiles", to_bits(base)[rows], oracle_rows(orc, pm, rows), pm.n_q_heads, rows)
+    say(f"  {rec}")
+    check_parity(rec)
     for rb in blocks:
         r0 = 64 * rb
         vis = (dp.mask[r0:r0 + 64] != 0) & _visible_rows(pm, np.arange(r0, r0 + 64), 0, pm.T, "cuda")
