@@ -19,6 +19,7 @@
 
 #include "gatedattn.h"
 #include "kernels.h"
+#include "schedule.h"
 #ifdef ATTN_TEST_HOOKS
 #include "test_hooks.h"
 #endif
@@ -42,6 +43,16 @@ struct attn_ctx {
     size_t batch_cap = 0;          // ints in each
     hipEvent_t batch_copied = nullptr;
     bool batch_pending = false;
+    // the attention kernel's work table (schedule.h's sched_plan) of the last
+    // launch shape, staged like the batch tables; kept while the shape repeats
+    int *sched_tab = nullptr;
+    int *sched_host = nullptr;
+    size_t sched_cap = 0;          // ints in each
+    hipEvent_t sched_copied = nullptr;
+    bool sched_pending = false;
+    bool sched_valid = false;      // sched_key holds the last shape planned
+    bool sched_use = false;        // and the table is in sched_tab (else the snake)
+    int sched_key[6] = {0, 0, 0, 0, 0, 0};
     // timing
     int timing = 0;                // bit (1 << ATTN_KERNEL_*) per timed kernel
     std::vector<hipEvent_t> pool;
@@ -182,6 +193,7 @@ void fill_attn_params_ws(ga::AttnParams &ap, const attn_geometry &g, const uint1
     ap.pairs = nullptr;
     ap.seg = nullptr;
     ap.ml = nullptr;
+    ap.sched = nullptr;
 }
 
 void fill_attn_params(ga::AttnParams &ap, const attn_ctx *ctx, const attn_inputs *in, int T, int q_base,
@@ -268,6 +280,49 @@ int plan_batch(const attn_geometry &g, int32_t n_seqs, const int32_t *lens, Batc
 
 // kind 4: `mask` is the caller's K/V cache; the prologue writes keys
 // q_base..T-1 into it (k and v hold only those rows) and attention reads it.
+// A work item's query prologue and epilogue, in key tiles of the walk (cycle
+// counts of the kernel: about 35 K cycles per item, 2.6 K per key tile).
+constexpr int kSchedOverheadTiles = 14;
+
+// The attention kernel's work table for ap's launch (a causal pass, row block
+// rbi walking the key tiles up to its last row's position): planned on the
+// host once per launch shape (schedule.h's sched_plan) and copied to the
+// device when it is more even than the snake order, which the kernel follows
+// otherwise.  The staging buffer is rewritten only after its previous copy
+// has landed.
+int attach_schedule(attn_ctx *ctx, ga::AttnParams &ap, hipStream_t s)
+{
+    const int key[6] = {ap.n_wg, ap.nrb, ap.Hkv, ap.n_hg, ap.T, ap.q_base};
+    if (!ctx->sched_valid || !std::equal(key, key + 6, ctx->sched_key)) {
+        std::vector<int> tiles((size_t)ap.nrb);
+        for (int rbi = 0; rbi < ap.nrb; ++rbi) {
+            const int p0 = ap.q_base + ga::kRowsPerBlock * (ap.nrb - 1 - rbi);
+            tiles[rbi] = std::min(p0 + ga::kRowsPerBlock - 1, ap.T - 1) / ga::kKeysPerTile + 1;
+        }
+        std::vector<int> table;
+        const bool use = ga::sched_plan(ap.n_wg, ap.nrb, ap.Hkv, ap.n_hg, tiles.data(), kSchedOverheadTiles, table);
+        ctx->sched_valid = false;
+        if (use) {
+            if (table.size() > ctx->sched_cap)
+                return ATTN_ERR_RANGE;
+            if (ctx->sched_pending && hipEventSynchronize(ctx->sched_copied) != hipSuccess)
+                return ATTN_ERR_LAUNCH;
+            ctx->sched_pending = false;
+            std::memcpy(ctx->sched_host, table.data(), table.size() * sizeof(int));
+            if (hipMemcpyAsync(ctx->sched_tab, ctx->sched_host, table.size() * sizeof(int), hipMemcpyHostToDevice,
+                               s) != hipSuccess ||
+                hipEventRecord(ctx->sched_copied, s) != hipSuccess)
+                return ATTN_ERR_LAUNCH;
+            ctx->sched_pending = true;
+        }
+        std::copy(key, key + 6, ctx->sched_key);
+        ctx->sched_valid = true;
+        ctx->sched_use = use;
+    }
+    ap.sched = ctx->sched_use ? ctx->sched_tab : nullptr;
+    return ATTN_OK;
+}
+
 int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kind, const uint8_t *mask,
         void *out, void *stream, void *weights = nullptr)
 {
@@ -353,6 +408,11 @@ int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kin
                               : kind == 3 ? ga::AttnMode::Bidirectional : ga::AttnMode::Causal;
     if (weights)
         ap.ml = ctx->row_stats;
+    if (mode != ga::AttnMode::Bidirectional) {
+        const int rc = attach_schedule(ctx, ap, s);
+        if (rc != ATTN_OK)
+            return rc;
+    }
     {
         Timer tm(ctx, s, ATTN_KERNEL_ATTENTION);
         if (ga::launch_attention(ap, mode, s) != hipSuccess)
@@ -463,6 +523,11 @@ int attn_ctx_create(const attn_geometry *geom, int device, attn_ctx **out)
     ok = ok && hipMalloc(&ctx->batch_tab, ctx->batch_cap * sizeof(int)) == hipSuccess &&
          hipHostMalloc(&ctx->batch_host, ctx->batch_cap * sizeof(int), hipHostMallocDefault) == hipSuccess &&
          hipEventCreateWithFlags(&ctx->batch_copied, hipEventDisableTiming) == hipSuccess;
+    const int n_hg = (geom->n_q_heads / geom->n_kv_heads + ga::kHeadsPerBlock - 1) / ga::kHeadsPerBlock;
+    ctx->sched_cap = (size_t)ctx->num_cus + 1 + nrb * geom->n_kv_heads * n_hg;
+    ok = ok && hipMalloc(&ctx->sched_tab, ctx->sched_cap * sizeof(int)) == hipSuccess &&
+         hipHostMalloc(&ctx->sched_host, ctx->sched_cap * sizeof(int), hipHostMallocDefault) == hipSuccess &&
+         hipEventCreateWithFlags(&ctx->sched_copied, hipEventDisableTiming) == hipSuccess;
     if (!ok) {
         (void)hipGetLastError();
         attn_ctx_destroy(ctx);
@@ -490,6 +555,11 @@ void attn_ctx_destroy(attn_ctx *ctx)
         (void)hipHostFree(ctx->batch_host);
     if (ctx->batch_copied)
         (void)hipEventDestroy(ctx->batch_copied);
+    (void)hipFree(ctx->sched_tab);
+    if (ctx->sched_host)
+        (void)hipHostFree(ctx->sched_host);
+    if (ctx->sched_copied)
+        (void)hipEventDestroy(ctx->sched_copied);
     for (hipEvent_t e : ctx->pool)
         (void)hipEventDestroy(e);
     if (prev >= 0 && prev != ctx->device)

@@ -68,6 +68,9 @@ struct AttnParams {
     // Optional (else null): per (row, query head) the softmax's final
     // reference max (raw score units) and row sum, [S][Hq][2] fp32.
     float *ml;
+    // Optional (else null: the snake order of schedule.h): the host's table of
+    // work items per workgroup (sched_plan), n_wg + 1 offsets then entries.
+    const int *sched;
 };
 
 constexpr int kRowsPerBlock = 64;

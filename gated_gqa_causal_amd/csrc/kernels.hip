@@ -1102,8 +1102,15 @@ void attn_fwd8(AttnParams pk)
 #pragma clang loop unroll(disable)
     for (int pass = 0;; ++pass) {
         SchedItem si;
-        if (!sched_item((int)blockIdx.x, P, pass, pk.nrb, pk.Hkv, pk.n_hg, si))
+        if (pk.sched) {
+            // (uniform values: the workgroup's own table entries)
+            const int o = __builtin_amdgcn_readfirstlane(pk.sched[blockIdx.x]) + pass;
+            if (o >= __builtin_amdgcn_readfirstlane(pk.sched[blockIdx.x + 1]))
+                break;
+            si = sched_unpack(__builtin_amdgcn_readfirstlane(pk.sched[P + 1 + o]));
+        } else if (!sched_item((int)blockIdx.x, P, pass, pk.nrb, pk.Hkv, pk.n_hg, si)) {
             break;
+        }
         if (pass > 0)
             __syncthreads();                         // the previous item is done with LDS
         // The lane index, rebuilt every pass by instructions the compiler

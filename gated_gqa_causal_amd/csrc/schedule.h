@@ -20,9 +20,19 @@
 // items are numbered (row block, KV head, head group), head group fastest,
 // over all workgroups.  Either way every item is taken exactly once, and what
 // an item computes does not depend on which workgroup takes it.
+//
+// A launch may instead carry a table made on the host by sched_plan (below):
+// per workgroup, the items it takes in order.  The snake keeps two rounds of
+// items level but not a third partial one (672 items on 256 workgroups: the
+// 160 that take a third item end up about 13% above the mean); the table
+// packs each KV head's items into that head's workgroups by first-fit
+// decreasing against the smallest capacity that fits them all.
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <vector>
 
 namespace ga {
 
@@ -37,19 +47,25 @@ __host__ __device__ inline bool sched_xcd_grouped(int P, int Hkv)
     return P % 8 == 0 && Hkv >= 1 && Hkv <= 8 && 8 % Hkv == 0;
 }
 
+// XCD-grouped form: the slot u (0 .. P/Hkv - 1) of workgroup b among the
+// workgroups of its KV head (b % 8) / (8 / Hkv).  The first W1 = W - W % n_hg
+// workgroups of every XCD (W = P / 8 on each) hold units of n_hg slots, unit
+// t on the head's XCD t % (8 / Hkv); the rest take the last slots in turn.
+__host__ __device__ inline int sched_slot(int b, int P, int Hkv, int n_hg)
+{
+    const int x = b % 8, k = b / 8, W = P / 8, xh = 8 / Hkv;
+    const int W1 = W - W % n_hg, xp = x % xh;
+    return (k < W1) ? ((k / n_hg) * xh + xp) * n_hg + k % n_hg : xh * W1 + (k - W1) * xh + xp;
+}
+
 // Item of workgroup b (of P) on pass `pass`; false once b has no more items
 // (then on every later pass too).
 __host__ __device__ inline bool sched_item(int b, int P, int pass, int nrb, int Hkv, int n_hg, SchedItem &it)
 {
     if (sched_xcd_grouped(P, Hkv)) {
-        const int x = b % 8, k = b / 8, W = P / 8, xh = 8 / Hkv;
-        const int Q = xh * W;                           // workgroups of one KV head
-        // Slot of workgroup (XCD x, k-th on it): the first W1 = W - W % n_hg
-        // workgroups of every XCD hold units of n_hg slots, unit t on the
-        // head's XCD t % xh; the rest take the last slots in turn.
-        const int W1 = W - W % n_hg, xp = x % xh;
-        const int u = (k < W1) ? ((k / n_hg) * xh + xp) * n_hg + k % n_hg
-                               : xh * W1 + (k - W1) * xh + xp;
+        const int x = b % 8, xh = 8 / Hkv;
+        const int Q = xh * (P / 8);                     // workgroups of one KV head
+        const int u = sched_slot(b, P, Hkv, n_hg);
         const int j = pass * Q + ((pass & 1) ? Q - 1 - u : u);
         if (j >= nrb * n_hg)
             return false;
@@ -66,6 +82,122 @@ __host__ __device__ inline bool sched_item(int b, int P, int pass, int nrb, int 
     it.rbi = item / per_rb;
     it.kvh = rem / n_hg;
     it.hg = rem % n_hg;
+    return true;
+}
+
+// A table entry: the item packed into one int.
+__host__ __device__ inline int sched_pack(int rbi, int kvh, int hg) { return (rbi << 16) | (kvh << 8) | hg; }
+__host__ __device__ inline SchedItem sched_unpack(int e) { return SchedItem{e >> 16, (e >> 8) & 0xff, e & 0xff}; }
+
+// Host only.  A table for the launch (P workgroups, nrb row blocks, Hkv KV
+// heads, n_hg head groups) when it is more even than the snake: weight of an
+// item = tiles[rbi] (key tiles its row block walks) + overhead (its prologue
+// and epilogue in tile units).  Per KV head (the whole launch when not
+// XCD-grouped) the items, heaviest first, go to the first of the head's
+// workgroups (in slot order) with room under a capacity C, C the smallest
+// that fits all (binary search from max(heaviest item, mean) up to the
+// snake's busiest).  table = P + 1 offsets, then per workgroup its entries
+// (sched_pack) in walk order.  Returns false, table empty, when the snake's
+// busiest workgroup is no heavier than the table's would be; *busiest_snake
+// and *busiest_table report the busiest load of the snake and of the schedule
+// kept (in weight units).
+inline bool sched_plan(int P, int nrb, int Hkv, int n_hg, const int *tiles, int overhead, std::vector<int> &table,
+                       long *busiest_snake = nullptr, long *busiest_table = nullptr)
+{
+    table.clear();
+    if (P <= 0 || nrb <= 0)
+        return false;
+    const bool grouped = sched_xcd_grouped(P, Hkv);
+    const int groups = grouped ? Hkv : 1;
+    // The snake's loads.
+    std::vector<long> snake(P, 0);
+    for (int b = 0; b < P; ++b) {
+        SchedItem it;
+        for (int pass = 0; sched_item(b, P, pass, nrb, Hkv, n_hg, it); ++pass)
+            snake[b] += tiles[it.rbi] + overhead;
+    }
+    const long snake_max = *std::max_element(snake.begin(), snake.end());
+    if (busiest_snake)
+        *busiest_snake = snake_max;
+    if (busiest_table)
+        *busiest_table = snake_max;
+    // Workgroups of each group in slot order; items of each group heaviest first.
+    std::vector<std::vector<int>> wg(groups);
+    if (grouped) {
+        const int xh = 8 / Hkv;
+        for (int c = 0; c < groups; ++c)
+            wg[c].assign(P / Hkv, -1);
+        for (int b = 0; b < P; ++b)
+            wg[(b % 8) / xh][sched_slot(b, P, Hkv, n_hg)] = b;
+    } else {
+        for (int b = 0; b < P; ++b)
+            wg[0].push_back(b);
+    }
+    std::vector<std::vector<int>> bins(P);
+    long plan_max = 0;
+    for (int c = 0; c < groups; ++c) {
+        std::vector<int> items;                          // packed entries
+        for (int rbi = 0; rbi < nrb; ++rbi)
+            for (int kvh = 0; kvh < Hkv; ++kvh)
+                if (!grouped || kvh == c)
+                    for (int hg = 0; hg < n_hg; ++hg)
+                        items.push_back(sched_pack(rbi, kvh, hg));
+        // rbi ascending is weight descending; the sort keeps that order on ties.
+        std::stable_sort(items.begin(), items.end(), [&](int a, int b) {
+            return tiles[sched_unpack(a).rbi] > tiles[sched_unpack(b).rbi];
+        });
+        const int Q = (int)wg[c].size();
+        long total = 0, heaviest = 0, group_snake = 0;
+        for (int e : items) {
+            total += tiles[sched_unpack(e).rbi] + overhead;
+            heaviest = std::max<long>(heaviest, tiles[sched_unpack(e).rbi] + overhead);
+        }
+        for (int b : wg[c])
+            group_snake = std::max(group_snake, snake[b]);
+        std::vector<long> load(Q);
+        std::vector<int> where(items.size());
+        auto fits = [&](long cap) {
+            std::fill(load.begin(), load.end(), 0);
+            for (size_t i = 0; i < items.size(); ++i) {
+                const long w = tiles[sched_unpack(items[i]).rbi] + overhead;
+                int q = 0;
+                while (q < Q && load[q] + w > cap)
+                    ++q;
+                if (q == Q)
+                    return false;
+                load[q] += w;
+                where[i] = q;
+            }
+            return true;
+        };
+        long lo = std::max(heaviest, (total + Q - 1) / Q), hi = group_snake;
+        if (!fits(hi))
+            return false;
+        while (lo < hi) {
+            const long mid = lo + (hi - lo) / 2;
+            if (fits(mid))
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        fits(hi);
+        plan_max = std::max(plan_max, *std::max_element(load.begin(), load.end()));
+        for (size_t i = 0; i < items.size(); ++i)
+            bins[wg[c][where[i]]].push_back(items[i]);
+    }
+    if (plan_max >= snake_max)
+        return false;
+    if (busiest_table)
+        *busiest_table = plan_max;
+    table.reserve(P + 1 + (size_t)nrb * Hkv * n_hg);
+    int off = 0;
+    for (int b = 0; b < P; ++b) {
+        table.push_back(off);
+        off += (int)bins[b].size();
+    }
+    table.push_back(off);
+    for (int b = 0; b < P; ++b)
+        table.insert(table.end(), bins[b].begin(), bins[b].end());
     return true;
 }
 

@@ -62,6 +62,51 @@ static void check(int T, int q_base, int Hq, int Hkv, int cus, bool print)
                     T, q_base, Hq, Hkv, cus, items, P, grouped ? "XCD-grouped" : "plain",
                     *std::max_element(load.begin(), load.end()), (double)total / P,
                     *std::max_element(xcd, xcd + 8), (double)total / std::min(P, 8));
+
+    // The host table (sched_plan), when it is more even than the snake.
+    std::vector<int> tiles(nrb);
+    for (int rbi = 0; rbi < nrb; ++rbi)
+        tiles[rbi] = tiles_of(nrb - 1 - rbi, T, q_base);
+    std::vector<int> table;
+    long bs = 0, bt = 0;
+    const bool use = ga::sched_plan(P, nrb, Hkv, n_hg, tiles.data(), 14, table, &bs, &bt);
+    CHECK(bs == *std::max_element(load.begin(), load.end()), "T=%d Hkv=%d: plan's snake busiest %ld", T, Hkv, bs);
+    if (!use) {
+        CHECK(table.empty() && bt == bs, "T=%d Hkv=%d: table returned with the snake kept", T, Hkv);
+        if (print)
+            std::printf("    table: none\n");
+        return;
+    }
+    CHECK(bt < bs, "T=%d Hkv=%d: table not more even (%ld vs %ld)", T, Hkv, bt, bs);
+    CHECK((long)table.size() == P + 1 + items, "T=%d Hkv=%d: table size %zu", T, Hkv, table.size());
+    if ((long)table.size() != P + 1 + items)
+        return;
+    std::vector<int> seen2((size_t)items, 0);
+    long tmax = 0;
+    CHECK(table[0] == 0 && table[P] == items, "T=%d Hkv=%d: table offsets", T, Hkv);
+    for (int b = 0; b < P; ++b) {
+        CHECK(table[b] <= table[b + 1], "T=%d Hkv=%d: offsets of workgroup %d", T, Hkv, b);
+        long l = 0;
+        for (int o = table[b]; o < table[b + 1]; ++o) {
+            const ga::SchedItem it = ga::sched_unpack(table[P + 1 + o]);
+            const bool ok = it.rbi >= 0 && it.rbi < nrb && it.kvh >= 0 && it.kvh < Hkv && it.hg >= 0 && it.hg < n_hg;
+            CHECK(ok, "T=%d Hkv=%d: table item out of range", T, Hkv);
+            if (!ok)
+                continue;
+            ++seen2[((size_t)it.rbi * Hkv + it.kvh) * n_hg + it.hg];
+            if (grouped)
+                CHECK((b % 8) / (8 / Hkv) == it.kvh, "T=%d Hkv=%d: table puts KV head %d on XCD %d", T, Hkv, it.kvh,
+                      b % 8);
+            l += tiles[it.rbi] + 14;
+        }
+        tmax = std::max(tmax, l);
+    }
+    for (size_t i = 0; i < seen2.size(); ++i)
+        CHECK(seen2[i] == 1, "T=%d q_base=%d Hq=%d Hkv=%d cus=%d: table item %zu taken %d times", T, q_base, Hq, Hkv,
+              cus, i, seen2[i]);
+    CHECK(tmax == bt, "T=%d Hkv=%d: table busiest %ld, reported %ld", T, Hkv, tmax, bt);
+    if (print)
+        std::printf("    table: busiest %ld (snake %ld)\n", bt, bs);
 }
 
 int main()
