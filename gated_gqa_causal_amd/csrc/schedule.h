@@ -25,7 +25,7 @@
 // per workgroup, the items it takes in order.  The snake keeps two rounds of
 // items level but not a third partial one (672 items on 256 workgroups: the
 // 160 that take a third item end up about 13% above the mean); the table
-// packs each KV head's items into that head's workgroups by first-fit
+// packs each KV head's row blocks into that head's workgroups by first-fit
 // decreasing against the smallest capacity that fits them all.
 #pragma once
 
@@ -92,15 +92,18 @@ __host__ __device__ inline SchedItem sched_unpack(int e) { return SchedItem{e >>
 // Host only.  A table for the launch (P workgroups, nrb row blocks, Hkv KV
 // heads, n_hg head groups) when it is more even than the snake: weight of an
 // item = tiles[rbi] (key tiles its row block walks) + overhead (its prologue
-// and epilogue in tile units).  Per KV head (the whole launch when not
-// XCD-grouped) the items, heaviest first, go to the first of the head's
-// workgroups (in slot order) with room under a capacity C, C the smallest
-// that fits all (binary search from max(heaviest item, mean) up to the
-// snake's busiest).  table = P + 1 offsets, then per workgroup its entries
-// (sched_pack) in walk order.  Returns false, table empty, when the snake's
-// busiest workgroup is no heavier than the table's would be; *busiest_snake
-// and *busiest_table report the busiest load of the snake and of the schedule
-// kept (in weight units).
+// and epilogue in tile units).  Per KV head in the XCD-grouped form (the
+// whole launch otherwise, item by item), row blocks heaviest first go to the
+// first unit with room under a capacity C: a unit is n_hg workgroups of
+// consecutive slots on one XCD (sched_slot's units), which take the row
+// block's n_hg items side by side as the snake does; a row block no unit has
+// room for goes item by item to the head's remaining workgroups.  C is the
+// smallest capacity that fits everything (binary search from max(heaviest
+// item, mean) up to the snake's busiest).  table = P + 1 offsets, then per
+// workgroup its entries (sched_pack) in walk order.  Returns false, table
+// empty, when the snake's busiest workgroup is no heavier than the table's
+// would be; *busiest_snake and *busiest_table report the busiest load of the
+// snake and of the schedule kept (in weight units).
 inline bool sched_plan(int P, int nrb, int Hkv, int n_hg, const int *tiles, int overhead, std::vector<int> &table,
                        long *busiest_snake = nullptr, long *busiest_table = nullptr)
 {
@@ -121,14 +124,17 @@ inline bool sched_plan(int P, int nrb, int Hkv, int n_hg, const int *tiles, int 
         *busiest_snake = snake_max;
     if (busiest_table)
         *busiest_table = snake_max;
-    // Workgroups of each group in slot order; items of each group heaviest first.
+    // Workgroups of each group in slot order.
     std::vector<std::vector<int>> wg(groups);
+    int g = 1, n_units = P;                              // unit size and units per group
     if (grouped) {
-        const int xh = 8 / Hkv;
+        const int xh = 8 / Hkv, W = P / 8;
         for (int c = 0; c < groups; ++c)
             wg[c].assign(P / Hkv, -1);
         for (int b = 0; b < P; ++b)
             wg[(b % 8) / xh][sched_slot(b, P, Hkv, n_hg)] = b;
+        g = n_hg;
+        n_units = xh * (W - W % n_hg) / n_hg;
     } else {
         for (int b = 0; b < P; ++b)
             wg[0].push_back(b);
@@ -136,37 +142,60 @@ inline bool sched_plan(int P, int nrb, int Hkv, int n_hg, const int *tiles, int 
     std::vector<std::vector<int>> bins(P);
     long plan_max = 0;
     for (int c = 0; c < groups; ++c) {
-        std::vector<int> items;                          // packed entries
-        for (int rbi = 0; rbi < nrb; ++rbi)
-            for (int kvh = 0; kvh < Hkv; ++kvh)
-                if (!grouped || kvh == c)
+        // Rows: a row block's items of this group placed together (grouped),
+        // or single items; heaviest first (rbi ascending is weight descending).
+        std::vector<std::vector<int>> rows;
+        for (int rbi = 0; rbi < nrb; ++rbi) {
+            if (grouped) {
+                std::vector<int> r;
+                for (int hg = 0; hg < n_hg; ++hg)
+                    r.push_back(sched_pack(rbi, c, hg));
+                rows.push_back(r);
+            } else {
+                for (int kvh = 0; kvh < Hkv; ++kvh)
                     for (int hg = 0; hg < n_hg; ++hg)
-                        items.push_back(sched_pack(rbi, kvh, hg));
-        // rbi ascending is weight descending; the sort keeps that order on ties.
-        std::stable_sort(items.begin(), items.end(), [&](int a, int b) {
-            return tiles[sched_unpack(a).rbi] > tiles[sched_unpack(b).rbi];
+                        rows.push_back({sched_pack(rbi, kvh, hg)});
+            }
+        }
+        std::stable_sort(rows.begin(), rows.end(), [&](const std::vector<int> &a, const std::vector<int> &b) {
+            return tiles[sched_unpack(a[0]).rbi] > tiles[sched_unpack(b[0]).rbi];
         });
         const int Q = (int)wg[c].size();
         long total = 0, heaviest = 0, group_snake = 0;
-        for (int e : items) {
-            total += tiles[sched_unpack(e).rbi] + overhead;
-            heaviest = std::max<long>(heaviest, tiles[sched_unpack(e).rbi] + overhead);
+        for (const auto &r : rows) {
+            const long w = tiles[sched_unpack(r[0]).rbi] + overhead;
+            total += w * (long)r.size();
+            heaviest = std::max(heaviest, w);
         }
         for (int b : wg[c])
             group_snake = std::max(group_snake, snake[b]);
-        std::vector<long> load(Q);
-        std::vector<int> where(items.size());
+        std::vector<long> load(Q);                       // per slot
+        std::vector<std::vector<int>> at(Q);             // entries per slot
         auto fits = [&](long cap) {
             std::fill(load.begin(), load.end(), 0);
-            for (size_t i = 0; i < items.size(); ++i) {
-                const long w = tiles[sched_unpack(items[i]).rbi] + overhead;
-                int q = 0;
-                while (q < Q && load[q] + w > cap)
-                    ++q;
-                if (q == Q)
-                    return false;
-                load[q] += w;
-                where[i] = q;
+            for (auto &a : at)
+                a.clear();
+            for (const auto &r : rows) {
+                const long w = tiles[sched_unpack(r[0]).rbi] + overhead;
+                int t = 0;
+                while (t < n_units && load[t * g] + w > cap)
+                    ++t;
+                if (t < n_units && (int)r.size() == g) {
+                    for (int i = 0; i < g; ++i) {
+                        load[t * g + i] += w;
+                        at[t * g + i].push_back(r[i]);
+                    }
+                    continue;
+                }
+                for (int e : r) {
+                    int q = n_units * g;
+                    while (q < Q && load[q] + w > cap)
+                        ++q;
+                    if (q == Q)
+                        return false;
+                    load[q] += w;
+                    at[q].push_back(e);
+                }
             }
             return true;
         };
@@ -182,8 +211,8 @@ inline bool sched_plan(int P, int nrb, int Hkv, int n_hg, const int *tiles, int 
         }
         fits(hi);
         plan_max = std::max(plan_max, *std::max_element(load.begin(), load.end()));
-        for (size_t i = 0; i < items.size(); ++i)
-            bins[wg[c][where[i]]].push_back(items[i]);
+        for (int u = 0; u < Q; ++u)
+            bins[wg[c][u]] = at[u];
     }
     if (plan_max >= snake_max)
         return false;
