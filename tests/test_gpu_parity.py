@@ -144,6 +144,32 @@ def test_parity_full_block_sparse_mask(orc):
     check_parity(rec)
 
 
+def test_host_schedule_table_equals_the_snake():
+    """The same pass under the two work schedules: S=8192, 24/2 (768 work items on 256
+    compute units, where the context's launch takes the host-planned table) through
+    attn_prefill_gated, and through the allocation-free entry point, which always
+    follows the snake order; bit-identical (an item computes the same on any
+    workgroup, in any order)."""
+    import gated_gqa_causal_amd as ga
+    p = synth.Problem(**{**cfg("c4_masked_s8192").__dict__, "mask": None})
+    say("schedule table vs snake at S=8192 24/2")
+    dp = DevProblem(p)
+    ctx = make_ctx(p)
+    table = to_bits(run(ctx, dp))
+    ctx.close()
+    out = torch.empty((p.T, p.n_q_heads * 256), dtype=torch.bfloat16, device="cuda")
+    geom = ga.geometry(p.n_q_heads, p.n_kv_heads, p.T, p.rms_eps)
+    inp = ga.attn_inputs(dp.qg.data_ptr(), dp.k.data_ptr(), dp.v.data_ptr(), dp.wq.data_ptr(), dp.wk.data_ptr(),
+                         dp.cos.data_ptr(), dp.sin.data_ptr(), dp.cos.shape[0])
+    assert ga.attn_prefill_gated_noalloc(geom, inp, p.T, out.data_ptr(),
+                                         torch.cuda.current_stream().cuda_stream) == ga.ATTN_OK
+    torch.cuda.synchronize()
+    snake = to_bits(out)
+    same = np.array_equal(table, snake)
+    say(f"  bit-identical: {same}")
+    assert same
+
+
 # --------------------------------------------------------------------------
 # The workloads at full size, in the benchmark's launch configuration,
 # on sampled rows the oracle computes one by one
