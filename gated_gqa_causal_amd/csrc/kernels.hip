@@ -972,6 +972,11 @@ template <typename Issue>
 __device__ __forceinline__ void s_half8(uint32_t kaddr, const uint4 (&qf)[16], f32x16 &s, Issue &&issue)
 {
     bf16x8 kf[16];
+    // The wave in its scores half issues first when both waves of the SIMD
+    // have an instruction ready (its MFMA stream keeps the matrix pipe fed
+    // while the other wave's context half interleaves the softmax); the
+    // context half drops back to the base level.
+    asm volatile("s_setprio 1");
     kf[0] = lds_read16(kaddr);
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
@@ -1031,6 +1036,7 @@ __device__ __forceinline__ void pv_half8(uint32_t vaddr, f32x16 (&o)[8], u32x4 (
 {
     SmTmp t;
     bf16x8 vf[16];
+    asm volatile("s_setprio 0");
     if (DO_PV)
         vf[0] = lds_read16(vaddr);
     // Masked: the 8 hide steps come first; the program then runs past the
