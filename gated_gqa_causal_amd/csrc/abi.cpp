@@ -287,8 +287,8 @@ constexpr int kSchedOverheadTiles = 14;
 // The attention kernel's work table for ap's launch (a causal pass, row block
 // rbi walking the key tiles up to its last row's position): planned on the
 // host once per launch shape (schedule.h's sched_plan) and copied to the
-// device when it is more even than the snake order, which the kernel follows
-// otherwise.  The staging buffer is rewritten only after its previous copy
+// device when its busiest workgroup is at least 1% lighter than the snake
+// order's, which the kernel follows otherwise.  The staging buffer is rewritten only after its previous copy
 // has landed.
 int attach_schedule(attn_ctx *ctx, ga::AttnParams &ap, hipStream_t s)
 {
@@ -300,7 +300,11 @@ int attach_schedule(attn_ctx *ctx, ga::AttnParams &ap, hipStream_t s)
             tiles[rbi] = std::min(p0 + ga::kRowsPerBlock - 1, ap.T - 1) / ga::kKeysPerTile + 1;
         }
         std::vector<int> table;
-        const bool use = ga::sched_plan(ap.n_wg, ap.nrb, ap.Hkv, ap.n_hg, tiles.data(), kSchedOverheadTiles, table);
+        long busiest_snake = 0, busiest_table = 0;
+        // The table only for a real gain (its busiest workgroup at least 1% lighter).
+        const bool use = ga::sched_plan(ap.n_wg, ap.nrb, ap.Hkv, ap.n_hg, tiles.data(), kSchedOverheadTiles, table,
+                                        &busiest_snake, &busiest_table) &&
+                         100 * busiest_table <= 99 * busiest_snake;
         ctx->sched_valid = false;
         if (use) {
             if (table.size() > ctx->sched_cap)
