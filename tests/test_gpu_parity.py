@@ -170,6 +170,36 @@ def test_host_schedule_table_equals_the_snake():
     assert same
 
 
+def test_host_schedule_without_xcd_grouping(orc):
+    """T=4096 with 48/6 heads (six KV heads do not divide the eight XCDs, so the work
+    is planned over all workgroups item by item): at q_base 0 (768 items) and 1024 (576)
+    the launches take host-planned tables.  Sampled rows match the oracle, the window's
+    rows equal the full pass's bit for bit, and the full pass equals the
+    allocation-free entry point's (the snake order) bit for bit."""
+    import gated_gqa_causal_amd as ga
+    say("schedule table without XCD grouping, T=4096 48/6")
+    p = synth.make_problem(name="sched_48_6", T=4096, n_q_heads=48, n_kv_heads=6, seed=44)
+    dp = DevProblem(p)
+    ctx = make_ctx(p)
+    full = to_bits(run(ctx, dp))
+    pw = synth.make_problem(name="sched_48_6_window", T=4096, n_q_heads=48, n_kv_heads=6, seed=44, q_base=1024)
+    win = to_bits(run(ctx, DevProblem(pw)))
+    ctx.close()
+    rows = sample_rows(p.rows, k=16, seed=5)
+    rec = parity_record("48/6 table", full[rows], oracle_rows(orc, p, rows), p.n_q_heads, rows)
+    say(f"  {rec}")
+    check_parity(rec)
+    assert np.array_equal(win, full[1024:]), "window rows differ from the full pass"
+    out = torch.empty((p.T, p.n_q_heads * 256), dtype=torch.bfloat16, device="cuda")
+    geom = ga.geometry(p.n_q_heads, p.n_kv_heads, p.T, p.rms_eps)
+    inp = ga.attn_inputs(dp.qg.data_ptr(), dp.k.data_ptr(), dp.v.data_ptr(), dp.wq.data_ptr(), dp.wk.data_ptr(),
+                         dp.cos.data_ptr(), dp.sin.data_ptr(), dp.cos.shape[0])
+    assert ga.attn_prefill_gated_noalloc(geom, inp, p.T, out.data_ptr(),
+                                         torch.cuda.current_stream().cuda_stream) == ga.ATTN_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(out), full), "table and snake passes differ"
+
+
 # --------------------------------------------------------------------------
 # The workloads at full size, in the benchmark's launch configuration,
 # on sampled rows the oracle computes one by one
