@@ -283,48 +283,40 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
         write_k_tile(ks, p.kp + tile_off, tid);
         return;
     }
-    // fp8 cache rows.  Row scales: thread (key r, sub) takes the largest
-    // magnitude of its 32 dims; three xor shuffles inside the key's 8 lanes
-    // give the row's.
-    __shared__ float sk[KT], sv[KT];
-    {
-        const int r = tid >> 3, sub = tid & 7;
-        float ak = 0.0f, av = 0.0f;
-#pragma unroll
-        for (int s = 0; s < 32; ++s) {
-            ak = fmaxf(ak, fabsf(bf2f(ks[r][sub + 8 * s])));
-            av = fmaxf(av, fabsf(bf2f(vs[r][sub + 8 * s])));
-        }
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) {
-            ak = fmaxf(ak, __shfl_xor(ak, o));
-            av = fmaxf(av, __shfl_xor(av, o));
-        }
-        if (sub == 0) {
-            sk[r] = (ak > 0.0f) ? ak / 448.0f : 1.0f;
-            sv[r] = (av > 0.0f) ? av / 448.0f : 1.0f;
-        }
-    }
-    __syncthreads();
-    // Codes: 32 key rows and 32 value rows of 256 bytes, 16 bytes per step.
+    // fp8 cache rows: 32 key rows and 32 value rows of 256 bytes.  Thread
+    // (row r, 16-value chunk ch) reads its chunk as two 16-byte words; the 16
+    // lanes of a row (consecutive) combine their largest magnitudes with xor
+    // shuffles into the row's, whose scale (amax / 448, 1 for an all-zero
+    // row) the chunk's codes use.
     for (int it = 0; it < 4; ++it) {
         const int idx = it * 256 + tid, isv = idx >> 9, r = (idx >> 4) & 31, ch = idx & 15;
         const int key = t0 + r;
+        const uint16_t *src = isv ? &vs[r][16 * ch] : &ks[r][16 * ch];
+        const uint4 u0 = *reinterpret_cast<const uint4 *>(src), u1 = *reinterpret_cast<const uint4 *>(src + 8);
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            x[t] = word_f(u0, t);
+            x[8 + t] = word_f(u1, t);
+        }
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            a = fmaxf(a, fabsf(x[e]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1)
+            a = fmaxf(a, __shfl_xor(a, o));
+        const float sc = (a > 0.0f) ? a / 448.0f : 1.0f;
         if (key < T) {
-            const uint16_t *src = isv ? &vs[r][16 * ch] : &ks[r][16 * ch];
-            const float sc = isv ? sv[r] : sk[r];
             uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int e = 0; e < 16; ++e)
-                w[e >> 2] |= enc_e4m3(bf2f(src[e]) / sc) << (8 * (e & 3));
+                w[e >> 2] |= enc_e4m3(x[e] / sc) << (8 * (e & 3));
             uint8_t *dst = (isv ? p.v8 : p.k8) + ((size_t)c * p.Tpad + key) * D + 16 * ch;
             *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+            if (ch == 0)
+                ((isv ? p.v8s : p.k8s))[(size_t)c * p.Tpad + key] = sc;
         }
-    }
-    if (tid < 2 * KT) {
-        const int r = tid & 31, key = t0 + r;
-        if (key < T)
-            ((tid < KT) ? p.k8s : p.v8s)[(size_t)c * p.Tpad + key] = (tid < KT) ? sk[r] : sv[r];
     }
 }
 
