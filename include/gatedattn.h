@@ -121,8 +121,9 @@ ATTN_EXPORT int attn_validate(const attn_geometry *geom, const attn_inputs *in, 
 /*
  * Creates a context on `device` for `geom`, allocating its workspace (about
  * 2 * Hkv * max_tokens * D * 2 bytes for prepared keys and values, plus
- * max_tokens^2 / 8 bytes of packed mask bits and max_tokens * Hq * 8 bytes
- * of softmax row statistics).  The device becomes current
+ * max_tokens^2 / 8 bytes of packed mask bits, max_tokens * Hq * 8 bytes
+ * of softmax row statistics, and small device and pinned host tables for
+ * packed batches and the attention kernel's work schedule).  The device becomes current
  * on the calling thread.  On success *out holds the context; on failure
  * *out is NULL and nothing stays allocated.
  */
