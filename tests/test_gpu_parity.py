@@ -108,6 +108,40 @@ FULL_CASES = [
 ]
 
 
+def _random_cases(n=40, seed=2026):
+    """Seeded random small problems: length 1..700 (ragged tails), a GQA shape with
+    G in 1..16, a q_base multiple of 128 below T for a third of the causal ones, a
+    mask of random budget for a third of the q_base = 0 ones, and bidirectional
+    passes; every element against the oracle."""
+    rng = np.random.default_rng(seed)
+    shapes = [(24, 2), (16, 4), (8, 8), (32, 2), (6, 1), (12, 3), (40, 5), (2, 2), (48, 6), (16, 1)]
+    cases = []
+    for i in range(n):
+        T = int(rng.integers(1, 701))
+        Hq, Hkv = shapes[int(rng.integers(len(shapes)))]
+        kw = dict(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=100 + i, gate_sigma=float(rng.choice([1.0, 2.0])))
+        kind = int(rng.integers(4))
+        if kind == 1 and T > 128:
+            kw["q_base"] = 128 * int(rng.integers(1, (T - 1) // 128 + 1))
+        elif kind == 2:
+            kw["mask_budget"] = int(rng.integers(1, max(2, T)))
+        elif kind == 3:
+            kw["causal"] = False
+        cases.append((f"r{i:02d}_T{T}_{Hq}x{Hkv}_k{kind}", kw))
+    return cases
+
+
+@pytest.mark.parametrize("name,kw", _random_cases(), ids=[c[0] for c in _random_cases()])
+def test_parity_random_shapes(orc, name, kw):
+    say(f"parity_random {name} {kw}")
+    p = synth.make_problem(name=name, **kw)
+    got = gpu_out(p)
+    want = orc.attention(p, threads=8)
+    rec = parity_record(f"random {name}", got, want, p.n_q_heads)
+    say(f"  {rec}")
+    check_parity(rec)
+
+
 @pytest.mark.parametrize("name,kw", FULL_CASES, ids=[c[0] for c in FULL_CASES])
 def test_parity_full(orc, name, kw):
     say(f"parity_full {name} {kw}")
