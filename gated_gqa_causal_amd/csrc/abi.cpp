@@ -815,6 +815,20 @@ int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t 
     }
     return ATTN_OK;
 }
+
+int attn_debug_fp8_encode(const float *x, const float *sc, float *q, uint8_t *codes, int64_t n, void *stream)
+{
+    if (n < 0 || n > ((int64_t)1 << 30))
+        return ATTN_ERR_RANGE;
+    if (n == 0)
+        return ATTN_OK;
+    if (!x || !sc || !q || !codes)
+        return ATTN_ERR_NULL_ARG;
+    (void)hipGetLastError();
+    if (ga::launch_fp8_encode_debug(x, sc, q, codes, n, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+    return ATTN_OK;
+}
 #endif  // ATTN_TEST_HOOKS
 
 int attn_ctx_set_timing_mask(attn_ctx *ctx, int kernel_mask)

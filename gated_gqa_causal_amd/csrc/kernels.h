@@ -96,9 +96,12 @@ hipError_t launch_attn_weights(const AttnParams &p, AttnMode mode, uint16_t *wei
                                hipStream_t stream);
 hipError_t launch_mfma_clock_probe(int iters, int n_wg, long long *rec, float *sink, hipStream_t stream);
 #ifdef ATTN_TEST_HOOKS
-// Test build only: prepared keys / queries back in plain layouts.
+// Test build only: prepared keys / queries back in plain layouts; the fp8
+// cache writer's division and encode on single values.
 hipError_t launch_kp_unpack(const uint16_t *kp, int Tpad, int T, int Hkv, uint16_t *out, hipStream_t stream);
 hipError_t launch_q_prologue_debug(const AttnParams &p, uint16_t *qp, hipStream_t stream);
+hipError_t launch_fp8_encode_debug(const float *x, const float *sc, float *q, uint8_t *codes, int64_t n,
+                                   hipStream_t stream);
 #endif
 
 }  // namespace ga

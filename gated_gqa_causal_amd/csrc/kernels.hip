@@ -50,6 +50,7 @@ namespace ga {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 256;          // head dim
 constexpr int HALF_R = 32;      // rotary pairs (rotary dim 64)
@@ -183,6 +184,28 @@ __device__ __forceinline__ uint32_t enc_e4m3(float x)
     return sign | (e << 3) | keep;                       // a < 448 never reaches the NaN code
 }
 
+// x / sc rounded to nearest even, given y = 1 / sc rounded to nearest (one
+// exact division per row instead of one per value): q = x y is within an ulp
+// of the quotient, the FMA yields the remainder x - q sc exactly, and q + r y
+// rounded once is the correctly rounded quotient (Markstein's theorem on
+// FMA-based division; it needs the remainder to stay in the normal range,
+// which holds for every quotient of 2^-11 or more when sc >= 2^-49).  The
+// sign comes from x, so that x = -0 gives -0.
+__device__ __forceinline__ float div_rn(float x, float sc, float y)
+{
+    const float q = __fmul_rn(x, y);
+    const float r = __builtin_fmaf(-q, sc, x);
+    return __builtin_copysignf(__builtin_fmaf(r, y, q), x);
+}
+
+// Four values to e4m3 codes (byte i = value i) by the hardware's OCP e4m3
+// convert, round to nearest even.
+__device__ __forceinline__ uint32_t enc4_e4m3(float a, float b, float c, float d)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)lo, true);
+}
+
 __device__ __forceinline__ float dec_e4m3(uint32_t c)
 {
     const uint32_t e = (c >> 3) & 15u, m = c & 7u;
@@ -286,32 +309,46 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
     // fp8 cache rows: 32 key rows and 32 value rows of 256 bytes.  Thread
     // (row r, 16-value chunk ch) reads its chunk as two 16-byte words; the 16
     // lanes of a row (consecutive) combine their largest magnitudes with xor
-    // shuffles into the row's, whose scale (amax / 448, 1 for an all-zero
-    // row) the chunk's codes use.
+    // shuffles into the row's, whose scale (amax / 448; 1 for an all-zero
+    // row and for a row holding a NaN, where amax is NaN) the chunk's codes
+    // use.  The largest magnitude is the integer max of the bf16 bit patterns
+    // with the sign cleared: finite magnitudes in order, inf above them, NaN
+    // above inf.
     for (int it = 0; it < 4; ++it) {
         const int idx = it * 256 + tid, isv = idx >> 9, r = (idx >> 4) & 31, ch = idx & 15;
         const int key = t0 + r;
         const uint16_t *src = isv ? &vs[r][16 * ch] : &ks[r][16 * ch];
         const uint4 u0 = *reinterpret_cast<const uint4 *>(src), u1 = *reinterpret_cast<const uint4 *>(src + 8);
-        float x[16];
+        const uint32_t wd[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        u16x2 m2 = {0, 0};
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            x[t] = word_f(u0, t);
-            x[8 + t] = word_f(u1, t);
-        }
-        float a = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            a = fmaxf(a, fabsf(x[e]));
+        for (int t = 0; t < 8; ++t)
+            m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, wd[t] & 0x7fff7fffu));
+        uint32_t mx = max((uint32_t)m2.x, (uint32_t)m2.y);
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1)
-            a = fmaxf(a, __shfl_xor(a, o));
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+        const float a = __uint_as_float(mx << 16);
         const float sc = (a > 0.0f) ? a / 448.0f : 1.0f;
         if (key < T) {
             uint32_t w[4] = {0u, 0u, 0u, 0u};
+            if (mx >= 0x2b80u && mx < 0x7f80u) {
+                // Finite row with amax >= 2^-40 (sc >= 2^-49): one division
+                // for the row, three operations per value.
+                const float y = 1.0f / sc;
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                w[e >> 2] |= enc_e4m3(x[e] / sc) << (8 * (e & 3));
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w0 = wd[2 * q], w1 = wd[2 * q + 1];
+                    w[q] = enc4_e4m3(div_rn(lo_f(w0), sc, y), div_rn(hi_f(w0), sc, y), div_rn(lo_f(w1), sc, y),
+                                     div_rn(hi_f(w1), sc, y));
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t we = wd[e >> 1];
+                    w[e >> 2] |= enc_e4m3(((e & 1) ? hi_f(we) : lo_f(we)) / sc) << (8 * (e & 3));
+                }
+            }
             uint8_t *dst = (isv ? p.v8 : p.k8) + ((size_t)c * p.Tpad + key) * D + 16 * ch;
             *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
             if (ch == 0)
@@ -335,10 +372,14 @@ __global__ __launch_bounds__(256) void kv_widen(KvWidenParams p)
             const uint4 cw = *reinterpret_cast<const uint4 *>((isv ? p.v8 : p.k8) + row * D + 16 * ch);
             const float sc = (isv ? p.v8s : p.k8s)[row];
             const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+            // The hardware's e4m3 -> fp32 convert is exact; fp32 product,
+            // one rounding to bf16.
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const uint32_t code = (words[e >> 2] >> (8 * (e & 3))) & 0xFFu;
-                o[e >> 1] |= (uint32_t)f2bf(dec_e4m3(code) * sc) << (16 * (e & 1));
+            for (int q = 0; q < 4; ++q) {
+                const auto v01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[q], false);
+                const auto v23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)words[q], true);
+                o[2 * q] = pack2(v01[0] * sc, v01[1] * sc);
+                o[2 * q + 1] = pack2(v23[0] * sc, v23[1] * sc);
             }
         }
         uint16_t *dst = isv ? &vs[r][16 * ch] : &ks[r][16 * ch];
@@ -350,6 +391,21 @@ __global__ __launch_bounds__(256) void kv_widen(KvWidenParams p)
 }
 
 #ifdef ATTN_TEST_HOOKS
+// Debug: the fp8 cache writer's arithmetic for finite rows on single values:
+// q[i] = x[i] / sc[i] (div_rn with y = 1 / sc[i]) and codes[i] = its e4m3
+// code (enc4_e4m3).  One value per thread; grid ceil(n / 256).
+__global__ __launch_bounds__(256) void fp8_encode_debug(const float *x, const float *sc, float *q, uint8_t *codes,
+                                                        int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n)
+        return;
+    const float s = sc[i];
+    const float v = div_rn(x[i], s, 1.0f / s);
+    q[i] = v;
+    codes[i] = (uint8_t)(enc4_e4m3(v, 0.0f, 0.0f, 0.0f) & 0xffu);
+}
+
 // Debug: prepared keys from the tiled layout back to plain [Hkv][T][D].
 // grid (ceil(T/32), Hkv), 256 threads.
 __global__ __launch_bounds__(256) void kp_unpack(const uint16_t *kp, int Tpad, int T, uint16_t *out)
@@ -1737,6 +1793,14 @@ hipError_t launch_q_prologue_debug(const AttnParams &p, uint16_t *qp, hipStream_
 {
     hipLaunchKernelGGL(q_prologue_debug, dim3((p.S + 63) / 64, (p.Hq + 3) / 4), dim3(256), 0,
                        stream, p, qp);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_encode_debug(const float *x, const float *sc, float *q, uint8_t *codes, int64_t n,
+                                   hipStream_t stream)
+{
+    hipLaunchKernelGGL(fp8_encode_debug, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, x, sc, q, codes,
+                       n);
     return hipGetLastError();
 }
 #endif  // ATTN_TEST_HOOKS

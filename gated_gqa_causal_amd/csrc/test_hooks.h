@@ -19,6 +19,19 @@ extern "C" {
 ATTN_EXPORT int attn_debug_prepare(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base,
                                    void *qp_out, void *kp_out, void *stream);
 
+/*
+ * The fp8 cache writer's arithmetic for rows of finite values on single
+ * values: q[i] = x[i] / sc[i] as the writer divides (one correctly rounded
+ * reciprocal of sc, then a multiply and two FMAs) and codes[i] = the e4m3
+ * code it stores for q[i].  x, sc, q: device fp32 [n]; codes: device uint8
+ * [n].  The writer takes this route for rows whose largest magnitude is
+ * finite and at least 2^-40 (sc >= 2^-49); other inputs are allowed and
+ * give whatever the arithmetic gives.  n outside 0 .. 2^30: ATTN_ERR_RANGE;
+ * a NULL pointer with n > 0: ATTN_ERR_NULL_ARG; n == 0 does nothing.
+ */
+ATTN_EXPORT int attn_debug_fp8_encode(const float *x, const float *sc, float *q, uint8_t *codes, int64_t n,
+                                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif

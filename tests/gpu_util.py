@@ -60,6 +60,8 @@ def test_lib():
         lib.attn_ctx_destroy.restype = None
         lib.attn_debug_prepare.argtypes = [vp, ctypes.POINTER(ga.attn_inputs), i32, i32, vp, vp, vp]
         lib.attn_debug_prepare.restype = ctypes.c_int
+        lib.attn_debug_fp8_encode.argtypes = [vp, vp, vp, vp, ctypes.c_int64, vp]
+        lib.attn_debug_fp8_encode.restype = ctypes.c_int
         _TEST_LIB = lib
     return _TEST_LIB
 
@@ -85,6 +87,23 @@ def debug_prepare(dp: "DevProblem", q_base: int = 0):
     lib.attn_ctx_destroy(h)
     assert rc == ga.ATTN_OK, rc
     return qp, kp
+
+
+def debug_fp8_encode(x: np.ndarray, sc: np.ndarray):
+    """(quotients, codes) of the fp8 cache writer's arithmetic for finite rows
+    on single values (fp32 arrays x and sc of one length), through the test
+    build's attn_debug_fp8_encode."""
+    import gated_gqa_causal_amd as ga
+    lib = test_lib()
+    xd = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    sd = torch.from_numpy(np.ascontiguousarray(sc, dtype=np.float32)).cuda()
+    q = torch.empty_like(xd)
+    codes = torch.empty(xd.shape, dtype=torch.uint8, device="cuda")
+    rc = lib.attn_debug_fp8_encode(xd.data_ptr(), sd.data_ptr(), q.data_ptr(), codes.data_ptr(), xd.numel(),
+                                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == ga.ATTN_OK, rc
+    return q.cpu().numpy(), codes.cpu().numpy()
 
 
 def make_ctx(p: synth.Problem, max_tokens=None):

@@ -313,14 +313,21 @@ def test_test_hooks_only_in_the_test_build(ga):
     the product library has none of them."""
     import ctypes
     prod = ctypes.CDLL(ga.LIBPATH)
-    assert not hasattr(prod, "attn_debug_prepare")
+    assert not hasattr(prod, "attn_debug_prepare") and not hasattr(prod, "attn_debug_fp8_encode")
     test = ctypes.CDLL(ga.LIBPATH.replace("libgatedattn.so", "libgatedattn_test.so"))
     src = open(os.path.join(ROOT, "gated_gqa_causal_amd", "csrc", "test_hooks.h")).read()
     hooks = sorted(set(re.findall(r"ATTN_EXPORT\s+[\w\s\*]*?\b(attn_\w+)\s*\(", src)))
-    assert hooks == ["attn_debug_prepare"]
+    assert hooks == ["attn_debug_fp8_encode", "attn_debug_prepare"]
     for n in declared_functions() + hooks:
         assert hasattr(test, n), f"{n} not exported by the test build"
     f = test.attn_debug_prepare
     f.argtypes = [ctypes.c_void_p, ctypes.POINTER(ga.attn_inputs), ctypes.c_int32, ctypes.c_int32,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     assert f(None, ctypes.byref(_inputs(ga)), 64, 0, FAKE, FAKE, None) == ga.ATTN_ERR_NULL_ARG
+    g = test.attn_debug_fp8_encode
+    g.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_void_p]
+    assert g(FAKE, FAKE, FAKE, FAKE, -1, None) == ga.ATTN_ERR_RANGE
+    assert g(FAKE, FAKE, FAKE, FAKE, (1 << 30) + 1, None) == ga.ATTN_ERR_RANGE
+    assert g(None, FAKE, FAKE, FAKE, 16, None) == ga.ATTN_ERR_NULL_ARG
+    assert g(FAKE, FAKE, FAKE, None, 16, None) == ga.ATTN_ERR_NULL_ARG
+    assert g(None, None, None, None, 0, None) == ga.ATTN_OK

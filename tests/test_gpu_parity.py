@@ -39,8 +39,8 @@ def gpu():
     yield
 
 
-from gpu_util import (DevProblem, bits_to_f32, check_parity, debug_prepare, gpu_out, make_ctx,  # noqa: E402
-                      parity_record, parity_report, run, to_bits)
+from gpu_util import (DevProblem, bits_to_f32, check_parity, debug_fp8_encode, debug_prepare, gpu_out,  # noqa: E402
+                      make_ctx, parity_record, parity_report, run, to_bits)
 
 _CFG = {}
 
@@ -886,6 +886,109 @@ def test_fp8_cache_rows_bit_exact(orc, T, Hq, Hkv):
     assert np.array_equal(vc[:, :T].cpu().numpy(), want["v_codes"]), "value codes"
     assert np.array_equal(ks[:, :T].cpu().numpy().view(np.uint32), want["k_scales"].view(np.uint32)), "key scales"
     assert np.array_equal(vs[:, :T].cpu().numpy().view(np.uint32), want["v_scales"].view(np.uint32)), "value scales"
+    ctx.close()
+
+
+def _f32_neighbours(vals, k):
+    """Every fp32 value within k ulps of each of vals (positive, finite)."""
+    u = np.asarray(vals, dtype=np.float32).view(np.int32).astype(np.int64)
+    off = np.arange(-k, k + 1, dtype=np.int64)
+    return np.unique((u[:, None] + off[None, :]).clip(0, 0x7F7FFFFF).astype(np.int32)).view(np.float32)
+
+
+def test_fp8_writer_encoder_against_oracle():
+    """The cache writer's e4m3 encode (the hardware convert) gives the
+    oracle's code for every fp32 value within 64 ulps of each e4m3 value and
+    of each midpoint between neighbours (ties to even), for 2^21 random
+    values, zeros of both signs and values just past 448 (the largest
+    quotient a row's scale can give is 448 (1 + 2^-23)); with sc = 1 the
+    writer's division returns x itself."""
+    from oracle import fp8
+    pos = fp8.e4m3_decode(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)
+    mids = (pos[:-1] + pos[1:]) / 2
+    anchors = np.concatenate([pos[1:], mids, [2.0 ** -10, 2.0 ** -11]])
+    near = _f32_neighbours(anchors, 64)
+    rng = np.random.default_rng(7)
+    rnd = (rng.integers(0x3A000000, 0x43E00000, 1 << 21, dtype=np.int64).astype(np.int32)).view(np.float32)
+    tiny = (rng.integers(0, 0x3A000000, 1 << 16, dtype=np.int64).astype(np.int32)).view(np.float32)
+    x = np.concatenate([near, rnd, tiny, [0.0, 448.0]]).astype(np.float32)
+    x = x[x <= np.float32(448.0 * (1 + 2.0 ** -21))]
+    x = np.concatenate([x, -x]).astype(np.float32)
+    say(f"fp8 writer encoder: {x.size} values")
+    q, codes = debug_fp8_encode(x, np.ones_like(x))
+    assert np.array_equal(q.view(np.uint32), x.view(np.uint32)), "division by 1"
+    want = fp8.e4m3_encode(x)
+    bad = np.nonzero(codes != want)[0]
+    assert bad.size == 0, [(float(x[i]), int(codes[i]), int(want[i])) for i in bad[:8]]
+
+
+def test_fp8_writer_division_against_ieee():
+    """The writer's division (a correctly rounded reciprocal per row, then a
+    multiply and two FMAs per value) equals fp32 division bit for bit over
+    2^20 quotients at scales from 2^-49 to 2^119, including quotients near
+    fp32 ties and each row maximum's own quotient near 448; its codes are the
+    oracle's codes of the true quotients."""
+    from oracle import fp8
+    rng = np.random.default_rng(11)
+    n = 1 << 20
+    sc = (rng.integers(0, 1 << 23, n) | (rng.integers(127 - 49, 127 + 119, n) << 23)).astype(np.int32)
+    sc = sc.view(np.float32)
+    mode = rng.integers(0, 3, n)
+    u = (rng.integers(0, 1 << 23, n) | (rng.integers(127 - 12, 127 + 9, n) << 23)).astype(np.int32)
+    u = np.minimum(u.view(np.float32).astype(np.float64), 448.0)          # quotients up to 448
+    e = np.floor(np.log2(u))
+    u = np.where(mode == 1, u + 2.0 ** (e - 24), u)                       # near an fp32 tie of the quotient
+    u = np.where(mode == 2, 448.0 * (1 + rng.integers(-8, 9, n) * 2.0 ** -24), u)
+    x = (u * sc.astype(np.float64)).astype(np.float32)
+    x = np.where(rng.random(n) < 0.5, -x, x).astype(np.float32)
+    say(f"fp8 writer division: {n} quotients")
+    q, codes = debug_fp8_encode(x, sc)
+    want = (x / sc).astype(np.float32)
+    bad = np.nonzero(q.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, [(float(x[i]), float(sc[i]), float(q[i]), float(want[i])) for i in bad[:8]]
+    assert np.array_equal(codes, fp8.e4m3_encode(want))
+
+
+def test_fp8_cache_rows_wide_range(orc):
+    """Value rows at magnitudes from bf16 subnormals to 2^120 (both sides of
+    the writer's 2^-40 switch between its two division routes), and rows
+    holding a NaN, +-inf, only zeros, only -0 or one nonzero value: codes and
+    scales equal the oracle's bit for bit (a NaN makes the row's amax NaN and
+    its scale 1; an infinite amax makes the scale inf)."""
+    from oracle import fp8
+    T, Hq, Hkv = 160, 16, 4
+    p = synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=77)
+    v = p.v.copy()                                                 # [T][Hkv][D] bf16 bits
+    base = synth.bf16_bits_to_f32(v).astype(np.float64)
+    exps = [-133, -126, -100, -60, -49, -42, -41, -40, -39, -30, -20, 0, 20, 60, 100, 120]
+    specials = ["nan", "inf", "-inf", "zero", "negzero", "one", "subnormal"]
+    kinds = exps + specials
+    for t in range(T):
+        for c in range(Hkv):
+            kind = kinds[(t * Hkv + c) % len(kinds)]
+            if isinstance(kind, int):
+                v[t, c] = synth.f32_to_bf16_bits((base[t, c] * 2.0 ** kind).astype(np.float32))
+            elif kind in ("zero", "negzero"):
+                v[t, c] = 0 if kind == "zero" else 0x8000
+            elif kind == "one":
+                v[t, c] = 0
+                v[t, c, (t * 7) % 256] = synth.f32_to_bf16_bits(np.array([base[t, c, 0] or 1.0], np.float32))[0]
+            elif kind == "subnormal":
+                v[t, c] = np.where(base[t, c] < 0, 0x8000, 0) | (np.arange(256) % 127 + 1)
+            else:
+                j = (t * 13) % 256
+                v[t, c, j] = {"nan": 0x7FC0, "inf": 0x7F80, "-inf": 0xFF80}[kind]
+    p.v = v.astype(np.uint16)
+    say(f"fp8 cache rows over magnitudes and special rows T={T} {Hq}/{Hkv}")
+    _, cache, ctx = _fp8_outputs(p, [T])
+    kc, vc, ks, vs = ctx.fp8_cache_views(cache)
+    want = fp8.fp8_cache_kv(orc, p)
+    assert np.array_equal(kc[:, :T].cpu().numpy(), want["k_codes"]), "key codes"
+    assert np.array_equal(ks[:, :T].cpu().numpy().view(np.uint32), want["k_scales"].view(np.uint32)), "key scales"
+    got_vc, got_vs = vc[:, :T].cpu().numpy(), vs[:, :T].cpu().numpy()
+    bad = np.argwhere((got_vc != want["v_codes"]).any(axis=-1)
+                      | (got_vs.view(np.uint32) != want["v_scales"].view(np.uint32)))
+    assert bad.size == 0, [(int(c), int(t), kinds[(int(t) * Hkv + int(c)) % len(kinds)]) for c, t in bad[:8]]
     ctx.close()
 
 
