@@ -1486,6 +1486,7 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
 {
     __shared__ __attribute__((aligned(16))) char smem[WT_SMEM];
     __shared__ __align__(16) float wq1[D];
+    __shared__ __align__(16) uint32_t wbits[MODE == 1 ? 2 : 1][QW];   // masked: a staged tile's row words
     fill_wq1(wq1, p.wq);
     __syncthreads();
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1551,14 +1552,30 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
                 return q;
         return nq;
     };
-    uint4 k0 = {}, k1 = {};
+    // Key tiles move global -> LDS with copies (two buffers, the next computed
+    // tile in flight while the current one is used); masked, wave 0 also
+    // copies the 64 rows' visibility words of the tile.  The vector memory
+    // counter counts copies and stores together and retires them in order, so
+    // a wait for a copy covers the stores issued before it, never those after:
+    // the wait before a tile's barrier leaves the stores issued since its copy
+    // (a whole group's four, when they were issued unconditionally) in flight.
+    const uint32_t smem_base = lds_addr(smem);
+    const uint32_t voff = (uint32_t)(wave * 2048 + lane * 16);
+    auto stage_tile = [&](int t, int b) {
+        const char *src = ktiles + (size_t)__builtin_amdgcn_readfirstlane(t) * TILE_BYTES;
+        const uint32_t m0 =
+            (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem_base + TILE_BYTES * b + wave * 2048));
+        dma16<0, true>(src, voff, m0);
+        dma16<1024, true>(src, voff, m0);
+        if (MODE == 1 && wave == 0)                      // row R0 + lane < bstride (pad rows hold zero words)
+            dma4(p.bits, (uint32_t)(((size_t)__builtin_amdgcn_readfirstlane(t) * p.bstride + R0 + lane) * 4),
+                 lds_addr(&wbits[b][0]));
+    };
     int qnext = next_computed(-1);
-    if (qnext < nq) {
-        const char *src = ktiles + (size_t)tile_of(qnext) * TILE_BYTES;
-        k0 = *reinterpret_cast<const uint4 *>(src + 16 * tid);
-        k1 = *reinterpret_cast<const uint4 *>(src + 8192 + 16 * tid);
-    }
     int nbuf = 0;
+    if (qnext < nq)
+        stage_tile(tile_of(qnext), 0);
+    int stores_since = 0;                                // unconditional stores issued since the last copy
     // Write-out lane map: WT_LPR lanes per row, 16 bytes (8 keys) each.
     constexpr int WT_LPR = WT_GROUP * KT * 2 / 16, WT_RPI = 64 / WT_LPR;
     const int wr = lane / WT_LPR, wc = lane % WT_LPR;
@@ -1570,15 +1587,18 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
             const int t = t0 + tl;
             uint32_t w[16];
             if (q == qnext) {                            // block-uniform
-                char *kb = smem + TILE_BYTES * nbuf;
-                *reinterpret_cast<uint4 *>(kb + 16 * tid) = k0;
-                *reinterpret_cast<uint4 *>(kb + 8192 + 16 * tid) = k1;
+                if (stores_since >= 4)
+                    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();                         // the tile is in place; the other buffer is free
+                const char *kb = smem + TILE_BYTES * nbuf;
+                const int cur = nbuf;
                 qnext = next_computed(q);
+                nbuf ^= 1;
                 if (qnext < nq) {
-                    const char *src = ktiles + (size_t)tile_of(qnext) * TILE_BYTES;
-                    k0 = *reinterpret_cast<const uint4 *>(src + 16 * tid);
-                    k1 = *reinterpret_cast<const uint4 *>(src + 8192 + 16 * tid);
+                    stage_tile(tile_of(qnext), nbuf);
+                    stores_since = 0;
                 }
                 f32x16 s;
 #pragma unroll
@@ -1588,9 +1608,8 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, __builtin_bit_cast(bf16x8, qf[c]), c ? s : z,
                                                                 0, 0, 0);
                 }
-                nbuf ^= 1;
                 if (MODE == 1)
-                    hide_all(s, p.bits[(size_t)t * p.bstride + rc] >> (4 * hh));
+                    hide_all(s, wbits[cur][QB * blk + j] >> (4 * hh));
                 else if (MODE == 0 && t >= diag)
                     hide_all(s, (t == diag ? diag_vis : 0u) >> (4 * hh));
                 // rbf, not the inline-asm round_op: the scores come from the
@@ -1612,26 +1631,39 @@ __global__ __launch_bounds__(512) void attn_weights(AttnParams p, uint16_t *wout
         }
         // The wave reads back only what it wrote: its own LDS accesses stay in
         // order, and the compiler waits for the writes before these reads.
+        // A group whose rows, keys and head all exist takes four unconditional
+        // 16-byte streaming stores per lane; the others store what exists.
+        const int key = t0 * KT + 8 * wc;
+        const bool whole = active && vec && r0 + 32 <= p.S && (t0 + WT_GROUP) * KT <= p.T;   // wave-uniform
+        if (whole) {
 #pragma unroll
-        for (int it = 0; it < 32 / WT_RPI; ++it) {
-            const int rr = WT_RPI * it + wr;
-            const int row = r0 + rr;
-            const int key = t0 * KT + 8 * wc;
-            const uint4 v = *reinterpret_cast<const uint4 *>(stage + rr * WT_ROW + 16 * wc);
-            if (!active || row >= p.S || key >= p.T)
-                continue;
-            uint16_t *dst = wout + ((size_t)row * p.Hq + h) * p.T + key;
-            if (vec) {
-                // Streaming store: the weights are not read again, and kept out
-                // of L2 they leave it to the key tiles the other blocks reuse.
+            for (int it = 0; it < 32 / WT_RPI; ++it) {
+                const int rr = WT_RPI * it + wr;
+                const uint4 v = *reinterpret_cast<const uint4 *>(stage + rr * WT_ROW + 16 * wc);
+                uint16_t *dst = wout + ((size_t)(r0 + rr) * p.Hq + h) * p.T + key;
                 __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(dst));
-            } else {
-                const uint32_t words[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    if (key + q < p.T)
-                        dst[q] = (uint16_t)(words[q >> 1] >> (16 * (q & 1)));
             }
+            stores_since += 32 / WT_RPI;
+        } else {
+#pragma unroll
+            for (int it = 0; it < 32 / WT_RPI; ++it) {
+                const int rr = WT_RPI * it + wr;
+                const int row = r0 + rr;
+                const uint4 v = *reinterpret_cast<const uint4 *>(stage + rr * WT_ROW + 16 * wc);
+                if (!active || row >= p.S || key >= p.T)
+                    continue;
+                uint16_t *dst = wout + ((size_t)row * p.Hq + h) * p.T + key;
+                if (vec) {
+                    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(dst));
+                } else {
+                    const uint32_t words[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        if (key + q < p.T)
+                            dst[q] = (uint16_t)(words[q >> 1] >> (16 * (q & 1)));
+                }
+            }
+            stores_since = 0;                            // count unknown: the next wait takes them all
         }
     }
 }
