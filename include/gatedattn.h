@@ -250,8 +250,10 @@ ATTN_EXPORT int attn_prefill_append(attn_ctx *ctx, const attn_inputs *in, int32_
  *   fp32 value scales[Hkv][tpad]        one per value row
  * E4M3 is the OCP 8-bit floating point format (bias 7, no infinities, 448
  * the largest finite magnitude).  A row's scale is amax / 448 (1 for an all
- * zero row); each value is encoded from value / scale to the nearest code,
- * ties to the even mantissa, magnitudes past 448 saturated; the attention
+ * zero row, and for a row holding a NaN, whose amax is NaN); each value is
+ * encoded from value / scale (fp32 division, correctly rounded) to the
+ * nearest code, ties to the even mantissa, magnitudes past 448 saturated,
+ * NaN to 0x7F; the attention
  * uses bf16(code value * scale).  attn_prefill_append_fp8 works as
  * attn_prefill_append (same arguments, alignment and limits): it encodes the
  * rows of positions q_base..T-1 into the cache, widens rows 0..T-1 into the
