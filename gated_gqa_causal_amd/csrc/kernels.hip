@@ -215,6 +215,53 @@ __device__ __forceinline__ float dec_e4m3(uint32_t c)
     return (c & 0x80u) ? -mag : mag;
 }
 
+// One 16-value chunk of an fp8 cache row (one key or value of one KV head)
+// to e4m3 codes at dst, by 16 consecutive lanes (lane ch of the row's group
+// takes chunk ch): the lanes combine their largest magnitudes with xor
+// shuffles into the row's, whose scale (amax / 448; 1 for an all-zero row and
+// for a row holding a NaN, where amax is NaN) the chunk's codes use; lane 0
+// of the group stores the scale.  The largest magnitude is the integer max of
+// the bf16 bit patterns with the sign cleared: finite magnitudes in order, inf
+// above them, NaN above inf.  keep: the row is a key position to store.
+__device__ __forceinline__ void fp8_row_chunk(const uint16_t *src, int ch, bool keep, uint8_t *dst, float *scale)
+{
+    const uint4 u0 = *reinterpret_cast<const uint4 *>(src), u1 = *reinterpret_cast<const uint4 *>(src + 8);
+    const uint32_t wd[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    u16x2 m2 = {0, 0};
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, wd[t] & 0x7fff7fffu));
+    uint32_t mx = max((uint32_t)m2.x, (uint32_t)m2.y);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    const float a = __uint_as_float(mx << 16);
+    const float sc = (a > 0.0f) ? a / 448.0f : 1.0f;
+    if (!keep)
+        return;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (mx >= 0x2b80u && mx < 0x7f80u) {
+        // Finite row with amax >= 2^-40 (sc >= 2^-49): one division for the
+        // row, three operations per value.
+        const float y = 1.0f / sc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w0 = wd[2 * q], w1 = wd[2 * q + 1];
+            w[q] = enc4_e4m3(div_rn(lo_f(w0), sc, y), div_rn(hi_f(w0), sc, y), div_rn(lo_f(w1), sc, y),
+                             div_rn(hi_f(w1), sc, y));
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t we = wd[e >> 1];
+            w[e >> 2] |= enc_e4m3(((e & 1) ? hi_f(we) : lo_f(we)) / sc) << (8 * (e & 3));
+        }
+    }
+    *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    if (ch == 0)
+        *scale = sc;
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
 {
@@ -269,9 +316,19 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
             }
         }
         rs[tid] = 1.0f / sqrtf(ss / (float)D + p.eps);
-    } else if (!FP8 && tid >= 64) {
-        // Meanwhile waves 1..3 store the transposed value tile.
-        write_vt_tile(vs, p.vt + tile_off, tid - 64, 192);
+    } else if (tid >= 64) {
+        // Meanwhile waves 1..3 store the transposed value tile, or encode the
+        // fp8 value rows (512 row chunks over 192 threads; a row's 16 chunks
+        // are 16 consecutive lanes of one wave).
+        if (!FP8) {
+            write_vt_tile(vs, p.vt + tile_off, tid - 64, 192);
+        } else {
+            for (int idx = tid - 64; idx < 32 * 16; idx += 192) {
+                const int r = idx >> 4, ch = idx & 15;
+                fp8_row_chunk(&vs[r][16 * ch], ch, t0 + r < T, p.v8 + ((size_t)c * p.Tpad + t0 + r) * D + 16 * ch,
+                              p.v8s + (size_t)c * p.Tpad + t0 + r);
+            }
+        }
     }
     __syncthreads();
 
@@ -306,54 +363,11 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
         write_k_tile(ks, p.kp + tile_off, tid);
         return;
     }
-    // fp8 cache rows: 32 key rows and 32 value rows of 256 bytes.  Thread
-    // (row r, 16-value chunk ch) reads its chunk as two 16-byte words; the 16
-    // lanes of a row (consecutive) combine their largest magnitudes with xor
-    // shuffles into the row's, whose scale (amax / 448; 1 for an all-zero
-    // row and for a row holding a NaN, where amax is NaN) the chunk's codes
-    // use.  The largest magnitude is the integer max of the bf16 bit patterns
-    // with the sign cleared: finite magnitudes in order, inf above them, NaN
-    // above inf.
-    for (int it = 0; it < 4; ++it) {
-        const int idx = it * 256 + tid, isv = idx >> 9, r = (idx >> 4) & 31, ch = idx & 15;
-        const int key = t0 + r;
-        const uint16_t *src = isv ? &vs[r][16 * ch] : &ks[r][16 * ch];
-        const uint4 u0 = *reinterpret_cast<const uint4 *>(src), u1 = *reinterpret_cast<const uint4 *>(src + 8);
-        const uint32_t wd[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-        u16x2 m2 = {0, 0};
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, wd[t] & 0x7fff7fffu));
-        uint32_t mx = max((uint32_t)m2.x, (uint32_t)m2.y);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1)
-            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-        const float a = __uint_as_float(mx << 16);
-        const float sc = (a > 0.0f) ? a / 448.0f : 1.0f;
-        if (key < T) {
-            uint32_t w[4] = {0u, 0u, 0u, 0u};
-            if (mx >= 0x2b80u && mx < 0x7f80u) {
-                // Finite row with amax >= 2^-40 (sc >= 2^-49): one division
-                // for the row, three operations per value.
-                const float y = 1.0f / sc;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t w0 = wd[2 * q], w1 = wd[2 * q + 1];
-                    w[q] = enc4_e4m3(div_rn(lo_f(w0), sc, y), div_rn(hi_f(w0), sc, y), div_rn(lo_f(w1), sc, y),
-                                     div_rn(hi_f(w1), sc, y));
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const uint32_t we = wd[e >> 1];
-                    w[e >> 2] |= enc_e4m3(((e & 1) ? hi_f(we) : lo_f(we)) / sc) << (8 * (e & 3));
-                }
-            }
-            uint8_t *dst = (isv ? p.v8 : p.k8) + ((size_t)c * p.Tpad + key) * D + 16 * ch;
-            *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-            if (ch == 0)
-                ((isv ? p.v8s : p.k8s))[(size_t)c * p.Tpad + key] = sc;
-        }
+    // fp8 key rows (the value rows were encoded during the chain above).
+    for (int it = 0; it < 2; ++it) {
+        const int idx = it * 256 + tid, r = idx >> 4, ch = idx & 15;
+        fp8_row_chunk(&ks[r][16 * ch], ch, t0 + r < T, p.k8 + ((size_t)c * p.Tpad + t0 + r) * D + 16 * ch,
+                      p.k8s + (size_t)c * p.Tpad + t0 + r);
     }
 }
 
