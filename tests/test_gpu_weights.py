@@ -137,6 +137,41 @@ def test_weights_vs_oracle(orc, name, kw):
     _check(p, rows, got_w, want, name)
 
 
+def _random_cases(n=24, seed=4049):
+    """Seeded random small problems for the weights entry point: length 1..600
+    (ragged tails, T % 8 != 0 taking the 2-byte stores), a GQA shape with G in
+    1..16, prefix windows, masks of random budget and bidirectional passes."""
+    rng = np.random.default_rng(seed)
+    shapes = [(24, 2), (16, 4), (8, 8), (32, 2), (6, 1), (12, 3), (2, 2), (16, 1)]
+    cases = []
+    for i in range(n):
+        T = int(rng.integers(1, 601))
+        Hq, Hkv = shapes[int(rng.integers(len(shapes)))]
+        kw = dict(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=300 + i)
+        kind = int(rng.integers(4))
+        if kind == 1 and T > 128:
+            kw["q_base"] = 128 * int(rng.integers(1, (T - 1) // 128 + 1))
+        elif kind == 2:
+            kw["mask_budget"] = int(rng.integers(1, max(2, T)))
+        elif kind == 3:
+            kw["causal"] = False
+        cases.append((f"w{i:02d}_T{T}_{Hq}x{Hkv}_k{kind}", kw))
+    return cases
+
+
+@pytest.mark.parametrize("name,kw", _random_cases(), ids=[c[0] for c in _random_cases()])
+def test_weights_random_shapes(orc, name, kw):
+    say(f"weights_random {name} {kw}")
+    p = synth.make_problem(name=name, **kw)
+    ctx = make_ctx(p)
+    out, plain, got_w = _weights(ctx, p)
+    ctx.close()
+    assert np.array_equal(out, plain), "the weights call changed the pass's output"
+    rows = np.arange(p.rows, dtype=np.int32)
+    want = orc.attention(p, rows=rows, want_weights=True, threads=8)
+    _check(p, rows, got_w, want, name)
+
+
 def test_weights_rows_with_no_visible_key(orc):
     # A mask that hides every key from some rows: those rows' weights are all 0.
     p = synth.make_problem(name="masked_empty_rows", T=160, n_q_heads=8, n_kv_heads=2, seed=29, mask_budget=16)
