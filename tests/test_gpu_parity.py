@@ -131,6 +131,40 @@ def _random_cases(n=40, seed=2026):
     return cases
 
 
+def _random_larger_cases(n=30, seed=11):
+    """Seeded random problems of 1..4096 keys over eleven GQA shapes (up to 64
+    query heads), prefix windows, masks of random budget and bidirectional
+    passes; sampled rows (tile boundaries, first and last) against the oracle."""
+    rng = np.random.default_rng(seed)
+    shapes = [(24, 2), (16, 4), (8, 8), (32, 2), (6, 1), (12, 3), (40, 5), (2, 2), (48, 6), (16, 1), (64, 4)]
+    cases = []
+    for i in range(n):
+        T = int(rng.integers(1, 4097))
+        Hq, Hkv = shapes[int(rng.integers(len(shapes)))]
+        kw = dict(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=7000 + i, gate_sigma=float(rng.choice([1.0, 2.0])))
+        kind = int(rng.integers(4))
+        if kind == 1 and T > 128:
+            kw["q_base"] = 128 * int(rng.integers(1, (T - 1) // 128 + 1))
+        elif kind == 2:
+            kw["mask_budget"] = int(rng.integers(1, max(2, T)))
+        elif kind == 3:
+            kw["causal"] = False
+        cases.append((f"L{i:02d}_T{T}_{Hq}x{Hkv}_k{kind}", kw))
+    return cases
+
+
+@pytest.mark.parametrize("name,kw", _random_larger_cases(), ids=[c[0] for c in _random_larger_cases()])
+def test_parity_random_larger_shapes(orc, name, kw):
+    say(f"parity_random_larger {name} {kw}")
+    p = synth.make_problem(name=name, **kw)
+    got = gpu_out(p)
+    rows = sample_rows(p.rows, k=16, seed=len(name))
+    want = orc.attention(p, rows=rows, threads=8)
+    rec = parity_record(f"random larger {name}", got[rows], want, p.n_q_heads, rows)
+    say(f"  {rec}")
+    check_parity(rec)
+
+
 @pytest.mark.parametrize("name,kw", _random_cases(), ids=[c[0] for c in _random_cases()])
 def test_parity_random_shapes(orc, name, kw):
     say(f"parity_random {name} {kw}")
