@@ -52,7 +52,8 @@ struct attn_ctx {
     bool sched_pending = false;
     bool sched_valid = false;      // sched_key holds the last shape planned
     bool sched_use = false;        // and the table is in sched_tab (else the snake)
-    int sched_key[6] = {0, 0, 0, 0, 0, 0};
+    int sched_P = 0;               // the table's workgroups (the launch grid)
+    int sched_key[7] = {0, 0, 0, 0, 0, 0, 0};
     // timing
     int timing = 0;                // bit (1 << ATTN_KERNEL_*) per timed kernel
     std::vector<hipEvent_t> pool;
@@ -290,21 +291,32 @@ constexpr int kSchedOverheadTiles = 14;
 // device when its busiest workgroup is at least 1% lighter than the snake
 // order's, which the kernel follows otherwise.  The staging buffer is rewritten only after its previous copy
 // has landed.
-int attach_schedule(attn_ctx *ctx, ga::AttnParams &ap, hipStream_t s)
+int attach_schedule(attn_ctx *ctx, ga::AttnParams &ap, hipStream_t s, bool masked)
 {
-    const int key[6] = {ap.n_wg, ap.nrb, ap.Hkv, ap.n_hg, ap.T, ap.q_base};
-    if (!ctx->sched_valid || !std::equal(key, key + 6, ctx->sched_key)) {
-        std::vector<int> tiles((size_t)ap.nrb);
+    const int key[7] = {ap.n_wg, ap.nrb, ap.Hkv, ap.n_hg, ap.T, ap.q_base, masked ? 1 : 0};
+    if (!ctx->sched_valid || !std::equal(key, key + 7, ctx->sched_key)) {
+        std::vector<int> tiles((size_t)ap.nrb), rows((size_t)ap.nrb);
         for (int rbi = 0; rbi < ap.nrb; ++rbi) {
-            const int p0 = ap.q_base + ga::kRowsPerBlock * (ap.nrb - 1 - rbi);
+            const int r0 = ga::kRowsPerBlock * (ap.nrb - 1 - rbi);
+            const int p0 = ap.q_base + r0;
             tiles[rbi] = std::min(p0 + ga::kRowsPerBlock - 1, ap.T - 1) / ga::kKeysPerTile + 1;
+            rows[rbi] = std::min(ga::kRowsPerBlock, ap.S - r0);
         }
         std::vector<int> table;
         long busiest_snake = 0, busiest_table = 0;
-        // The table only for a real gain (its busiest workgroup at least 1% lighter).
-        const bool use = ga::sched_plan(ap.n_wg, ap.nrb, ap.Hkv, ap.n_hg, tiles.data(), kSchedOverheadTiles, table,
-                                        &busiest_snake, &busiest_table) &&
-                         100 * busiest_table <= 99 * busiest_snake;
+        int P = ap.n_wg;
+        // Fewer items than compute units (dense causal): the heaviest split in
+        // halves, one item per workgroup.  Otherwise the table only for a real
+        // gain (its busiest workgroup at least 1% lighter than the snake's).
+        bool use = false;
+        if (!masked && ga::sched_plan_split(ctx->num_cus, ap.nrb, ap.Hkv, ap.n_hg, rows.data(), table)) {
+            use = true;
+            P = ctx->num_cus;
+        } else {
+            use = ga::sched_plan(ap.n_wg, ap.nrb, ap.Hkv, ap.n_hg, tiles.data(), kSchedOverheadTiles, table,
+                                 &busiest_snake, &busiest_table) &&
+                  100 * busiest_table <= 99 * busiest_snake;
+        }
         ctx->sched_valid = false;
         if (use) {
             if (table.size() > ctx->sched_cap)
@@ -319,11 +331,14 @@ int attach_schedule(attn_ctx *ctx, ga::AttnParams &ap, hipStream_t s)
                 return ATTN_ERR_LAUNCH;
             ctx->sched_pending = true;
         }
-        std::copy(key, key + 6, ctx->sched_key);
+        std::copy(key, key + 7, ctx->sched_key);
         ctx->sched_valid = true;
         ctx->sched_use = use;
+        ctx->sched_P = P;
     }
     ap.sched = ctx->sched_use ? ctx->sched_tab : nullptr;
+    if (ctx->sched_use)
+        ap.n_wg = ctx->sched_P;
     return ATTN_OK;
 }
 
@@ -413,7 +428,7 @@ int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kin
     if (weights)
         ap.ml = ctx->row_stats;
     if (mode != ga::AttnMode::Bidirectional) {
-        const int rc = attach_schedule(ctx, ap, s);
+        const int rc = attach_schedule(ctx, ap, s, mode == ga::AttnMode::Masked);
         if (rc != ATTN_OK)
             return rc;
     }
@@ -528,7 +543,9 @@ int attn_ctx_create(const attn_geometry *geom, int device, attn_ctx **out)
          hipHostMalloc(&ctx->batch_host, ctx->batch_cap * sizeof(int), hipHostMallocDefault) == hipSuccess &&
          hipEventCreateWithFlags(&ctx->batch_copied, hipEventDisableTiming) == hipSuccess;
     const int n_hg = (geom->n_q_heads / geom->n_kv_heads + ga::kHeadsPerBlock - 1) / ga::kHeadsPerBlock;
-    ctx->sched_cap = (size_t)ctx->num_cus + 1 + nrb * geom->n_kv_heads * n_hg;
+    // offsets for the workgroups, then one entry per item (at most one per
+    // workgroup when items are split)
+    ctx->sched_cap = (size_t)ctx->num_cus + 1 + std::max<size_t>(nrb * geom->n_kv_heads * n_hg, ctx->num_cus);
     ok = ok && hipMalloc(&ctx->sched_tab, ctx->sched_cap * sizeof(int)) == hipSuccess &&
          hipHostMalloc(&ctx->sched_host, ctx->sched_cap * sizeof(int), hipHostMallocDefault) == hipSuccess &&
          hipEventCreateWithFlags(&ctx->sched_copied, hipEventDisableTiming) == hipSuccess;

@@ -1207,11 +1207,19 @@ void attn_fwd8(AttnParams pk)
         const bool active = gidx < p.G;
         const int h = kvh * p.G + (active ? gidx : 0);
         const int r0 = rb * QW;
-        const int rbase = r0 + QB * blk;                 // this wave's rows rbase .. rbase + 31
+        // A split item (half 1 or 2, dense causal launches with fewer items
+        // than compute units) computes one 32-row block on waves 0..3 alone;
+        // waves 4..7 then only copy their parts of the tiles and keep the
+        // barrier count.  A row's arithmetic is the same either way.
+        const int half = si.half;
+        const bool idle = half != 0 && blk == 1;
+        const int bq = half != 0 ? half - 1 : blk;       // this wave's 32-row block of the 64
+        const int rbase = r0 + QB * bq;                  // this wave's rows rbase .. rbase + 31
 
         const int P0 = p.q_base + r0;
-        const int ntiles = BIDIR ? (p.T + KT - 1) / KT : min(P0 + QW - 1, p.T - 1) / KT + 1;
-        const int diag = P0 / KT + blk;                  // this block's diagonal tile
+        const int last_row = P0 + (half == 1 ? QB - 1 : QW - 1);
+        const int ntiles = BIDIR ? (p.T + KT - 1) / KT : min(last_row, p.T - 1) / KT + 1;
+        const int diag = P0 / KT + bq;                   // this block's diagonal tile
 
         // The walk: every tile up to the diagonal (>= 1: row r0 sees key 0), or
         // (masked) the tiles with a visible key for some row of the 64, ascending.
@@ -1325,6 +1333,27 @@ void attn_fwd8(AttnParams pk)
             load_tile(false, 0);
         }
 
+        if (idle) {
+            // The other block's waves of a split item: their parts of every
+            // copy, and the computing waves' barrier count (the prologue's, one
+            // per interval, one after the last context half, the epilogue's).
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+#pragma clang loop unroll(disable)
+            for (int k = 0; k < n; ++k) {
+                auto iss = issue_loads(k);
+                iss(1);
+                iss(5);
+                iss(9);
+                iss(13);
+                close_interval();
+            }
+            close_interval();
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            continue;
+        }
+
         uint4 qf[16];
         load_queries1(p, rbase, h, lane, qf, wq1);
         const FragOffsets fo = frag_offsets(j, hh);
@@ -1351,7 +1380,7 @@ void attn_fwd8(AttnParams pk)
 
         // Visibility of walk tile u for this block, as this lane's bits >> 4hh.
         auto masked_vh = [&](int u) -> uint32_t {
-            return MASKED ? (bitsbuf[u & 7][QB * blk + j] >> (4 * hh)) : 0u;
+            return MASKED ? (bitsbuf[u & 7][QB * bq + j] >> (4 * hh)) : 0u;
         };
         auto causal_hide = [&](int u, f32x16 &sc) {
             if (MASKED) {

@@ -40,6 +40,7 @@ struct SchedItem {
     int rbi;    // row block, heaviest first
     int kvh;    // KV head
     int hg;     // group of four query heads
+    int half;   // 0: the block's 64 rows; 1 / 2: only rows 0..31 / 32..63 (a split item)
 };
 
 __host__ __device__ inline bool sched_xcd_grouped(int P, int Hkv)
@@ -72,6 +73,7 @@ __host__ __device__ inline bool sched_item(int b, int P, int pass, int nrb, int 
         it.kvh = x / xh;
         it.rbi = j / n_hg;
         it.hg = j % n_hg;
+        it.half = 0;
         return true;
     }
     const int per_rb = Hkv * n_hg;
@@ -82,12 +84,20 @@ __host__ __device__ inline bool sched_item(int b, int P, int pass, int nrb, int 
     it.rbi = item / per_rb;
     it.kvh = rem / n_hg;
     it.hg = rem % n_hg;
+    it.half = 0;
     return true;
 }
 
-// A table entry: the item packed into one int.
-__host__ __device__ inline int sched_pack(int rbi, int kvh, int hg) { return (rbi << 16) | (kvh << 8) | hg; }
-__host__ __device__ inline SchedItem sched_unpack(int e) { return SchedItem{e >> 16, (e >> 8) & 0xff, e & 0xff}; }
+// A table entry: the item packed into one int (n_hg <= 4 leaves bits 4..5 of
+// the low byte for the half).
+__host__ __device__ inline int sched_pack(int rbi, int kvh, int hg, int half = 0)
+{
+    return (rbi << 16) | (kvh << 8) | (half << 4) | hg;
+}
+__host__ __device__ inline SchedItem sched_unpack(int e)
+{
+    return SchedItem{e >> 16, (e >> 8) & 0xff, e & 0xf, (e >> 4) & 3};
+}
 
 // Host only.  A table for the launch (P workgroups, nrb row blocks, Hkv KV
 // heads, n_hg head groups) when it is more even than the snake: weight of an
@@ -219,6 +229,58 @@ inline bool sched_plan(int P, int nrb, int Hkv, int n_hg, const int *tiles, int 
     if (busiest_table)
         *busiest_table = plan_max;
     table.reserve(P + 1 + (size_t)nrb * Hkv * n_hg);
+    int off = 0;
+    for (int b = 0; b < P; ++b) {
+        table.push_back(off);
+        off += (int)bins[b].size();
+    }
+    table.push_back(off);
+    for (int b = 0; b < P; ++b)
+        table.insert(table.end(), bins[b].begin(), bins[b].end());
+    return true;
+}
+
+// Host only.  A causal launch with fewer work items than the P workgroups
+// (compute units) leaves workgroups idle while the longest walks run.  The
+// table gives each workgroup at most one item and splits the heaviest items
+// of each KV head into their two 32-row halves (sched_pack half 1 and 2; each
+// half runs on one wave per SIMD, about 0.64 of the whole item's time) as far
+// as the head's workgroups allow; row blocks with 32 rows or fewer (a ragged
+// last block) stay whole.  rows_in_block[rbi] = the block's rows below S.
+// Needs the XCD-grouped form (a head's items on its own XCDs); false, table
+// empty, when there is nothing to split.
+inline bool sched_plan_split(int P, int nrb, int Hkv, int n_hg, const int *rows_in_block, std::vector<int> &table)
+{
+    table.clear();
+    const long items = (long)nrb * Hkv * n_hg;
+    if (P <= 0 || items <= 0 || items >= P || !sched_xcd_grouped(P, Hkv))
+        return false;
+    const int xh = 8 / Hkv, Q = P / Hkv, per_head = nrb * n_hg;
+    int splits = Q - per_head;                           // per head
+    if (splits <= 0)
+        return false;
+    std::vector<std::vector<int>> bins(P);
+    int done = 0;
+    for (int c = 0; c < Hkv; ++c) {
+        std::vector<int> wgs;                            // the head's workgroups
+        for (int b = 0; b < P; ++b)
+            if ((b % 8) / xh == c)
+                wgs.push_back(b);
+        int u = 0, left = splits;
+        for (int rbi = 0; rbi < nrb; ++rbi)              // heaviest first
+            for (int hg = 0; hg < n_hg; ++hg) {
+                if (left > 0 && rows_in_block[rbi] > 32) {
+                    bins[wgs[u++]].push_back(sched_pack(rbi, c, hg, 1));
+                    bins[wgs[u++]].push_back(sched_pack(rbi, c, hg, 2));
+                    --left;
+                    ++done;
+                } else {
+                    bins[wgs[u++]].push_back(sched_pack(rbi, c, hg, 0));
+                }
+            }
+    }
+    if (done == 0)
+        return false;
     int off = 0;
     for (int b = 0; b < P; ++b) {
         table.push_back(off);

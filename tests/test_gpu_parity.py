@@ -800,6 +800,24 @@ def test_batch_equals_sequences_alone(lens, Hq, Hkv):
         assert np.array_equal(got[off[i]:off[i + 1]], alone), f"sequence {i} (len {p.T}) differs"
 
 
+@pytest.mark.parametrize("T,Hq,Hkv,q_base", [(2048, 24, 2, 0), (64, 24, 2, 0), (1000, 16, 4, 0), (8192, 24, 2, 7680),
+                                             (2085, 8, 8, 0)])
+def test_split_items_equal_whole_items(T, Hq, Hkv, q_base):
+    """Launches with fewer work items than compute units split their heaviest
+    items into 32-row halves, each on one wave per SIMD (the host table); a
+    packed batch of the same one sequence never splits.  The rows agree bit for
+    bit (a prefix window against the full pass's rows of the same sequence)."""
+    say(f"split items T={T} {Hq}/{Hkv} q_base={q_base}")
+    full = synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=T + Hq)
+    packed = _batch_out(synth.Batch(name="one", seqs=[full]))
+    if q_base == 0:
+        got = gpu_out(full)
+        assert np.array_equal(got, packed)
+    else:
+        got = gpu_out(synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=T + Hq, q_base=q_base))
+        assert np.array_equal(got, packed[q_base:])
+
+
 def test_batch_order_does_not_matter():
     lens = [200, 33, 0, 130, 64]
     b = synth.make_batch(lens, n_q_heads=8, n_kv_heads=2, seed=11)
