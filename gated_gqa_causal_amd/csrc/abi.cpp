@@ -305,11 +305,11 @@ int attach_schedule(attn_ctx *ctx, ga::AttnParams &ap, hipStream_t s, bool maske
         std::vector<int> table;
         long busiest_snake = 0, busiest_table = 0;
         int P = ap.n_wg;
-        // Fewer items than compute units (dense causal): the heaviest split in
-        // halves, one item per workgroup.  Otherwise the table only for a real
-        // gain (its busiest workgroup at least 1% lighter than the snake's).
+        // Fewer items than compute units: the heaviest split in halves, one
+        // item per workgroup.  Otherwise the table only for a real gain (its
+        // busiest workgroup at least 1% lighter than the snake's).
         bool use = false;
-        if (!masked && ga::sched_plan_split(ctx->num_cus, ap.nrb, ap.Hkv, ap.n_hg, rows.data(), table)) {
+        if (ga::sched_plan_split(ctx->num_cus, ap.nrb, ap.Hkv, ap.n_hg, rows.data(), table)) {
             use = true;
             P = ctx->num_cus;
         } else {

@@ -1207,8 +1207,8 @@ void attn_fwd8(AttnParams pk)
         const bool active = gidx < p.G;
         const int h = kvh * p.G + (active ? gidx : 0);
         const int r0 = rb * QW;
-        // A split item (half 1 or 2, dense causal launches with fewer items
-        // than compute units) computes one 32-row block on waves 0..3 alone;
+        // A split item (half 1 or 2, causal or masked launches with fewer
+        // items than compute units) computes one 32-row block on waves 0..3 alone;
         // waves 4..7 then only copy their parts of the tiles and keep the
         // barrier count.  A row's arithmetic is the same either way.
         const int half = si.half;
@@ -1335,20 +1335,26 @@ void attn_fwd8(AttnParams pk)
 
         if (idle) {
             // The other block's waves of a split item: their parts of every
-            // copy, and the computing waves' barrier count (the prologue's, one
-            // per interval, one after the last context half, the epilogue's).
+            // copy (and of the mask words), the walk window, and the computing
+            // waves' barriers: the prologue's; with a walk, one per interval and
+            // one after the last context half; the epilogue's.
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+            if (!MASKED || n > 0) {
 #pragma clang loop unroll(disable)
-            for (int k = 0; k < n; ++k) {
-                auto iss = issue_loads(k);
-                iss(1);
-                iss(5);
-                iss(9);
-                iss(13);
+                for (int k = 0; k < n; ++k) {
+                    if (MASKED && ((k + 1) & 31) == 0)
+                        walk_window(k + 1);
+                    auto iss = issue_loads(k);
+                    iss(1);
+                    iss(3);
+                    iss(5);
+                    iss(9);
+                    iss(13);
+                    close_interval();
+                }
                 close_interval();
             }
-            close_interval();
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             continue;

@@ -240,7 +240,7 @@ inline bool sched_plan(int P, int nrb, int Hkv, int n_hg, const int *tiles, int 
     return true;
 }
 
-// Host only.  A causal launch with fewer work items than the P workgroups
+// Host only.  A causal or masked launch with fewer work items than the P workgroups
 // (compute units) leaves workgroups idle while the longest walks run.  The
 // table gives each workgroup at most one item and splits the heaviest items
 // of each KV head into their two 32-row halves (sched_pack half 1 and 2; each

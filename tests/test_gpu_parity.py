@@ -818,6 +818,21 @@ def test_split_items_equal_whole_items(T, Hq, Hkv, q_base):
         assert np.array_equal(got, packed[q_base:])
 
 
+@pytest.mark.parametrize("T,big,Hq,Hkv,budget", [(2048, 4096, 24, 2, 512), (1000, 4096, 16, 4, 300),
+                                                  (64, 8192, 24, 2, 16)])
+def test_masked_split_items_equal_whole_items(T, big, Hq, Hkv, budget):
+    """Masked: a T-key problem (fewer items than compute units, so split) and the
+    first T rows of a larger one with the same first T keys, rows and mask rows
+    (enough items that nothing splits).  A row sees keys up to itself only, so
+    the rows agree bit for bit."""
+    say(f"masked split items T={T} (whole in a {big}-key pass) {Hq}/{Hkv} budget {budget}")
+    pb = synth.make_problem(T=big, n_q_heads=Hq, n_kv_heads=Hkv, seed=T + Hq, mask_budget=budget)
+    assert (big // 64) * Hkv * -(-(Hq // Hkv) // 4) >= 256
+    ps = synth.Problem(**{**pb.__dict__, "T": T, "qg": pb.qg[:T], "k": pb.k[:T], "v": pb.v[:T],
+                          "cos": pb.cos[:T], "sin": pb.sin[:T], "mask": np.ascontiguousarray(pb.mask[:T, :T])})
+    assert np.array_equal(gpu_out(ps), gpu_out(pb)[:T])
+
+
 def test_batch_order_does_not_matter():
     lens = [200, 33, 0, 130, 64]
     b = synth.make_batch(lens, n_q_heads=8, n_kv_heads=2, seed=11)
