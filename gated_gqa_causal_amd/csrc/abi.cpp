@@ -285,12 +285,13 @@ int plan_batch(const attn_geometry &g, int32_t n_seqs, const int32_t *lens, Batc
 // counts of the kernel: about 35 K cycles per item, 2.6 K per key tile).
 constexpr int kSchedOverheadTiles = 14;
 
-// The attention kernel's work table for ap's launch (a causal pass, row block
-// rbi walking the key tiles up to its last row's position): planned on the
-// host once per launch shape (schedule.h's sched_plan) and copied to the
-// device when its busiest workgroup is at least 1% lighter than the snake
-// order's, which the kernel follows otherwise.  The staging buffer is rewritten only after its previous copy
-// has landed.
+// The attention kernel's work table for ap's launch (a causal or masked pass,
+// row block rbi walking the key tiles up to its last row's position): planned
+// on the host once per launch shape (schedule.h's sched_plan, and
+// sched_plan_halves with items split into 32-row halves over every compute
+// unit) and copied to the device when its busiest workgroup is at least 1%
+// lighter than the snake order's, which the kernel follows otherwise.  The
+// staging buffer is rewritten only after its previous copy has landed.
 int attach_schedule(attn_ctx *ctx, ga::AttnParams &ap, hipStream_t s, bool masked)
 {
     const int key[7] = {ap.n_wg, ap.nrb, ap.Hkv, ap.n_hg, ap.T, ap.q_base, masked ? 1 : 0};
@@ -302,20 +303,27 @@ int attach_schedule(attn_ctx *ctx, ga::AttnParams &ap, hipStream_t s, bool maske
             tiles[rbi] = std::min(p0 + ga::kRowsPerBlock - 1, ap.T - 1) / ga::kKeysPerTile + 1;
             rows[rbi] = std::min(ga::kRowsPerBlock, ap.S - r0);
         }
-        std::vector<int> table;
-        long busiest_snake = 0, busiest_table = 0;
+        std::vector<int> table, halves;
+        long busiest_snake = 0, busiest_table = 0, busiest_halves = 0;
         int P = ap.n_wg;
-        // Fewer items than compute units: the heaviest split in halves, one
-        // item per workgroup.  Otherwise the table only for a real gain (its
-        // busiest workgroup at least 1% lighter than the snake's).
-        bool use = false;
-        if (ga::sched_plan_split(ctx->num_cus, ap.nrb, ap.Hkv, ap.n_hg, rows.data(), table)) {
+        // The table only for a real gain (its busiest workgroup at least 1%
+        // lighter than the snake's); then items split into 32-row halves and
+        // dealt over every compute unit where that makes the busiest workgroup
+        // at least 1/8 lighter still (few items per workgroup, the heaviest far
+        // above the mean).  A split item costs about 1.28 whole ones in all, and
+        // on the power-limited chip that extra work slows every compute unit:
+        // measured, plans 6-8% lighter in this model ran 1-6% slower, plans
+        // 16-28% lighter 5-6% faster.
+        bool use = ga::sched_plan(ap.n_wg, ap.nrb, ap.Hkv, ap.n_hg, tiles.data(), kSchedOverheadTiles, table,
+                                  &busiest_snake, &busiest_table) &&
+                   100 * busiest_table <= 99 * busiest_snake;
+        const long busiest = use ? busiest_table : busiest_snake;
+        if (ga::sched_plan_halves(ctx->num_cus, ap.nrb, ap.Hkv, ap.n_hg, tiles.data(), rows.data(),
+                                  kSchedOverheadTiles, halves, &busiest_halves) &&
+            8 * busiest_halves <= 7 * busiest) {
+            table.swap(halves);
             use = true;
             P = ctx->num_cus;
-        } else {
-            use = ga::sched_plan(ap.n_wg, ap.nrb, ap.Hkv, ap.n_hg, tiles.data(), kSchedOverheadTiles, table,
-                                 &busiest_snake, &busiest_table) &&
-                  100 * busiest_table <= 99 * busiest_snake;
         }
         ctx->sched_valid = false;
         if (use) {
@@ -543,9 +551,9 @@ int attn_ctx_create(const attn_geometry *geom, int device, attn_ctx **out)
          hipHostMalloc(&ctx->batch_host, ctx->batch_cap * sizeof(int), hipHostMallocDefault) == hipSuccess &&
          hipEventCreateWithFlags(&ctx->batch_copied, hipEventDisableTiming) == hipSuccess;
     const int n_hg = (geom->n_q_heads / geom->n_kv_heads + ga::kHeadsPerBlock - 1) / ga::kHeadsPerBlock;
-    // offsets for the workgroups, then one entry per item (at most one per
-    // workgroup when items are split)
-    ctx->sched_cap = (size_t)ctx->num_cus + 1 + std::max<size_t>(nrb * geom->n_kv_heads * n_hg, ctx->num_cus);
+    // offsets for the workgroups, then the entries: every item once, or both
+    // halves of a split one
+    ctx->sched_cap = (size_t)ctx->num_cus + 1 + 2 * std::max<size_t>(nrb * geom->n_kv_heads * n_hg, ctx->num_cus);
     ok = ok && hipMalloc(&ctx->sched_tab, ctx->sched_cap * sizeof(int)) == hipSuccess &&
          hipHostMalloc(&ctx->sched_host, ctx->sched_cap * sizeof(int), hipHostMallocDefault) == hipSuccess &&
          hipEventCreateWithFlags(&ctx->sched_copied, hipEventDisableTiming) == hipSuccess;

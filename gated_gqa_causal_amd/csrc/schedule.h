@@ -26,12 +26,18 @@
 // items level but not a third partial one (672 items on 256 workgroups: the
 // 160 that take a third item end up about 13% above the mean); the table
 // packs each KV head's row blocks into that head's workgroups by first-fit
-// decreasing against the smallest capacity that fits them all.
+// decreasing against the smallest capacity that fits them all.  A table by
+// sched_plan_halves may also split items into their two 32-row halves (few
+// items per workgroup, the heaviest far above the mean).
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
+#include <functional>
+#include <queue>
+#include <utility>
 #include <vector>
 
 namespace ga {
@@ -240,47 +246,174 @@ inline bool sched_plan(int P, int nrb, int Hkv, int n_hg, const int *tiles, int 
     return true;
 }
 
-// Host only.  A causal or masked launch with fewer work items than the P workgroups
-// (compute units) leaves workgroups idle while the longest walks run.  The
-// table gives each workgroup at most one item and splits the heaviest items
-// of each KV head into their two 32-row halves (sched_pack half 1 and 2; each
-// half runs on one wave per SIMD, about 0.64 of the whole item's time) as far
-// as the head's workgroups allow; row blocks with 32 rows or fewer (a ragged
-// last block) stay whole.  rows_in_block[rbi] = the block's rows below S.
-// Needs the XCD-grouped form (a head's items on its own XCDs); false, table
-// empty, when there is nothing to split.
-inline bool sched_plan_split(int P, int nrb, int Hkv, int n_hg, const int *rows_in_block, std::vector<int> &table)
+// Host only.  Weight of one 32-row half of an item of weight w (key tiles
+// plus overhead): a half runs on one wave per SIMD and takes about 0.64 of
+// the whole item's time.
+inline long sched_half_weight(long w)
+{
+    return (16 * w + 12) / 25;
+}
+
+// Host only.  A table that may split items into their two 32-row halves
+// (sched_pack half 1 and 2; a half runs on waves 0..3), for launches whose
+// whole items leave the busiest workgroup far above the mean: few items per
+// workgroup, the heaviest walking much longer than the rest (a 2048-token
+// pass, a short window over a long prefix).  The s heaviest splittable items
+// (row blocks of more than 32 rows) are split, and the pieces go, heaviest
+// first, to the least loaded of the KV head's P / Hkv workgroups (ties: the
+// lowest slot); s is the count that gives the lightest busiest workgroup,
+// scanned in steps of about 1/16 of the candidates, then one by one around
+// the best step (counts that a lower bound rules out are skipped).  Every KV head gets the same plan on its own XCDs (slot q of
+// head c is the head's q-th workgroup in index order).  tiles[rbi] and
+// rows_in_block[rbi] as for sched_plan; weights in its units.  table = P + 1
+// offsets, then per workgroup its entries in walk order (heaviest first);
+// *busiest = the plan's busiest load.  Needs the XCD-grouped form and at most
+// 2 P / Hkv items per KV head (beyond that whole items pack well and the scan
+// would cost more host time); false, table empty, when no split makes the
+// busiest workgroup lighter than whole items packed the same way.
+inline bool sched_plan_halves(int P, int nrb, int Hkv, int n_hg, const int *tiles, const int *rows_in_block,
+                              int overhead, std::vector<int> &table, long *busiest = nullptr)
 {
     table.clear();
-    const long items = (long)nrb * Hkv * n_hg;
-    if (P <= 0 || items <= 0 || items >= P || !sched_xcd_grouped(P, Hkv))
+    if (P <= 0 || nrb <= 0 || n_hg <= 0 || !sched_xcd_grouped(P, Hkv))
         return false;
-    const int xh = 8 / Hkv, Q = P / Hkv, per_head = nrb * n_hg;
-    int splits = Q - per_head;                           // per head
-    if (splits <= 0)
+    const int Q = P / Hkv, xh = 8 / Hkv;
+    const long per_head = (long)nrb * n_hg;
+    if (per_head > 2L * Q)
         return false;
-    std::vector<std::vector<int>> bins(P);
-    int done = 0;
-    for (int c = 0; c < Hkv; ++c) {
-        std::vector<int> wgs;                            // the head's workgroups
-        for (int b = 0; b < P; ++b)
-            if ((b % 8) / xh == c)
-                wgs.push_back(b);
-        int u = 0, left = splits;
-        for (int rbi = 0; rbi < nrb; ++rbi)              // heaviest first
-            for (int hg = 0; hg < n_hg; ++hg) {
-                if (left > 0 && rows_in_block[rbi] > 32) {
-                    bins[wgs[u++]].push_back(sched_pack(rbi, c, hg, 1));
-                    bins[wgs[u++]].push_back(sched_pack(rbi, c, hg, 2));
-                    --left;
-                    ++done;
-                } else {
-                    bins[wgs[u++]].push_back(sched_pack(rbi, c, hg, 0));
-                }
+    struct Item {
+        long w;
+        int rbi, hg;
+    };
+    std::vector<Item> items;
+    for (int rbi = 0; rbi < nrb; ++rbi)
+        for (int hg = 0; hg < n_hg; ++hg)
+            items.push_back({(long)tiles[rbi] + overhead, rbi, hg});
+    std::stable_sort(items.begin(), items.end(), [](const Item &a, const Item &b) { return a.w > b.w; });
+    std::vector<int> splittable;                          // item indices, heaviest first
+    for (int i = 0; i < (int)items.size(); ++i)
+        if (rows_in_block[items[i].rbi] > 32)
+            splittable.push_back(i);
+    struct Piece {
+        long w;
+        int item, half;
+    };
+    std::vector<Piece> pieces, halves, wholes;
+    std::vector<int> slot_of;                             // per piece
+    std::vector<std::pair<long, int>> heap;               // (load, slot), least on top
+    pieces.reserve(2 * items.size());
+    halves.reserve(2 * items.size());
+    wholes.reserve(items.size());
+    slot_of.reserve(2 * items.size());
+    heap.reserve(Q);
+    const auto later = std::greater<std::pair<long, int>>();
+    // Split the first s splittable items and deal the pieces, heaviest first
+    // (the halves and the whole items, each list already in weight order, are
+    // merged; a whole item goes first on equal weight); returns the busiest
+    // load, or stops as soon as it reaches `limit`.
+    auto deal = [&](int s, long limit) {
+        halves.clear();
+        wholes.clear();
+        int k = 0;
+        for (int i = 0; i < (int)items.size(); ++i) {
+            if (k < s && splittable[k] == i) {
+                const long hw = sched_half_weight(items[i].w);
+                halves.push_back({hw, i, 1});
+                halves.push_back({hw, i, 2});
+                ++k;
+            } else {
+                wholes.push_back({items[i].w, i, 0});
             }
+        }
+        pieces.resize(halves.size() + wholes.size());
+        std::merge(wholes.begin(), wholes.end(), halves.begin(), halves.end(), pieces.begin(),
+                   [](const Piece &a, const Piece &b) { return a.w > b.w; });
+        // The first Q pieces take slots 0, 1, ... in turn (every load is still
+        // 0 when each is dealt, and weights are positive); the rest go through
+        // the heap.
+        const size_t first = std::min(pieces.size(), (size_t)Q);
+        slot_of.assign(pieces.size(), 0);
+        heap.clear();
+        long mx = 0;
+        for (size_t m = 0; m < first; ++m) {
+            slot_of[m] = (int)m;
+            heap.push_back(std::make_pair(pieces[m].w, (int)m));
+            mx = std::max(mx, pieces[m].w);
+        }
+        if (mx >= limit)
+            return mx;
+        for (int q = (int)first; q < Q; ++q)
+            heap.push_back(std::make_pair(0L, q));
+        std::make_heap(heap.begin(), heap.end(), later);
+        for (size_t m = first; m < pieces.size(); ++m) {
+            std::pop_heap(heap.begin(), heap.end(), later);
+            heap.back().first += pieces[m].w;
+            slot_of[m] = heap.back().second;
+            mx = std::max(mx, heap.back().first);
+            if (mx >= limit)
+                return mx;
+            std::push_heap(heap.begin(), heap.end(), later);
+        }
+        return mx;
+    };
+    // A lower bound on the busiest load with s splits (the heaviest piece, and
+    // the mean load rounded up): a count whose bound is no lighter than the
+    // best load found is not dealt, and dealing stops as soon as it reaches
+    // that load.
+    const int n_spl = (int)splittable.size();
+    std::vector<long> bound(n_spl + 1);
+    {
+        long total = 0;
+        for (const Item &it : items)
+            total += it.w;
+        int next_whole = 0;                               // first item not split
+        std::vector<char> split(items.size(), 0);
+        for (int s = 0; s <= n_spl; ++s) {
+            if (s > 0) {
+                const Item &it = items[splittable[s - 1]];
+                total += 2 * sched_half_weight(it.w) - it.w;
+                split[splittable[s - 1]] = 1;
+            }
+            while (next_whole < (int)items.size() && split[next_whole])
+                ++next_whole;
+            long heaviest = next_whole < (int)items.size() ? items[next_whole].w : 0;
+            if (s > 0)
+                heaviest = std::max(heaviest, sched_half_weight(items[splittable[0]].w));
+            bound[s] = std::max(heaviest, (total + Q - 1) / Q);
+        }
     }
-    if (done == 0)
+    const long whole = deal(0, LONG_MAX);
+    long best = whole;
+    int best_s = 0;
+    auto consider = [&](int s) {
+        if (bound[s] >= best)
+            return;
+        const long m = deal(s, best);
+        if (m < best) {
+            best = m;
+            best_s = s;
+        }
+    };
+    const int step = std::max(1, n_spl / 16);
+    for (int s = step; s <= n_spl; s += step)
+        consider(s);
+    const int lo = std::max(1, best_s - step + 1), hi = std::min(n_spl, best_s + step - 1);
+    for (int s = lo; s <= hi; ++s)
+        if (s % step != 0)
+            consider(s);
+    if (best_s == 0 || best >= whole)
         return false;
+    deal(best_s, LONG_MAX);
+    // Slot q of each head -> its workgroups in index order.
+    std::vector<std::vector<int>> wgs(Hkv);
+    for (int b = 0; b < P; ++b)
+        wgs[(b % 8) / xh].push_back(b);
+    std::vector<std::vector<int>> bins(P);
+    for (int c = 0; c < Hkv; ++c)
+        for (size_t k = 0; k < pieces.size(); ++k) {
+            const Item &it = items[pieces[k].item];
+            bins[wgs[c][slot_of[k]]].push_back(sched_pack(it.rbi, c, it.hg, pieces[k].half));
+        }
     int off = 0;
     for (int b = 0; b < P; ++b) {
         table.push_back(off);
@@ -289,6 +422,8 @@ inline bool sched_plan_split(int P, int nrb, int Hkv, int n_hg, const int *rows_
     table.push_back(off);
     for (int b = 0; b < P; ++b)
         table.insert(table.end(), bins[b].begin(), bins[b].end());
+    if (busiest)
+        *busiest = best;
     return true;
 }
 

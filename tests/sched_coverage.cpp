@@ -63,49 +63,64 @@ static void check(int T, int q_base, int Hq, int Hkv, int cus, bool print)
                     *std::max_element(load.begin(), load.end()), (double)total / P,
                     *std::max_element(xcd, xcd + 8), (double)total / std::min(P, 8));
 
-    // The split table (fewer items than workgroups): every item's two 32-row
-    // halves taken exactly once (a whole item takes both), at most one item per
-    // workgroup, each KV head on its XCDs, no split of a block of 32 rows or fewer.
+    // The halves table (sched_plan_halves over every compute unit): every
+    // item's two 32-row halves taken exactly once (a whole item takes both),
+    // each KV head on its XCDs, no split of a block of 32 rows or fewer, and
+    // the busiest load it reports is the one its entries give.
     {
-        std::vector<int> rows(nrb), split;
-        for (int rbi = 0; rbi < nrb; ++rbi)
+        std::vector<int> rows(nrb), tl(nrb), split;
+        for (int rbi = 0; rbi < nrb; ++rbi) {
             rows[rbi] = std::min(64, S - 64 * (nrb - 1 - rbi));
-        const bool sp = ga::sched_plan_split(cus, nrb, Hkv, n_hg, rows.data(), split);
-        const bool expect = items < cus && ga::sched_xcd_grouped(cus, Hkv);
+            tl[rbi] = tiles_of(nrb - 1 - rbi, T, q_base);
+        }
+        long hb = -1;
+        const bool sp = ga::sched_plan_halves(cus, nrb, Hkv, n_hg, tl.data(), rows.data(), 14, split, &hb);
         if (sp) {
-            CHECK(expect, "T=%d Hkv=%d cus=%d: split table where none is expected", T, Hkv, cus);
+            CHECK(ga::sched_xcd_grouped(cus, Hkv), "T=%d Hkv=%d cus=%d: halves table without XCD grouping", T, Hkv,
+                  cus);
             std::vector<int> halves((size_t)items * 2, 0);
-            CHECK((int)split.size() >= cus + 1 && split[0] == 0, "T=%d Hkv=%d: split table offsets", T, Hkv);
-            int n_split = 0;
+            CHECK((int)split.size() >= cus + 1 && split[0] == 0, "T=%d Hkv=%d: halves table offsets", T, Hkv);
+            int n_split = 0, max_per = 0;
+            long busiest = 0;
             for (int b = 0; b < cus && (int)split.size() >= cus + 1; ++b) {
-                CHECK(split[b + 1] - split[b] <= 1, "T=%d Hkv=%d: workgroup %d takes %d items", T, Hkv, b,
-                      split[b + 1] - split[b]);
+                long ld = 0;
+                max_per = std::max(max_per, split[b + 1] - split[b]);
                 for (int o = split[b]; o < split[b + 1]; ++o) {
                     const ga::SchedItem it = ga::sched_unpack(split[cus + 1 + o]);
                     const bool ok = it.rbi >= 0 && it.rbi < nrb && it.kvh >= 0 && it.kvh < Hkv && it.hg >= 0 &&
                                     it.hg < n_hg && it.half >= 0 && it.half <= 2;
-                    CHECK(ok, "T=%d Hkv=%d: split item out of range", T, Hkv);
+                    CHECK(ok, "T=%d Hkv=%d: halves table item out of range", T, Hkv);
                     if (!ok)
                         continue;
-                    CHECK((b % 8) / (8 / Hkv) == it.kvh, "T=%d Hkv=%d: split table puts KV head %d on XCD %d", T,
+                    CHECK((b % 8) / (8 / Hkv) == it.kvh, "T=%d Hkv=%d: halves table puts KV head %d on XCD %d", T,
                           Hkv, it.kvh, b % 8);
                     const size_t i = ((size_t)it.rbi * Hkv + it.kvh) * n_hg + it.hg;
                     if (it.half != 2)
                         ++halves[2 * i];
                     if (it.half != 1)
                         ++halves[2 * i + 1];
+                    const long w = tl[it.rbi] + 14;
+                    ld += it.half ? ga::sched_half_weight(w) : w;
                     if (it.half == 1) {
                         ++n_split;
                         CHECK(rows[it.rbi] > 32, "T=%d Hkv=%d: split of a block with %d rows", T, Hkv, rows[it.rbi]);
                     }
                 }
+                busiest = std::max(busiest, ld);
             }
             for (size_t i = 0; i < halves.size(); ++i)
                 CHECK(halves[i] == 1, "T=%d q_base=%d Hq=%d Hkv=%d cus=%d: half %zu taken %d times", T, q_base, Hq,
                       Hkv, cus, i, halves[i]);
+            CHECK(n_split > 0, "T=%d Hkv=%d: halves table with no split", T, Hkv);
+            CHECK(busiest == hb, "T=%d Hkv=%d: halves table reports busiest %ld, entries give %ld", T, Hkv, hb,
+                  busiest);
             if (print)
-                std::printf("    split table: %d of %ld items in halves on %d workgroups\n", n_split, items, cus);
+                std::printf("    halves table: %d of %ld items split, busiest %ld, up to %d entries a workgroup\n",
+                            n_split, items, busiest, max_per);
         }
+        // A 2048-token pass with 24 / 2 heads on 256 compute units gets one.
+        if (T == 2048 && q_base == 0 && Hq == 24 && Hkv == 2 && cus == 256)
+            CHECK(sp, "T=2048 24/2 on 256 compute units: no halves table");
     }
 
     // The host table (sched_plan), when it is more even than the snake.

@@ -801,12 +801,14 @@ def test_batch_equals_sequences_alone(lens, Hq, Hkv):
 
 
 @pytest.mark.parametrize("T,Hq,Hkv,q_base", [(2048, 24, 2, 0), (64, 24, 2, 0), (1000, 16, 4, 0), (8192, 24, 2, 7680),
-                                             (2085, 8, 8, 0)])
+                                             (2085, 8, 8, 0), (3072, 24, 2, 0), (4096, 16, 4, 0),
+                                             (8192, 24, 2, 6144)])
 def test_split_items_equal_whole_items(T, Hq, Hkv, q_base):
-    """Launches with fewer work items than compute units split their heaviest
-    items into 32-row halves, each on one wave per SIMD (the host table); a
-    packed batch of the same one sequence never splits.  The rows agree bit for
-    bit (a prefix window against the full pass's rows of the same sequence)."""
+    """Launches with few work items per compute unit split their heaviest
+    items into 32-row halves, each on one wave per SIMD, and deal the pieces
+    over every compute unit, some taking several (the host table); a packed
+    batch of the same one sequence never splits.  The rows agree bit for bit
+    (a prefix window against the full pass's rows of the same sequence)."""
     say(f"split items T={T} {Hq}/{Hkv} q_base={q_base}")
     full = synth.make_problem(T=T, n_q_heads=Hq, n_kv_heads=Hkv, seed=T + Hq)
     packed = _batch_out(synth.Batch(name="one", seqs=[full]))
@@ -818,16 +820,16 @@ def test_split_items_equal_whole_items(T, Hq, Hkv, q_base):
         assert np.array_equal(got, packed[q_base:])
 
 
-@pytest.mark.parametrize("T,big,Hq,Hkv,budget", [(2048, 4096, 24, 2, 512), (1000, 4096, 16, 4, 300),
-                                                  (64, 8192, 24, 2, 16)])
+@pytest.mark.parametrize("T,big,Hq,Hkv,budget", [(2048, 8192, 24, 2, 512), (1000, 8192, 32, 4, 300),
+                                                  (64, 8192, 24, 2, 16), (3072, 8192, 24, 2, 768)])
 def test_masked_split_items_equal_whole_items(T, big, Hq, Hkv, budget):
-    """Masked: a T-key problem (fewer items than compute units, so split) and the
+    """Masked: a T-key problem (few items per compute unit, so split) and the
     first T rows of a larger one with the same first T keys, rows and mask rows
     (enough items that nothing splits).  A row sees keys up to itself only, so
     the rows agree bit for bit."""
     say(f"masked split items T={T} (whole in a {big}-key pass) {Hq}/{Hkv} budget {budget}")
     pb = synth.make_problem(T=big, n_q_heads=Hq, n_kv_heads=Hkv, seed=T + Hq, mask_budget=budget)
-    assert (big // 64) * Hkv * -(-(Hq // Hkv) // 4) >= 256
+    assert (big // 64) * -(-(Hq // Hkv) // 4) > 2 * (256 // Hkv)     # whole items only (items a KV head > 2 P / Hkv)
     ps = synth.Problem(**{**pb.__dict__, "T": T, "qg": pb.qg[:T], "k": pb.k[:T], "v": pb.v[:T],
                           "cos": pb.cos[:T], "sin": pb.sin[:T], "mask": np.ascontiguousarray(pb.mask[:T, :T])})
     assert np.array_equal(gpu_out(ps), gpu_out(pb)[:T])
