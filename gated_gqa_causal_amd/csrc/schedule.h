@@ -263,8 +263,9 @@ inline long sched_half_weight(long w)
 // first, to the least loaded of the KV head's P / Hkv workgroups (ties: the
 // lowest slot); s is the count that gives the lightest busiest workgroup,
 // scanned in steps of about 1/16 of the candidates, then one by one around
-// the best step (counts that a lower bound rules out are skipped).  Every KV head gets the same plan on its own XCDs (slot q of
-// head c is the head's q-th workgroup in index order).  tiles[rbi] and
+// the best step (counts that a lower bound rules out are skipped).  Every KV
+// head gets the same plan on its own XCDs (slot q of head c is the head's
+// q-th workgroup in index order).  tiles[rbi] and
 // rows_in_block[rbi] as for sched_plan; weights in its units.  table = P + 1
 // offsets, then per workgroup its entries in walk order (heaviest first);
 // *busiest = the plan's busiest load.  Needs the XCD-grouped form and at most
