@@ -125,7 +125,10 @@ ATTN_EXPORT int attn_validate(const attn_geometry *geom, const attn_inputs *in, 
  * of softmax row statistics, and small device and pinned host tables for
  * packed batches and the attention kernel's work schedule).  The device becomes current
  * on the calling thread.  On success *out holds the context; on failure
- * *out is NULL and nothing stays allocated.
+ * *out is NULL and nothing stays allocated.  The context keeps the work
+ * schedule of its last launch shape (tokens, q_base, masked or not): a call
+ * with another shape plans a new one on the host first (tens of
+ * microseconds; packed batches plan on every call).
  */
 ATTN_EXPORT int attn_ctx_create(const attn_geometry *geom, int device, attn_ctx **out);
 
