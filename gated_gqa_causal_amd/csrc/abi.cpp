@@ -44,8 +44,8 @@ struct attn_ctx {
     hipEvent_t batch_copied = nullptr;
     bool batch_pending = false;
     // the attention kernel's work table (schedule.h's sched_plan or
-    // sched_plan_halves) of the last
-    // launch shape, staged like the batch tables; kept while the shape repeats
+    // sched_plan_halves) of the last launch shape, staged like the batch
+    // tables; kept while the shape repeats
     int *sched_tab = nullptr;
     int *sched_host = nullptr;
     size_t sched_cap = 0;          // ints in each
