@@ -802,7 +802,7 @@ def test_batch_equals_sequences_alone(lens, Hq, Hkv):
 
 @pytest.mark.parametrize("T,Hq,Hkv,q_base", [(2048, 24, 2, 0), (64, 24, 2, 0), (1000, 16, 4, 0), (8192, 24, 2, 7680),
                                              (2085, 8, 8, 0), (3072, 24, 2, 0), (4096, 16, 4, 0),
-                                             (8192, 24, 2, 6144)])
+                                             (8192, 24, 2, 5120)])
 def test_split_items_equal_whole_items(T, Hq, Hkv, q_base):
     """Launches with few work items per compute unit split their heaviest
     items into 32-row halves, each on one wave per SIMD, and deal the pieces
