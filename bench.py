@@ -18,7 +18,10 @@ of the same workload.
 
 A packed-batch workload (``--workload c6_varlen_16x128_2048``) runs its
 sequences in one ``attn_prefill_gated_batch`` call per step; its CPU baseline
-samples the longest sequence.
+samples the longest sequence.  The shared-prefix workload (``--workload
+c8_shared_4096_16x128_512``) runs its branches in one
+``attn_prefill_shared_batch`` call per step over a prefix cache filled once
+before the timing; its CPU baseline and parity sample the longest branch.
 
 ``--mode copy`` runs only a plain device copy of known size (used to scale the
 HBM byte counters of a ``rocprofv3 --pmc`` run).  ``--mode gemm`` times the
@@ -334,8 +337,16 @@ def main():
         return
 
     t0 = time.perf_counter()
-    batch = None
-    if args.workload in synth.BATCH_CONFIGS:
+    batch = shared = None
+    if args.workload in synth.SHARED_CONFIGS:
+        # Branches of one shared prefix: p stands for the longest branch (a window
+        # over prefix + branch) where one problem is needed.
+        shared = synth.config_shared(args.workload)
+        p = max(shared.branches, key=lambda q: q.rows)
+        log(f"workload {args.workload}: prefix {shared.P} tokens, {len(shared.branches)} branches, "
+            f"{shared.total} new tokens (lengths {min(shared.lens)}..{max(shared.lens)}), Hq={p.n_q_heads} "
+            f"Hkv={p.n_kv_heads}; generated in {time.perf_counter() - t0:.1f}s")
+    elif args.workload in synth.BATCH_CONFIGS:
         # A packed batch: p stands for its longest sequence where one problem is
         # needed (shapes, the CPU baseline's sample).
         batch = synth.config_batch(args.workload)
@@ -351,16 +362,20 @@ def main():
     def dev_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    src = batch if batch is not None else p
+    src = batch if batch is not None else shared if shared is not None else p
     qg, k, v = dev_bf16(src.qg), dev_bf16(src.k), dev_bf16(src.v)
     wq, wk = dev_bf16(p.q_norm_w), dev_bf16(p.k_norm_w)
     cos = torch.from_numpy(p.cos).to(dev)
     sin = torch.from_numpy(p.sin).to(dev)
     mask = None if p.mask is None else torch.from_numpy(p.mask).to(dev)
-    rows = batch.total if batch is not None else p.rows
+    rows = batch.total if batch is not None else shared.total if shared is not None else p.rows
     out = torch.empty((rows, p.n_q_heads * 256), dtype=torch.bfloat16, device=dev)
     # A batch's sequences each start on a 32-key tile of the workspace.
     cap = sum((L + 31) // 32 * 32 for L in batch.lens) if batch is not None else p.T
+    if shared is not None:
+        # positions up to the prefix plus the longest branch; every branch's own
+        # keys on 32-key tiles of the workspace
+        cap = max(shared.P + max(shared.lens), sum((L + 31) // 32 * 32 for L in shared.lens))
     ctx = ga.Context(p.n_q_heads, p.n_kv_heads, cap, p.rms_eps)
     stream = torch.cuda.current_stream()
 
@@ -378,9 +393,20 @@ def main():
         append(zero_qg, k[:qb], v[:qb], wq, wk, cos, sin, qb, 0, cache)
         k_new, v_new = k[qb:], v[qb:]
 
+    shared_cache = None
+    if shared is not None:
+        if args.cached or fp8:
+            raise SystemExit("--cached / --fp8-cache do not apply to a shared-prefix workload")
+        # The prefix's keys, prepared once outside the timing into the cache the
+        # branches read (its query rows are not part of this workload).
+        shared_cache = ctx.kv_cache()
+        pre = shared.prefix
+        zero_qg = torch.zeros((shared.P,) + tuple(qg.shape[1:]), dtype=torch.bfloat16, device=dev)
+        ctx.prefill_append(zero_qg, dev_bf16(pre.k), dev_bf16(pre.v), wq, wk, cos, sin, shared.P, 0, shared_cache)
+
     wbuf = None
     if args.weights:
-        if batch is not None or cache is not None:
+        if batch is not None or cache is not None or shared is not None:
             raise SystemExit("--weights covers the single-sequence passes (gated, prefix, masked, bidirectional)")
         wbuf = torch.empty((rows, p.n_q_heads, p.T), dtype=torch.bfloat16, device=dev)
         wkind = 2 if mask is not None else 3 if not p.causal else 1 if p.q_base else 0
@@ -391,6 +417,9 @@ def main():
                                 weights=wbuf, stream=stream)
         elif batch is not None:
             ctx.prefill_gated_batch(qg, k, v, wq, wk, cos, sin, batch.lens, out=out, stream=stream)
+        elif shared is not None:
+            ctx.prefill_shared_batch(qg, k, v, wq, wk, cos, sin, shared.P, shared_cache, shared.lens, out=out,
+                                     stream=stream)
         elif cache is not None:
             append(qg, k_new, v_new, wq, wk, cos, sin, p.T, p.q_base, cache, out=out, stream=stream)
         elif not p.causal:
@@ -478,6 +507,17 @@ def main():
                   "from": "a second run of K steps, a timing-only event between consecutive steps"}
     out_bits = out.view(torch.int16).cpu().numpy().view(np.uint16) if batch is None else None
     bit_exact = None
+    if shared is not None:
+        # The longest branch's rows of the timed launch (parity below), and the
+        # bit-exact check: they equal that branch's own prefix window over prefix + branch.
+        bi = shared.branches.index(p)
+        b0 = int(sum(shared.lens[:bi]))
+        out_bits = out_bits[b0:b0 + p.rows]
+        win = ctx.prefill_prefix(dev_bf16(p.qg), dev_bf16(p.k), dev_bf16(p.v), wq, wk, cos, sin, p.q_base,
+                                 stream=stream)
+        torch.cuda.synchronize()
+        bit_exact = {f"branch_{bi}_equals_its_own_window_pass":
+                     bool(torch.equal(win, out[b0:b0 + p.rows]))}
     if (not args.no_cpu_baseline and batch is None and cache is None and wbuf is None and mask is None
             and p.causal and p.rows >= 2048):
         # The bit-exact index check on the benchmark's own inputs: a prefix
@@ -491,7 +531,7 @@ def main():
     traffic_key = " ".join([args.workload] + [f for f, on in (("--cached", args.cached),
                                                               ("--fp8-cache", args.fp8_cache),
                                                               ("--weights", args.weights)) if on])
-    flops = batch.flops() if batch is not None else p.flops()
+    flops = batch.flops() if batch is not None else shared.flops() if shared is not None else p.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     attn_avg_ms = attn_ms / max(attn_n, 1)
     achieved = flops / (attn_avg_ms * 1e-3) / 1e12
@@ -513,13 +553,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": batch.total if batch is not None else p.T,
+        "config": {"workload": args.workload,
+                   "tokens": batch.total if batch is not None else shared.total if shared is not None else p.T,
                    "q_base": p.q_base, "n_q_heads": p.n_q_heads,
                    "n_kv_heads": p.n_kv_heads, "head_dim": p.head_dim, "rotary_dim": p.rotary_dim,
                    "masked": p.mask is not None, "causal": p.causal,
                    "cached_prefix": bool(args.cached or args.fp8_cache), "fp8_cache": fp8,
                    "weights": bool(args.weights),
-                   "seed": synth.BATCH_CONFIGS[args.workload]["seed"] if batch is not None else p.seed,
+                   "seed": (synth.BATCH_CONFIGS[args.workload]["seed"] if batch is not None else
+                            synth.SHARED_CONFIGS[args.workload]["seed"] if shared is not None else p.seed),
                    "algorithmic_gflop": round(flops / 1e9, 3)},
         "step_ms": None if step_ms is None else {
             "median": round(float(np.median(step_ms)), 5),
@@ -553,10 +595,18 @@ def main():
                                    "bytes_per_launch": wbytes}
     keys = batch.total if batch is not None else p.T
     new_keys = keys - p.q_base if cache is not None else keys
+    if shared is not None:
+        # the prefix's keys (read from the cache) and every branch's own
+        keys, new_keys = shared.P + shared.total, shared.total
     rec["kernels_algorithmic"] = kernel_algorithmic(p, rows, keys, new_keys, flops, bool(w_n), fp8)
     if batch is not None:
         rec["config"]["sequences"] = len(batch.seqs)
         rec["config"]["seq_lens"] = batch.lens
+    if shared is not None:
+        rec["config"]["q_base"] = 0
+        rec["config"]["prefix_len"] = shared.P
+        rec["config"]["branches"] = len(shared.branches)
+        rec["config"]["branch_lens"] = shared.lens
     ctx.close()
     rec["parity"] = None
     if not args.no_cpu_baseline:

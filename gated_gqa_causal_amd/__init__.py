@@ -20,7 +20,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBPATH = os.path.join(_HERE, "libgatedattn.so")
 
-ATTN_ABI_VERSION = 1
+ATTN_ABI_VERSION = 2
 ATTN_HEAD_DIM = 256
 ATTN_ROTARY_DIM = 64
 ATTN_MAX_GROUP = 16
@@ -110,6 +110,10 @@ def _load():
                                                ctypes.POINTER(i32), vp]),
         "attn_prefill_gated_batch": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, ctypes.POINTER(i32),
                                                     vp, vp]),
+        "attn_validate_shared_batch": (ctypes.c_int, [ctypes.POINTER(attn_geometry), ctypes.POINTER(attn_inputs),
+                                                      i32, vp, i32, ctypes.POINTER(i32), vp]),
+        "attn_prefill_shared_batch": (ctypes.c_int, [vp, ctypes.POINTER(attn_inputs), i32, vp, i32,
+                                                     ctypes.POINTER(i32), vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -241,6 +245,18 @@ def attn_prefill_gated_batch(ctx, inputs: attn_inputs, seq_lens, out: int, strea
     return lib.attn_prefill_gated_batch(ctx, ctypes.byref(inputs), n, arr, out, stream)
 
 
+def attn_validate_shared_batch(geom: attn_geometry, inputs, prefix_len: int, kv_cache, branch_lens, out) -> int:
+    n, arr = _lens_array(branch_lens)
+    return lib.attn_validate_shared_batch(ctypes.byref(geom), ctypes.byref(inputs) if inputs is not None else None,
+                                          prefix_len, kv_cache, n, arr, out)
+
+
+def attn_prefill_shared_batch(ctx, inputs: attn_inputs, prefix_len: int, kv_cache, branch_lens, out: int,
+                              stream: int) -> int:
+    n, arr = _lens_array(branch_lens)
+    return lib.attn_prefill_shared_batch(ctx, ctypes.byref(inputs), prefix_len, kv_cache, n, arr, out, stream)
+
+
 def attn_mfma_clock_probe(iters: int, stream: int = 0):
     """(shader clock MHz, bf16 MFMA TFLOP/s) of the current device under a
     pure matrix-core load with pseudo-random operands (blocking)."""
@@ -352,6 +368,29 @@ class Context:
         rc = attn_prefill_gated_batch(self.handle, inp, list(seq_lens), out.data_ptr(), self._stream(stream))
         if rc != ATTN_OK:
             raise AttnError(rc, "attn_prefill_gated_batch")
+        return out
+
+    def prefill_shared_batch(self, qg, k, v, q_norm_w, k_norm_w, cos, sin, prefix_len: int, kv_cache, branch_lens,
+                             out=None, stream=None):
+        """Branches of one shared prefix in one launch: the branches' new rows back to
+        back in qg / k / v / out, each at positions prefix_len..prefix_len+len-1 over
+        the prefix keys in kv_cache (filled by prefill_append, only read here) and its
+        own keys (branch_lens: host list of lengths)."""
+        import torch
+        total = int(sum(int(x) for x in branch_lens))
+        inp = self.inputs(qg, k, v, q_norm_w, k_norm_w, cos, sin, total, total)
+        cache_ptr = None
+        if kv_cache is not None:
+            rc, n = attn_kv_cache_bytes(self.geom)
+            if rc != ATTN_OK:
+                raise AttnError(rc, "attn_kv_cache_bytes")
+            self._check("kv_cache", kv_cache, torch.uint8, (n,))
+            cache_ptr = kv_cache.data_ptr()
+        out = self._out(out, total)
+        rc = attn_prefill_shared_batch(self.handle, inp, prefix_len, cache_ptr, list(branch_lens), out.data_ptr(),
+                                       self._stream(stream))
+        if rc != ATTN_OK:
+            raise AttnError(rc, "attn_prefill_shared_batch")
         return out
 
     def kv_cache(self):

@@ -194,6 +194,7 @@ void fill_attn_params_ws(ga::AttnParams &ap, const attn_geometry &g, const uint1
     ap.n_wg = (int)std::min<int64_t>((int64_t)ap.nrb * ap.Hkv * ap.n_hg, num_cus);
     ap.pairs = nullptr;
     ap.seg = nullptr;
+    ap.ckp = ap.cvt = nullptr;
     ap.ml = nullptr;
     ap.sched = nullptr;
 }
@@ -225,8 +226,10 @@ struct BatchPlan {
 
 // Checks the lengths (and, with `tab`, writes the table): every length in
 // [0, max_tokens], their sum <= max_tokens, and their 32-key tiles within the
-// workspace (each sequence starts on a tile boundary).
-int plan_batch(const attn_geometry &g, int32_t n_seqs, const int32_t *lens, BatchPlan *plan, int *tab)
+// workspace (each sequence starts on a tile boundary).  pos0: the position of
+// every sequence's first key (0, or a shared prefix's length).
+int plan_batch(const attn_geometry &g, int32_t n_seqs, const int32_t *lens, BatchPlan *plan, int *tab,
+               int pos0 = 0)
 {
     if (n_seqs < 0 || n_seqs > ATTN_MAX_SEQS)
         return ATTN_ERR_RANGE;
@@ -255,11 +258,11 @@ int plan_batch(const attn_geometry &g, int32_t n_seqs, const int32_t *lens, Batc
             seg[4 * i] = L;
             seg[4 * i + 1] = row;
             seg[4 * i + 2] = tile;
-            seg[4 * i + 3] = 0;
+            seg[4 * i + 3] = pos0;
             for (int t = 0; t < nt; ++t)
                 tile_seg[tile + t] = i;
             for (int rb = 0; rb * 64 < L; ++rb)
-                pairs.push_back({std::min(rb * 64 + 63, L - 1) / 32 + 1, i, rb});
+                pairs.push_back({(pos0 + std::min(rb * 64 + 63, L - 1)) / 32 + 1, i, rb});
             row += L;
             tile += nt;
         }
@@ -450,6 +453,69 @@ int run(attn_ctx *ctx, const attn_inputs *in, int32_t T, int32_t q_base, int kin
     if (weights) {
         Timer tm(ctx, s, ATTN_KERNEL_WEIGHTS);
         if (ga::launch_attn_weights(ap, mode, static_cast<uint16_t *>(weights), ctx->num_cus, s) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+        tm.stop();
+    }
+    return ATTN_OK;
+}
+
+// A packed batch (validated): sequences of lens[i] rows back to back, each at
+// positions pos0 .. pos0 + len - 1.  With pos0 > 0 they are branches of one
+// shared prefix whose prepared keys 0..pos0-1 the caller's cache holds; each
+// branch's own keys go to the workspace, the cache is only read.
+int run_batch(attn_ctx *ctx, const attn_inputs *in, int32_t n_seqs, const int32_t *lens, int32_t pos0,
+              const void *kv_cache, void *out, void *stream)
+{
+    BatchPlan pl;
+    (void)plan_batch(ctx->geom, n_seqs, lens, &pl, nullptr);
+    if (pl.total == 0)
+        return ATTN_OK;
+    int rc = current_device_matches(ctx);
+    if (rc != ATTN_OK)
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    // The staging buffer is reused: the previous call's copy must have landed.
+    if (ctx->batch_pending && hipEventSynchronize(ctx->batch_copied) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+    ctx->batch_pending = false;
+    (void)plan_batch(ctx->geom, n_seqs, lens, &pl, ctx->batch_host, pos0);
+    const size_t n_int = 4 * (size_t)n_seqs + (size_t)pl.tiles + 2 * (size_t)pl.pairs;
+    if (n_int > ctx->batch_cap)
+        return ATTN_ERR_RANGE;
+    if (hipMemcpyAsync(ctx->batch_tab, ctx->batch_host, n_int * sizeof(int), hipMemcpyHostToDevice, s) !=
+            hipSuccess ||
+        hipEventRecord(ctx->batch_copied, s) != hipSuccess)
+        return ATTN_ERR_LAUNCH;
+    ctx->batch_pending = true;
+    const int *seg = ctx->batch_tab, *tile_seg = seg + 4 * n_seqs, *pairs = tile_seg + pl.tiles;
+
+    ga::KvPrologueParams kvp;
+    fill_kv_params(kvp, ctx, in, pos0 + pl.max_len);
+    kvp.tile_seg = tile_seg;
+    kvp.seg = seg;
+    {
+        Timer tm(ctx, s, ATTN_KERNEL_KV_PROLOGUE);
+        if (ga::launch_kv_prologue(kvp, (int)pl.tiles, s) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+        tm.stop();
+    }
+    ga::AttnParams ap;
+    fill_attn_params(ap, ctx, in, pos0 + pl.max_len, pos0, out);
+    ap.pairs = pairs;
+    ap.seg = seg;
+    ap.nrb = pl.pairs;
+    ap.n_wg = (int)std::min<int64_t>((int64_t)ap.nrb * ap.Hkv * ap.n_hg, ctx->num_cus);
+    ga::AttnMode mode = ga::AttnMode::Causal;
+    if (pos0 > 0) {
+        const uint16_t *ck = static_cast<const uint16_t *>(kv_cache);
+        ap.ckp = ck;
+        ap.cvt = ck + (size_t)ctx->geom.n_kv_heads * ctx->tpad * ATTN_HEAD_DIM;
+        mode = ga::AttnMode::SharedPrefix;
+    }
+    {
+        Timer tm(ctx, s, ATTN_KERNEL_ATTENTION);
+        if (ga::launch_attention(ap, mode, s) != hipSuccess)
             return ATTN_ERR_LAUNCH;
         tm.stop();
     }
@@ -755,53 +821,52 @@ int attn_prefill_gated_batch(attn_ctx *ctx, const attn_inputs *in, int32_t n_seq
     int rc = attn_validate_batch(&ctx->geom, in, n_seqs, seq_lens, out);
     if (rc != ATTN_OK)
         return rc;
-    BatchPlan pl;
-    (void)plan_batch(ctx->geom, n_seqs, seq_lens, &pl, nullptr);
-    if (pl.total == 0)
-        return ATTN_OK;
-    rc = current_device_matches(ctx);
+    return run_batch(ctx, in, n_seqs, seq_lens, 0, nullptr, out, stream);
+}
+
+int attn_validate_shared_batch(const attn_geometry *geom, const attn_inputs *in, int32_t prefix_len,
+                               const void *kv_cache, int32_t n_branches, const int32_t *branch_lens, const void *out)
+{
+    int rc = check_geometry(geom);
     if (rc != ATTN_OK)
         return rc;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    // The staging buffer is reused: the previous call's copy must have landed.
-    if (ctx->batch_pending && hipEventSynchronize(ctx->batch_copied) != hipSuccess)
-        return ATTN_ERR_LAUNCH;
-    ctx->batch_pending = false;
-    (void)plan_batch(ctx->geom, n_seqs, seq_lens, &pl, ctx->batch_host);
-    const size_t n_int = 4 * (size_t)n_seqs + (size_t)pl.tiles + 2 * (size_t)pl.pairs;
-    if (n_int > ctx->batch_cap)
+    if (prefix_len < 0 || prefix_len > geom->max_tokens)
         return ATTN_ERR_RANGE;
-    if (hipMemcpyAsync(ctx->batch_tab, ctx->batch_host, n_int * sizeof(int), hipMemcpyHostToDevice, s) !=
-            hipSuccess ||
-        hipEventRecord(ctx->batch_copied, s) != hipSuccess)
-        return ATTN_ERR_LAUNCH;
-    ctx->batch_pending = true;
-    const int *seg = ctx->batch_tab, *tile_seg = seg + 4 * n_seqs, *pairs = tile_seg + pl.tiles;
-
-    ga::KvPrologueParams kvp;
-    fill_kv_params(kvp, ctx, in, pl.max_len);
-    kvp.tile_seg = tile_seg;
-    kvp.seg = seg;
-    {
-        Timer tm(ctx, s, ATTN_KERNEL_KV_PROLOGUE);
-        if (ga::launch_kv_prologue(kvp, (int)pl.tiles, s) != hipSuccess)
-            return ATTN_ERR_LAUNCH;
-        tm.stop();
-    }
-    ga::AttnParams ap;
-    fill_attn_params(ap, ctx, in, pl.max_len, 0, out);
-    ap.pairs = pairs;
-    ap.seg = seg;
-    ap.nrb = pl.pairs;
-    ap.n_wg = (int)std::min<int64_t>((int64_t)ap.nrb * ap.Hkv * ap.n_hg, ctx->num_cus);
-    {
-        Timer tm(ctx, s, ATTN_KERNEL_ATTENTION);
-        if (ga::launch_attention(ap, ga::AttnMode::Causal, s) != hipSuccess)
-            return ATTN_ERR_LAUNCH;
-        tm.stop();
-    }
+    if (prefix_len % ATTN_QBASE_ALIGN != 0)
+        return ATTN_ERR_ALIGN;
+    BatchPlan pl;
+    rc = plan_batch(*geom, n_branches, branch_lens, &pl, nullptr);
+    if (rc != ATTN_OK)
+        return rc;
+    if ((int64_t)prefix_len + pl.max_len > geom->max_tokens)
+        return ATTN_ERR_RANGE;      // a branch's positions past the geometry
+    if (pl.total == 0)
+        return ATTN_OK;             // nothing to do: pointers unused
+    if (!in || !out)
+        return ATTN_ERR_NULL_ARG;
+    if (!in->qg || !in->k || !in->v || !in->q_norm_w || !in->k_norm_w || !in->cos_tab || !in->sin_tab)
+        return ATTN_ERR_NULL_ARG;
+    if (prefix_len > 0 && !kv_cache)
+        return ATTN_ERR_NULL_ARG;
+    if (in->n_pos < (int64_t)prefix_len + pl.max_len)
+        return ATTN_ERR_RANGE;
+    if (!aligned16(in->qg) || !aligned16(in->k) || !aligned16(in->v) || !aligned16(in->q_norm_w) ||
+        !aligned16(in->k_norm_w) || !aligned16(in->cos_tab) || !aligned16(in->sin_tab) || !aligned16(out))
+        return ATTN_ERR_ALIGN;
+    if (kv_cache && !aligned16(kv_cache))
+        return ATTN_ERR_ALIGN;
     return ATTN_OK;
+}
+
+int attn_prefill_shared_batch(attn_ctx *ctx, const attn_inputs *in, int32_t prefix_len, const void *kv_cache,
+                              int32_t n_branches, const int32_t *branch_lens, void *out, void *stream)
+{
+    if (!ctx)
+        return ATTN_ERR_NULL_ARG;
+    int rc = attn_validate_shared_batch(&ctx->geom, in, prefix_len, kv_cache, n_branches, branch_lens, out);
+    if (rc != ATTN_OK)
+        return rc;
+    return run_batch(ctx, in, n_branches, branch_lens, prefix_len, kv_cache, out, stream);
 }
 
 #ifdef ATTN_TEST_HOOKS

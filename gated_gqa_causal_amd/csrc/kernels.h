@@ -20,7 +20,9 @@ struct KvPrologueParams {
     int k_row0;               // position of row 0 of k and v
     float eps;
     // Packed batch (else null): tile_seg[x] = sequence of prepared tile x;
-    // seg[4 s ..] = {length, first row in k/v, first prepared tile, 0}.
+    // seg[4 s ..] = {length, first row in k/v, first prepared tile, position
+    // of its first key} (the position is 0 but for the branches of a shared
+    // prefix, which continue from the prefix's length).
     const int *tile_seg;
     const int *seg;
     // fp8 cache rows (kv_prologue<true> only): codes [Hkv][Tpad][256] and one
@@ -62,7 +64,9 @@ struct AttnParams {
     float eps;
     // Packed batch (else null): pairs[2 i ..] = {sequence, row block} of the
     // i-th (64-row block) in walk order, nrb = their count; seg as in
-    // KvPrologueParams.  Each sequence is a causal pass at positions 0..len-1.
+    // KvPrologueParams.  Each sequence is a causal pass at positions 0..len-1,
+    // or (attn_fwd8_shared) a branch at positions pos0..pos0+len-1 over the
+    // shared prefix's keys 0..pos0-1 (tiles of ckp / cvt) and its own.
     const int *pairs;
     const int *seg;
     // Optional (else null): per (row, query head) the softmax's final
@@ -71,6 +75,9 @@ struct AttnParams {
     // Optional (else null: the snake order of schedule.h): the host's table of
     // work items per workgroup (sched_plan), n_wg + 1 offsets then entries.
     const int *sched;
+    // attn_fwd8_shared only (else null): the shared prefix's prepared key
+    // and transposed value tiles (the caller's cache, Tpad as above).
+    const uint16_t *ckp, *cvt;
 };
 
 constexpr int kRowsPerBlock = 64;
@@ -90,7 +97,7 @@ hipError_t launch_kv_prologue(const KvPrologueParams &p, int ntiles, hipStream_t
 hipError_t launch_kv_prologue_fp8(const KvPrologueParams &p, int ntiles, hipStream_t stream);
 hipError_t launch_kv_widen(const KvWidenParams &p, int ntiles, int Hkv, hipStream_t stream);
 hipError_t launch_mask_pack(const MaskPackParams &p, int nrb, hipStream_t stream);
-enum class AttnMode { Causal, Masked, Bidirectional };
+enum class AttnMode { Causal, Masked, Bidirectional, SharedPrefix };
 hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stream);
 hipError_t launch_attn_weights(const AttnParams &p, AttnMode mode, uint16_t *weights, int num_cus,
                                hipStream_t stream);

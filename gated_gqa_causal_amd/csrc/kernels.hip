@@ -274,10 +274,12 @@ __global__ __launch_bounds__(256) void kv_prologue(KvPrologueParams p)
     const int tile = p.tile0 + (int)blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
     int t0 = tile * KT, T = p.T, row_base = -p.k_row0;
     if (p.tile_seg) {
-        const int sq = p.tile_seg[blockIdx.x];
-        T = p.seg[4 * sq];
-        row_base = p.seg[4 * sq + 1];
-        t0 = (tile - p.seg[4 * sq + 2]) * KT;
+        // sequence sq: len keys at positions pos0 .. pos0 + len - 1 (pos0 = 0
+        // but for the branches of a shared prefix), raw rows from its first row
+        const int sq = p.tile_seg[blockIdx.x], pos0 = p.seg[4 * sq + 3];
+        T = pos0 + p.seg[4 * sq];
+        row_base = p.seg[4 * sq + 1] - pos0;
+        t0 = pos0 + (tile - p.seg[4 * sq + 2]) * KT;
     }
     const size_t tile_off = ((size_t)c * (p.Tpad / KT) + tile) * (size_t)(KT * D);
 
@@ -1145,7 +1147,11 @@ __device__ __forceinline__ void pv_half8(uint32_t vaddr, f32x16 (&o)[8], u32x4 (
         sm_tail8(s, l, alpha, pw, t);
 }
 
-template <bool MASKED, bool BIDIR>
+// The attention pass.  SHARED: a packed batch of branches that continue one
+// shared prefix (key tiles below the prefix's length come from the caller's
+// cache, the branch's own tiles from the workspace, positions from the
+// prefix's length on).
+template <bool MASKED, bool BIDIR, bool SHARED>
 __global__ __attribute__((amdgpu_flat_work_group_size(ATHREADS8, ATHREADS8), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd8(AttnParams pk)
 {
@@ -1190,8 +1196,8 @@ void attn_fwd8(AttnParams pk)
         // The item's problem: the launch's, or one sequence of a packed batch
         // (its rows, its prepared key tiles, positions from 0).
         AttnParams p = pk;
-        int rb, ktile0 = 0;
-        if (!BIDIR && !MASKED && pk.pairs) {
+        int rb, ktile0 = 0, ptiles = 0;
+        if (SHARED || (!BIDIR && !MASKED && pk.pairs)) {
             const int sq = pk.pairs[2 * si.rbi];
             rb = pk.pairs[2 * si.rbi + 1];
             p.S = p.T = pk.seg[4 * sq];
@@ -1199,6 +1205,13 @@ void attn_fwd8(AttnParams pk)
             p.qg = pk.qg + (size_t)pk.seg[4 * sq + 1] * pk.Hq * 2 * D;
             p.out = pk.out + (size_t)pk.seg[4 * sq + 1] * pk.Hq * D;
             ktile0 = pk.seg[4 * sq + 2];
+            if (SHARED) {
+                // A branch: query positions and keys continue from the prefix.
+                const int pos0 = __builtin_amdgcn_readfirstlane(pk.seg[4 * sq + 3]);
+                p.T += pos0;
+                p.q_base = pos0;
+                ptiles = pos0 / KT;
+            }
         } else {
             rb = pk.nrb - 1 - si.rbi;
         }
@@ -1264,8 +1277,16 @@ void attn_fwd8(AttnParams pk)
             return (uint32_t)__builtin_amdgcn_readfirstlane(
                 (int)(smem_base + TILE_BYTES * ((is_k ? 0 : 4) + (u & 3)) + wave * 2048));
         };
+        // (a branch's tiles below ptiles are the shared prefix's, in the cache)
+        const uint16_t *ckbase = SHARED ? pk.ckp + (size_t)kvh * (p.Tpad / KT) * (KT * D) : nullptr;
+        const uint16_t *cvbase = SHARED ? pk.cvt + (size_t)kvh * (p.Tpad / KT) * (KT * D) : nullptr;
         auto src_of = [&](bool is_k, int tile) {
             tile = __builtin_amdgcn_readfirstlane(tile);
+            if (SHARED) {
+                if (tile < ptiles)
+                    return (is_k ? ckbase : cvbase) + (size_t)tile * (KT * D);
+                tile -= ptiles;
+            }
             return (is_k ? kbase : vbase) + (size_t)tile * (KT * D);
         };
         auto tile_clamped = [&](int u) -> int {
@@ -1827,13 +1848,16 @@ hipError_t launch_attention(const AttnParams &p, AttnMode mode, hipStream_t stre
     const int nblocks = p.n_wg;
     switch (mode) {
     case AttnMode::Masked:
-        hipLaunchKernelGGL((attn_fwd8<true, false>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd8<true, false, false>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
         break;
     case AttnMode::Bidirectional:
-        hipLaunchKernelGGL((attn_fwd8<false, true>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd8<false, true, false>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
+        break;
+    case AttnMode::SharedPrefix:
+        hipLaunchKernelGGL((attn_fwd8<false, false, true>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
         break;
     default:
-        hipLaunchKernelGGL((attn_fwd8<false, false>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd8<false, false, false>), dim3(nblocks), dim3(ATHREADS8), 0, stream, p);
     }
     return hipGetLastError();
 }

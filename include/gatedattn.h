@@ -56,7 +56,7 @@ extern "C" {
 #define ATTN_EXPORT
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 #define ATTN_HEAD_DIM 256
 #define ATTN_ROTARY_DIM 64
 #define ATTN_MAX_GROUP 16         /* query heads per KV head, 1..16          */
@@ -291,6 +291,38 @@ ATTN_EXPORT int attn_validate_batch(const attn_geometry *geom, const attn_inputs
                                     const int32_t *seq_lens, const void *out);
 ATTN_EXPORT int attn_prefill_gated_batch(attn_ctx *ctx, const attn_inputs *in, int32_t n_seqs,
                                          const int32_t *seq_lens, void *out, void *stream);
+
+/*
+ * Branches of one shared prefix, packed into one launch (the serving page's
+ * shared-prefix batched gated attention; the shared-prefix page runs a prefix
+ * once and continues every branch from its state, positions and the causal
+ * mask continuing after the prefix).  kv_cache: a caller-owned cache of this
+ * context's geometry (attn_kv_cache_bytes) whose positions 0..prefix_len-1
+ * earlier attn_prefill_append calls prepared; this call only reads it.
+ * branch_lens: host int32 [n_branches], read during the call only.  Rows of
+ * qg, k, v and out hold the branches' new tokens back to back, as in
+ * attn_prefill_gated_batch.  Branch b's tokens sit at positions prefix_len ..
+ * prefix_len + len_b - 1 (cos/sin rows by position, so n_pos >= prefix_len +
+ * the longest branch); its queries attend to the prefix's keys and to its own
+ * keys up to their position, never to another branch's.  Its own keys are
+ * prepared into the context's workspace, not into the cache.  Its output rows
+ * equal, bit for bit, attn_prefill_append with q_base = prefix_len on a copy of
+ * the cache holding that branch alone, and so the rows prefix_len.. of
+ * attn_prefill_gated over the prefix and that branch.  prefix_len must be a
+ * multiple of ATTN_QBASE_ALIGN (else ATTN_ERR_ALIGN) with prefix_len + every
+ * length <= max_tokens; the branch lengths follow attn_prefill_gated_batch's
+ * limits (else ATTN_ERR_RANGE).  prefix_len == 0 is a plain packed batch (the
+ * cache is then unused and may be NULL; otherwise NULL gives
+ * ATTN_ERR_NULL_ARG, a pointer off 16 bytes ATTN_ERR_ALIGN); a total of 0 new
+ * tokens is a no-op.  The table goes through the same staging buffer as a
+ * packed batch.  attn_validate_shared_batch runs the same host-only checks.
+ */
+ATTN_EXPORT int attn_validate_shared_batch(const attn_geometry *geom, const attn_inputs *in, int32_t prefix_len,
+                                           const void *kv_cache, int32_t n_branches, const int32_t *branch_lens,
+                                           const void *out);
+ATTN_EXPORT int attn_prefill_shared_batch(attn_ctx *ctx, const attn_inputs *in, int32_t prefix_len,
+                                          const void *kv_cache, int32_t n_branches, const int32_t *branch_lens,
+                                          void *out, void *stream);
 
 /*
  * Per-kernel timing with HIP events recorded on the call's stream around

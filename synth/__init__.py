@@ -284,6 +284,63 @@ def make_batch(lens, *, n_q_heads: int = 24, n_kv_heads: int = 2, seed: int = 0,
     return Batch(name=name, seqs=seqs)
 
 
+@dataclasses.dataclass
+class SharedPrefix:
+    """Branches of one shared prefix: ``prefix`` is the prefix's own causal
+    problem (positions 0..P-1); branch i is a window problem (T = P + len_i,
+    q_base = P) whose keys 0..P-1 are the prefix's and whose query rows and
+    keys P.. are its own.  All share the norm weights and the rotary table."""
+    name: str
+    prefix: Problem
+    branches: list
+
+    @property
+    def P(self) -> int:
+        return self.prefix.T
+
+    @property
+    def lens(self):
+        return [b.rows for b in self.branches]
+
+    @property
+    def total(self) -> int:
+        return int(sum(self.lens))
+
+    @property
+    def qg(self):
+        return np.concatenate([b.qg for b in self.branches], axis=0)
+
+    @property
+    def k(self):
+        return np.concatenate([b.k[self.P:] for b in self.branches], axis=0)
+
+    @property
+    def v(self):
+        return np.concatenate([b.v[self.P:] for b in self.branches], axis=0)
+
+    def flops(self) -> float:
+        return float(sum(b.flops() for b in self.branches))
+
+
+def make_shared_prefix(P: int, lens, *, n_q_heads: int = 24, n_kv_heads: int = 2, seed: int = 0,
+                       gate_sigma: float = 1.0, name: str = "shared") -> SharedPrefix:
+    """The prefix draws under ``seed``, branch i's rows and keys under
+    ``seed * 1009 + 1 + i`` (a table of P + max(lens) positions)."""
+    n_pos = P + max([int(x) for x in lens] + [1])
+    pre = make_problem(T=max(P, 1), n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, seed=seed, gate_sigma=gate_sigma,
+                       n_pos=n_pos, name=f"{name}.prefix")
+    if P == 0:
+        pre = dataclasses.replace(pre, T=0, qg=pre.qg[:0], k=pre.k[:0], v=pre.v[:0])
+    branches = []
+    for i, L in enumerate(lens):
+        own = make_problem(T=P + int(L), q_base=P, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
+                           seed=seed * 1009 + 1 + i, gate_sigma=gate_sigma, n_pos=n_pos, name=f"{name}[{i}]")
+        branches.append(dataclasses.replace(
+            own, k=np.concatenate([pre.k, own.k[P:]], axis=0), v=np.concatenate([pre.v, own.v[P:]], axis=0),
+            q_norm_w=pre.q_norm_w, k_norm_w=pre.k_norm_w, cos=pre.cos, sin=pre.sin))
+    return SharedPrefix(name=name, prefix=pre, branches=branches)
+
+
 def batch_lens(n: int, lo: int, hi: int, seed: int):
     """n lengths uniform in [lo, hi] from the counter-based stream (stream 7)."""
     u = splitmix64(seed, 7, 0, n)
@@ -301,6 +358,20 @@ def config_batch(name: str) -> Batch:
     kw = dict(BATCH_CONFIGS[name])
     lens = batch_lens(kw.pop("n"), kw.pop("lo"), kw.pop("hi"), kw["seed"])
     return make_batch(lens, name=name, **kw)
+
+
+# Shared-prefix workload: one 4096-token prefix continued by 16 branches of
+# 128..512 tokens (lengths as in batch_lens), the 24/2 head geometry; stands in
+# for a serving request whose candidates share a long prompt.
+SHARED_CONFIGS = {
+    "c8_shared_4096_16x128_512": dict(P=4096, n=16, lo=128, hi=512, n_q_heads=24, n_kv_heads=2, seed=8),
+}
+
+
+def config_shared(name: str) -> SharedPrefix:
+    kw = dict(SHARED_CONFIGS[name])
+    lens = batch_lens(kw.pop("n"), kw.pop("lo"), kw.pop("hi"), kw["seed"])
+    return make_shared_prefix(kw.pop("P"), lens, name=name, **kw)
 
 
 # The workloads: (keys, q heads, kv heads, q_base, seed, gate sigma, mask budget, causal).

@@ -119,6 +119,27 @@ int main()
     EXPECT(attn_validate_batch(&gb, &in, 4, lens.data(), M), ATTN_ERR_ALIGN);
     EXPECT(attn_prefill_gated_batch(nullptr, &in, 4, lens.data(), A, nullptr), ATTN_ERR_NULL_ARG);
 
+    // branches of a shared prefix (lens 100, 0, 33, 200 after a 512-token prefix)
+    attn_inputs longb = in; longb.n_pos = 1024;
+    EXPECT(attn_validate_shared_batch(&gb, &longb, 512, A, 4, lens.data(), A), ATTN_OK);
+    EXPECT(attn_validate_shared_batch(&gb, &longb, 0, nullptr, 4, lens.data(), A), ATTN_OK);
+    EXPECT(attn_validate_shared_batch(&gb, &longb, 64, A, 4, lens.data(), A), ATTN_ERR_ALIGN);
+    EXPECT(attn_validate_shared_batch(&gb, &longb, -128, A, 4, lens.data(), A), ATTN_ERR_RANGE);
+    EXPECT(attn_validate_shared_batch(&gb, &longb, INT32_MIN, A, 4, lens.data(), A), ATTN_ERR_RANGE);
+    EXPECT(attn_validate_shared_batch(&gb, &longb, 1152, A, 4, lens.data(), A), ATTN_ERR_RANGE);
+    EXPECT(attn_validate_shared_batch(&gb, &longb, 896, A, 4, lens.data(), A), ATTN_ERR_RANGE);  // 896 + 200
+    EXPECT(attn_validate_shared_batch(&gb, &longb, 512, nullptr, 4, lens.data(), A), ATTN_ERR_NULL_ARG);
+    EXPECT(attn_validate_shared_batch(&gb, &longb, 512, M, 4, lens.data(), A), ATTN_ERR_ALIGN);
+    EXPECT(attn_validate_shared_batch(&gb, &longb, 512, A, 4, nullptr, A), ATTN_ERR_NULL_ARG);
+    EXPECT(attn_validate_shared_batch(&gb, &longb, 512, A, ATTN_MAX_SEQS + 1, lens.data(), A), ATTN_ERR_RANGE);
+    EXPECT(attn_validate_shared_batch(&gb, &longb, 512, A, 0, nullptr, nullptr), ATTN_OK);
+    EXPECT(attn_validate_shared_batch(&gb, &longb, 512, A, ATTN_MAX_SEQS, zeros.data(), nullptr), ATTN_OK);
+    EXPECT(attn_validate_shared_batch(&gb, &longb, 512, A, ATTN_MAX_SEQS, many.data(), A), ATTN_ERR_RANGE);
+    longb.n_pos = 711;
+    EXPECT(attn_validate_shared_batch(&gb, &longb, 512, A, 4, lens.data(), A), ATTN_ERR_RANGE);
+    EXPECT(attn_validate_shared_batch(nullptr, &in, 512, A, 4, lens.data(), A), ATTN_ERR_NULL_ARG);
+    EXPECT(attn_prefill_shared_batch(nullptr, &in, 512, A, 4, lens.data(), A, nullptr), ATTN_ERR_NULL_ARG);
+
     // size queries
     size_t bytes = 1;
     EXPECT(attn_kv_cache_bytes(&g, nullptr), ATTN_ERR_NULL_ARG);

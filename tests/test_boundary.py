@@ -233,6 +233,56 @@ def test_batch_valid_and_empty(ga):
     assert ga.attn_validate_batch(g, _inputs(ga, n_pos=33), [32] * 7 + [1, 1], FAKE) == ga.ATTN_ERR_RANGE
 
 
+SHARED_REFUSALS = [
+    # (geometry overrides, prefix_len, cache, branch_lens, out, inputs overrides, expected)
+    ({}, 64, FAKE, [10], FAKE, {}, "ALIGN"),                   # prefix not a multiple of ATTN_QBASE_ALIGN
+    ({}, -128, FAKE, [10], FAKE, {}, "RANGE"),
+    ({}, 384, FAKE, [10], FAKE, {}, "RANGE"),                  # prefix past max_tokens (256)
+    ({}, 128, FAKE, [64, 129], FAKE, {}, "RANGE"),             # 128 + 129 positions > max_tokens
+    ({}, 128, FAKE, [64, -1], FAKE, {}, "RANGE"),
+    ({}, 0, FAKE, [200, 57], FAKE, {}, "RANGE"),               # new tokens > max_tokens
+    ({}, 128, FAKE, [64, 100], FAKE, dict(n_pos=227), "RANGE"),  # table shorter than prefix + longest branch
+    ({}, 128, None, [64, 100], FAKE, {}, "NULL_ARG"),          # a prefix needs its cache
+    ({}, 128, FAKE, [64, 100], None, {}, "NULL_ARG"),
+    ({}, 128, FAKE, [64, 100], FAKE, dict(v=0), "NULL_ARG"),
+    ({}, 128, FAKE + 8, [64, 100], FAKE, {}, "ALIGN"),
+    ({}, 128, FAKE, [64, 100], FAKE + 8, {}, "ALIGN"),
+    (dict(n_q_heads=24, n_kv_heads=5), 128, FAKE, [64], FAKE, {}, "GEOMETRY"),
+]
+
+
+@pytest.mark.parametrize("case", SHARED_REFUSALS, ids=lambda c: f"{c[-1]}")
+def test_shared_batch_refusals(ga, case):
+    geo, P, cache, lens, out, inov, want = case
+    inp = _inputs(ga, n_pos=256)
+    for k, v in inov.items():
+        setattr(inp, k, v)
+    rc = ga.attn_validate_shared_batch(_geom(ga, **geo), inp, P, cache, lens, out)
+    assert rc == getattr(ga, "ATTN_ERR_" + want), (rc, ga.attn_status_string(rc))
+
+
+def test_shared_batch_valid_and_empty(ga):
+    g = _geom(ga)
+    # nothing new: a no-op whatever the pointers (a misaligned prefix still refused first)
+    assert ga.attn_validate_shared_batch(g, None, 128, None, [], None) == ga.ATTN_OK
+    assert ga.attn_validate_shared_batch(g, None, 128, None, [0, 0], None) == ga.ATTN_OK
+    assert ga.attn_validate_shared_batch(g, None, 64, None, [0], None) == ga.ATTN_ERR_ALIGN
+    assert ga.attn_validate_shared_batch(g, _inputs(ga, n_pos=228), 128, FAKE, [64, 0, 100, 31], FAKE) == ga.ATTN_OK
+    # the branches' own keys fill the 256-key workspace exactly
+    assert ga.attn_validate_shared_batch(g, _inputs(ga, n_pos=160), 128, FAKE, [32] * 8, FAKE) == ga.ATTN_OK
+    assert ga.attn_validate_shared_batch(g, _inputs(ga, n_pos=160), 128, FAKE, [32] * 7 + [1, 1], FAKE) == \
+        ga.ATTN_ERR_RANGE
+    # no prefix: a plain packed batch, the cache unused
+    assert ga.attn_validate_shared_batch(g, _inputs(ga, n_pos=100), 0, None, [64, 100], FAKE) == ga.ATTN_OK
+    n = ctypes.c_int32(1)
+    assert ga.lib.attn_validate_shared_batch(ctypes.byref(g), None, 128, None, ga.ATTN_MAX_SEQS + 1, None,
+                                             None) == ga.ATTN_ERR_RANGE
+    assert ga.lib.attn_validate_shared_batch(ctypes.byref(g), None, 128, None, 1, None, None) == \
+        ga.ATTN_ERR_NULL_ARG
+    assert ga.lib.attn_validate_shared_batch(ctypes.byref(g), None, 128, None, 1, ctypes.byref(n), None) == \
+        ga.ATTN_ERR_NULL_ARG
+
+
 def test_kv_cache_fp8_bytes(ga):
     g = _geom(ga, n_q_heads=24, n_kv_heads=2, max_tokens=200)     # tpad 256
     rc, n = ga.attn_kv_cache_fp8_bytes(g)

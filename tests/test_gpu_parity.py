@@ -916,6 +916,139 @@ def test_batch_reuses_context_back_to_back():
 
 
 # --------------------------------------------------------------------------
+# Branches of one shared prefix in one launch
+# --------------------------------------------------------------------------
+
+def _shared_ctx(sp):
+    """A context holding the prefix plus the longest branch (positions) and every
+    branch's own keys on 32-key tiles (workspace)."""
+    import gated_gqa_causal_amd as ga
+    pre = sp.prefix
+    need = max([sp.P + max(sp.lens + [0]), sum((L + 31) // 32 * 32 for L in sp.lens), 1])
+    return ga.Context(pre.n_q_heads, pre.n_kv_heads, need, pre.rms_eps)
+
+
+def _shared_run(sp, ctx=None):
+    """The prefix appended to a fresh cache, then every branch through one
+    attn_prefill_shared_batch call; (output bits, cache, context)."""
+    from gpu_util import bf16_tensor
+    own = ctx is None
+    ctx = ctx or _shared_ctx(sp)
+    pre = sp.prefix
+    wq, wk = bf16_tensor(pre.q_norm_w), bf16_tensor(pre.k_norm_w)
+    cos = torch.from_numpy(np.ascontiguousarray(pre.cos)).to("cuda")
+    sin = torch.from_numpy(np.ascontiguousarray(pre.sin)).to("cuda")
+    cache = ctx.kv_cache()
+    if sp.P:
+        ctx.prefill_append(bf16_tensor(pre.qg), bf16_tensor(pre.k), bf16_tensor(pre.v), wq, wk, cos, sin, sp.P, 0,
+                           cache)
+    out = ctx.prefill_shared_batch(bf16_tensor(sp.qg), bf16_tensor(sp.k), bf16_tensor(sp.v), wq, wk, cos, sin,
+                                   sp.P, cache if sp.P else None, sp.lens)
+    torch.cuda.synchronize()
+    got = to_bits(out)
+    if own:
+        ctx.close()
+        return got, None, None
+    return got, cache, ctx
+
+
+@pytest.mark.parametrize("P,lens,Hq,Hkv", [(128, [1, 31, 32, 33, 0, 64, 65, 200, 130], 24, 2),
+                                           (1024, [300, 7, 128], 16, 4), (256, [5], 6, 1),
+                                           (384, [0, 0, 97, 0], 2, 2), (2048, [64] * 12 + [1, 190], 8, 8)])
+def test_shared_batch_equals_branches_alone(P, lens, Hq, Hkv):
+    """Each branch of one launch gets, bit for bit, the rows of its own prefix
+    window over prefix + branch (the full pass's rows P..)."""
+    say(f"shared prefix P={P} branches {lens} {Hq}/{Hkv}")
+    sp = synth.make_shared_prefix(P, lens, n_q_heads=Hq, n_kv_heads=Hkv, seed=P + len(lens))
+    got, _, _ = _shared_run(sp)
+    off = _offsets(lens)
+    for i, b in enumerate(sp.branches):
+        if b.rows == 0:
+            continue
+        assert np.array_equal(got[off[i]:off[i + 1]], gpu_out(b)), f"branch {i} (len {b.rows}) differs"
+
+
+def test_shared_batch_equals_appends_and_leaves_the_cache():
+    """The same branches continued one call each from the cache (each append
+    over a copy of it) give the launch's bits; the launch does not write the
+    cache, and a second launch on the same context gives the same bits."""
+    from gpu_util import bf16_tensor
+    P, lens = 512, [200, 1, 37, 128]
+    say(f"shared prefix vs appends P={P} {lens}")
+    sp = synth.make_shared_prefix(P, lens, n_q_heads=16, n_kv_heads=4, seed=77)
+    ctx = _shared_ctx(sp)
+    got, cache, ctx = _shared_run(sp, ctx)
+    before = cache.clone()
+    pre = sp.prefix
+    wq, wk = bf16_tensor(pre.q_norm_w), bf16_tensor(pre.k_norm_w)
+    cos = torch.from_numpy(np.ascontiguousarray(pre.cos)).to("cuda")
+    sin = torch.from_numpy(np.ascontiguousarray(pre.sin)).to("cuda")
+    again = ctx.prefill_shared_batch(bf16_tensor(sp.qg), bf16_tensor(sp.k), bf16_tensor(sp.v), wq, wk, cos, sin,
+                                     P, cache, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(cache, before), "the shared launch wrote the prefix cache"
+    assert np.array_equal(to_bits(again), got)
+    off = _offsets(lens)
+    for i, b in enumerate(sp.branches):
+        c = before.clone()
+        o = ctx.prefill_append(bf16_tensor(b.qg), bf16_tensor(b.k[P:]), bf16_tensor(b.v[P:]), wq, wk, cos, sin,
+                               b.T, P, c)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(o), got[off[i]:off[i + 1]]), f"branch {i}"
+    ctx.close()
+
+
+def test_shared_batch_without_prefix_is_a_packed_batch():
+    lens = [1, 31, 32, 33, 0, 64, 65, 200, 130]
+    sp = synth.make_shared_prefix(0, lens, n_q_heads=24, n_kv_heads=2, seed=9)
+    b = synth.make_batch(lens, n_q_heads=24, n_kv_heads=2, seed=9)
+    got, _, _ = _shared_run(sp)
+    assert np.array_equal(got, _batch_out(b))
+
+
+def test_shared_batch_order_does_not_matter():
+    P, lens = 256, [200, 33, 0, 130, 64]
+    sp = synth.make_shared_prefix(P, lens, n_q_heads=8, n_kv_heads=2, seed=12)
+    got, _, _ = _shared_run(sp)
+    perm = [3, 0, 4, 2, 1]
+    spp = synth.SharedPrefix(name="perm", prefix=sp.prefix, branches=[sp.branches[i] for i in perm])
+    gotp, _, _ = _shared_run(spp)
+    off, offp = _offsets(lens), _offsets([lens[i] for i in perm])
+    for jp, i in enumerate(perm):
+        assert np.array_equal(got[off[i]:off[i + 1]], gotp[offp[jp]:offp[jp + 1]])
+
+
+def test_shared_batch_vs_oracle(orc):
+    sp = synth.make_shared_prefix(256, [97, 1, 160, 33], n_q_heads=24, n_kv_heads=2, seed=21, gate_sigma=2.0)
+    got, _, _ = _shared_run(sp)
+    off = _offsets(sp.lens)
+    for i, b in enumerate(sp.branches):
+        rec = parity_record(f"shared prefix 256 branch {i} len {b.rows}", got[off[i]:off[i + 1]],
+                            orc.attention(b, threads=8), b.n_q_heads)
+        say(f"  {rec}")
+        check_parity(rec)
+
+
+def test_shared_batch_workload_sampled(orc):
+    """The measured workload (a 4096-token prefix, 16 branches of 128-512
+    tokens, 24/2): every branch bit for bit against its own window pass, and
+    sampled rows of three branches against the oracle."""
+    sp = synth.config_shared("c8_shared_4096_16x128_512")
+    say(f"shared workload P={sp.P} lens {sp.lens}")
+    got, _, _ = _shared_run(sp)
+    off = _offsets(sp.lens)
+    for i, b in enumerate(sp.branches):
+        assert np.array_equal(got[off[i]:off[i + 1]], gpu_out(b)), f"branch {i}"
+    for i in (0, 7, 15):
+        b = sp.branches[i]
+        rows = sample_rows(b.rows, k=8, seed=i)
+        rec = parity_record(f"c8 branch {i} sampled rows", got[off[i]:off[i + 1]][rows],
+                            oracle_rows(orc, b, rows), b.n_q_heads)
+        say(f"  {rec}")
+        check_parity(rec)
+
+
+# --------------------------------------------------------------------------
 # fp8 (e4m3) K/V cache rows
 # --------------------------------------------------------------------------
 
