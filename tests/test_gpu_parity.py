@@ -1029,6 +1029,30 @@ def test_shared_batch_vs_oracle(orc):
         check_parity(rec)
 
 
+def test_shared_batch_at_the_token_cap(orc):
+    """Branches reaching the library's token cap: a 30720-token prefix and four
+    branches of up to 2048 tokens (positions to 32767), 4/1 heads; every branch
+    bit for bit against its own window pass, sampled rows of the longest
+    against the oracle."""
+    import gated_gqa_causal_amd as ga
+    T = ga.ATTN_MAX_TOKENS
+    P, lens = T - 2048, [2048, 1, 1000, 2047]
+    say(f"shared prefix at the cap: P={P} branches {lens}, 4/1 heads")
+    sp = synth.make_shared_prefix(P, lens, n_q_heads=4, n_kv_heads=1, seed=43)
+    ctx = ga.Context(4, 1, T)
+    got, _, ctx = _shared_run(sp, ctx)
+    off = _offsets(lens)
+    for i, b in enumerate(sp.branches):
+        assert np.array_equal(got[off[i]:off[i + 1]], gpu_out(b, ctx)), f"branch {i} (len {b.rows})"
+    ctx.close()
+    b = sp.branches[0]
+    rows = sample_rows(b.rows, k=12, seed=5)
+    rec = parity_record(f"shared prefix cap {T} branch 0", got[off[0]:off[1]][rows], oracle_rows(orc, b, rows),
+                        b.n_q_heads, rows)
+    say(f"  {rec}")
+    check_parity(rec)
+
+
 def test_shared_batch_workload_sampled(orc):
     """The measured workload (a 4096-token prefix, 16 branches of 128-512
     tokens, 24/2): every branch bit for bit against its own window pass, and
