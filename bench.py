@@ -282,8 +282,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the path shards by KV head or query rows with no exchange, and no multi-GPU run "
-              "is part of this build.", file=sys.stderr, flush=True)
+              "the path would shard by KV head or by query rows with no exchange, but the "
+              "library and this benchmark run on one GPU.", file=sys.stderr, flush=True)
         sys.exit(2)
 
     import numpy as np
