@@ -53,6 +53,7 @@ class _Problem(ctypes.Structure):
         ("n_pos", ctypes.c_int32),
         ("mask", ctypes.c_void_p), ("kp", ctypes.c_void_p),
         ("causal", ctypes.c_int32),
+        ("score_f64", ctypes.c_int32),
     ]
 
 
@@ -60,7 +61,7 @@ def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-ORACLE_ABI = 2      # layout of _Problem; oracle.c's oracle_abi() must agree
+ORACLE_ABI = 3      # layout of _Problem; oracle.c's oracle_abi() must agree
 
 
 class Oracle:
@@ -121,7 +122,7 @@ class Oracle:
                      p.q_base, _ptr(arrs["qg"]), _ptr(arrs["k"]), _ptr(arrs["v"]),
                      _ptr(arrs["wq"]), _ptr(arrs["wk"]), _ptr(arrs["cos"]), _ptr(arrs["sin"]),
                      arrs["cos"].shape[0], _ptr(arrs["mask"]), _ptr(kp),
-                     1 if getattr(p, "causal", True) else 0)
+                     1 if getattr(p, "causal", True) else 0, 0)
         return s, arrs
 
     def prepare_keys(self, p) -> np.ndarray:
@@ -142,8 +143,12 @@ class Oracle:
 
     def attention(self, p, rows: Optional[Sequence[int]] = None, *, kp: Optional[np.ndarray] = None,
                   want_ctx: bool = False, want_wsum: bool = False, want_weights: bool = False,
-                  threads: int = 1):
+                  threads: int = 1, score_f64: bool = False):
         """Gated outputs [n_rows][Hq*D] (bf16 bits) for the listed window rows.
+
+        ``score_f64`` takes the other reading of the score's dot product (summed
+        in double and rounded once to fp32, instead of ascending fp32 sums); the
+        rest of the arithmetic is unchanged.
 
         Returns ``out`` alone, or a dict with ``out`` plus the requested
         intermediates (``ctx``, ``wsum``, ``weights``).  ``threads`` spreads
@@ -159,6 +164,7 @@ class Oracle:
         wsum = np.empty((n, Hq), dtype=np.float32) if want_wsum else None
         wts = np.empty((n, Hq, T), dtype=np.float32) if want_weights else None
         s, keep = self._struct(p, kp=np.ascontiguousarray(kp, dtype=np.uint16))
+        s.score_f64 = 1 if score_f64 else 0
         errors = []
 
         def run(a: int, b: int):

@@ -89,9 +89,10 @@ typedef struct {
     const uint8_t *mask;    /* [T-q_base][T] or NULL                        */
     const bf16_t *kp;       /* prepared keys [Hkv][T][D] from oracle_prepare_keys */
     int32_t causal;         /* 1: causal pass; 0: bidirectional (q_base 0)   */
+    int32_t score_f64;      /* 0: q . k summed in fp32, ascending; 1: summed in double, rounded once to fp32 */
 } oracle_problem;
 
-int oracle_abi(void) { return 2; }   /* 2: oracle_problem.causal */
+int oracle_abi(void) { return 3; }   /* 2: oracle_problem.causal; 3: .score_f64 */
 int oracle_mutation(void) { return ORACLE_MUTATION; }
 
 void oracle_bf16_round(const float *in, bf16_t *out, int64_t n)
@@ -273,9 +274,20 @@ int oracle_attention(const oracle_problem *p, const int32_t *rows, int32_t n_row
                 if (!vis[j])
                     continue;
                 const bf16_t *kr = p->kp + ((size_t)c * T + j) * D;
+                /* The pages fix the score as the bf16 rounding of the fp32 dot
+                   product but not the order of its sum: by default it runs in
+                   ascending dimension order in fp32; score_f64 sums in double
+                   (each product of two bf16 values is exact) and rounds once. */
                 float dot = 0.0f;
-                for (int32_t d = 0; d < D; ++d)
-                    dot += bf16_to_f32(qr[d]) * bf16_to_f32(kr[d]);
+                if (p->score_f64) {
+                    double acc = 0.0;
+                    for (int32_t d = 0; d < D; ++d)
+                        acc += (double)bf16_to_f32(qr[d]) * (double)bf16_to_f32(kr[d]);
+                    dot = (float)acc;
+                } else {
+                    for (int32_t d = 0; d < D; ++d)
+                        dot += bf16_to_f32(qr[d]) * bf16_to_f32(kr[d]);
+                }
 #if ORACLE_MUTATION == 6
                 sc[j] = rb(dot);                          /* scale dropped */
 #else

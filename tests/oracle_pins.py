@@ -427,4 +427,74 @@ def pin_frozen_regression(o):
     assert np.array_equal(o.attention(p), want), "oracle drifted from its frozen output"
 
 
+# --------------------------------------------------------------------------
+# The other reading of the score's dot product (summed in double)
+# --------------------------------------------------------------------------
+
+def _scores_two_ways(qp, kp, G):
+    """bf16 scores (float64 values) of every (row, head, key) from prepared
+    queries [rows][Hq][D] and keys [Hkv][T][D] (float64 values of bf16): summed
+    in ascending order in float32, and exactly in float64 then rounded once to
+    float32; each then rounded to bf16 by torch's round-to-nearest-even cast."""
+    rows, Hq, D = qp.shape
+    kk = np.repeat(kp, G, axis=0).astype(np.float32)               # [Hq][T][D]
+    q32 = qp.astype(np.float32)
+    serial = np.zeros((rows, Hq, kk.shape[1]), np.float32)
+    for d in range(D):
+        serial = (serial + q32[:, :, d][:, :, None] * kk[None, :, :, d]).astype(np.float32)
+    exact = np.einsum("rhd,htd->rht", qp, kk.astype(np.float64)).astype(np.float32)
+    return torch_bf16(serial.astype(np.float64)), torch_bf16(exact.astype(np.float64))
+
+
+def pin_score_f64_vs_sdpa(o):
+    """The double-summed reading passes the float64 attention pin's bound too."""
+    for n, (T, Hq, Hkv, qb, mb) in enumerate(_GEOMS):
+        p = _problem(T, Hq, Hkv, q_base=qb, seed=100 + n, mask_budget=mb)
+        r = o.attention(p, want_ctx=True, score_f64=True)
+        qp, kp, v = bf(o.prepare_queries(p)), bf(o.prepare_keys(p)), bf(p.v)
+        want = sdpa_f64(qp, kp, v, qb, p.mask)
+        absv = sdpa_f64(qp, kp, np.abs(v), qb, p.mask)
+        smax = score_max_f64(qp, kp, qb, p.mask)
+        got = bf(r["ctx"]).reshape(want.shape)
+        tol = 1.5 * (U * np.abs(want) + U * (1.0 + 2.0 * smax[..., None]) * absv) + 1e-7
+        assert not (np.abs(got - want) > tol).any(), f"score_f64 context vs float64 attention, geometry {n}"
+
+
+def pin_score_readings_agree_unless_a_score_rounds_apart(o):
+    """The two readings give bit-identical row-heads wherever every visible key's
+    bf16 score is the same both ways (scores recomputed here in numpy), and
+    differ only in row-heads holding a key whose two scores differ."""
+    for n, (T, Hq, Hkv, qb, mb) in enumerate(_GEOMS + [(300, 8, 2, 0, None), (200, 16, 1, 64, None)]):
+        p = _problem(T, Hq, Hkv, q_base=qb, seed=300 + n, mask_budget=mb)
+        a = o.attention(p).reshape(p.rows, Hq, -1)
+        b = o.attention(p, score_f64=True).reshape(p.rows, Hq, -1)
+        qp, kp = bf(o.prepare_queries(p)), bf(o.prepare_keys(p))
+        s0, s1 = _scores_two_ways(qp, kp, Hq // Hkv)
+        vis = np.arange(T)[None, :] <= (qb + np.arange(p.rows))[:, None]
+        if p.mask is not None:
+            vis &= np.asarray(p.mask) != 0
+        apart = ((s0 != s1) & vis[:, None, :]).any(axis=-1)             # [rows][Hq]
+        same = (a == b).all(axis=-1)
+        assert same[~apart].all(), f"geometry {n}: the readings differ where every score agrees"
+
+
+def pin_score_f64_rounds_a_near_tie_up(o):
+    """A case found by a parity sweep (a 1280-token prefix, a 267-token branch,
+    48/6 heads): row 202, head 3's heaviest key (weight 0.028) has the exact
+    dot product 69.750007, just above the bf16 tie between 69.5 and 70.  The
+    ascending fp32 sum rounds to 69.5, the double sum to 70: the heaviest key's
+    weight rises by about exp(0.5/16) and the row-head moves."""
+    sp = synth.make_shared_prefix(1280, [45, 236, 195, 267], n_q_heads=48, n_kv_heads=6, seed=518)
+    b = sp.branches[3]
+    row = np.array([202], np.int32)
+    r0 = o.attention(b, rows=row, want_weights=True)
+    r1 = o.attention(b, rows=row, want_weights=True, score_f64=True)
+    w0, w1 = r0["weights"][0, 3], r1["weights"][0, 3]
+    j = int(np.argmax(w0))
+    assert j == 600, j
+    ratio = float(w1[j] / w0[j])
+    assert 1.025 < ratio < 1.04, ratio                                  # exp(1/32) = 1.0317, renormalised
+    assert not np.array_equal(r0["out"].reshape(48, -1)[3], r1["out"].reshape(48, -1)[3])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

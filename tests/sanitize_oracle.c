@@ -59,6 +59,7 @@ static void run_case(int T, int Hq, int Hkv, int q_base, int masked, int causal)
     p.T = T;
     p.q_base = q_base;
     p.causal = causal;
+    p.score_f64 = T & 1;      /* both readings of the score's dot product */
     bf16_t *qg = bf16_buf((size_t)rows * Hq * 2 * D, 2.0f);
     bf16_t *k = bf16_buf((size_t)T * Hkv * D, 2.0f);
     bf16_t *v = bf16_buf((size_t)T * Hkv * D, 2.0f);
@@ -134,7 +135,7 @@ int main(void)
     oracle_norm_rope(x, w, &one, &zero, 256, 0, 1e-6f, o);
     free(x);
     free(w);
-    EXPECT(oracle_abi() == 2 && oracle_mutation() == 0);
+    EXPECT(oracle_abi() == 3 && oracle_mutation() == 0);
     printf("%s (%d failures)\n", failures ? "FAILED" : "oracle checks ok", failures);
     return failures ? 1 : 0;
 }

@@ -39,8 +39,8 @@ def gpu():
     yield
 
 
-from gpu_util import (DevProblem, bits_to_f32, check_parity, debug_fp8_encode, debug_prepare, gpu_out,  # noqa: E402
-                      make_ctx, parity_record, parity_report, run, to_bits)
+from gpu_util import (DevProblem, bits_to_f32, check_parity, check_parity_either_reading, debug_fp8_encode,  # noqa: E402
+                      debug_prepare, gpu_out, make_ctx, parity_record, parity_report, run, to_bits)
 
 _CFG = {}
 
@@ -1027,6 +1027,40 @@ def test_shared_batch_vs_oracle(orc):
                             orc.attention(b, threads=8), b.n_q_heads)
         say(f"  {rec}")
         check_parity(rec)
+
+
+def _random_shared_cases(n=20, seed=77):
+    """Seeded random shared-prefix launches: a prefix of 0..1536 tokens (a
+    multiple of 128), 1..6 branches of 0..300 tokens, a GQA shape with G in 1..16."""
+    rng = np.random.default_rng(seed)
+    shapes = [(24, 2), (16, 4), (8, 8), (32, 2), (6, 1), (12, 3), (40, 5), (2, 2), (48, 6), (16, 1)]
+    cases = []
+    for i in range(n):
+        P = 128 * int(rng.integers(0, 13))
+        lens = [int(x) for x in rng.integers(0, 301, size=int(rng.integers(1, 7)))]
+        Hq, Hkv = shapes[int(rng.integers(len(shapes)))]
+        cases.append((f"s{i:02d}_P{P}_{Hq}x{Hkv}_n{len(lens)}", P, lens, Hq, Hkv, 500 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_shared_cases(), ids=[c[0] for c in _random_shared_cases()])
+def test_shared_batch_random(orc, case):
+    """Every branch of a random launch bit for bit against its own window pass
+    and, every row and head, against the oracle (a row-head over the row-scale
+    bounds may meet them under the other reading of the score's dot product)."""
+    name, P, lens, Hq, Hkv, sd = case
+    say(f"shared prefix random {name}: lens {lens}")
+    sp = synth.make_shared_prefix(P, lens, n_q_heads=Hq, n_kv_heads=Hkv, seed=sd)
+    got, _, _ = _shared_run(sp)
+    off = _offsets(lens)
+    for i, b in enumerate(sp.branches):
+        if b.rows == 0:
+            continue
+        mine = got[off[i]:off[i + 1]]
+        assert np.array_equal(mine, gpu_out(b)), f"branch {i} (len {b.rows}) differs from its window pass"
+        rec = check_parity_either_reading(orc, b, mine, f"shared random {name} branch {i}")
+        if rec["other_reading_row_heads"]:
+            say(f"  {rec}")
 
 
 def test_shared_batch_at_the_token_cap(orc):
