@@ -505,8 +505,17 @@ def main():
         spread = {"median": round(float(np.median(sp)), 5), "p10": round(float(np.percentile(sp, 10)), 5),
                   "p90": round(float(np.percentile(sp, 90)), 5),
                   "from": "a second run of K steps, a timing-only event between consecutive steps"}
-    out_bits = out.view(torch.int16).cpu().numpy().view(np.uint16) if batch is None else None
+    out_bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
     bit_exact = None
+    if batch is not None:
+        # The longest sequence's rows of the timed launch (parity below), and the
+        # bit-exact check: they equal that sequence's own launch.
+        si = batch.seqs.index(p)
+        s0 = int(sum(batch.lens[:si]))
+        out_bits = out_bits[s0:s0 + p.T]
+        alone = ctx.prefill_gated(dev_bf16(p.qg), dev_bf16(p.k), dev_bf16(p.v), wq, wk, cos, sin, stream=stream)
+        torch.cuda.synchronize()
+        bit_exact = {f"sequence_{si}_equals_its_own_launch": bool(torch.equal(alone, out[s0:s0 + p.T]))}
     if shared is not None:
         # The longest branch's rows of the timed launch (parity below), and the
         # bit-exact check: they equal that branch's own prefix window over prefix + branch.
