@@ -294,11 +294,12 @@ ATTN_EXPORT int attn_prefill_gated_batch(attn_ctx *ctx, const attn_inputs *in, i
 
 /*
  * Branches of one shared prefix, packed into one launch (the serving page's
- * shared-prefix batched gated attention; the shared-prefix page runs a prefix
- * once and continues every branch from its state, positions and the causal
- * mask continuing after the prefix).  kv_cache: a caller-owned cache of this
- * context's geometry (attn_kv_cache_bytes) whose positions 0..prefix_len-1
- * earlier attn_prefill_append calls prepared; this call only reads it.
+ * shared-prefix batched gated attention; on the shared-prefix page a common
+ * prefix is computed a single time and each branch then resumes from the state
+ * it left, its tokens placed after the prefix and still causal).  kv_cache: a
+ * caller-owned cache of this context's geometry (attn_kv_cache_bytes) whose
+ * positions 0..prefix_len-1 earlier attn_prefill_append calls prepared; this
+ * call only reads it.
  * branch_lens: host int32 [n_branches], read during the call only.  Rows of
  * qg, k, v and out hold the branches' new tokens back to back, as in
  * attn_prefill_gated_batch.  Branch b's tokens sit at positions prefix_len ..
