@@ -78,3 +78,26 @@ def test_batch_lengths_are_seeded_and_in_range():
     a = synth.batch_lens(64, 128, 2048, 6)
     assert a == synth.batch_lens(64, 128, 2048, 6)
     assert min(a) >= 128 and max(a) <= 2048 and len(set(a)) > 32
+
+
+def test_shared_prefix_branches_share_the_prefix():
+    """Branches of a shared prefix: each is a window over prefix + its own tokens,
+    its keys 0..P-1 the prefix's, its query rows and keys after P drawn as a plain
+    problem of P + len keys would draw them, and every branch shares the prefix's
+    norm weights and table; P = 0 gives the packed batch's sequences."""
+    sp = synth.make_shared_prefix(256, [1, 0, 70], n_q_heads=8, n_kv_heads=2, seed=4)
+    assert sp.P == 256 and sp.lens == [1, 0, 70] and sp.total == 71
+    for i, b in enumerate(sp.branches):
+        assert (b.T, b.q_base, b.rows) == (256 + sp.lens[i], 256, sp.lens[i])
+        assert np.array_equal(b.k[:256], sp.prefix.k) and np.array_equal(b.v[:256], sp.prefix.v)
+        own = synth.make_problem(T=b.T, q_base=256, n_q_heads=8, n_kv_heads=2, seed=4 * 1009 + 1 + i,
+                                 n_pos=256 + 70)
+        assert np.array_equal(b.qg, own.qg) and np.array_equal(b.k[256:], own.k[256:])
+        assert np.array_equal(b.q_norm_w, sp.prefix.q_norm_w) and np.array_equal(b.cos, sp.prefix.cos)
+    assert sp.qg.shape == (71, 8, 2, 256) and sp.k.shape == (71, 2, 256)
+    assert np.array_equal(sp.k[1:], sp.branches[2].k[256:])
+    b0 = synth.make_batch([5, 3], n_q_heads=8, n_kv_heads=2, seed=9)
+    s0 = synth.make_shared_prefix(0, [5, 3], n_q_heads=8, n_kv_heads=2, seed=9)
+    for a, b in zip(b0.seqs, s0.branches):
+        assert np.array_equal(a.qg, b.qg) and np.array_equal(a.k, b.k) and np.array_equal(a.v, b.v)
+        assert np.array_equal(a.q_norm_w, b.q_norm_w) and np.array_equal(a.cos, b.cos)
